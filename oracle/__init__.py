@@ -1,0 +1,7 @@
+"""Float64 CPU oracle for the fused linear cross-entropy head.
+
+Test infrastructure only: imported by tests/, the smoke check and the
+benchmark's CPU-baseline leg, never by the product library.
+"""
+from .flce_oracle import (flce_reference, flce_bruteforce, flce_rows, validity,  # noqa: F401
+                          count_valid, scale_factor, loss_only)

@@ -1,0 +1,246 @@
+"""Float64 CPU oracle for the fused linear cross-entropy head.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only tests, the smoke check and the benchmark's CPU
+baseline leg do.  It shares no code with the HIP library.
+
+What it computes, written out plainly from the pages (sources cited per
+function by page title and section):
+
+  z_tv   = sum_h X_th W_vh                       (logits = X @ W^T)
+  m_t    = max_v z_tv
+  lse_t  = m_t + ln sum_v exp(z_tv - m_t)        (stable logsumexp, two passes)
+  valid_t = [y_t != ignore_index]
+  l_t    = valid_t (lse_t - z_{t, y_t})          (NLL of log-softmax)
+  loss   = sum_t l_t / n_valid   (mean)  or  sum_t l_t  (sum)
+  s      = 1 / n_valid           (mean)  or  1          (sum)
+  dZ_tv  = s valid_t (exp(z_tv - lse_t) - [v = y_t])
+  dX     = dZ W,    dW = dZ^T X
+  argmax_t = smallest v with z_tv = m_t
+
+Readings where the pages are silent:
+  * mean with n_valid = 0 returns loss 0 and zero gradients (the literal
+    masked mean would be 0/0);
+  * lse and argmax are reported for every row, ignored or not (they depend
+    only on X and W);
+  * a target outside [0, V) that is not ignore_index is an error here.
+
+All arithmetic is float64 on the exact input values (bf16 or fp32 inputs are
+upcast without rounding).  The token loop processes `chunk` rows at a time so
+that no T x V float64 array is ever held; the chunking does not change the
+mathematics (each row's softmax is independent, dW is a plain sum over rows).
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, Optional
+
+import numpy as np
+
+__all__ = ["flce_reference", "flce_bruteforce", "flce_rows", "validity",
+           "count_valid", "scale_factor"]
+
+
+def validity(y: np.ndarray, ignore_index: int) -> np.ndarray:
+    """valid_t = [y_t != ignore_index].
+
+    Alisa's book of LLMs, Mathy things > Information theory > implementing the
+    loss: tokens equal to the padding index are masked out of the loss.
+    """
+    return np.asarray(y) != ignore_index
+
+
+def count_valid(y: np.ndarray, ignore_index: int) -> int:
+    """n_valid = mask.sum() (same section: the masked mean divides by it)."""
+    return int(validity(y, ignore_index).sum())
+
+
+def scale_factor(n_valid: int, reduction: str) -> float:
+    """Seed of the backward pass for the chosen reduction.
+
+    Alisa's book of LLMs, Backpropagation: backward is seeded with 1 and, for
+    a mean over per-token losses, linearity gives each token a factor
+    1/n.  Reading: n_valid = 0 under mean gives 0 (no NaN).
+    """
+    if reduction == "sum":
+        return 1.0
+    if reduction != "mean":
+        raise ValueError(reduction)
+    return 0.0 if n_valid == 0 else 1.0 / n_valid
+
+
+def _check_targets(y: np.ndarray, V: int, ignore_index: int) -> None:
+    valid = validity(y, ignore_index)
+    bad = valid & ((y < 0) | (y >= V))
+    if bad.any():
+        raise ValueError(f"{int(bad.sum())} target(s) outside [0, {V})")
+
+
+def flce_reference(X: np.ndarray, W: np.ndarray, y: np.ndarray,
+                   ignore_index: int = -100, reduction: str = "mean",
+                   chunk: int = 1024, want_grads: bool = True) -> Dict[str, np.ndarray]:
+    """Loss, per-token lse, argmax/top-2 gap, dX and dW in float64.
+
+    Steps, in the pages' order:
+      1. logits z = X W^T -- Alisa's book of LLMs, Neural net basics >
+         Multi-layer perceptrons (PyTorch stores W as (out, in) and the
+         forward multiplies by its transpose); efficient-llm-anatomy,
+         Selected insights > Fused cross-entropy computes backward during
+         forward (the three matmuls per token chunk).
+      2. stable logsumexp, max first and then the shifted sum --
+         Alisa's book of LLMs, Numerical stability and other tricks.
+      3. NLL of log-softmax = z - lse, masked mean --
+         Alisa's book of LLMs, Mathy things > Information theory.
+      4. dZ = softmax - onehot(target), scaled and masked --
+         Alisa's book of LLMs, gradient of softmax + CE loss; Backpropagation
+         (mean seeds each token with 1/n).
+      5. dX = dZ W (per-token activation grad) and dW = dZ^T X (parameter
+         grad, summed over the batch) -- Alisa's book of LLMs, Neural net
+         basics (batch rule for gradients: shared weights contract over the
+         batch) and the efficient-llm-anatomy insight above.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    y = np.asarray(y, dtype=np.int64)
+    T, H = X.shape
+    V, H2 = W.shape
+    if H2 != H or y.shape != (T,):
+        raise ValueError("shape mismatch")
+    _check_targets(y, V, ignore_index)
+    valid = validity(y, ignore_index)
+    n_valid = int(valid.sum())
+    s = scale_factor(n_valid, reduction)
+
+    lse = np.empty(T, dtype=np.float64)
+    zmax = np.empty(T, dtype=np.float64)
+    gap = np.full(T, np.inf, dtype=np.float64)
+    amax = np.empty(T, dtype=np.int64)
+    ztgt = np.zeros(T, dtype=np.float64)
+    nll = np.zeros(T, dtype=np.float64)
+    dX = np.zeros((T, H), dtype=np.float64) if want_grads else None
+    dW = np.zeros((V, H), dtype=np.float64) if want_grads else None
+
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        Xc = X[t0:t1]
+        yc = y[t0:t1]
+        vc = valid[t0:t1]
+        Z = Xc @ W.T                                   # step 1
+        m = Z.max(axis=1)                              # step 2, pass 1
+        E = np.exp(Z - m[:, None])                     # step 2, pass 2
+        l = m + np.log(E.sum(axis=1))
+        lse[t0:t1] = l
+        zmax[t0:t1] = m
+        amax[t0:t1] = Z.argmax(axis=1)                 # first index of the max
+        if V >= 2:
+            top2 = np.partition(Z, V - 2, axis=1)[:, V - 2]
+            gap[t0:t1] = m - top2
+        rows = np.arange(t1 - t0)
+        yv = np.where(vc, yc, 0)
+        zt = np.where(vc, Z[rows, yv], 0.0)
+        ztgt[t0:t1] = zt
+        nll[t0:t1] = np.where(vc, l - zt, 0.0)         # step 3
+        if want_grads:
+            P = np.exp(Z - l[:, None])                 # step 4: softmax
+            P[rows[vc], yc[vc]] -= 1.0                 #          - onehot
+            dZ = P * (s * vc.astype(np.float64))[:, None]
+            dX[t0:t1] = dZ @ W                         # step 5
+            dW += dZ.T @ Xc
+    total = float(nll.sum())
+    loss = total * s if reduction == "mean" else total
+    out = dict(loss=loss, lse=lse, zmax=zmax, argmax=amax, gap=gap,
+               ztarget=ztgt, nll=nll, n_valid=n_valid, scale=s)
+    if want_grads:
+        out.update(dX=dX, dW=dW)
+    return out
+
+
+def flce_rows(X: np.ndarray, W: np.ndarray, y: np.ndarray, rows: Iterable[int],
+              n_valid: int, ignore_index: int = -100, reduction: str = "mean",
+              want_dx: bool = True) -> Dict[str, np.ndarray]:
+    """Per-token outputs for a sample of rows, one row at a time.
+
+    Same definitions as flce_reference, but only for the listed rows; the
+    global n_valid (a count over all targets, see count_valid) is passed in so
+    that the mean's scale matches the full problem.  Used to check outputs of
+    full-size problems whose complete oracle would take minutes.
+    """
+    W64 = None
+    rows = list(rows)
+    V, H = W.shape
+    s = scale_factor(n_valid, reduction)
+    res = dict(rows=np.array(rows, dtype=np.int64), lse=[], zmax=[], argmax=[], gap=[],
+               nll=[], dX=[])
+    for t in rows:
+        x = np.asarray(X[t], dtype=np.float64)
+        # z_v = W_v . x, in row blocks so W is never fully upcast at once
+        z = np.empty(V, dtype=np.float64)
+        for v0 in range(0, V, 16384):
+            z[v0:v0 + 16384] = np.asarray(W[v0:v0 + 16384], dtype=np.float64) @ x
+        m = z.max()
+        l = m + math.log(np.exp(z - m).sum())
+        yt = int(y[t])
+        val = yt != ignore_index
+        if val and not (0 <= yt < V):
+            raise ValueError("target out of range")
+        res["lse"].append(l)
+        res["zmax"].append(m)
+        res["argmax"].append(int(z.argmax()))
+        res["gap"].append(m - np.partition(z, V - 2)[V - 2] if V >= 2 else np.inf)
+        res["nll"].append((l - z[yt]) if val else 0.0)
+        if want_dx:
+            p = np.exp(z - l)
+            if val:
+                p[yt] -= 1.0
+            dz = p * (s if val else 0.0)
+            dx = np.zeros(H, dtype=np.float64)
+            for v0 in range(0, V, 16384):
+                dx += dz[v0:v0 + 16384] @ np.asarray(W[v0:v0 + 16384], dtype=np.float64)
+            res["dX"].append(dx)
+    for k in ("lse", "zmax", "gap", "nll"):
+        res[k] = np.array(res[k], dtype=np.float64)
+    res["argmax"] = np.array(res["argmax"], dtype=np.int64)
+    res["dX"] = np.array(res["dX"], dtype=np.float64) if want_dx else None
+    res["scale"] = s
+    return res
+
+
+def flce_bruteforce(X, W, y, ignore_index: int = -100, reduction: str = "mean") -> Dict[str, object]:
+    """Pure-Python triple loops over the same definitions, for tiny inputs.
+
+    No numpy arithmetic at all: every logit, exponential and product is a
+    Python float operation, so a mistake in the vectorised oracle (a wrong
+    axis, a broadcast, a transposed operand) cannot be shared by this one.
+    """
+    X = [[float(v) for v in row] for row in np.asarray(X)]
+    W = [[float(v) for v in row] for row in np.asarray(W)]
+    y = [int(v) for v in np.asarray(y)]
+    T, V = len(X), len(W)
+    H = len(X[0]) if T else len(W[0])
+    valid = [yt != ignore_index for yt in y]
+    n_valid = sum(valid)
+    s = 1.0 if reduction == "sum" else (0.0 if n_valid == 0 else 1.0 / n_valid)
+    dX = [[0.0] * H for _ in range(T)]
+    dW = [[0.0] * H for _ in range(V)]
+    lse, amax, total = [], [], 0.0
+    for t in range(T):
+        z = [sum(X[t][h] * W[v][h] for h in range(H)) for v in range(V)]
+        m = max(z)
+        l = m + math.log(sum(math.exp(zv - m) for zv in z))
+        lse.append(l)
+        amax.append(z.index(m))
+        if not valid[t]:
+            continue
+        total += l - z[y[t]]
+        for v in range(V):
+            g = s * (math.exp(z[v] - l) - (1.0 if v == y[t] else 0.0))
+            for h in range(H):
+                dX[t][h] += g * W[v][h]
+                dW[v][h] += g * X[t][h]
+    loss = total * s if reduction == "mean" else total
+    return dict(loss=loss, lse=lse, argmax=amax, dX=dX, dW=dW, n_valid=n_valid)
+
+
+def loss_only(X, W, y, ignore_index: int = -100, reduction: str = "mean") -> float:
+    """Scalar loss alone (used by finite-difference checks)."""
+    return flce_reference(X, W, y, ignore_index, reduction, want_grads=False)["loss"]
