@@ -1,0 +1,146 @@
+/*
+ * flce.h -- fused linear cross-entropy head for AMD Instinct MI355X (gfx950).
+ *
+ * One call computes, for hidden states X (T x H), an lm_head weight W (V x H,
+ * nn.Linear layout) and integer targets y:
+ *
+ *   z      = X W^T                          logits, never stored whole
+ *   lse_t  = logsumexp_v z_tv
+ *   loss   = sum_t valid_t (lse_t - z_{t,y_t})  [ / n_valid for the mean ]
+ *   dZ_tv  = s valid_t (softmax(z_t)_v - [v = y_t]),  s = 1/n_valid or 1
+ *   dX     = dZ W          dW = dZ^T X
+ *
+ * Sources: the softmax+CE gradient (p - onehot) from "Alisa's book of LLMs",
+ * section "gradient of softmax + CE loss"; the masked mean with an ignore
+ * (padding) index from its "Information theory > implementing the loss"; the
+ * stable and online logsumexp from its "Numerical stability and other
+ * tricks"; and the fused structure -- per token chunk the three matmuls run
+ * inside the forward, so the gradients are finished when the scalar loss
+ * returns and the T x V logits are never materialised -- from the
+ * efficient-llm-anatomy README, "Selected insights > Fused cross-entropy
+ * computes backward during forward".
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller, row-major and
+ *    contiguous, 16-byte aligned.  The library never frees them.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    All device work is enqueued on it; flce_fwd_bwd never synchronises.
+ *  - Every function returns a status; on an argument error nothing is
+ *    enqueued and no output is touched.
+ *  - A handle is bound to the device that was current at flce_create and
+ *    must be used with that device current.  A handle is not thread-safe and
+ *    calls that share a handle must be ordered (one stream per handle, or
+ *    external synchronisation): the workspace is reused by every call.
+ */
+#ifndef FLCE_H
+#define FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLCE_OK = 0,
+  FLCE_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size or enum   */
+  FLCE_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement */
+  FLCE_ERR_HIP = 3,              /* a HIP runtime call failed                    */
+  FLCE_ERR_OUT_OF_MEMORY = 4,    /* workspace allocation failed                  */
+  FLCE_ERR_BAD_TARGET = 5        /* (flce_query_error) targets outside [0, V)    */
+} flce_status_t;
+
+/* Element type of X, W and dX.  dW, loss and lse are always float32. */
+typedef enum { FLCE_F32 = 0, FLCE_BF16 = 1 } flce_dtype_t;
+
+/* Reduction of the per-token losses.  There is no "none": the fused
+ * backward needs a scalar loss whose gradient seed is 1 ("Alisa's book of
+ * LLMs", Backpropagation: backward starts from a scalar seeded with 1). */
+typedef enum { FLCE_MEAN = 1, FLCE_SUM = 2 } flce_reduction_t;
+
+typedef struct {
+  int64_t hidden;       /* H: > 0, multiple of 8 (bf16) or 4 (fp32)          */
+  int64_t vocab;        /* V: > 0                                              */
+  int32_t dtype;        /* flce_dtype_t                                        */
+  int32_t reserved;     /* must be 0                                           */
+  int64_t chunk_tokens; /* C: tokens per chunk; 0 = default (4096).  Rounded up
+                           to a multiple of 256.  The workspace is O(C*V + V*H)
+                           and does not depend on the number of tokens T.     */
+} flce_config_t;
+
+typedef struct flce_handle* flce_handle_t;
+
+/* Create a handle for fixed (H, V, dtype, C) on the current HIP device and
+ * allocate its workspace.  Returns INVALID_ARGUMENT for a bad config (no
+ * device call is made), OUT_OF_MEMORY / HIP if allocation fails. *out is
+ * set to NULL on failure. */
+flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out);
+
+/* Bytes of device workspace the handle owns (independent of T). */
+size_t flce_workspace_bytes(flce_handle_t h);
+
+/* Tokens per chunk after rounding (C). */
+int64_t flce_chunk_tokens(flce_handle_t h);
+
+/*
+ * Fused forward + backward of the linear cross-entropy head.
+ *
+ *   X        [T x H]  dtype          hidden states (device)
+ *   W        [V x H]  dtype          lm_head weight (device)
+ *   targets  [T]      int64          target ids (device)
+ *   T        >= 0                    number of tokens (T = 0 is valid)
+ *   ignore_index                     tokens whose target equals it are
+ *                                    excluded (it may be a real vocab id)
+ *   reduction                        FLCE_MEAN or FLCE_SUM
+ * Outputs (device, overwritten, never accumulated):
+ *   loss     [1]      float32        the reduced loss (required)
+ *   dX       [T x H]  dtype          gradient wrt X for grad_output = 1 (required)
+ *   dW       [V x H]  float32        gradient wrt W for grad_output = 1 (required)
+ *   lse      [T]      float32        per-token logsumexp (nullable)
+ *   argmax   [T]      int32          per-token argmax of z, lowest index on
+ *                                    ties (nullable)
+ *   n_valid  [1]      int64          number of non-ignored tokens (nullable)
+ *
+ * Mean with n_valid = 0 gives loss 0 and zero gradients.  A target that is
+ * neither ignore_index nor in [0, V) is treated as ignored and counted on
+ * the device; flce_query_error reports it.  dW and dX must not alias X, W or
+ * each other.  Returns without enqueuing anything on an argument error.
+ */
+flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W,
+                           const int64_t* targets, int64_t T, int64_t ignore_index,
+                           int32_t reduction, float* loss, void* dX, float* dW,
+                           float* lse, int32_t* argmax, int64_t* n_valid,
+                           void* stream);
+
+/* Synchronise `stream` and read the number of out-of-range targets seen by
+ * the last flce_fwd_bwd on this handle.  Returns FLCE_ERR_BAD_TARGET when it
+ * is > 0, FLCE_OK otherwise.  bad_targets may be NULL. */
+flce_status_t flce_query_error(flce_handle_t h, void* stream, int64_t* bad_targets);
+
+/* Per-kernel timing with HIP events recorded on the call's stream around
+ * every launch of flce_fwd_bwd while enabled (adds two event records per
+ * launch; off by default).  flce_timing_read synchronises the events and
+ * returns, for kernel class `kind` (0 .. flce_timing_kinds()-1), the summed
+ * duration in milliseconds and the number of launches since the last reset;
+ * flce_timing_enable(h, 1) resets the counters. */
+flce_status_t flce_timing_enable(flce_handle_t h, int32_t enable);
+int32_t flce_timing_kinds(void);
+const char* flce_timing_kind_name(int32_t kind);
+flce_status_t flce_timing_read(flce_handle_t h, int32_t kind, double* total_ms,
+                               int64_t* launches);
+
+/* Free the workspace and the handle (NULL is accepted). */
+flce_status_t flce_destroy(flce_handle_t h);
+
+/* Static, human-readable name of a status code. */
+const char* flce_status_string(flce_status_t s);
+
+/* Text of the last HIP error seen by this library on the calling thread
+ * (empty when none). */
+const char* flce_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLCE_H */

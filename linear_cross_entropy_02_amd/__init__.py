@@ -1,0 +1,245 @@
+"""Python binding of libflce (fused linear cross-entropy head for MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/flce.h.  PyTorch supplies device
+memory and the current stream.  The binding refuses to work without the built
+library -- there is no fallback path.
+
+Entry points mirror the C names (flce_create, flce_fwd_bwd, flce_destroy,
+flce_query_error, flce_workspace_bytes, flce_status_string, timing calls);
+`FusedLinearCrossEntropy` wraps a handle and allocates the outputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflce.so")
+
+FLCE_OK = 0
+FLCE_ERR_INVALID_ARGUMENT = 1
+FLCE_ERR_UNSUPPORTED = 2
+FLCE_ERR_HIP = 3
+FLCE_ERR_OUT_OF_MEMORY = 4
+FLCE_ERR_BAD_TARGET = 5
+
+FLCE_F32 = 0
+FLCE_BF16 = 1
+FLCE_MEAN = 1
+FLCE_SUM = 2
+
+EXPORTED = (
+    "flce_create", "flce_workspace_bytes", "flce_chunk_tokens", "flce_fwd_bwd",
+    "flce_query_error", "flce_timing_enable", "flce_timing_kinds", "flce_timing_kind_name",
+    "flce_timing_read", "flce_destroy", "flce_status_string", "flce_last_error",
+)
+
+
+class flce_config_t(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int64), ("vocab", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("chunk_tokens", ctypes.c_int64)]
+
+
+class FlceError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} {last_error()}".rstrip())
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libflce.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m linear_cross_entropy_02_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i64, i32, st = ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    lib.flce_create.argtypes = [ctypes.POINTER(flce_config_t), ctypes.POINTER(P)]
+    lib.flce_create.restype = st
+    lib.flce_workspace_bytes.argtypes = [P]
+    lib.flce_workspace_bytes.restype = ctypes.c_size_t
+    lib.flce_chunk_tokens.argtypes = [P]
+    lib.flce_chunk_tokens.restype = i64
+    lib.flce_fwd_bwd.argtypes = [P, P, P, P, i64, i64, i32, P, P, P, P, P, P, P]
+    lib.flce_fwd_bwd.restype = st
+    lib.flce_query_error.argtypes = [P, P, ctypes.POINTER(i64)]
+    lib.flce_query_error.restype = st
+    lib.flce_timing_enable.argtypes = [P, i32]
+    lib.flce_timing_enable.restype = st
+    lib.flce_timing_kinds.argtypes = []
+    lib.flce_timing_kinds.restype = i32
+    lib.flce_timing_kind_name.argtypes = [i32]
+    lib.flce_timing_kind_name.restype = ctypes.c_char_p
+    lib.flce_timing_read.argtypes = [P, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    lib.flce_timing_read.restype = st
+    lib.flce_destroy.argtypes = [P]
+    lib.flce_destroy.restype = st
+    lib.flce_status_string.argtypes = [st]
+    lib.flce_status_string.restype = ctypes.c_char_p
+    lib.flce_last_error.argtypes = []
+    lib.flce_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().flce_status_string(status).decode()
+
+
+def last_error() -> str:
+    return load().flce_last_error().decode()
+
+
+# ------------------------------------------------------------ C-name calls ---
+def flce_create(hidden: int, vocab: int, dtype: int, chunk_tokens: int = 0, reserved: int = 0):
+    """Returns (status, handle)."""
+    cfg = flce_config_t(hidden, vocab, dtype, reserved, chunk_tokens)
+    h = ctypes.c_void_p()
+    st = load().flce_create(ctypes.byref(cfg), ctypes.byref(h))
+    return st, h
+
+
+def flce_destroy(handle) -> int:
+    return load().flce_destroy(handle)
+
+
+def flce_workspace_bytes(handle) -> int:
+    return load().flce_workspace_bytes(handle)
+
+
+def flce_chunk_tokens(handle) -> int:
+    return load().flce_chunk_tokens(handle)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def flce_fwd_bwd(handle, X, W, targets, T: int, ignore_index: int, reduction: int,
+                 loss, dX, dW, lse=None, argmax=None, n_valid=None, stream=None) -> int:
+    """Direct call: tensors (or raw device addresses as ints) are passed as
+    pointers; `stream` is a hipStream_t handle (int) or None for torch's
+    current stream."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    return load().flce_fwd_bwd(handle, _ptr(X), _ptr(W), _ptr(targets), T, ignore_index,
+                               reduction, _ptr(loss), _ptr(dX), _ptr(dW), _ptr(lse),
+                               _ptr(argmax), _ptr(n_valid), stream)
+
+
+def flce_query_error(handle, stream=None):
+    """Synchronises the stream; returns (status, bad_targets)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    bad = ctypes.c_int64(0)
+    st = load().flce_query_error(handle, stream, ctypes.byref(bad))
+    return st, bad.value
+
+
+def flce_timing_enable(handle, enable: bool) -> int:
+    return load().flce_timing_enable(handle, 1 if enable else 0)
+
+
+def flce_timing_kinds() -> list:
+    lib = load()
+    return [lib.flce_timing_kind_name(k).decode() for k in range(lib.flce_timing_kinds())]
+
+
+def flce_timing_read(handle, kind: int):
+    """Returns (total_ms, launches) for one kernel class."""
+    ms = ctypes.c_double(0)
+    n = ctypes.c_int64(0)
+    st = load().flce_timing_read(handle, kind, ctypes.byref(ms), ctypes.byref(n))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_timing_read")
+    return ms.value, n.value
+
+
+# ------------------------------------------------------------ torch facade ---
+class FusedLinearCrossEntropy:
+    """A handle for fixed (H, V, dtype, chunk) plus output allocation.
+
+    fwd_bwd(X, W, y) returns a dict of device tensors: loss (float32 scalar),
+    dX (X's dtype), dW (float32), lse (float32 [T]), argmax (int32 [T]) and
+    n_valid (int64 scalar).  Gradients are for a loss gradient seed of 1.
+    """
+
+    def __init__(self, hidden: int, vocab: int, dtype="bf16", chunk_tokens: int = 0):
+        import torch
+        if not torch.cuda.is_available():
+            raise RuntimeError("FusedLinearCrossEntropy needs a HIP device")
+        self.torch_dtype = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+        self.dtype = FLCE_BF16 if dtype == "bf16" else FLCE_F32
+        self.hidden, self.vocab = hidden, vocab
+        st, h = flce_create(hidden, vocab, self.dtype, chunk_tokens)
+        if st != FLCE_OK:
+            raise FlceError(st, "flce_create")
+        self.handle = h
+
+    @property
+    def workspace_bytes(self) -> int:
+        return flce_workspace_bytes(self.handle)
+
+    @property
+    def chunk_tokens(self) -> int:
+        return flce_chunk_tokens(self.handle)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            flce_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc_outputs(self, T: int, device):
+        import torch
+        return dict(
+            loss=torch.empty((), dtype=torch.float32, device=device),
+            dX=torch.empty((T, self.hidden), dtype=self.torch_dtype, device=device),
+            dW=torch.empty((self.vocab, self.hidden), dtype=torch.float32, device=device),
+            lse=torch.empty((T,), dtype=torch.float32, device=device),
+            argmax=torch.empty((T,), dtype=torch.int32, device=device),
+            n_valid=torch.empty((), dtype=torch.int64, device=device),
+        )
+
+    def fwd_bwd(self, X, W, y, ignore_index: int = -100, reduction: str = "mean", out=None):
+        T = X.shape[0] if X is not None else 0
+        self._check(X, W, y, T)
+        if out is None:
+            out = self.alloc_outputs(T, W.device)
+        red = FLCE_MEAN if reduction == "mean" else FLCE_SUM if reduction == "sum" else -1
+        st = flce_fwd_bwd(self.handle, X, W, y, T, ignore_index, red, out["loss"], out["dX"],
+                          out["dW"], out.get("lse"), out.get("argmax"), out.get("n_valid"))
+        if st != FLCE_OK:
+            raise FlceError(st, "flce_fwd_bwd")
+        return out
+
+    def _check(self, X, W, y, T):
+        if W.dtype != self.torch_dtype or tuple(W.shape) != (self.vocab, self.hidden):
+            raise ValueError("W must be [V, H] in the handle's dtype")
+        if not W.is_contiguous():
+            raise ValueError("W must be contiguous")
+        if T:
+            if X.dtype != self.torch_dtype or X.shape[1] != self.hidden or not X.is_contiguous():
+                raise ValueError("X must be a contiguous [T, H] tensor in the handle's dtype")
+            if y.dtype.is_floating_point or y.element_size() != 8 or y.shape != (T,):
+                raise ValueError("targets must be int64 [T]")

@@ -1,0 +1,492 @@
+// C ABI of the fused linear cross-entropy head (see include/flce.h).
+//
+// Host side only: argument validation, the per-handle workspace, the token
+// chunk loop and optional per-kernel event timing.  Every arithmetic step
+// runs in the kernels of kernels.hip.
+#include "../../include/flce.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace flce;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+enum Kind {
+  K_COUNT = 0,
+  K_TRANSPOSE_W,
+  K_TRANSPOSE_X,
+  K_LOGITS,
+  K_FINALIZE,
+  K_FIXUP,
+  K_DX,
+  K_SPLITK,
+  K_DW,
+  K_LOSS,
+  K_ZERO,
+  K_NUM
+};
+const char* kKindNames[K_NUM] = {"count_valid",   "transpose_w", "transpose_x", "logits_gemm",
+                                 "finalize",      "fixup_dz",    "dx_gemm",     "splitk_reduce",
+                                 "dw_gemm",       "loss",        "zero_fill"};
+
+constexpr int64_t kDefaultChunk = 4096;
+
+inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Pending {
+  int kind;
+  hipEvent_t start, stop;
+};
+
+}  // namespace
+
+struct flce_handle {
+  int device = 0;
+  Dt dt = Dt::BF16;
+  int64_t H = 0, V = 0, C = 0, Vpad = 0, nt = 0;
+  int splitk_alloc = 1;  // split-K planes the workspace holds for a full chunk
+  size_t ws_bytes = 0;
+  char* ws = nullptr;
+  void* Wt = nullptr;      // W^T           [H x Vpad]
+  void* P = nullptr;       // exp / dZ      [C x Vpad]
+  void* Pt = nullptr;      // dZ^T          [Vpad x C]
+  void* Xt = nullptr;      // X_c^T         [H x C]
+  float* pm = nullptr;     // tile max / alpha [C x nt]
+  float* ps = nullptr;     // tile sum      [C x nt]
+  int* pa = nullptr;       // tile argmax   [C x nt]
+  float* ztgt = nullptr;   // [C]
+  float* dzt = nullptr;    // [C]
+  double* loss_part = nullptr;  // [C / 4]
+  float* splitk = nullptr;      // [splitk_alloc x C x H]
+  int64_t* nvalid = nullptr;
+  float* scale = nullptr;
+  int64_t* bad = nullptr;
+  // timing
+  bool timing = false;
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> pool;
+  double total_ms[K_NUM] = {};
+  int64_t launches[K_NUM] = {};
+};
+
+namespace {
+
+flce_status_t hip_fail(hipError_t e, const char* what) {
+  char buf[256];
+  snprintf(buf, sizeof buf, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+  g_last_error = buf;
+  return e == hipErrorOutOfMemory ? FLCE_ERR_OUT_OF_MEMORY : FLCE_ERR_HIP;
+}
+
+hipEvent_t take_event(flce_handle* h) {
+  if (!h->pool.empty()) {
+    hipEvent_t e = h->pool.back();
+    h->pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs one launch, bracketed by events when timing is on.
+template <class F>
+hipError_t timed(flce_handle* h, int kind, hipStream_t s, F&& launch) {
+  if (!h->timing) return launch();
+  hipEvent_t a = take_event(h), b = take_event(h);
+  if (!a || !b) return launch();
+  (void)hipEventRecord(a, s);
+  hipError_t e = launch();
+  (void)hipEventRecord(b, s);
+  h->pending.push_back({kind, a, b});
+  return e;
+}
+
+flce_status_t drain_timing(flce_handle* h) {
+  for (auto& p : h->pending) {
+    hipError_t e = hipEventSynchronize(p.stop);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, p.start, p.stop);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    h->total_ms[p.kind] += ms;
+    h->launches[p.kind] += 1;
+    h->pool.push_back(p.start);
+    h->pool.push_back(p.stop);
+  }
+  h->pending.clear();
+  return FLCE_OK;
+}
+
+int elems_per_vec(Dt dt) { return dt == Dt::BF16 ? 8 : 4; }
+size_t elem_size(Dt dt) { return dt == Dt::BF16 ? 2 : 4; }
+
+// Tile shape and split-K factor for an output of M x N with K-depth K.
+void plan_gemm(int64_t M, int64_t N, int64_t K, int max_splits, TileCfg* tc, int* splits) {
+  const int64_t t256 = cdiv64(M, 256) * cdiv64(N, 256);
+  const int64_t t128 = cdiv64(M, 128) * cdiv64(N, 128);
+  *splits = 1;
+  if (t256 >= 240) {
+    *tc = TileCfg::T256;
+    return;
+  }
+  *tc = TileCfg::T128;
+  if (t128 >= 256 || max_splits <= 1) return;
+  int64_t s = cdiv64(512, t128);
+  const int64_t ksteps = cdiv64(K, 64);
+  if (s > ksteps / 4) s = ksteps / 4;
+  if (s > max_splits) s = max_splits;
+  if (s < 1) s = 1;
+  *splits = (int)s;
+}
+
+std::once_flag g_setup_once;
+hipError_t g_setup_err = hipSuccess;
+
+}  // namespace
+
+extern "C" {
+
+const char* flce_status_string(flce_status_t s) {
+  switch (s) {
+    case FLCE_OK: return "FLCE_OK";
+    case FLCE_ERR_INVALID_ARGUMENT: return "FLCE_ERR_INVALID_ARGUMENT";
+    case FLCE_ERR_UNSUPPORTED: return "FLCE_ERR_UNSUPPORTED";
+    case FLCE_ERR_HIP: return "FLCE_ERR_HIP";
+    case FLCE_ERR_OUT_OF_MEMORY: return "FLCE_ERR_OUT_OF_MEMORY";
+    case FLCE_ERR_BAD_TARGET: return "FLCE_ERR_BAD_TARGET";
+  }
+  return "FLCE_ERR_UNKNOWN";
+}
+
+const char* flce_last_error(void) { return g_last_error.c_str(); }
+
+int32_t flce_timing_kinds(void) { return K_NUM; }
+
+const char* flce_timing_kind_name(int32_t kind) {
+  if (kind < 0 || kind >= K_NUM) return "";
+  return kKindNames[kind];
+}
+
+flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out) {
+  if (!out) return FLCE_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  if (!cfg) return FLCE_ERR_INVALID_ARGUMENT;
+  if (cfg->dtype != FLCE_F32 && cfg->dtype != FLCE_BF16) return FLCE_ERR_INVALID_ARGUMENT;
+  if (cfg->reserved != 0) return FLCE_ERR_INVALID_ARGUMENT;
+  const Dt dt = cfg->dtype == FLCE_BF16 ? Dt::BF16 : Dt::F32;
+  const int64_t H = cfg->hidden, V = cfg->vocab;
+  if (H <= 0 || V <= 0) return FLCE_ERR_INVALID_ARGUMENT;
+  if (H % elems_per_vec(dt) != 0) return FLCE_ERR_INVALID_ARGUMENT;
+  if (cfg->chunk_tokens < 0) return FLCE_ERR_INVALID_ARGUMENT;
+  // 32-bit tile indexing inside the kernels
+  if (H > (1 << 20) || V > (int64_t)1 << 30) return FLCE_ERR_UNSUPPORTED;
+  int64_t C = cfg->chunk_tokens ? cfg->chunk_tokens : kDefaultChunk;
+  C = round_up(C, 256);
+  if (C > (1 << 20)) return FLCE_ERR_UNSUPPORTED;
+
+  flce_handle* h = new (std::nothrow) flce_handle();
+  if (!h) return FLCE_ERR_OUT_OF_MEMORY;
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail(e, "hipGetDevice");
+  }
+  std::call_once(g_setup_once, [] { g_setup_err = gemm_setup(); });
+  if (g_setup_err != hipSuccess) {
+    delete h;
+    return hip_fail(g_setup_err, "gemm_setup");
+  }
+  h->dt = dt;
+  h->H = H;
+  h->V = V;
+  h->C = C;
+  h->Vpad = round_up(V, 256);
+  h->nt = cdiv64(V, kPartialWidth);
+  {
+    TileCfg tc;
+    int s;
+    plan_gemm(C, H, round_up(V, 64), 8, &tc, &s);
+    h->splitk_alloc = s;
+  }
+  const size_t es = elem_size(dt);
+  size_t off = 0;
+  auto carve = [&](size_t bytes) {
+    const size_t o = off;
+    off += round_up((int64_t)bytes, 256);
+    return o;
+  };
+  const size_t oWt = carve((size_t)H * h->Vpad * es);
+  const size_t oP = carve((size_t)C * h->Vpad * es);
+  const size_t oPt = carve((size_t)h->Vpad * C * es);
+  const size_t oXt = carve((size_t)H * C * es);
+  const size_t opm = carve((size_t)C * h->nt * 4);
+  const size_t ops = carve((size_t)C * h->nt * 4);
+  const size_t opa = carve((size_t)C * h->nt * 4);
+  const size_t ozt = carve((size_t)C * 4);
+  const size_t odz = carve((size_t)C * 4);
+  const size_t olp = carve((size_t)(C / 4) * 8);
+  const size_t osk = h->splitk_alloc > 1 ? carve((size_t)h->splitk_alloc * C * H * 4) : 0;
+  const size_t osc = carve(64);
+  h->ws_bytes = off;
+  e = hipMalloc((void**)&h->ws, h->ws_bytes);
+  if (e != hipSuccess) {
+    flce_status_t st = hip_fail(e, "hipMalloc(workspace)");
+    delete h;
+    (void)hipGetLastError();
+    return st == FLCE_ERR_HIP ? FLCE_ERR_OUT_OF_MEMORY : st;
+  }
+  h->Wt = h->ws + oWt;
+  h->P = h->ws + oP;
+  h->Pt = h->ws + oPt;
+  h->Xt = h->ws + oXt;
+  h->pm = (float*)(h->ws + opm);
+  h->ps = (float*)(h->ws + ops);
+  h->pa = (int*)(h->ws + opa);
+  h->ztgt = (float*)(h->ws + ozt);
+  h->dzt = (float*)(h->ws + odz);
+  h->loss_part = (double*)(h->ws + olp);
+  h->splitk = h->splitk_alloc > 1 ? (float*)(h->ws + osk) : nullptr;
+  h->nvalid = (int64_t*)(h->ws + osc);
+  h->scale = (float*)(h->ws + osc + 16);
+  h->bad = (int64_t*)(h->ws + osc + 32);
+  e = hipMemset(h->ws + osc, 0, 64);
+  if (e != hipSuccess) {
+    (void)hipFree(h->ws);
+    delete h;
+    return hip_fail(e, "hipMemset");
+  }
+  *out = h;
+  return FLCE_OK;
+}
+
+size_t flce_workspace_bytes(flce_handle_t h) { return h ? h->ws_bytes : 0; }
+
+int64_t flce_chunk_tokens(flce_handle_t h) { return h ? h->C : 0; }
+
+flce_status_t flce_destroy(flce_handle_t h) {
+  if (!h) return FLCE_OK;
+  drain_timing(h);
+  for (hipEvent_t e : h->pool) (void)hipEventDestroy(e);
+  if (h->ws) (void)hipFree(h->ws);
+  delete h;
+  return FLCE_OK;
+}
+
+flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const int64_t* targets,
+                           int64_t T, int64_t ignore_index, int32_t reduction, float* loss,
+                           void* dX, float* dW, float* lse, int32_t* argmax, int64_t* n_valid,
+                           void* stream) {
+  if (!h) return FLCE_ERR_INVALID_ARGUMENT;
+  if (T < 0) return FLCE_ERR_INVALID_ARGUMENT;
+  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!W || !loss || !dW) return FLCE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!X || !targets || !dX)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(W) || !aligned16(dW) || (T > 0 && (!aligned16(X) || !aligned16(dX))))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)loss & 3u) || ((uintptr_t)lse & 3u) || ((uintptr_t)argmax & 3u) ||
+      ((uintptr_t)n_valid & 7u) || ((uintptr_t)targets & 7u))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != h->device) {
+    g_last_error = "flce_fwd_bwd: current device differs from the handle's device";
+    return FLCE_ERR_INVALID_ARGUMENT;
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  const Dt dt = h->dt;
+  const size_t es = elem_size(dt);
+  const int64_t H = h->H, V = h->V, C = h->C, Vpad = h->Vpad, nt = h->nt;
+  const int rsum = reduction == FLCE_SUM ? 1 : 0;
+
+#define FLCE_LAUNCH(kind, expr)                                      \
+  do {                                                               \
+    hipError_t _e = timed(h, kind, s, [&] { return (expr); });       \
+    if (_e != hipSuccess) return hip_fail(_e, kKindNames[kind]);     \
+  } while (0)
+
+  FLCE_LAUNCH(K_COUNT, launch_count(targets, T, ignore_index, V, rsum, h->nvalid, h->scale, h->bad,
+                                    n_valid, s));
+  if (T == 0) {
+    FLCE_LAUNCH(K_ZERO, launch_zero(dW, (size_t)V * H * 4, s));
+    FLCE_LAUNCH(K_ZERO, launch_zero(h->loss_part, 8, s));
+    FLCE_LAUNCH(K_LOSS, launch_loss(h->loss_part, 1, h->nvalid, rsum, loss, s));
+    return FLCE_OK;
+  }
+
+  // W^T (zero-padded to Vpad columns): K-contiguous operand of dX = dZ W.
+  FLCE_LAUNCH(K_TRANSPOSE_W,
+              launch_transpose(dt, W, (int)V, (int)H, H, h->Wt, Vpad, (int)Vpad, s));
+
+  const int64_t KV = round_up(V, 64);  // K-depth of the dX GEMM
+  for (int64_t t0 = 0, c = 0; t0 < T; t0 += C, ++c) {
+    const int64_t Cc = (T - t0 < C) ? (T - t0) : C;
+    const int64_t Ck = round_up(Cc, 64);
+    const char* Xc = (const char*)X + (size_t)t0 * H * es;
+    const int64_t* yc = targets + t0;
+
+    FLCE_LAUNCH(K_TRANSPOSE_X,
+                launch_transpose(dt, Xc, (int)Cc, (int)H, H, h->Xt, C, (int)Ck, s));
+
+    LogitsArgs la{};
+    la.X = Xc;
+    la.W = W;
+    la.M = (int)Cc;
+    la.V = (int)V;
+    la.H = (int)H;
+    la.P = h->P;
+    la.ldp = Vpad;
+    la.pm = h->pm;
+    la.ps = h->ps;
+    la.pa = h->pa;
+    la.nt = (int)nt;
+    la.ztgt = h->ztgt;
+    la.y = yc;
+    la.ignore_index = ignore_index;
+    FLCE_LAUNCH(K_LOGITS, launch_logits(dt, la, s));
+
+    FinalizeArgs fa{};
+    fa.M = (int)Cc;
+    fa.nt = (int)nt;
+    fa.V = (int)V;
+    fa.pm = h->pm;
+    fa.ps = h->ps;
+    fa.pa = h->pa;
+    fa.ztgt = h->ztgt;
+    fa.dzt = h->dzt;
+    fa.y = yc;
+    fa.ignore_index = ignore_index;
+    fa.scale = h->scale;
+    fa.lse_out = lse ? lse + t0 : nullptr;
+    fa.argmax_out = argmax ? argmax + t0 : nullptr;
+    fa.loss_part = h->loss_part;
+    fa.first_chunk = c == 0;
+    FLCE_LAUNCH(K_FINALIZE, launch_finalize(fa, s));
+
+    FixupArgs xa{};
+    xa.P = h->P;
+    xa.ldp = Vpad;
+    xa.Pt = h->Pt;
+    xa.ldpt = C;
+    xa.M = (int)Cc;
+    xa.rows_out = (int)Ck;
+    xa.V = (int)V;
+    xa.Vpad = (int)Vpad;
+    xa.nt = (int)nt;
+    xa.alpha = h->pm;
+    xa.dzt = h->dzt;
+    xa.y = yc;
+    xa.ignore_index = ignore_index;
+    FLCE_LAUNCH(K_FIXUP, launch_fixup(dt, xa, s));
+
+    // dX_c = dZ W   (M = Cc, N = H, K = vocabulary)
+    {
+      TileCfg tc;
+      int splits;
+      int max_splits = h->splitk_alloc > 1 ? (int)((h->splitk_alloc * C) / Ck) : 1;
+      if (max_splits > 8) max_splits = 8;
+      plan_gemm(Cc, H, KV, max_splits, &tc, &splits);
+      GemmOutArgs ga{};
+      ga.A = h->P;
+      ga.lda = Vpad;
+      ga.B = h->Wt;
+      ga.ldb = Vpad;
+      ga.M = (int)Cc;
+      ga.N = (int)H;
+      ga.K = (int)KV;
+      ga.accumulate = false;
+      char* dXc = (char*)dX + (size_t)t0 * H * es;
+      if (splits == 1) {
+        ga.out = dXc;
+        ga.ldo = H;
+        ga.out_f32 = dt == Dt::F32;
+        ga.splits = 1;
+        ga.split_stride = 0;
+        FLCE_LAUNCH(K_DX, launch_gemm_store(dt, tc, ga, s));
+      } else {
+        ga.out = h->splitk;
+        ga.ldo = H;
+        ga.out_f32 = true;
+        ga.splits = splits;
+        ga.split_stride = Ck * H;
+        FLCE_LAUNCH(K_DX, launch_gemm_store(dt, tc, ga, s));
+        FLCE_LAUNCH(K_SPLITK, launch_splitk_reduce(dt, h->splitk, splits, Ck * H, (int)Cc,
+                                                   (int)H, dXc, H, s));
+      }
+    }
+    // dW (+)= dZ^T X_c   (M = V, N = H, K = Ck); the first chunk stores.
+    {
+      TileCfg tc;
+      int splits;
+      plan_gemm(V, H, Ck, 1, &tc, &splits);
+      GemmOutArgs ga{};
+      ga.A = h->Pt;
+      ga.lda = C;
+      ga.B = h->Xt;
+      ga.ldb = C;
+      ga.M = (int)V;
+      ga.N = (int)H;
+      ga.K = (int)Ck;
+      ga.out = dW;
+      ga.ldo = H;
+      ga.out_f32 = true;
+      ga.accumulate = c > 0;
+      ga.splits = 1;
+      ga.split_stride = 0;
+      FLCE_LAUNCH(K_DW, launch_gemm_store(dt, tc, ga, s));
+    }
+  }
+  const int nparts = (int)cdiv64(T < C ? T : C, 4);
+  FLCE_LAUNCH(K_LOSS, launch_loss(h->loss_part, nparts, h->nvalid, rsum, loss, s));
+#undef FLCE_LAUNCH
+  return FLCE_OK;
+}
+
+flce_status_t flce_query_error(flce_handle_t h, void* stream, int64_t* bad_targets) {
+  if (!h) return FLCE_ERR_INVALID_ARGUMENT;
+  int64_t bad = 0;
+  hipError_t e = hipMemcpyAsync(&bad, h->bad, sizeof bad, hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "flce_query_error");
+  if (bad_targets) *bad_targets = bad;
+  return bad > 0 ? FLCE_ERR_BAD_TARGET : FLCE_OK;
+}
+
+flce_status_t flce_timing_enable(flce_handle_t h, int32_t enable) {
+  if (!h) return FLCE_ERR_INVALID_ARGUMENT;
+  flce_status_t st = drain_timing(h);
+  if (st != FLCE_OK) return st;
+  h->timing = enable != 0;
+  if (h->timing) {
+    for (int k = 0; k < K_NUM; ++k) {
+      h->total_ms[k] = 0.0;
+      h->launches[k] = 0;
+    }
+  }
+  return FLCE_OK;
+}
+
+flce_status_t flce_timing_read(flce_handle_t h, int32_t kind, double* total_ms, int64_t* launches) {
+  if (!h || kind < 0 || kind >= K_NUM) return FLCE_ERR_INVALID_ARGUMENT;
+  flce_status_t st = drain_timing(h);
+  if (st != FLCE_OK) return st;
+  if (total_ms) *total_ms = h->total_ms[kind];
+  if (launches) *launches = h->launches[kind];
+  return FLCE_OK;
+}
+
+}  // extern "C"

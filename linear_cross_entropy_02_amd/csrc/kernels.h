@@ -1,0 +1,94 @@
+// Launch wrappers for the fused linear cross-entropy kernels.  Host code
+// calls only these; every function enqueues on `stream` and returns the
+// hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flce {
+
+enum class Dt { F32 = 0, BF16 = 1 };
+
+// Tile shape of a GEMM launch: 256 x 256 blocks for large problems, 128 x 128
+// when the 256 x 256 grid would leave compute units idle.
+enum class TileCfg { T256 = 0, T128 = 1 };
+
+struct LogitsArgs {
+  const void* X;        // chunk rows, [M x H]
+  const void* W;        // [V x H]
+  int M, V, H;
+  void* P;              // exp(z - m_tile), [M x ldp] in the input dtype
+  int64_t ldp;
+  float* pm;            // partial tile max        [M x nt]
+  float* ps;            // partial tile sum of exp  [M x nt]
+  int* pa;              // partial tile argmax      [M x nt]
+  int nt;               // number of partial tiles per row (= ceil(V / kPartialWidth))
+  float* ztgt;          // logit of the target, [M]
+  const int64_t* y;     // chunk targets, [M]
+  int64_t ignore_index;
+};
+// Width in columns of one online-logsumexp partial (the wave tile width of
+// the 256 x 256 logits GEMM).
+constexpr int kPartialWidth = 128;
+
+hipError_t launch_logits(Dt dt, const LogitsArgs& a, hipStream_t s);
+
+struct GemmOutArgs {
+  const void* A; int64_t lda;
+  const void* B; int64_t ldb;
+  int M, N, K;
+  void* out; int64_t ldo;
+  bool out_f32;           // store fp32 (dW, split-K partials) or the input dtype
+  bool accumulate;        // out += result (fp32 only)
+  int splits;             // split-K factor; partial planes `split_stride` apart
+  int64_t split_stride;
+};
+hipError_t launch_gemm_store(Dt dt, TileCfg tc, const GemmOutArgs& a, hipStream_t s);
+
+hipError_t launch_count(const int64_t* y, int64_t T, int64_t ignore_index, int64_t V,
+                        int reduction_sum, int64_t* n_valid, float* scale, int64_t* bad,
+                        int64_t* n_valid_out, hipStream_t s);
+
+// dst[c][r] = src[r][c] for r < rows, 0 for rows <= r < rows_out; c < cols.
+hipError_t launch_transpose(Dt dt, const void* src, int rows, int cols, int64_t ld_src,
+                            void* dst, int64_t ld_dst, int rows_out, hipStream_t s);
+
+struct FinalizeArgs {
+  int M, nt, V;
+  float* pm; const float* ps; const int* pa;   // pm is overwritten by alpha
+  const float* ztgt;
+  float* dzt;
+  const int64_t* y; int64_t ignore_index;
+  const float* scale;
+  float* lse_out;        // nullable, chunk-relative
+  int32_t* argmax_out;   // nullable, chunk-relative
+  double* loss_part;     // one slot per block
+  int first_chunk;
+};
+hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
+
+struct FixupArgs {
+  void* P; int64_t ldp;          // in: exp(z - m_tile); out: dZ (in place)
+  void* Pt; int64_t ldpt;        // out: dZ^T, [Vpad x ldpt]
+  int M;                         // valid rows
+  int rows_out;                  // rows written to Pt (zero beyond M)
+  int V, Vpad, nt;
+  const float* alpha;            // [M x nt]
+  const float* dzt;              // [M]
+  const int64_t* y; int64_t ignore_index;
+};
+hipError_t launch_fixup(Dt dt, const FixupArgs& a, hipStream_t s);
+
+hipError_t launch_splitk_reduce(Dt dt, const float* part, int splits, int64_t stride, int M,
+                                int N, void* out, int64_t ldo, hipStream_t s);
+
+hipError_t launch_loss(const double* loss_part, int nparts, const int64_t* n_valid,
+                       int reduction_sum, float* loss, hipStream_t s);
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+// Dynamic LDS opt-in for the GEMM kernels (call once per process/device).
+hipError_t gemm_setup();
+
+}  // namespace flce

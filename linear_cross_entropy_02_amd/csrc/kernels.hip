@@ -1,0 +1,573 @@
+// Device kernels of the fused linear cross-entropy head (gfx950).
+//
+// Per token chunk of C rows the host enqueues:
+//   logits GEMM   z = X_c W^T on MFMA, with an epilogue that reduces each row
+//                 over its 128-column wave tile to (max, sum exp(z - max),
+//                 argmax), records the target logit and stores
+//                 exp(z - tile max) -- the online-softmax partials of
+//                 "Alisa's book of LLMs", Numerical stability and other tricks
+//                 (running max with a rescaled denominator);
+//   finalize      merges the partials of every row into lse, argmax and the
+//                 per-token NLL, and turns each tile max into the factor
+//                 alpha = s valid exp(m_tile - lse) that rescales the stored
+//                 exponentials into softmax probabilities;
+//   fixup         forms dZ = s valid (softmax - onehot) ("gradient of
+//                 softmax + CE loss" on the same page) in place and its
+//                 transpose;
+//   dX GEMM       dX_c = dZ W     (K = vocabulary)
+//   dW GEMM       dW  += dZ^T X_c (K = chunk tokens), first chunk stores.
+#include "kernels.h"
+
+#include "common.h"
+#include "gemm.h"
+
+namespace flce {
+
+// ------------------------------------------------------------ epilogues ---
+
+// Logits epilogue: online-logsumexp partials per (row, 128-column wave tile).
+template <typename T>
+struct LogitsEpi {
+  T* P;
+  int64_t ldp;
+  float* pm;
+  float* ps;
+  int* pa;
+  int nt;
+  float* ztgt;
+  const int64_t* y;
+  int64_t ignore_index;
+  int M, V;
+
+  template <int FM, int FN>
+  __device__ __forceinline__ void apply(f4 (&acc)[FM][FN], const EpiCoord& ec) const {
+    const int g = ec.lane >> 4, c = ec.lane & 15;
+    const int ptile = ec.col0 / (FN * 16);
+    const bool tile_live = ec.col0 < V;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = ec.row0 + 16 * i + 4 * g + r;
+        const bool row_ok = row < M;
+        const int64_t yt = row_ok ? y[row] : -1;
+        const bool yv = row_ok && target_valid(yt, ignore_index, V);
+        float mx = kNegInf;
+        int ai = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = ec.col0 + 16 * j + c;
+          const float z = acc[i][j][r];
+          if (col < V && z > mx) {
+            mx = z;
+            ai = col;
+          }
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+          const float om = shfl_xor_f(mx, off);
+          const int oa = shfl_xor_i(ai, off);
+          if (om > mx || (om == mx && oa < ai)) {
+            mx = om;
+            ai = oa;
+          }
+        }
+        const float mb = (mx == kNegInf) ? 0.f : mx * kLog2e;
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = ec.col0 + 16 * j + c;
+          const float z = acc[i][j][r];
+          if (yv && (int64_t)col == yt) ztgt[row] = z;
+          const float e = (col < V) ? __builtin_amdgcn_exp2f(__builtin_fmaf(z, kLog2e, -mb)) : 0.f;
+          sum += e;
+          acc[i][j][r] = e;
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) sum += shfl_xor_f(sum, off);
+        if (c == 0 && row_ok && tile_live) {
+          const int64_t o = (int64_t)row * nt + ptile;
+          pm[o] = mx;
+          ps[o] = sum;
+          pa[o] = ai;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = ec.row0 + 16 * i + 4 * g + r;
+        if (row >= M) continue;
+        T* prow = P + (int64_t)row * ldp;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) prow[ec.col0 + 16 * j + c] = Elem<T>::from_f32(acc[i][j][r]);
+      }
+  }
+};
+
+// Plain store epilogue (dX, dW, split-K partials).
+template <typename TO>
+struct StoreEpi {
+  TO* out;
+  int64_t ldo;
+  int M, N;
+  int64_t split_stride;
+  bool accumulate;
+
+  template <int FM, int FN>
+  __device__ __forceinline__ void apply(f4 (&acc)[FM][FN], const EpiCoord& ec) const {
+    const int g = ec.lane >> 4, c = ec.lane & 15;
+    TO* o = out + (int64_t)ec.split * split_stride;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = ec.row0 + 16 * i + 4 * g + r;
+        if (row >= M) continue;
+        TO* orow = o + (int64_t)row * ldo;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = ec.col0 + 16 * j + c;
+          if (col >= N) continue;
+          float v = acc[i][j][r];
+          if (accumulate) v += Elem<TO>::to_f32(orow[col]);
+          orow[col] = Elem<TO>::from_f32(v);
+        }
+      }
+  }
+};
+
+// ------------------------------------------------------------ launchers ---
+
+static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+template <typename T, int BM, int BN, class Epi>
+static hipError_t run_gemm(const GemmShape& g0, const Epi& epi, hipStream_t s) {
+  using G = TileGeom<BM, BN>;
+  GemmShape g = g0;
+  g.tiles_m = cdiv(g.M, BM);
+  g.tiles_n = cdiv(g.N, BN);
+  if (g.tiles_m == 0 || g.tiles_n == 0) return hipSuccess;
+  if (g.splits < 1) g.splits = 1;
+  if (g.group_m < 1) g.group_m = 1;
+  if (g.group_m > g.tiles_m) g.group_m = g.tiles_m;
+  const int nblk = g.tiles_m * g.tiles_n * g.splits;
+  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, Epi>), dim3(nblk), dim3(G::kThreads), G::kLdsBytes,
+                     s, g, epi);
+  return hipGetLastError();
+}
+
+template <typename T, int BM, int BN, class Epi>
+static hipError_t set_lds_attr() {
+  using G = TileGeom<BM, BN>;
+  return hipFuncSetAttribute((const void*)gemm_nt_kernel<T, BM, BN, Epi>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, G::kLdsBytes);
+}
+
+template <typename T>
+static hipError_t setup_t() {
+  hipError_t e;
+  if ((e = set_lds_attr<T, 256, 256, LogitsEpi<T>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 256, 256, StoreEpi<T>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 256, 256, StoreEpi<float>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 128, 128, StoreEpi<T>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 128, 128, StoreEpi<float>>()) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+hipError_t gemm_setup() {
+  hipError_t e = setup_t<bf16>();
+  if (e != hipSuccess) return e;
+  return setup_t<float>();
+}
+
+template <typename T>
+static hipError_t logits_t(const LogitsArgs& a, hipStream_t s) {
+  GemmShape g{};
+  g.A = a.X;
+  g.B = a.W;
+  g.lda = a.H;
+  g.ldb = a.H;
+  g.M = a.M;
+  g.N = a.V;
+  g.K = a.H;
+  g.splits = 1;
+  g.group_m = 1 << 30;  // all row tiles of the chunk share each W tile
+  LogitsEpi<T> epi;
+  epi.P = (T*)a.P;
+  epi.ldp = a.ldp;
+  epi.pm = a.pm;
+  epi.ps = a.ps;
+  epi.pa = a.pa;
+  epi.nt = a.nt;
+  epi.ztgt = a.ztgt;
+  epi.y = a.y;
+  epi.ignore_index = a.ignore_index;
+  epi.M = a.M;
+  epi.V = a.V;
+  return run_gemm<T, 256, 256>(g, epi, s);
+}
+
+hipError_t launch_logits(Dt dt, const LogitsArgs& a, hipStream_t s) {
+  return dt == Dt::BF16 ? logits_t<bf16>(a, s) : logits_t<float>(a, s);
+}
+
+template <typename T, typename TO>
+static hipError_t store_t2(TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
+  GemmShape g{};
+  g.A = a.A;
+  g.B = a.B;
+  g.lda = a.lda;
+  g.ldb = a.ldb;
+  g.M = a.M;
+  g.N = a.N;
+  g.K = a.K;
+  g.splits = a.splits < 1 ? 1 : a.splits;
+  if (g.splits > 1) {
+    constexpr int BK = 8 * Elem<T>::kVec;
+    const int ksteps = cdiv(a.K, BK);
+    g.k_per_split = cdiv(ksteps, g.splits) * BK;
+  }
+  g.group_m = 4;
+  StoreEpi<TO> epi;
+  epi.out = (TO*)a.out;
+  epi.ldo = a.ldo;
+  epi.M = a.M;
+  epi.N = a.N;
+  epi.split_stride = a.split_stride;
+  epi.accumulate = a.accumulate;
+  if (tc == TileCfg::T256) return run_gemm<T, 256, 256>(g, epi, s);
+  return run_gemm<T, 128, 128>(g, epi, s);
+}
+
+template <typename T>
+static hipError_t store_t(TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
+  return a.out_f32 ? store_t2<T, float>(tc, a, s) : store_t2<T, T>(tc, a, s);
+}
+
+hipError_t launch_gemm_store(Dt dt, TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
+  return dt == Dt::BF16 ? store_t<bf16>(tc, a, s) : store_t<float>(tc, a, s);
+}
+
+// ------------------------------------------------- n_valid and the scale ---
+// n_valid = number of targets that are not the ignore index (the masked
+// mean's denominator, "Information theory > implementing the loss");
+// out-of-range targets are counted separately and treated as ignored.
+__global__ void __launch_bounds__(1024) count_kernel(const int64_t* __restrict__ y, int64_t T,
+                                                     int64_t ignore_index, int64_t V,
+                                                     int reduction_sum, int64_t* n_valid,
+                                                     float* scale, int64_t* bad,
+                                                     int64_t* n_valid_out) {
+  __shared__ long long s_nv[1024], s_nb[1024];
+  long long nv = 0, nb = 0;
+  for (int64_t t = threadIdx.x; t < T; t += 1024) {
+    const int64_t v = y[t];
+    if (v != ignore_index) {
+      if (v >= 0 && v < V)
+        ++nv;
+      else
+        ++nb;
+    }
+  }
+  s_nv[threadIdx.x] = nv;
+  s_nb[threadIdx.x] = nb;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      s_nv[threadIdx.x] += s_nv[threadIdx.x + w];
+      s_nb[threadIdx.x] += s_nb[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const long long n = s_nv[0];
+    *n_valid = n;
+    *bad = s_nb[0];
+    // backward seed: 1 for the sum, 1/n for the mean (0 when n = 0)
+    *scale = reduction_sum ? 1.f : (n > 0 ? 1.f / (float)n : 0.f);
+    if (n_valid_out) *n_valid_out = n;
+  }
+}
+
+hipError_t launch_count(const int64_t* y, int64_t T, int64_t ignore_index, int64_t V,
+                        int reduction_sum, int64_t* n_valid, float* scale, int64_t* bad,
+                        int64_t* n_valid_out, hipStream_t s) {
+  hipLaunchKernelGGL(count_kernel, dim3(1), dim3(1024), 0, s, y, T, ignore_index, V, reduction_sum,
+                     n_valid, scale, bad, n_valid_out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ transpose ---
+// 64 x 64 tiles through LDS, 16-byte global accesses on both sides.
+template <typename T>
+__global__ void __launch_bounds__(256) transpose_kernel(const T* __restrict__ src, int rows, int cols,
+                                                        int64_t ld_src, T* __restrict__ dst,
+                                                        int64_t ld_dst, int rows_out) {
+  constexpr int EPV = Elem<T>::kVec;
+  constexpr int VPR = 64 / EPV;              // vectors per 64-element row
+  constexpr int PER = 64 * VPR / 256;        // vectors per thread
+  __shared__ T tile[64][64 + 2];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int v = tid + 256 * p;
+    const int r = v / VPR, cv = v % VPR;
+    const int gr = r0 + r, gc = c0 + cv * EPV;
+    uint4 val = {0u, 0u, 0u, 0u};
+    if (gr < rows && gc < cols) val = *(const uint4*)(src + (int64_t)gr * ld_src + gc);
+    const T* e = (const T*)&val;
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) tile[r][cv * EPV + k] = e[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int v = tid + 256 * p;
+    const int c = v / VPR, rv = v % VPR;
+    const int gc = c0 + c, gr = r0 + rv * EPV;
+    if (gc >= cols || gr >= rows_out) continue;
+    uint4 val;
+    T* e = (T*)&val;
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) e[k] = tile[rv * EPV + k][c];
+    *(uint4*)(dst + (int64_t)gc * ld_dst + gr) = val;
+  }
+}
+
+hipError_t launch_transpose(Dt dt, const void* src, int rows, int cols, int64_t ld_src, void* dst,
+                            int64_t ld_dst, int rows_out, hipStream_t s) {
+  if (rows_out <= 0 || cols <= 0) return hipSuccess;
+  dim3 grid(cdiv(rows_out, 64), cdiv(cols, 64));
+  if (dt == Dt::BF16)
+    hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)src, rows, cols,
+                       ld_src, (bf16*)dst, ld_dst, rows_out);
+  else
+    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s, (const float*)src, rows,
+                       cols, ld_src, (float*)dst, ld_dst, rows_out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- finalize ---
+// Merge rule for two online-softmax states (m, sum, argmax): the larger max
+// wins and the other sum is rescaled by exp(m_other - m); the rescale factor
+// is 1 when the max does not change.  Empty states (sum == 0) are skipped so
+// that two empty states never form (-inf) - (-inf).
+__device__ __forceinline__ void merge_state(float& m, float& s, int& a, float m2, float s2, int a2) {
+  if (s2 == 0.f) return;
+  if (s == 0.f) {
+    m = m2;
+    s = s2;
+    a = a2;
+    return;
+  }
+  if (m2 > m) {
+    s = s * exp_fast(m - m2) + s2;
+    m = m2;
+    a = a2;
+  } else if (m2 == m) {
+    s += s2;
+    a = min(a, a2);
+  } else {
+    s += s2 * exp_fast(m2 - m);
+  }
+}
+
+// One wave per row.
+__global__ void __launch_bounds__(256) finalize_kernel(FinalizeArgs a) {
+  __shared__ double s_nll[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + wave;
+  double nll = 0.0;
+  if (row < a.M) {
+    const int64_t base = (int64_t)row * a.nt;
+    float m = kNegInf, s = 0.f;
+    int am = 0x7fffffff;
+    for (int j = lane; j < a.nt; j += 64) merge_state(m, s, am, a.pm[base + j], a.ps[base + j], a.pa[base + j]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float m2 = shfl_xor_f(m, off);
+      const float s2 = shfl_xor_f(s, off);
+      const int a2 = shfl_xor_i(am, off);
+      merge_state(m, s, am, m2, s2, a2);
+    }
+    const float lse = m + log_fast(s);
+    const int64_t yt = a.y[row];
+    const bool valid = target_valid(yt, a.ignore_index, a.V);
+    const float sc = valid ? *a.scale : 0.f;
+    // alpha_j = s valid exp(m_j - lse): rescales the stored exp(z - m_j)
+    // into s valid softmax(z).
+    for (int j = lane; j < a.nt; j += 64) {
+      const float mj = a.pm[base + j];
+      const float sj = a.ps[base + j];
+      a.pm[base + j] = (sj > 0.f) ? sc * exp_fast(mj - lse) : 0.f;
+    }
+    if (lane == 0) {
+      const float zt = valid ? a.ztgt[row] : 0.f;
+      a.dzt[row] = valid ? sc * (exp_fast(zt - lse) - 1.f) : 0.f;
+      if (a.lse_out) a.lse_out[row] = lse;
+      if (a.argmax_out) a.argmax_out[row] = am;
+      nll = valid ? (double)lse - (double)zt : 0.0;
+    }
+  }
+  if (lane == 0) s_nll[wave] = nll;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double sum = ((s_nll[0] + s_nll[1]) + s_nll[2]) + s_nll[3];
+    a.loss_part[blockIdx.x] = a.first_chunk ? sum : a.loss_part[blockIdx.x] + sum;
+  }
+}
+
+hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {
+  if (a.M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(finalize_kernel, dim3(cdiv(a.M, 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fixup ---
+// dZ = alpha_tile * exp(z - m_tile) except on the target column, where the
+// exact s (p_y - 1) from the fp32 target logit is used; written in place and
+// transposed.  64 x 64 tiles; a 64-column tile never straddles a partial.
+template <typename T>
+__global__ void __launch_bounds__(256) fixup_kernel(FixupArgs a) {
+  constexpr int EPV = Elem<T>::kVec;
+  constexpr int VPR = 64 / EPV;
+  constexpr int PER = 64 * VPR / 256;
+  __shared__ T tile[64][64 + 2];
+  const int v0 = blockIdx.x * 64, t0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  T* P = (T*)a.P;
+  T* Pt = (T*)a.Pt;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int q = tid + 256 * p;
+    const int r = q / VPR, cv = q % VPR;
+    const int t = t0 + r, v = v0 + cv * EPV;
+    float d[EPV];
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) d[k] = 0.f;
+    if (t < a.M) {
+      T* src = P + (int64_t)t * a.ldp + v;
+      uint4 pv = *(const uint4*)src;
+      const T* pe = (const T*)&pv;
+      const float al = (v < a.V) ? a.alpha[(int64_t)t * a.nt + v / kPartialWidth] : 0.f;
+      const int64_t yt = a.y[t];
+      const bool valid = target_valid(yt, a.ignore_index, a.V);
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) d[k] = (v + k < a.V) ? al * Elem<T>::to_f32(pe[k]) : 0.f;
+      if (valid && yt >= v && yt < v + EPV) d[yt - v] = a.dzt[t];
+      uint4 ov;
+      T* oe = (T*)&ov;
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) oe[k] = Elem<T>::from_f32(d[k]);
+      *(uint4*)src = ov;
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) tile[r][cv * EPV + k] = oe[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) tile[r][cv * EPV + k] = Elem<T>::from_f32(0.f);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int q = tid + 256 * p;
+    const int c = q / VPR, rv = q % VPR;
+    const int v = v0 + c, t = t0 + rv * EPV;
+    if (v >= a.Vpad || t >= a.rows_out) continue;
+    uint4 val;
+    T* e = (T*)&val;
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) e[k] = tile[rv * EPV + k][c];
+    *(uint4*)(Pt + (int64_t)v * a.ldpt + t) = val;
+  }
+}
+
+hipError_t launch_fixup(Dt dt, const FixupArgs& a, hipStream_t s) {
+  if (a.rows_out <= 0) return hipSuccess;
+  dim3 grid(cdiv(a.Vpad, 64), cdiv(a.rows_out, 64));
+  if (dt == Dt::BF16)
+    hipLaunchKernelGGL(fixup_kernel<bf16>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(fixup_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------- split-K reduce ---
+template <typename T>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, int splits,
+                                                            int64_t stride, int M, int N,
+                                                            T* __restrict__ out, int64_t ldo) {
+  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const int64_t total = (int64_t)M * N;
+  if (idx >= total) return;
+  const int row = (int)(idx / N), col = (int)(idx % N);  // N % 4 == 0
+  f4 s = *(const f4*)(part + idx);
+  for (int k = 1; k < splits; ++k) s += *(const f4*)(part + (int64_t)k * stride + idx);
+  T* o = out + (int64_t)row * ldo + col;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = Elem<T>::from_f32(s[e]);
+}
+
+hipError_t launch_splitk_reduce(Dt dt, const float* part, int splits, int64_t stride, int M, int N,
+                                void* out, int64_t ldo, hipStream_t s) {
+  const int64_t total = (int64_t)M * N / 4;
+  if (total <= 0) return hipSuccess;
+  dim3 grid(cdiv(total, 256));
+  if (dt == Dt::BF16)
+    hipLaunchKernelGGL(splitk_reduce_kernel<bf16>, grid, dim3(256), 0, s, part, splits, stride, M,
+                       N, (bf16*)out, ldo);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<float>, grid, dim3(256), 0, s, part, splits, stride, M,
+                       N, (float*)out, ldo);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------- loss ---
+// Fixed-order float64 sum of the per-block NLL partials, then the mean's
+// division by n_valid (0 when n_valid = 0).
+__global__ void __launch_bounds__(256) loss_kernel(const double* __restrict__ part, int n,
+                                                   const int64_t* __restrict__ n_valid,
+                                                   int reduction_sum, float* loss) {
+  __shared__ double s[256];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < n; i += 256) acc += part[i];
+  s[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) s[threadIdx.x] += s[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const long long nv = *n_valid;
+    double total = s[0];
+    if (!reduction_sum) total = nv > 0 ? total / (double)nv : 0.0;
+    *loss = (float)total;
+  }
+}
+
+hipError_t launch_loss(const double* loss_part, int nparts, const int64_t* n_valid, int reduction_sum,
+                       float* loss, hipStream_t s) {
+  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(256), 0, s, loss_part, nparts, n_valid,
+                     reduction_sum, loss);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------- zero ---
+__global__ void zero_kernel(uint32_t* p, size_t words) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t words = bytes / 4;
+  if (words == 0) return hipSuccess;
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t*)p, words);
+  return hipGetLastError();
+}
+
+}  // namespace flce

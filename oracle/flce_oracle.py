@@ -157,51 +157,42 @@ def flce_reference(X: np.ndarray, W: np.ndarray, y: np.ndarray,
 
 def flce_rows(X: np.ndarray, W: np.ndarray, y: np.ndarray, rows: Iterable[int],
               n_valid: int, ignore_index: int = -100, reduction: str = "mean",
-              want_dx: bool = True) -> Dict[str, np.ndarray]:
-    """Per-token outputs for a sample of rows, one row at a time.
+              want_dx: bool = True, block: int = 8192) -> Dict[str, np.ndarray]:
+    """Per-token outputs for a sample of rows.
 
-    Same definitions as flce_reference, but only for the listed rows; the
+    Same definitions as flce_reference, restricted to the listed rows; the
     global n_valid (a count over all targets, see count_valid) is passed in so
-    that the mean's scale matches the full problem.  Used to check outputs of
-    full-size problems whose complete oracle would take minutes.
+    that the mean's scale matches the full problem.  W is upcast to float64
+    one block of vocabulary rows at a time, so full-size problems (W of
+    several GB) are checked row-exactly without the complete oracle.
     """
-    W64 = None
-    rows = list(rows)
+    rows = np.array(list(rows), dtype=np.int64)
     V, H = W.shape
     s = scale_factor(n_valid, reduction)
-    res = dict(rows=np.array(rows, dtype=np.int64), lse=[], zmax=[], argmax=[], gap=[],
-               nll=[], dX=[])
-    for t in rows:
-        x = np.asarray(X[t], dtype=np.float64)
-        # z_v = W_v . x, in row blocks so W is never fully upcast at once
-        z = np.empty(V, dtype=np.float64)
-        for v0 in range(0, V, 16384):
-            z[v0:v0 + 16384] = np.asarray(W[v0:v0 + 16384], dtype=np.float64) @ x
-        m = z.max()
-        l = m + math.log(np.exp(z - m).sum())
-        yt = int(y[t])
-        val = yt != ignore_index
-        if val and not (0 <= yt < V):
-            raise ValueError("target out of range")
-        res["lse"].append(l)
-        res["zmax"].append(m)
-        res["argmax"].append(int(z.argmax()))
-        res["gap"].append(m - np.partition(z, V - 2)[V - 2] if V >= 2 else np.inf)
-        res["nll"].append((l - z[yt]) if val else 0.0)
-        if want_dx:
-            p = np.exp(z - l)
-            if val:
-                p[yt] -= 1.0
-            dz = p * (s if val else 0.0)
-            dx = np.zeros(H, dtype=np.float64)
-            for v0 in range(0, V, 16384):
-                dx += dz[v0:v0 + 16384] @ np.asarray(W[v0:v0 + 16384], dtype=np.float64)
-            res["dX"].append(dx)
-    for k in ("lse", "zmax", "gap", "nll"):
-        res[k] = np.array(res[k], dtype=np.float64)
-    res["argmax"] = np.array(res["argmax"], dtype=np.int64)
-    res["dX"] = np.array(res["dX"], dtype=np.float64) if want_dx else None
-    res["scale"] = s
+    Xs = np.asarray(X[rows], dtype=np.float64)
+    ys = np.asarray(y, dtype=np.int64)[rows]
+    valid = validity(ys, ignore_index)
+    if np.any(valid & ((ys < 0) | (ys >= V))):
+        raise ValueError("target out of range")
+    Z = np.empty((len(rows), V), dtype=np.float64)           # logits of the sample
+    for v0 in range(0, V, block):
+        Z[:, v0:v0 + block] = Xs @ np.asarray(W[v0:v0 + block], dtype=np.float64).T
+    m = Z.max(axis=1)
+    lse = m + np.log(np.exp(Z - m[:, None]).sum(axis=1))
+    k = np.arange(len(rows))
+    yv = np.where(valid, ys, 0)
+    nll = np.where(valid, lse - Z[k, yv], 0.0)
+    gap = (m - np.partition(Z, V - 2, axis=1)[:, V - 2]) if V >= 2 else np.full(len(rows), np.inf)
+    res = dict(rows=rows, lse=lse, zmax=m, argmax=Z.argmax(axis=1), gap=gap, nll=nll,
+               ztarget=np.where(valid, Z[k, yv], 0.0), scale=s, dX=None)
+    if want_dx:
+        P = np.exp(Z - lse[:, None])
+        P[k[valid], ys[valid]] -= 1.0
+        dZ = P * (s * valid.astype(np.float64))[:, None]
+        dX = np.zeros((len(rows), H), dtype=np.float64)
+        for v0 in range(0, V, block):
+            dX += dZ[:, v0:v0 + block] @ np.asarray(W[v0:v0 + block], dtype=np.float64)
+        res["dX"] = dX
     return res
 
 

@@ -1,0 +1,89 @@
+"""Comparison helpers for GPU parity tests (GPU outputs vs the float64 oracle).
+
+Tolerances are the ones the method is held to: loss within 1e-3 relative,
+lse within 1e-3 absolute, dX and dW within 2e-2 relative Frobenius error for
+bf16 inputs (1e-5 for fp32), n_valid and the ignore mask exact, argmax exact
+outside an fp32 rounding margin.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+LOSS_RTOL = 1e-3
+LSE_ATOL = 1e-3
+GRAD_RTOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+def rel_frob(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    if nb == 0:
+        return float(np.linalg.norm(a))
+    return float(np.linalg.norm(a - b) / nb)
+
+
+def to_np(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy()
+
+
+def argmax_margin(X: np.ndarray, W: np.ndarray, rows) -> np.ndarray:
+    """delta_t = 8 sqrt(H) 2^-24 ||X_t|| max_v ||W_v||: a bound on the fp32
+    accumulation error of one logit (Cauchy-Schwarz bounds sum_h |X_th W_vh|)."""
+    H = X.shape[1]
+    wmax = 0.0
+    for v0 in range(0, W.shape[0], 16384):
+        blk = np.asarray(W[v0:v0 + 16384], dtype=np.float64)
+        wmax = max(wmax, float(np.sqrt((blk * blk).sum(axis=1)).max()))
+    xn = np.sqrt((np.asarray(X[rows], dtype=np.float64) ** 2).sum(axis=1))
+    return 8.0 * math.sqrt(H) * 2.0 ** -24 * xn * wmax
+
+
+def check_argmax(gpu_idx, ora_idx, ora_zmax, X, W, rows, delta):
+    """Exact where the oracle's max is unambiguous; elsewhere the GPU's index
+    must have a logit within delta of the max.  Returns #ambiguous rows."""
+    gpu_idx = np.asarray(gpu_idx, dtype=np.int64)
+    ora_idx = np.asarray(ora_idx, dtype=np.int64)
+    mism = np.nonzero(gpu_idx != ora_idx)[0]
+    for k in mism:
+        t = rows[k]
+        a = int(gpu_idx[k])
+        assert 0 <= a < W.shape[0], f"row {t}: argmax {a} out of range"
+        z = float(np.dot(np.asarray(X[t], np.float64), np.asarray(W[a], np.float64)))
+        assert ora_zmax[k] - z <= delta[k], (
+            f"row {t}: gpu argmax {a} (z={z}) vs oracle {ora_idx[k]} (max={ora_zmax[k]}), "
+            f"margin {delta[k]}")
+    return len(mism)
+
+
+def check_full(out, ref, inp, wl):
+    """Element-by-element parity of every output against the full oracle."""
+    tol = GRAD_RTOL[wl.dtype]
+    loss = float(out["loss"].item())
+    if ref["loss"] == 0.0:
+        assert loss == 0.0
+    else:
+        assert abs(loss - ref["loss"]) <= LOSS_RTOL * abs(ref["loss"]), (loss, ref["loss"])
+    assert int(out["n_valid"].item()) == ref["n_valid"]
+    T = inp.X.shape[0]
+    if T:
+        lse = to_np(out["lse"])
+        assert np.isfinite(lse).all()
+        assert np.abs(lse - ref["lse"]).max() <= LSE_ATOL, np.abs(lse - ref["lse"]).max()
+        dX = to_np(out["dX"])
+        ign = inp.y == wl.ignore_index
+        assert np.all(dX[ign] == 0.0), "ignored rows of dX must be exactly zero"
+        e = rel_frob(dX, ref["dX"])
+        assert e <= tol, f"dX rel err {e}"
+        rows = np.arange(T)
+        delta = argmax_margin(inp.X, inp.W, rows)
+        check_argmax(to_np(out["argmax"]), ref["argmax"], ref["zmax"], inp.X, inp.W, rows, delta)
+    dW = to_np(out["dW"])
+    assert np.isfinite(dW).all()
+    e = rel_frob(dW, ref["dW"])
+    assert e <= tol, f"dW rel err {e}"

@@ -1,0 +1,89 @@
+"""Host-side checks of the C ABI that need no GPU.
+
+The library must load, export every function include/flce.h declares, and
+reject bad arguments before touching a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_cross_entropy_02_amd as flce
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flce.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flce_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(flce.LIB_PATH):
+        pytest.fail("libflce.so is not built (run __graft_entry__.build())")
+    return flce.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("flce_create", "flce_fwd_bwd", "flce_destroy", "flce_query_error",
+                     "flce_workspace_bytes", "flce_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(flce.EXPORTED) == set(declared_functions())
+
+
+def test_status_strings(lib):
+    for code, name in [(0, "FLCE_OK"), (1, "FLCE_ERR_INVALID_ARGUMENT"), (2, "FLCE_ERR_UNSUPPORTED"),
+                       (3, "FLCE_ERR_HIP"), (4, "FLCE_ERR_OUT_OF_MEMORY"), (5, "FLCE_ERR_BAD_TARGET")]:
+        assert flce.status_string(code) == name
+    assert flce.status_string(99) == "FLCE_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("hidden,vocab,dtype,chunk,reserved", [
+    (0, 100, flce.FLCE_BF16, 0, 0),       # H <= 0
+    (-8, 100, flce.FLCE_BF16, 0, 0),
+    (64, 0, flce.FLCE_BF16, 0, 0),        # V <= 0
+    (12, 100, flce.FLCE_BF16, 0, 0),      # H not a multiple of 8 (bf16)
+    (6, 100, flce.FLCE_F32, 0, 0),        # H not a multiple of 4 (fp32)
+    (64, 100, 7, 0, 0),                   # bad dtype
+    (64, 100, flce.FLCE_BF16, -1, 0),     # negative chunk
+    (64, 100, flce.FLCE_BF16, 0, 1),      # reserved != 0
+])
+def test_create_rejects_bad_config_without_device(lib, hidden, vocab, dtype, chunk, reserved):
+    st, h = flce.flce_create(hidden, vocab, dtype, chunk, reserved)
+    assert st == flce.FLCE_ERR_INVALID_ARGUMENT
+    assert not h.value
+
+
+def test_create_null_arguments(lib):
+    assert lib.flce_create(None, None) == flce.FLCE_ERR_INVALID_ARGUMENT
+    h = ctypes.c_void_p()
+    assert lib.flce_create(None, ctypes.byref(h)) == flce.FLCE_ERR_INVALID_ARGUMENT
+
+
+def test_fwd_bwd_null_handle(lib):
+    st = lib.flce_fwd_bwd(None, 16, 16, 16, 4, -100, flce.FLCE_MEAN, 16, 16, 16, None, None,
+                          None, None)
+    assert st == flce.FLCE_ERR_INVALID_ARGUMENT
+
+
+def test_misc_null_handle_calls(lib):
+    assert lib.flce_destroy(None) == flce.FLCE_OK
+    assert lib.flce_workspace_bytes(None) == 0
+    assert lib.flce_query_error(None, None, None) == flce.FLCE_ERR_INVALID_ARGUMENT
+    assert lib.flce_timing_enable(None, 1) == flce.FLCE_ERR_INVALID_ARGUMENT
+
+
+def test_timing_kinds(lib):
+    kinds = flce.flce_timing_kinds()
+    assert "logits_gemm" in kinds and "dx_gemm" in kinds and "dw_gemm" in kinds
+    assert lib.flce_timing_kind_name(-1) == b""

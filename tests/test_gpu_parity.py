@@ -1,0 +1,190 @@
+"""GPU parity: the HIP path through the C ABI vs the float64 oracle.
+
+Sizes here let the full oracle finish in seconds while spanning several
+GEMM tiles, several token chunks and ragged tails in every dimension.
+"""
+import numpy as np
+import pytest
+
+import linear_cross_entropy_02_amd as flce
+import workloads
+from flce_check import check_full, rel_frob, to_np
+from oracle import flce_reference
+
+pytestmark = pytest.mark.gpu
+
+
+def run(wl, chunk=0, inp=None, out=None, op=None):
+    import torch
+    if inp is None:
+        inp = workloads.generate(wl)
+    X, W, y = workloads.to_torch(inp, "cuda")
+    own = op is None
+    if own:
+        op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=chunk)
+    print(f"[gpu] {wl.name} T={wl.T} H={wl.H} V={wl.V} {wl.dtype} chunk={op.chunk_tokens}",
+          flush=True)
+    res = op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction, out=out)
+    torch.cuda.synchronize()
+    if own:
+        op.close()
+    return inp, res
+
+
+def oracle(inp, wl):
+    return flce_reference(inp.X, inp.W, inp.y, wl.ignore_index, wl.reduction)
+
+
+CASES = [
+    # (workload, chunk)
+    (workloads.WORKLOADS[1], 0),                                            # tiny fp32, full
+    (workloads.WORKLOADS[1].with_shape(T=200, V=777, seed=7), 64),          # fp32 ragged, 4 chunks
+    (workloads.WORKLOADS[2], 0),                                            # page-1 layer shape, full
+    (workloads.WORKLOADS[2].with_shape(T=1000, H=96, V=1000, seed=11), 256),  # ragged T/H/V
+    (workloads.WORKLOADS[2].with_shape(T=777, H=264, V=2049, seed=12), 512),  # H % 64 != 0
+    (workloads.WORKLOADS[4].with_shape(T=600, H=1024, V=20000, seed=13), 256),  # zipf head
+    (workloads.WORKLOADS[5].with_shape(T=700, H=512, V=12345, seed=14), 256),   # outliers, runs, sum
+]
+
+
+@pytest.mark.parametrize("wl,chunk", CASES, ids=[c[0].name for c in CASES])
+def test_parity_vs_oracle(wl, chunk):
+    inp, out = run(wl, chunk)
+    ref = oracle(inp, wl)
+    check_full(out, ref, inp, wl)
+
+
+def test_all_tokens_ignored():
+    wl = workloads.WORKLOADS[2].with_shape(T=300, H=128, V=1000, seed=21)
+    inp = workloads.generate(wl)
+    inp.y[:] = wl.ignore_index
+    inp, out = run(wl, 0, inp=inp)
+    assert float(out["loss"].item()) == 0.0
+    assert int(out["n_valid"].item()) == 0
+    assert np.all(to_np(out["dX"]) == 0.0)
+    assert np.all(to_np(out["dW"]) == 0.0)
+    ref = oracle(inp, wl)
+    assert np.abs(to_np(out["lse"]) - ref["lse"]).max() <= 1e-3
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_none_ignored_and_vocab_ends(reduction):
+    import dataclasses
+    wl = dataclasses.replace(workloads.WORKLOADS[2].with_shape(T=500, H=128, V=3000, seed=22),
+                             ignore_frac=0.0, reduction=reduction)
+    inp = workloads.generate(wl)
+    inp.y[::2] = 0
+    inp.y[1::2] = wl.V - 1
+    inp, out = run(wl, 128, inp=inp)
+    check_full(out, oracle(inp, wl), inp, wl)
+
+
+def test_ignore_index_is_a_real_vocab_id():
+    import dataclasses
+    wl = dataclasses.replace(workloads.WORKLOADS[2].with_shape(T=400, H=64, V=500, seed=23),
+                             ignore_index=7, ignore_frac=0.0)
+    inp = workloads.generate(wl)
+    inp.y[::5] = 7
+    inp, out = run(wl, 0, inp=inp)
+    check_full(out, oracle(inp, wl), inp, wl)
+
+
+def test_empty_batch():
+    import torch
+    wl = workloads.WORKLOADS[2].with_shape(T=0, H=64, V=300, seed=24)
+    op = flce.FusedLinearCrossEntropy(wl.H, wl.V, "bf16")
+    W = torch.randn(wl.V, wl.H, device="cuda").to(torch.bfloat16)
+    out = op.alloc_outputs(0, "cuda")
+    out["dW"].fill_(1.0)
+    st = flce.flce_fwd_bwd(op.handle, None, W, None, 0, -100, flce.FLCE_MEAN, out["loss"], None,
+                           out["dW"], None, None, out["n_valid"])
+    assert st == flce.FLCE_OK
+    torch.cuda.synchronize()
+    assert float(out["loss"].item()) == 0.0
+    assert int(out["n_valid"].item()) == 0
+    assert torch.all(out["dW"] == 0).item()
+    op.close()
+
+
+def test_out_of_range_targets_are_counted_and_ignored():
+    wl = workloads.WORKLOADS[2].with_shape(T=256, H=64, V=400, seed=25)
+    inp = workloads.generate(wl)
+    y_bad = inp.y.copy()
+    y_bad[[3, 50, 51]] = [wl.V, -5, 10 ** 9]
+    inp_bad = workloads.Inputs(wl, inp.X, inp.W, y_bad, inp.x_bits, inp.w_bits)
+    import torch
+    X, W, y = workloads.to_torch(inp_bad, "cuda")
+    op = flce.FusedLinearCrossEntropy(wl.H, wl.V, "bf16")
+    out = op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction)
+    st, bad = flce.flce_query_error(op.handle)
+    assert st == flce.FLCE_ERR_BAD_TARGET and bad == 3
+    y_ref = y_bad.copy()
+    y_ref[[3, 50, 51]] = wl.ignore_index
+    inp_ref = workloads.Inputs(wl, inp.X, inp.W, y_ref, inp.x_bits, inp.w_bits)
+    check_full(out, oracle(inp_ref, wl), inp_ref, wl)
+    # a clean call resets the count
+    out = op.fwd_bwd(*workloads.to_torch(inp, "cuda"), wl.ignore_index, wl.reduction)
+    st, bad = flce.flce_query_error(op.handle)
+    assert st == flce.FLCE_OK and bad == 0
+    op.close()
+
+
+def test_bad_arguments_rejected_without_work():
+    import torch
+    op = flce.FusedLinearCrossEntropy(64, 300, "bf16")
+    X = torch.zeros(10, 64, dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros(300, 64, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(10, dtype=torch.int64, device="cuda")
+    out = op.alloc_outputs(10, "cuda")
+    h = op.handle
+    call = lambda **kw: flce.flce_fwd_bwd(h, kw.get("X", X), kw.get("W", W), kw.get("y", y),
+                                          kw.get("T", 10), -100, kw.get("red", flce.FLCE_MEAN),
+                                          kw.get("loss", out["loss"]), kw.get("dX", out["dX"]),
+                                          kw.get("dW", out["dW"]))
+    E = flce.FLCE_ERR_INVALID_ARGUMENT
+    assert call(T=-1) == E
+    assert call(red=0) == E
+    assert call(red=3) == E
+    assert call(X=0) == E
+    assert call(W=0) == E
+    assert call(y=0) == E
+    assert call(loss=0) == E
+    assert call(dX=0) == E
+    assert call(dW=0) == E
+    assert call(X=X.data_ptr() + 2) == E          # misaligned
+    assert call() == flce.FLCE_OK
+    torch.cuda.synchronize()
+    op.close()
+
+
+def test_deterministic_bitwise():
+    wl = workloads.WORKLOADS[2].with_shape(T=1500, H=256, V=5000, seed=26)
+    inp = workloads.generate(wl)
+    _, a = run(wl, 512, inp=inp)
+    _, b = run(wl, 512, inp=inp)
+    for k in ("loss", "dX", "dW", "lse", "argmax"):
+        assert np.array_equal(to_np(a[k]), to_np(b[k])), k
+
+
+def test_chunk_size_invariance():
+    wl = workloads.WORKLOADS[4].with_shape(T=1100, H=256, V=7000, seed=27)
+    inp = workloads.generate(wl)
+    outs = [run(wl, c, inp=inp)[1] for c in (256, 512, 2048)]
+    ref = oracle(inp, wl)
+    for o in outs:
+        check_full(o, ref, inp, wl)
+    assert rel_frob(to_np(outs[0]["dW"]), to_np(outs[2]["dW"])) < 1e-2
+
+
+def test_workspace_does_not_depend_on_tokens():
+    """The workspace is sized at create time from (H, V, C) only; the part
+    that holds logit-shaped chunk buffers is C x V, below T x V."""
+    op = flce.FusedLinearCrossEntropy(512, 16000, "bf16", chunk_tokens=1024)
+    ws = op.workspace_bytes
+    wl = workloads.WORKLOADS[2]
+    for T in (1024, 4096):
+        inp = workloads.generate(wl.with_shape(T=T))
+        run(wl.with_shape(T=T), inp=inp, op=op)
+        assert op.workspace_bytes == ws
+    assert ws < 4096 * 16000 * 2
+    op.close()
