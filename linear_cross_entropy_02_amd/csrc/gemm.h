@@ -68,9 +68,17 @@ __device__ __forceinline__ TileCoord map_tile(const GemmShape& g) {
 }
 
 template <typename T> __device__ __forceinline__ f4 mma16(uint4 a, uint4 b, f4 c);
+// bf16: in-place accumulate in one AGPR quad.  The tied operand keeps every
+// accumulator in the same registers across the K-loop (the builtin lets the
+// allocator rotate accumulators between iterations, which costs copies).
 template <> __device__ __forceinline__ f4 mma16<bf16>(uint4 a, uint4 b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+#if defined(__HIP_DEVICE_COMPILE__)  // AMDGPU asm; the host pass only parses this
+  typedef int i4v __attribute__((ext_vector_type(4)));
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+               : "+a"(c)
+               : "v"(__builtin_bit_cast(i4v, a)), "v"(__builtin_bit_cast(i4v, b)));
+#endif
+  return c;
 }
 template <> __device__ __forceinline__ f4 mma16<float>(uint4 a, uint4 b, f4 c) {
   c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.x),
@@ -106,12 +114,33 @@ struct EpiCoord {
   int split;
 };
 
+// Buffer resource for raw loads of `bytes` bytes from `base`: an offset at or
+// beyond `bytes` reads zero, which supplies the M/N tails of a tile.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// K-loop schedule (one barrier per 128-byte K-stage, two LDS stages):
+//   barrier    stage kt has landed in LDS and every wave is done reading the
+//              other stage;
+//   LDS reads  all fragments of stage kt (both 32-deep k-substeps);
+//   DMA        stage kt+1 into the other buffer -- issued after the reads, so
+//              no LDS read ever has to wait for a DMA still in flight;
+//   MFMAs      on the fragments, covering the DMA latency.
 template <typename T, int BM, int BN, class Epi>
 __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmShape g, Epi epi) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the launch stub
   using G = TileGeom<BM, BN>;
   constexpr int EPV = Elem<T>::kVec;
   constexpr int BK = 8 * EPV;
-  extern __shared__ uint4 smem[];
+  constexpr int ES = (int)sizeof(T);
+  constexpr int A_INS = BM / 32;  // 16-byte loads per lane per stage (A)
+  constexpr int B_INS = BN / 32;
+  constexpr int FM = G::FM, FN = G::FN;
+  extern __shared__ uint4 lds[];  // 2 * kStageVecs, sized at launch
 
   const TileCoord tc = map_tile(g);
   const int tid = threadIdx.x;
@@ -126,79 +155,117 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmShape g, Epi epi) {
   }
   const int nk = (k_end - k_begin + BK - 1) / BK;
 
-  const T* __restrict__ Ablk = (const T*)g.A + (int64_t)m0 * g.lda;
-  const T* __restrict__ Bblk = (const T*)g.B + (int64_t)n0 * g.ldb;
-  const int lrow = tid >> 3, lkv = tid & 7;
   const int a_rows = min(BM, g.M - m0), b_rows = min(BN, g.N - n0);
+  const __amdgpu_buffer_rsrc_t rA =
+      make_rsrc((const T*)g.A + (int64_t)m0 * g.lda, (uint32_t)((int64_t)a_rows * g.lda * ES));
+  const __amdgpu_buffer_rsrc_t rB =
+      make_rsrc((const T*)g.B + (int64_t)n0 * g.ldb, (uint32_t)((int64_t)b_rows * g.ldb * ES));
 
-  f4 acc[G::FM][G::FN];
+  // Direct-to-LDS loads write lane i of a wave's load to the LDS slot
+  // base + 16 i.  Slot p of a stage holds row p / 8 and logical k-vector
+  // (p % 8) ^ (row % 8), i.e. the XOR-swizzled layout read by swz().
+  uint32_t a_off[A_INS], b_off[B_INS];
+  int a_k[A_INS], b_k[B_INS];
 #pragma unroll
-  for (int i = 0; i < G::FM; ++i)
+  for (int j = 0; j < A_INS; ++j) {
+    const int p = wave * (BM * 2) + 64 * j + lane;
+    const int row = p >> 3, kv = (p & 7) ^ (row & 7);
+    a_k[j] = kv * EPV;
+    a_off[j] = (uint32_t)(((int64_t)row * g.lda + kv * EPV) * ES);
+  }
 #pragma unroll
-    for (int j = 0; j < G::FN; ++j) acc[i][j] = (f4){0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < B_INS; ++j) {
+    const int p = wave * (BN * 2) + 64 * j + lane;
+    const int row = p >> 3, kv = (p & 7) ^ (row & 7);
+    b_k[j] = kv * EPV;
+    b_off[j] = (uint32_t)(((int64_t)row * g.ldb + kv * EPV) * ES);
+  }
 
-  uint4 ra[G::kAVec], rb[G::kBVec];
-  const uint4 zero4 = {0u, 0u, 0u, 0u};
+  f4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = (f4){0.f, 0.f, 0.f, 0.f};
 
-  auto gload = [&](int k0) {
-    const int k = k0 + lkv * EPV;
-    const bool kok = k < k_end;
-#pragma unroll
-    for (int i = 0; i < G::kAVec; ++i) {
-      const int r = lrow + 32 * i;
-      ra[i] = (kok && r < a_rows) ? *(const uint4*)(Ablk + (int64_t)r * g.lda + k) : zero4;
-    }
-#pragma unroll
-    for (int i = 0; i < G::kBVec; ++i) {
-      const int r = lrow + 32 * i;
-      rb[i] = (kok && r < b_rows) ? *(const uint4*)(Bblk + (int64_t)r * g.ldb + k) : zero4;
-    }
-  };
-  auto sstore = [&](int stage) {
-    uint4* sa = smem + stage * G::kStageVecs;
-    uint4* sb = sa + BM * 8;
-#pragma unroll
-    for (int i = 0; i < G::kAVec; ++i) sa[swz(lrow + 32 * i, lkv)] = ra[i];
-#pragma unroll
-    for (int i = 0; i < G::kBVec; ++i) sb[swz(lrow + 32 * i, lkv)] = rb[i];
-  };
-  auto compute = [&](int stage) {
-    const uint4* sa = smem + stage * G::kStageVecs;
-    const uint4* sb = sa + BM * 8;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int kv = 4 * s + (lane >> 4);
-      uint4 af[G::FM], bfr[G::FN];
-#pragma unroll
-      for (int i = 0; i < G::FM; ++i) af[i] = sa[swz(wm * G::WM + 16 * i + (lane & 15), kv)];
-#pragma unroll
-      for (int j = 0; j < G::FN; ++j) bfr[j] = sb[swz(wn * G::WN + 16 * j + (lane & 15), kv)];
-#pragma unroll
-      for (int i = 0; i < G::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < G::FN; ++j) acc[i][j] = mma16<T>(af[i], bfr[j], acc[i][j]);
+  // One direct-to-LDS load: index j < A_INS loads A, the rest load B.
+  auto issue_one = [&](uint4* stage, int k0, int j) {
+    const int rem = k_end - k0;
+    if (j < A_INS) {
+      char* sa = (char*)stage + wave * (BM * 2) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(sa + 1024 * j), 16,
+                                               a_k[j] < rem ? a_off[j] : kOobOffset, k0 * ES, 0, 0);
+    } else {
+      const int jb = j - A_INS;
+      char* sb = (char*)stage + BM * 8 * 16 + wave * (BN * 2) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(sb + 1024 * jb), 16,
+                                               b_k[jb] < rem ? b_off[jb] : kOobOffset, k0 * ES, 0,
+                                               0);
     }
   };
+  // Fragment read r of a substep: r < FM reads A fragment r, else B fragment r - FM.
+  auto read_one = [&](const uint4* stage, int s, int r, uint4 (&fa)[FM], uint4 (&fb)[FN]) {
+    const int kv = 4 * s + (lane >> 4);
+    if (r < FM)
+      fa[r] = stage[swz(wm * G::WM + 16 * r + (lane & 15), kv)];
+    else
+      fb[r - FM] = stage[BM * 8 + swz(wn * G::WN + 16 * (r - FM) + (lane & 15), kv)];
+  };
 
+  // Per K-stage: fragment reads of substep 0; substep-0 MFMAs with the
+  // substep-1 reads and then the next stage's DMA issues threaded through
+  // them (every DMA after every read); substep-1 MFMAs.  The MFMAs are
+  // volatile asm, so this source order is the issue order.
+  constexpr int NR = FM + FN;         // fragment reads per substep
+  constexpr int NM = FM * FN;         // MFMAs per substep
+  constexpr int NDMA = A_INS + B_INS;
+  constexpr int NSIDE = NR + NDMA;
+  constexpr int SP = (NM / NSIDE) > 0 ? (NM / NSIDE) : 1;
+  static_assert(NSIDE * SP <= 2 * NM, "side operations must fit in the MFMA stream");
+
+  uint4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
   if (nk > 0) {
-    gload(k_begin);
-    sstore(0);
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) issue_one(lds, k_begin, j);
     for (int kt = 0; kt < nk; ++kt) {
-      const bool more = kt + 1 < nk;
-      if (more) gload(k_begin + (kt + 1) * BK);
-      compute(kt & 1);
-      if (more) sstore((kt + 1) & 1);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA landed
       __syncthreads();
+      uint4* cur = lds + (kt & 1) * G::kStageVecs;
+      uint4* nxt = lds + ((kt + 1) & 1) * G::kStageVecs;
+      const int knext = k_begin + (kt + 1) * BK;  // past the end: zero fill, unused
+#pragma unroll
+      for (int r = 0; r < NR; ++r) read_one(cur, 0, r, fa0, fb0);
+#pragma unroll
+      for (int q = 0; q < 2 * NM; ++q) {
+        if (q < NM)
+          acc[q / FN][q % FN] = mma16<T>(fa0[q / FN], fb0[q % FN], acc[q / FN][q % FN]);
+        else
+          acc[(q - NM) / FN][(q - NM) % FN] =
+              mma16<T>(fa1[(q - NM) / FN], fb1[(q - NM) % FN], acc[(q - NM) / FN][(q - NM) % FN]);
+        if (q % SP == SP - 1 && q / SP < NSIDE) {
+          const int k = q / SP;
+          if (k < NR)
+            read_one(cur, 1, k, fa1, fb1);
+          else
+            issue_one(nxt, knext, k - NR);
+        }
+      }
     }
   }
+  // The last (unused) DMA may still be in flight; results of the asm MFMAs
+  // are read by ordinary code next, so let the last ones drain (the hazard
+  // recognizer does not see inside asm).
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#endif
 
   EpiCoord ec;
   ec.row0 = m0 + wm * G::WM;
   ec.col0 = n0 + wn * G::WN;
   ec.lane = lane;
   ec.split = tc.split;
-  epi.template apply<G::FM, G::FN>(acc, ec);
+  epi.template apply<FM, FN>(acc, ec);
+#endif
 }
 
 }  // namespace flce

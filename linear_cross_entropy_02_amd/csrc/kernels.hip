@@ -153,11 +153,12 @@ static hipError_t run_gemm(const GemmShape& g0, const Epi& epi, hipStream_t s) {
   if (g.group_m < 1) g.group_m = 1;
   if (g.group_m > g.tiles_m) g.group_m = g.tiles_m;
   const int nblk = g.tiles_m * g.tiles_n * g.splits;
-  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, Epi>), dim3(nblk), dim3(G::kThreads), G::kLdsBytes,
-                     s, g, epi);
+  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, Epi>), dim3(nblk), dim3(G::kThreads),
+                     G::kLdsBytes, s, g, epi);
   return hipGetLastError();
 }
 
+// The GEMM kernels use more than the default 64 KB of dynamic LDS.
 template <typename T, int BM, int BN, class Epi>
 static hipError_t set_lds_attr() {
   using G = TileGeom<BM, BN>;

@@ -87,3 +87,18 @@ def test_timing_kinds(lib):
     kinds = flce.flce_timing_kinds()
     assert "logits_gemm" in kinds and "dx_gemm" in kinds and "dw_gemm" in kinds
     assert lib.flce_timing_kind_name(-1) == b""
+
+
+def test_library_has_no_undefined_internal_symbols(lib):
+    """Every kernel launch stub must be defined in the library itself (a
+    kernel template that fails to instantiate in the host pass leaves an
+    undefined stub that only shows up at load time on the GPU machine)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", flce.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    bad = [l for l in out.splitlines() if "flce" in l]
+    assert not bad, bad
