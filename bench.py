@@ -35,11 +35,28 @@ def parse():
                    help="tokens of the workload the CPU oracle is timed on (0 = skip)")
     p.add_argument("--no-timing", action="store_true",
                    help="time without per-kernel events (no roofline)")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB (3 times), "
+                        "to scale HBM byte counters")
     return p.parse_args()
+
+
+def calibrate_copy(mib: int):
+    import torch
+    n = mib * 2 ** 20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n * 4, "repeats": 3}), flush=True)
 
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)

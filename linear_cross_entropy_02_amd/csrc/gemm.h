@@ -11,8 +11,10 @@
 // a (BM/2) x (BN/2) accumulator tile made of 16 x 16 MFMA fragments.  One
 // K-stage covers 128 bytes per row (64 bf16 or 32 fp32), staged through LDS
 // with a double buffer; rows are stored as eight 16-byte vectors whose
-// positions are XOR-swizzled by the row index so that both the row-wise
-// stores and the fragment reads are free of bank conflicts.
+// positions are XOR-swizzled by the row index so that both the direct-to-LDS
+// writes and the fragment reads are free of bank conflicts.  (Full 128-byte
+// row segments per load matter: a deeper ring of 64-byte stages in the same
+// LDS was measured slower.)
 //
 // MFMA layouts used (16 x 16 output fragments):
 //   bf16:  v_mfma_f32_16x16x32_bf16, lane l holds A[l%16][8 consecutive k]
@@ -92,18 +94,28 @@ template <> __device__ __forceinline__ f4 mma16<float>(uint4 a, uint4 b, f4 c) {
   return c;
 }
 
+// Orders every accumulator after the preceding asm statements (the MFMA
+// drain): each empty asm claims to modify one accumulator.
+template <int FM, int FN>
+__device__ __forceinline__ void drain_fence(f4 (&acc)[FM][FN]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(acc[i][j]));
+#endif
+}
+
 template <int BM, int BN>
 struct TileGeom {
   static constexpr int kThreads = 256;
   static constexpr int WM = BM / 2, WN = BN / 2;  // wave tile
   static constexpr int FM = WM / 16, FN = WN / 16;
-  static constexpr int kAVec = BM * 8 / kThreads;  // 16-B vectors per thread per stage
-  static constexpr int kBVec = BN * 8 / kThreads;
-  static constexpr int kStageVecs = (BM + BN) * 8;
+  static constexpr int kStageVecs = (BM + BN) * 8;  // 16-byte vectors per stage
   static constexpr int kLdsBytes = 2 * kStageVecs * 16;
 };
 
-// Position of vector `kv` (0..7) of LDS row `row`.
+// Position of k-vector `kv` (0..7) of LDS row `row` within a stage.
 __device__ __forceinline__ int swz(int row, int kv) { return row * 8 + (kv ^ (row & 7)); }
 
 // What every epilogue receives: the wave's accumulator fragments and where
@@ -114,22 +126,43 @@ struct EpiCoord {
   int split;
 };
 
-// Buffer resource for raw loads of `bytes` bytes from `base`: an offset at or
-// beyond `bytes` reads zero, which supplies the M/N tails of a tile.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+// Buffer resource (4 SGPRs) for raw loads of `bytes` bytes from `base`: an
+// offset at or beyond `bytes` reads zero, which supplies the M/N tails of a
+// tile.  Word 3 selects 32-bit raw (untyped) access.
+typedef int i4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i4v make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return (i4v){(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), (int)bytes, 0x00020000};
 }
 constexpr uint32_t kOobOffset = 0x80000000u;
 
+// 16 bytes per lane from global memory straight into LDS at
+// lds_addr + 16 * lane (buffer_load_dwordx4 ... lds; M0 holds the LDS base).
+// Issued as asm so the compiler does not treat it as an LDS store it must
+// wait on before unrelated LDS reads; callers wait on vmcnt before the
+// barrier that publishes the stage.
+__device__ __forceinline__ void dma16(i4v rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // One wait state between the M0 write and the LDS DMA that reads it.
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory");
+#endif
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// K-loop schedule (one barrier per 128-byte K-stage, two LDS stages):
-//   barrier    stage kt has landed in LDS and every wave is done reading the
-//              other stage;
-//   LDS reads  all fragments of stage kt (both 32-deep k-substeps);
-//   DMA        stage kt+1 into the other buffer -- issued after the reads, so
-//              no LDS read ever has to wait for a DMA still in flight;
-//   MFMAs      on the fragments, covering the DMA latency.
+// K-loop schedule, one 128-byte K-stage per iteration, two LDS stages:
+//   [A] substep-0 MFMAs on fragments already in registers, with the
+//       substep-1 fragment reads of the same stage threaded through them;
+//   barrier: this wave's reads of the stage are done and the next stage's
+//       DMA has landed (vmcnt), in every wave;
+//   [B] substep-1 MFMAs, with the DMA of the stage after next (into the
+//       buffer just released) and then the next stage's substep-0 fragment
+//       reads threaded through them.
+// The wave never waits on LDS after the barrier: the fragments its MFMAs
+// need were read before it.
 template <typename T, int BM, int BN, class Epi>
 __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmShape g, Epi epi) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the launch stub
@@ -140,11 +173,13 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmShape g, Epi epi) {
   constexpr int A_INS = BM / 32;  // 16-byte loads per lane per stage (A)
   constexpr int B_INS = BN / 32;
   constexpr int FM = G::FM, FN = G::FN;
+  constexpr uint32_t kStageBytes = G::kStageVecs * 16;
   extern __shared__ uint4 lds[];  // 2 * kStageVecs, sized at launch
 
   const TileCoord tc = map_tile(g);
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = tc.tm * BM, n0 = tc.tn * BN;
 
@@ -156,30 +191,31 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmShape g, Epi epi) {
   const int nk = (k_end - k_begin + BK - 1) / BK;
 
   const int a_rows = min(BM, g.M - m0), b_rows = min(BN, g.N - n0);
-  const __amdgpu_buffer_rsrc_t rA =
+  const i4v rA =
       make_rsrc((const T*)g.A + (int64_t)m0 * g.lda, (uint32_t)((int64_t)a_rows * g.lda * ES));
-  const __amdgpu_buffer_rsrc_t rB =
+  const i4v rB =
       make_rsrc((const T*)g.B + (int64_t)n0 * g.ldb, (uint32_t)((int64_t)b_rows * g.ldb * ES));
 
   // Direct-to-LDS loads write lane i of a wave's load to the LDS slot
   // base + 16 i.  Slot p of a stage holds row p / 8 and logical k-vector
-  // (p % 8) ^ (row % 8), i.e. the XOR-swizzled layout read by swz().
+  // (p % 8) ^ (row % 8), i.e. the XOR-swizzled layout read by swz().  Every
+  // load of a wave covers 8 whole rows, so the k-vector of a lane is the
+  // same in all of its loads.
   uint32_t a_off[A_INS], b_off[B_INS];
-  int a_k[A_INS], b_k[B_INS];
+  const int kv_lane = (lane & 7) ^ ((lane >> 3) & 7);
 #pragma unroll
   for (int j = 0; j < A_INS; ++j) {
-    const int p = wave * (BM * 2) + 64 * j + lane;
-    const int row = p >> 3, kv = (p & 7) ^ (row & 7);
-    a_k[j] = kv * EPV;
-    a_off[j] = (uint32_t)(((int64_t)row * g.lda + kv * EPV) * ES);
+    const int row = wave * (BM / 4) + 8 * j + (lane >> 3);
+    a_off[j] = (uint32_t)(((int64_t)row * g.lda + kv_lane * EPV) * ES);
   }
 #pragma unroll
   for (int j = 0; j < B_INS; ++j) {
-    const int p = wave * (BN * 2) + 64 * j + lane;
-    const int row = p >> 3, kv = (p & 7) ^ (row & 7);
-    b_k[j] = kv * EPV;
-    b_off[j] = (uint32_t)(((int64_t)row * g.ldb + kv * EPV) * ES);
+    const int row = wave * (BN / 4) + 8 * j + (lane >> 3);
+    b_off[j] = (uint32_t)(((int64_t)row * g.ldb + kv_lane * EPV) * ES);
   }
+  const uint32_t lds_base = (uint32_t)(size_t)((lds_ptr_t)lds);
+  const uint32_t lds_a = lds_base + wave * (BM * 2) * 16;
+  const uint32_t lds_b = lds_base + BM * 8 * 16 + wave * (BN * 2) * 16;
 
   f4 acc[FM][FN];
 #pragma unroll
@@ -187,23 +223,21 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmShape g, Epi epi) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = (f4){0.f, 0.f, 0.f, 0.f};
 
-  // One direct-to-LDS load: index j < A_INS loads A, the rest load B.
-  auto issue_one = [&](uint4* stage, int k0, int j) {
-    const int rem = k_end - k0;
-    if (j < A_INS) {
-      char* sa = (char*)stage + wave * (BM * 2) * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(sa + 1024 * j), 16,
-                                               a_k[j] < rem ? a_off[j] : kOobOffset, k0 * ES, 0, 0);
-    } else {
-      const int jb = j - A_INS;
-      char* sb = (char*)stage + BM * 8 * 16 + wave * (BN * 2) * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(sb + 1024 * jb), 16,
-                                               b_k[jb] < rem ? b_off[jb] : kOobOffset, k0 * ES, 0,
-                                               0);
-    }
+  // DMA j of stage `st` (0/1) for K-offset k0: j < A_INS loads A, else B.
+  // Past the end of K every offset is out of range and the stage fills
+  // with zeros.
+  auto issue_one = [&](int st, int k0, int j) {
+    const bool kin = kv_lane * EPV < k_end - k0;
+    const uint32_t so = (uint32_t)st * kStageBytes;
+    if (j < A_INS)
+      dma16(rA, lds_a + so + 1024 * j, kin ? a_off[j] : kOobOffset, k0 * ES);
+    else
+      dma16(rB, lds_b + so + 1024 * (j - A_INS), kin ? b_off[j - A_INS] : kOobOffset, k0 * ES);
   };
-  // Fragment read r of a substep: r < FM reads A fragment r, else B fragment r - FM.
-  auto read_one = [&](const uint4* stage, int s, int r, uint4 (&fa)[FM], uint4 (&fb)[FN]) {
+  // Fragment read r of substep s of stage st: r < FM reads A fragment r,
+  // else B fragment r - FM.
+  auto read_one = [&](int st, int s, int r, uint4 (&fa)[FM], uint4 (&fb)[FN]) {
+    const uint4* stage = lds + st * G::kStageVecs;
     const int kv = 4 * s + (lane >> 4);
     if (r < FM)
       fa[r] = stage[swz(wm * G::WM + 16 * r + (lane & 15), kv)];
@@ -211,53 +245,62 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmShape g, Epi epi) {
       fb[r - FM] = stage[BM * 8 + swz(wn * G::WN + 16 * (r - FM) + (lane & 15), kv)];
   };
 
-  // Per K-stage: fragment reads of substep 0; substep-0 MFMAs with the
-  // substep-1 reads and then the next stage's DMA issues threaded through
-  // them (every DMA after every read); substep-1 MFMAs.  The MFMAs are
-  // volatile asm, so this source order is the issue order.
-  constexpr int NR = FM + FN;         // fragment reads per substep
-  constexpr int NM = FM * FN;         // MFMAs per substep
+  constexpr int NR = FM + FN;  // fragment reads per substep
+  constexpr int NM = FM * FN;  // MFMAs per substep
   constexpr int NDMA = A_INS + B_INS;
-  constexpr int NSIDE = NR + NDMA;
-  constexpr int SP = (NM / NSIDE) > 0 ? (NM / NSIDE) : 1;
-  static_assert(NSIDE * SP <= 2 * NM, "side operations must fit in the MFMA stream");
+  constexpr int SPA = NM / NR > 0 ? NM / NR : 1;                    // [A]: reads
+  constexpr int SPB = NM / (NR + NDMA) > 0 ? NM / (NR + NDMA) : 1;  // [B]: DMA + reads
+  static_assert(NR * SPA <= NM && (NR + NDMA) * SPB <= NM, "side operations must fit");
+  static_assert(NDMA < 64, "vmcnt field");
+  // s_waitcnt vmcnt(NDMA), expcnt/lgkmcnt not waited on
+  constexpr int kWaitStage0 = (NDMA & 0xF) | ((NDMA >> 4) << 14) | 0x0F70;
 
   uint4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
   if (nk > 0) {
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) issue_one(lds, k_begin, j);
+    for (int j = 0; j < NDMA; ++j) issue_one(0, k_begin, j);
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) issue_one(1, k_begin + BK, j);
+    __builtin_amdgcn_s_waitcnt(kWaitStage0);  // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_one(0, 0, r, fa0, fb0);
     for (int kt = 0; kt < nk; ++kt) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA landed
-      __syncthreads();
-      uint4* cur = lds + (kt & 1) * G::kStageVecs;
-      uint4* nxt = lds + ((kt + 1) & 1) * G::kStageVecs;
-      const int knext = k_begin + (kt + 1) * BK;  // past the end: zero fill, unused
+      const int cur = kt & 1, nxt = cur ^ 1;
+      // [A]
 #pragma unroll
-      for (int r = 0; r < NR; ++r) read_one(cur, 0, r, fa0, fb0);
+      for (int q = 0; q < NM; ++q) {
+        acc[q / FN][q % FN] = mma16<T>(fa0[q / FN], fb0[q % FN], acc[q / FN][q % FN]);
+        if (q % SPA == SPA - 1 && q / SPA < NR) read_one(cur, 1, q / SPA, fa1, fb1);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      // [B]
+      const int k2 = k_begin + (kt + 2) * BK;  // past the end: zero fill, unused
 #pragma unroll
-      for (int q = 0; q < 2 * NM; ++q) {
-        if (q < NM)
-          acc[q / FN][q % FN] = mma16<T>(fa0[q / FN], fb0[q % FN], acc[q / FN][q % FN]);
-        else
-          acc[(q - NM) / FN][(q - NM) % FN] =
-              mma16<T>(fa1[(q - NM) / FN], fb1[(q - NM) % FN], acc[(q - NM) / FN][(q - NM) % FN]);
-        if (q % SP == SP - 1 && q / SP < NSIDE) {
-          const int k = q / SP;
-          if (k < NR)
-            read_one(cur, 1, k, fa1, fb1);
+      for (int q = 0; q < NM; ++q) {
+        acc[q / FN][q % FN] = mma16<T>(fa1[q / FN], fb1[q % FN], acc[q / FN][q % FN]);
+        // DMAs first (longest lead before the barrier that needs them),
+        // then the fragment reads, B fragments before A fragments: [A]
+        // consumes all B fragments in its first FN MFMAs but A fragment i
+        // only from MFMA i * FN on.
+        if (q % SPB == SPB - 1 && q / SPB < NR + NDMA) {
+          const int k = q / SPB;
+          if (k < NDMA)
+            issue_one(cur, k2, k);
           else
-            issue_one(nxt, knext, k - NR);
+            read_one(nxt, 0, (k - NDMA + FM) % NR, fa0, fb0);
         }
       }
     }
   }
-  // The last (unused) DMA may still be in flight; results of the asm MFMAs
+  // The last (unused) DMAs may still be in flight; results of the asm MFMAs
   // are read by ordinary code next, so let the last ones drain (the hazard
-  // recognizer does not see inside asm).
+  // recognizer does not see inside asm), and tie every accumulator to an
+  // empty asm after the drain so no read of it can be scheduled earlier.
   __builtin_amdgcn_s_waitcnt(0x0F70);
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-#endif
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  drain_fence(acc);
 
   EpiCoord ec;
   ec.row0 = m0 + wm * G::WM;
