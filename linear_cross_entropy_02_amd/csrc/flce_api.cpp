@@ -63,12 +63,12 @@ struct flce_handle {
   void* P = nullptr;       // exp / dZ      [C x Vpad]
   void* Pt = nullptr;      // dZ^T          [Vpad x C]
   void* Xt = nullptr;      // X_c^T         [H x C]
-  float* pm = nullptr;     // tile max / alpha [C x nt]
-  float* ps = nullptr;     // tile sum      [C x nt]
-  int* pa = nullptr;       // tile argmax   [C x nt]
+  float* pm = nullptr;     // tile max / alpha [nt x C], tile-major
+  float* ps = nullptr;     // tile sum      [nt x C]
+  int* pa = nullptr;       // tile argmax   [nt x C]
   float* ztgt = nullptr;   // [C]
   float* dzt = nullptr;    // [C]
-  double* loss_part = nullptr;  // [C / 4]
+  double* loss_part = nullptr;  // [C / 32]
   float* splitk = nullptr;      // [splitk_alloc x C x H]
   int64_t* nvalid = nullptr;
   float* scale = nullptr;
@@ -237,7 +237,7 @@ flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out) {
   const size_t opa = carve((size_t)C * h->nt * 4);
   const size_t ozt = carve((size_t)C * 4);
   const size_t odz = carve((size_t)C * 4);
-  const size_t olp = carve((size_t)(C / 4) * 8);
+  const size_t olp = carve((size_t)(C / 32) * 8);
   const size_t osk = h->splitk_alloc > 1 ? carve((size_t)h->splitk_alloc * C * H * 4) : 0;
   const size_t osc = carve(64);
   h->ws_bytes = off;
@@ -353,7 +353,7 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const 
     la.pm = h->pm;
     la.ps = h->ps;
     la.pa = h->pa;
-    la.nt = (int)nt;
+    la.ldr = C;
     la.ztgt = h->ztgt;
     la.y = yc;
     la.ignore_index = ignore_index;
@@ -366,6 +366,7 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const 
     fa.pm = h->pm;
     fa.ps = h->ps;
     fa.pa = h->pa;
+    fa.ldr = C;
     fa.ztgt = h->ztgt;
     fa.dzt = h->dzt;
     fa.y = yc;
@@ -387,6 +388,7 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const 
     xa.V = (int)V;
     xa.Vpad = (int)Vpad;
     xa.nt = (int)nt;
+    xa.ldr = C;
     xa.alpha = h->pm;
     xa.dzt = h->dzt;
     xa.y = yc;
@@ -450,7 +452,7 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const 
       FLCE_LAUNCH(K_DW, launch_gemm_store(dt, tc, ga, s));
     }
   }
-  const int nparts = (int)cdiv64(T < C ? T : C, 4);
+  const int nparts = (int)cdiv64(T < C ? T : C, 32);  // finalize blocks of the first chunk
   FLCE_LAUNCH(K_LOSS, launch_loss(h->loss_part, nparts, h->nvalid, rsum, loss, s));
 #undef FLCE_LAUNCH
   return FLCE_OK;

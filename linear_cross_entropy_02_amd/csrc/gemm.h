@@ -120,11 +120,50 @@ __device__ __forceinline__ int swz(int row, int kv) { return row * 8 + (kv ^ (ro
 
 // What every epilogue receives: the wave's accumulator fragments and where
 // they sit.  acc[i][j][r] is C[row0 + 16 i + 4 (lane/16) + r][col0 + 16 j + lane%16].
+// `scratch` is this wave's private part of the (then idle) LDS: kLdsBytes / 4
+// bytes.
 struct EpiCoord {
   int row0, col0;  // first row / column of this wave's tile
   int lane;
   int split;
+  float* scratch;
 };
+
+// Writes the wave's (16 FM) x (16 FN) fp32 tile out as 16-byte row segments:
+// 32 rows at a time are transposed through the wave's LDS scratch, then each
+// lane hands `sink(row, col, float4)` four consecutive columns of one row
+// (a wave covers whole rows, 64 lanes x 16 bytes per step), with `row` and
+// `col` relative to the wave tile.  The padded row stride keeps both the
+// 4-byte writes and the 16-byte reads free of bank conflicts.
+template <int FM, int FN, class Sink>
+__device__ __forceinline__ void staged_rows(const f4 (&acc)[FM][FN], int lane, float* scratch,
+                                            Sink&& sink) {
+  constexpr int WN = FN * 16;
+  constexpr int STRIDE = WN + 4;  // floats; 4 * STRIDE = 16 (mod 64) banks
+  constexpr int CH = 2;           // fragment rows (32 tile rows) per pass
+  constexpr int VPR = WN / 4;     // 16-byte vectors per row
+  constexpr int RPI = 64 / VPR;   // rows per wave-wide read
+  constexpr int NRD = 16 * CH / RPI;
+  static_assert(FM % CH == 0 && 64 % VPR == 0, "tile shape");
+  const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int i0 = 0; i0 < FM; i0 += CH) {
+#pragma unroll
+    for (int ii = 0; ii < CH; ++ii)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) scratch[(16 * ii + 4 * g + r) * STRIDE + 16 * j + c] = acc[i0 + ii][j][r];
+    wave_lds_fence();
+#pragma unroll
+    for (int k = 0; k < NRD; ++k) {
+      const int rr = k * RPI + lane / VPR, cv = lane % VPR;
+      const f4 v = *(const f4*)&scratch[rr * STRIDE + 4 * cv];
+      sink(16 * i0 + rr, 4 * cv, v);
+    }
+    wave_lds_fence();
+  }
+}
 
 // Buffer resource (4 SGPRs) for raw loads of `bytes` bytes from `base`: an
 // offset at or beyond `bytes` reads zero, which supplies the M/N tails of a
@@ -143,10 +182,15 @@ constexpr uint32_t kOobOffset = 0x80000000u;
 // barrier that publishes the stage.
 __device__ __forceinline__ void dma16(i4v rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  // One wait state between the M0 write and the LDS DMA that reads it.
+  // The LDS base, descriptor and scalar offset are wave-uniform: keep them
+  // in SGPRs.  One wait state between the M0 write and the LDS DMA that
+  // reads it.
+  const i4v r = {__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
+                 __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(r),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
                : "memory");
 #endif
 }
@@ -302,11 +346,13 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmShape g, Epi epi) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   drain_fence(acc);
 
+  __syncthreads();  // every wave is done with the stages: LDS becomes scratch
   EpiCoord ec;
   ec.row0 = m0 + wm * G::WM;
   ec.col0 = n0 + wn * G::WN;
   ec.lane = lane;
   ec.split = tc.split;
+  ec.scratch = (float*)((char*)lds + wave * (G::kLdsBytes / 4));
   epi.template apply<FM, FN>(acc, ec);
 #endif
 }

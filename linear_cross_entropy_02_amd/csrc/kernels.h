@@ -20,10 +20,10 @@ struct LogitsArgs {
   int M, V, H;
   void* P;              // exp(z - m_tile), [M x ldp] in the input dtype
   int64_t ldp;
-  float* pm;            // partial tile max        [M x nt]
-  float* ps;            // partial tile sum of exp  [M x nt]
-  int* pa;              // partial tile argmax      [M x nt]
-  int nt;               // number of partial tiles per row (= ceil(V / kPartialWidth))
+  float* pm;            // partial tile max         [nt x ldr], tile-major
+  float* ps;            // partial tile sum of exp  [nt x ldr]
+  int* pa;              // partial tile argmax      [nt x ldr]
+  int64_t ldr;          // row stride of the partials (>= M)
   float* ztgt;          // logit of the target, [M]
   const int64_t* y;     // chunk targets, [M]
   int64_t ignore_index;
@@ -56,6 +56,7 @@ hipError_t launch_transpose(Dt dt, const void* src, int rows, int cols, int64_t 
 
 struct FinalizeArgs {
   int M, nt, V;
+  int64_t ldr;           // row stride of the tile-major partials
   float* pm; const float* ps; const int* pa;   // pm is overwritten by alpha
   const float* ztgt;
   float* dzt;
@@ -63,7 +64,7 @@ struct FinalizeArgs {
   const float* scale;
   float* lse_out;        // nullable, chunk-relative
   int32_t* argmax_out;   // nullable, chunk-relative
-  double* loss_part;     // one slot per block
+  double* loss_part;     // one slot per 32 rows
   int first_chunk;
 };
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
@@ -74,7 +75,8 @@ struct FixupArgs {
   int M;                         // valid rows
   int rows_out;                  // rows written to Pt (zero beyond M)
   int V, Vpad, nt;
-  const float* alpha;            // [M x nt]
+  int64_t ldr;
+  const float* alpha;            // [nt x ldr], tile-major
   const float* dzt;              // [M]
   const int64_t* y; int64_t ignore_index;
 };

@@ -25,7 +25,26 @@ namespace flce {
 
 // ------------------------------------------------------------ epilogues ---
 
+// Stores four consecutive values of one row in the output type.
+__device__ __forceinline__ void store4(float* p, f4 v) { *(f4*)p = v; }
+__device__ __forceinline__ void store4(bf16* p, f4 v) {
+  uint2 w;
+  w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f4){v[0], v[1], 0, 0}.xy, bf16x2));
+  w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f4){v[2], v[3], 0, 0}.xy, bf16x2));
+  *(uint2*)p = w;
+}
+__device__ __forceinline__ f4 load4(const float* p) { return *(const f4*)p; }
+__device__ __forceinline__ f4 load4(const bf16* p) {
+  const uint2 w = *(const uint2*)p;
+  return (f4){__builtin_bit_cast(float, w.x << 16), __builtin_bit_cast(float, w.x & 0xffff0000u),
+              __builtin_bit_cast(float, w.y << 16), __builtin_bit_cast(float, w.y & 0xffff0000u)};
+}
+
 // Logits epilogue: online-logsumexp partials per (row, 128-column wave tile).
+// Row reductions run in the MFMA layout (a row's 128 columns sit in 16
+// lanes x 8 fragments) with DPP moves; the partials are written tile-major
+// ([tile][row], 16 consecutive rows per store); exp(z - tile max) goes out
+// through the LDS-staged row store.
 template <typename T>
 struct LogitsEpi {
   T* P;
@@ -33,7 +52,7 @@ struct LogitsEpi {
   float* pm;
   float* ps;
   int* pa;
-  int nt;
+  int64_t ldr;  // row stride of the tile-major partial arrays
   float* ztgt;
   const int64_t* y;
   int64_t ignore_index;
@@ -46,12 +65,13 @@ struct LogitsEpi {
     const bool tile_live = ec.col0 < V;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      float mxr[4], smr[4];
+      int air[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = ec.row0 + 16 * i + 4 * g + r;
-        const bool row_ok = row < M;
-        const int64_t yt = row_ok ? y[row] : -1;
-        const bool yv = row_ok && target_valid(yt, ignore_index, V);
+        const int64_t yt = row < M ? y[row] : -1;
+        const bool yv = row < M && target_valid(yt, ignore_index, V);
         float mx = kNegInf;
         int ai = 0x7fffffff;
 #pragma unroll
@@ -63,15 +83,7 @@ struct LogitsEpi {
             ai = col;
           }
         }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-          const float om = shfl_xor_f(mx, off);
-          const int oa = shfl_xor_i(ai, off);
-          if (om > mx || (om == mx && oa < ai)) {
-            mx = om;
-            ai = oa;
-          }
-        }
+        row16_argmax(mx, ai);
         const float mb = (mx == kNegInf) ? 0.f : mx * kLog2e;
         float sum = 0.f;
 #pragma unroll
@@ -83,30 +95,32 @@ struct LogitsEpi {
           sum += e;
           acc[i][j][r] = e;
         }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) sum += shfl_xor_f(sum, off);
-        if (c == 0 && row_ok && tile_live) {
-          const int64_t o = (int64_t)row * nt + ptile;
-          pm[o] = mx;
-          ps[o] = sum;
-          pa[o] = ai;
-        }
+        mxr[r] = mx;
+        air[r] = ai;
+        smr[r] = row16_sum(sum);
+      }
+      // lane (g, c < 4) writes row 16 i + 4 g + c: 16 consecutive rows per store
+      const int row = ec.row0 + 16 * i + 4 * g + c;
+      if (c < 4 && tile_live && row < M) {
+        const float m = c == 0 ? mxr[0] : c == 1 ? mxr[1] : c == 2 ? mxr[2] : mxr[3];
+        const float sm = c == 0 ? smr[0] : c == 1 ? smr[1] : c == 2 ? smr[2] : smr[3];
+        const int am = c == 0 ? air[0] : c == 1 ? air[1] : c == 2 ? air[2] : air[3];
+        const int64_t o = (int64_t)ptile * ldr + row;
+        pm[o] = m;
+        ps[o] = sm;
+        pa[o] = am;
       }
     }
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = ec.row0 + 16 * i + 4 * g + r;
-        if (row >= M) continue;
-        T* prow = P + (int64_t)row * ldp;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) prow[ec.col0 + 16 * j + c] = Elem<T>::from_f32(acc[i][j][r]);
-      }
+    T* const base = P + (int64_t)ec.row0 * ldp + ec.col0;
+    const int rows = M - ec.row0;
+    staged_rows(acc, ec.lane, ec.scratch, [&](int rr, int cc, f4 v) {
+      if (rr < rows) store4(base + (int64_t)rr * ldp + cc, v);
+    });
   }
 };
 
-// Plain store epilogue (dX, dW, split-K partials).
+// Plain store epilogue (dX, dW, split-K partials): 16-byte row segments,
+// optionally accumulating into the fp32 output.
 template <typename TO>
 struct StoreEpi {
   TO* out;
@@ -117,24 +131,16 @@ struct StoreEpi {
 
   template <int FM, int FN>
   __device__ __forceinline__ void apply(f4 (&acc)[FM][FN], const EpiCoord& ec) const {
-    const int g = ec.lane >> 4, c = ec.lane & 15;
-    TO* o = out + (int64_t)ec.split * split_stride;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = ec.row0 + 16 * i + 4 * g + r;
-        if (row >= M) continue;
-        TO* orow = o + (int64_t)row * ldo;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = ec.col0 + 16 * j + c;
-          if (col >= N) continue;
-          float v = acc[i][j][r];
-          if (accumulate) v += Elem<TO>::to_f32(orow[col]);
-          orow[col] = Elem<TO>::from_f32(v);
-        }
+    TO* const base = out + (int64_t)ec.split * split_stride + (int64_t)ec.row0 * ldo + ec.col0;
+    const int rows = M - ec.row0, cols = N - ec.col0;  // N % 4 == 0
+    const bool acc_in = accumulate;
+    staged_rows(acc, ec.lane, ec.scratch, [&](int rr, int cc, f4 v) {
+      if (rr < rows && cc < cols) {
+        TO* p = base + (int64_t)rr * ldo + cc;
+        if (acc_in) v += load4(p);
+        store4(p, v);
       }
+    });
   }
 };
 
@@ -201,7 +207,7 @@ static hipError_t logits_t(const LogitsArgs& a, hipStream_t s) {
   epi.pm = a.pm;
   epi.ps = a.ps;
   epi.pa = a.pa;
-  epi.nt = a.nt;
+  epi.ldr = a.ldr;
   epi.ztgt = a.ztgt;
   epi.y = a.y;
   epi.ignore_index = a.ignore_index;
@@ -375,54 +381,68 @@ __device__ __forceinline__ void merge_state(float& m, float& s, int& a, float m2
   }
 }
 
-// One wave per row.
+// Block of 32 rows x 8 slices of the partial tiles: each thread merges the
+// tiles j = slice, slice + 8, ... of its row (coalesced across rows in the
+// tile-major layout), the 8 slice states merge through LDS, then every
+// thread rescales its tiles' maxima into alpha.
+constexpr int kFinRows = 32, kFinSlices = 8;
 __global__ void __launch_bounds__(256) finalize_kernel(FinalizeArgs a) {
-  __shared__ double s_nll[4];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + wave;
-  double nll = 0.0;
-  if (row < a.M) {
-    const int64_t base = (int64_t)row * a.nt;
-    float m = kNegInf, s = 0.f;
-    int am = 0x7fffffff;
-    for (int j = lane; j < a.nt; j += 64) merge_state(m, s, am, a.pm[base + j], a.ps[base + j], a.pa[base + j]);
+  __shared__ float s_m[kFinSlices][kFinRows], s_s[kFinSlices][kFinRows], s_lse[kFinRows];
+  __shared__ int s_a[kFinSlices][kFinRows];
+  __shared__ double s_nll[kFinRows];
+  const int rl = threadIdx.x % kFinRows, sl = threadIdx.x / kFinRows;
+  const int row = blockIdx.x * kFinRows + rl;
+  const bool live = row < a.M;
+  float m = kNegInf, sm = 0.f;
+  int am = 0x7fffffff;
+  if (live)
+    for (int j = sl; j < a.nt; j += kFinSlices) {
+      const int64_t o = (int64_t)j * a.ldr + row;
+      merge_state(m, sm, am, a.pm[o], a.ps[o], a.pa[o]);
+    }
+  s_m[sl][rl] = m;
+  s_s[sl][rl] = sm;
+  s_a[sl][rl] = am;
+  __syncthreads();
+  if (sl == 0) {
+    double nll = 0.0;
+    if (live) {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float m2 = shfl_xor_f(m, off);
-      const float s2 = shfl_xor_f(s, off);
-      const int a2 = shfl_xor_i(am, off);
-      merge_state(m, s, am, m2, s2, a2);
-    }
-    const float lse = m + log_fast(s);
-    const int64_t yt = a.y[row];
-    const bool valid = target_valid(yt, a.ignore_index, a.V);
-    const float sc = valid ? *a.scale : 0.f;
-    // alpha_j = s valid exp(m_j - lse): rescales the stored exp(z - m_j)
-    // into s valid softmax(z).
-    for (int j = lane; j < a.nt; j += 64) {
-      const float mj = a.pm[base + j];
-      const float sj = a.ps[base + j];
-      a.pm[base + j] = (sj > 0.f) ? sc * exp_fast(mj - lse) : 0.f;
-    }
-    if (lane == 0) {
+      for (int k = 1; k < kFinSlices; ++k) merge_state(m, sm, am, s_m[k][rl], s_s[k][rl], s_a[k][rl]);
+      const float lse = m + log_fast(sm);
+      const int64_t yt = a.y[row];
+      const bool valid = target_valid(yt, a.ignore_index, a.V);
+      const float sc = valid ? *a.scale : 0.f;
       const float zt = valid ? a.ztgt[row] : 0.f;
       a.dzt[row] = valid ? sc * (exp_fast(zt - lse) - 1.f) : 0.f;
       if (a.lse_out) a.lse_out[row] = lse;
       if (a.argmax_out) a.argmax_out[row] = am;
       nll = valid ? (double)lse - (double)zt : 0.0;
+      s_lse[rl] = lse;
+      s_s[0][rl] = sc;
+    }
+    s_nll[rl] = nll;
+  }
+  __syncthreads();
+  if (live) {
+    // alpha_j = s valid exp(m_j - lse): rescales the stored exp(z - m_j)
+    // into s valid softmax(z).
+    const float lse = s_lse[rl], sc = s_s[0][rl];
+    for (int j = sl; j < a.nt; j += kFinSlices) {
+      const int64_t o = (int64_t)j * a.ldr + row;
+      a.pm[o] = (a.ps[o] > 0.f) ? sc * exp_fast(a.pm[o] - lse) : 0.f;
     }
   }
-  if (lane == 0) s_nll[wave] = nll;
-  __syncthreads();
   if (threadIdx.x == 0) {
-    const double sum = ((s_nll[0] + s_nll[1]) + s_nll[2]) + s_nll[3];
+    double sum = 0.0;
+    for (int k = 0; k < kFinRows; ++k) sum += s_nll[k];
     a.loss_part[blockIdx.x] = a.first_chunk ? sum : a.loss_part[blockIdx.x] + sum;
   }
 }
 
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(finalize_kernel, dim3(cdiv(a.M, 4)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(finalize_kernel, dim3(cdiv(a.M, kFinRows)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -452,7 +472,7 @@ __global__ void __launch_bounds__(256) fixup_kernel(FixupArgs a) {
       T* src = P + (int64_t)t * a.ldp + v;
       uint4 pv = *(const uint4*)src;
       const T* pe = (const T*)&pv;
-      const float al = (v < a.V) ? a.alpha[(int64_t)t * a.nt + v / kPartialWidth] : 0.f;
+      const float al = (v < a.V) ? a.alpha[(int64_t)(v / kPartialWidth) * a.ldr + t] : 0.f;
       const int64_t yt = a.y[t];
       const bool valid = target_valid(yt, a.ignore_index, a.V);
 #pragma unroll
