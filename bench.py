@@ -22,6 +22,26 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused linear-CE fwd+bwd tokens/s and % bf16 MFMA peak, H=4096 V=128256"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA (bf16) / fp32 vector
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_JSON = os.path.join(PROFILES, "traffic.json")
+KERNEL_SOURCES = ("linear_cross_entropy_02_amd/csrc/gemm.h",
+                  "linear_cross_entropy_02_amd/csrc/common.h",
+                  "linear_cross_entropy_02_amd/csrc/kernels.hip",
+                  "linear_cross_entropy_02_amd/csrc/kernels.h",
+                  "linear_cross_entropy_02_amd/csrc/flce_api.cpp")
+# rocprofv3 runs whose CSV output --summarize-profiles reads (run from the repo root)
+PROFILE_CMDS = {
+    "kt": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_kt -o run -- "
+          "python3 bench.py --steps 3 --warmup 1 --cpu-sample 0",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o run -- "
+             "python3 bench.py --steps 1 --warmup 1 --cpu-sample 0 --no-timing",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o run -- "
+             "python3 bench.py --steps 1 --warmup 1 --cpu-sample 0 --no-timing",
+    "cal_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_cal_fetch -o run -- "
+                 "python3 bench.py --calibrate-copy 1024",
+    "cal_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_cal_write -o run -- "
+                 "python3 bench.py --calibrate-copy 1024",
+}
 
 
 def parse():
@@ -38,7 +58,110 @@ def parse():
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (3 times), "
                         "to scale HBM byte counters")
+    p.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                   help="turn the rocprofv3 CSV output of the PROFILE_CMDS runs under DIR "
+                        "into the summaries in profiles/ (no GPU needed)")
     return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short_kernel_name(name: str) -> str:
+    import re
+    n = name.replace("flce::", "")
+    m = re.match(r"void gemm_nt_kernel<([^,]+), (\d+), (\d+), (\d+), (\w+)<([^>]*)>", n)
+    if m:
+        return (f"gemm<{m.group(1)},{m.group(2)}x{m.group(3)},{m.group(4)}w,"
+                f"{m.group(5)}<{m.group(6).strip()}>>")
+    return n.split("(")[0].replace("void ", "")
+
+
+def summarize_profiles(d: str):
+    """Kernel-time and HBM-traffic summaries from the PROFILE_CMDS outputs."""
+    import collections
+    import csv
+
+    def rows(sub, fname):
+        path = os.path.join(d, sub, fname)
+        with open(path) as f:
+            return list(csv.DictReader(f))
+
+    stats = rows("prof_kt", "run_kernel_stats.csv")
+    lines = ["# Kernel time, fused linear-CE fwd+bwd, llama3-8b head (T=16384, H=4096, V=128256, "
+             "bf16, chunk 4096)", "",
+             "Command (repo root, MI355X):", "", "    " + PROFILE_CMDS["kt"], "",
+             "3 timed + 1 warm-up steps (4 calls of flce_fwd_bwd), per-kernel HIP event timing on.",
+             "", "| kernel | calls | total ms | avg ms | % time |", "|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {short_kernel_name(r['Name'])} | {r['Calls']} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['AverageNs']) / 1e6:.4f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, "kernel_stats_llama3_8b_head.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def per_kernel(sub, counter):
+        acc = collections.defaultdict(list)
+        for r in rows(sub, "run_counter_collection.csv"):
+            if r["Counter_Name"] == counter:
+                acc[short_kernel_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    cal_bytes = 1024 * 2 ** 20
+    cf = per_kernel("prof_cal_fetch", "FETCH_SIZE")
+    cw = per_kernel("prof_cal_write", "WRITE_SIZE")
+    copy = [k for k in cf if "copyBuffer" in k or "copy" in k.lower()]
+    f_scale = cal_bytes / (cf[copy[0]] * 1024)
+    w_scale = cal_bytes / (cw[copy[0]] * 1024)
+    fetch = per_kernel("prof_fetch", "FETCH_SIZE")
+    write = per_kernel("prof_write", "WRITE_SIZE")
+    traffic = {"source_hash": kernel_source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
+               "kernels": {}}
+    lines = ["# HBM traffic per launch, fused linear-CE fwd+bwd, llama3-8b head "
+             "(T=16384, H=4096, V=128256, bf16, chunk 4096)", "",
+             "Commands (repo root, MI355X), one counter pass each:", ""]
+    lines += ["    " + PROFILE_CMDS[k] for k in ("fetch", "write", "cal_fetch", "cal_write")]
+    lines += ["", f"Calibration: a 1 GiB device-to-device copy reads FETCH_SIZE x {f_scale:.3f} and "
+                  f"WRITE_SIZE x {w_scale:.3f} of its true bytes; the figures below are scaled by "
+                  "those factors.", "",
+              "| kernel | read GB/launch | written GB/launch |", "|---|---|---|"]
+    for k in fetch:
+        rd = fetch[k] * 1024 * f_scale
+        wr = write.get(k, 0.0) * 1024 * w_scale
+        traffic["kernels"][k] = {"read_bytes": rd, "write_bytes": wr}
+        lines.append(f"| {k} | {rd / 1e9:.3f} | {wr / 1e9:.3f} |")
+    lines += ["", f"Kernel sources hash at measurement: {traffic['source_hash']}"]
+    with open(os.path.join(PROFILES, "hbm_traffic_llama3_8b_head.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(traffic, f, indent=1)
+    print("\n".join(lines))
+
+
+def measured_traffic(kernel_kind: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    # logits: LogitsEpi; dX: stores the input dtype; dW: stores fp32
+    tag = {"logits_gemm": "LogitsEpi", "dx_gemm": "StoreEpi<bf16>",
+           "dw_gemm": "StoreEpi<float>"}.get(kernel_kind)
+    for k, v in t["kernels"].items():
+        if tag and tag in k:
+            return round(v["read_bytes"] + v["write_bytes"])
+    return None
 
 
 def calibrate_copy(mib: int):
@@ -54,6 +177,9 @@ def calibrate_copy(mib: int):
 
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return
@@ -122,7 +248,7 @@ def main():
             achieved = flop_per_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
             roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                         "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                        "traffic": None}
+                        "traffic": measured_traffic(dom)}
         else:
             roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": 8000.0,
                         "unit": "GB/s", "frac": None, "traffic": None}

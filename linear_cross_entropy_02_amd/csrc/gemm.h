@@ -7,8 +7,9 @@
 //   dX         = dZ * W        A = dZ  (C x V),   B = W^T (H x V)
 //   dW        += dZ^T * X      A = dZ^T(V x C),   B = X^T (H x C)
 //
-// Block tile BM x BN, 256 threads = 4 waves in a 2 x 2 layout, each wave owns
-// a (BM/2) x (BN/2) accumulator tile made of 16 x 16 MFMA fragments.  One
+// Block tile BM x BN, 4 waves in a 2 x 2 layout or 8 waves in a 2 x 4
+// layout; each wave owns a (BM/2) x (BN/(WAVES/2)) accumulator tile made of
+// 16 x 16 MFMA fragments.  One
 // K-stage covers 128 bytes per row (64 bf16 or 32 fp32), staged through LDS
 // with a double buffer; rows are stored as eight 16-byte vectors whose
 // positions are XOR-swizzled by the row index so that both the direct-to-LDS
@@ -106,10 +107,14 @@ __device__ __forceinline__ void drain_fence(f4 (&acc)[FM][FN]) {
 #endif
 }
 
-template <int BM, int BN>
+// WAVES = 4 (2 x 2 waves, one per SIMD) or 8 (2 x 4 waves, two per SIMD:
+// while one wave waits to issue a load the other keeps the MFMA pipe busy).
+template <int BM, int BN, int WAVES = 4>
 struct TileGeom {
-  static constexpr int kThreads = 256;
-  static constexpr int WM = BM / 2, WN = BN / 2;  // wave tile
+  static constexpr int kWaves = WAVES;
+  static constexpr int kWavesN = WAVES / 2;
+  static constexpr int kThreads = 64 * WAVES;
+  static constexpr int WM = BM / 2, WN = BN / kWavesN;  // wave tile
   static constexpr int FM = WM / 16, FN = WN / 16;
   static constexpr int kStageVecs = (BM + BN) * 8;  // 16-byte vectors per stage
   static constexpr int kLdsBytes = 2 * kStageVecs * 16;
@@ -120,8 +125,8 @@ __device__ __forceinline__ int swz(int row, int kv) { return row * 8 + (kv ^ (ro
 
 // What every epilogue receives: the wave's accumulator fragments and where
 // they sit.  acc[i][j][r] is C[row0 + 16 i + 4 (lane/16) + r][col0 + 16 j + lane%16].
-// `scratch` is this wave's private part of the (then idle) LDS: kLdsBytes / 4
-// bytes.
+// `scratch` is this wave's private part of the (then idle) LDS: kLdsBytes /
+// WAVES bytes.
 struct EpiCoord {
   int row0, col0;  // first row / column of this wave's tile
   int lane;
@@ -203,19 +208,54 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 //   barrier: this wave's reads of the stage are done and the next stage's
 //       DMA has landed (vmcnt), in every wave;
 //   [B] substep-1 MFMAs, with the DMA of the stage after next (into the
-//       buffer just released) and then the next stage's substep-0 fragment
-//       reads threaded through them.
+//       buffer just released) and the next stage's substep-0 fragment reads
+//       threaded through them.
 // The wave never waits on LDS after the barrier: the fragments its MFMAs
 // need were read before it.
-template <typename T, int BM, int BN, class Epi>
-__global__ void __launch_bounds__(256) gemm_nt_kernel(GemmShape g, Epi epi) {
+// staged_rows for a read-modify-write: `load(row, col)` fetches the old
+// four values of every segment of a pass before the pass goes through LDS,
+// `sink(row, col, old + new)` stores them.
+template <int FM, int FN, class Load, class Sink>
+__device__ __forceinline__ void staged_rows_rmw(const f4 (&acc)[FM][FN], int lane, float* scratch,
+                                                Load&& load, Sink&& sink) {
+  constexpr int WN = FN * 16;
+  constexpr int STRIDE = WN + 4;
+  constexpr int CH = 2;
+  constexpr int VPR = WN / 4;
+  constexpr int RPI = 64 / VPR;
+  constexpr int NRD = 16 * CH / RPI;
+  const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int i0 = 0; i0 < FM; i0 += CH) {
+    f4 old[NRD];
+#pragma unroll
+    for (int k = 0; k < NRD; ++k) old[k] = load(16 * i0 + k * RPI + lane / VPR, 4 * (lane % VPR));
+#pragma unroll
+    for (int ii = 0; ii < CH; ++ii)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) scratch[(16 * ii + 4 * g + r) * STRIDE + 16 * j + c] = acc[i0 + ii][j][r];
+    wave_lds_fence();
+#pragma unroll
+    for (int k = 0; k < NRD; ++k) {
+      const int rr = k * RPI + lane / VPR, cv = lane % VPR;
+      const f4 v = *(const f4*)&scratch[rr * STRIDE + 4 * cv];
+      sink(16 * i0 + rr, 4 * cv, v + old[k]);
+    }
+    wave_lds_fence();
+  }
+}
+
+template <typename T, int BM, int BN, int WAVES, class Epi>
+__global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi epi) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the launch stub
-  using G = TileGeom<BM, BN>;
+  using G = TileGeom<BM, BN, WAVES>;
   constexpr int EPV = Elem<T>::kVec;
   constexpr int BK = 8 * EPV;
   constexpr int ES = (int)sizeof(T);
-  constexpr int A_INS = BM / 32;  // 16-byte loads per lane per stage (A)
-  constexpr int B_INS = BN / 32;
+  constexpr int A_INS = BM / (8 * WAVES);  // 16-byte loads per lane per stage (A)
+  constexpr int B_INS = BN / (8 * WAVES);
   constexpr int FM = G::FM, FN = G::FN;
   constexpr uint32_t kStageBytes = G::kStageVecs * 16;
   extern __shared__ uint4 lds[];  // 2 * kStageVecs, sized at launch
@@ -224,7 +264,7 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmShape g, Epi epi) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / G::kWavesN, wn = wave % G::kWavesN;
   const int m0 = tc.tm * BM, n0 = tc.tn * BN;
 
   int k_begin = 0, k_end = g.K;
@@ -249,17 +289,17 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmShape g, Epi epi) {
   const int kv_lane = (lane & 7) ^ ((lane >> 3) & 7);
 #pragma unroll
   for (int j = 0; j < A_INS; ++j) {
-    const int row = wave * (BM / 4) + 8 * j + (lane >> 3);
+    const int row = wave * (BM / WAVES) + 8 * j + (lane >> 3);
     a_off[j] = (uint32_t)(((int64_t)row * g.lda + kv_lane * EPV) * ES);
   }
 #pragma unroll
   for (int j = 0; j < B_INS; ++j) {
-    const int row = wave * (BN / 4) + 8 * j + (lane >> 3);
+    const int row = wave * (BN / WAVES) + 8 * j + (lane >> 3);
     b_off[j] = (uint32_t)(((int64_t)row * g.ldb + kv_lane * EPV) * ES);
   }
   const uint32_t lds_base = (uint32_t)(size_t)((lds_ptr_t)lds);
-  const uint32_t lds_a = lds_base + wave * (BM * 2) * 16;
-  const uint32_t lds_b = lds_base + BM * 8 * 16 + wave * (BN * 2) * 16;
+  const uint32_t lds_a = lds_base + wave * (BM * 8 / WAVES) * 16;
+  const uint32_t lds_b = lds_base + BM * 8 * 16 + wave * (BN * 8 / WAVES) * 16;
 
   f4 acc[FM][FN];
 #pragma unroll
@@ -324,16 +364,16 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmShape g, Epi epi) {
 #pragma unroll
       for (int q = 0; q < NM; ++q) {
         acc[q / FN][q % FN] = mma16<T>(fa1[q / FN], fb1[q % FN], acc[q / FN][q % FN]);
-        // DMAs first (longest lead before the barrier that needs them),
-        // then the fragment reads, B fragments before A fragments: [A]
-        // consumes all B fragments in its first FN MFMAs but A fragment i
-        // only from MFMA i * FN on.
+        // DMAs alternate with the fragment reads (bursts of DMA issue from
+        // all waves at once stall on the address unit); reads go B
+        // fragments first: [A] consumes all B fragments in its first FN
+        // MFMAs but A fragment i only from MFMA i * FN on.
         if (q % SPB == SPB - 1 && q / SPB < NR + NDMA) {
           const int k = q / SPB;
-          if (k < NDMA)
-            issue_one(cur, k2, k);
+          if ((k & 1) == 0 && k / 2 < NDMA)
+            issue_one(cur, k2, k / 2);
           else
-            read_one(nxt, 0, (k - NDMA + FM) % NR, fa0, fb0);
+            read_one(nxt, 0, ((k - min(k / 2 + 1, NDMA)) + FM) % NR, fa0, fb0);
         }
       }
     }
@@ -352,7 +392,7 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmShape g, Epi epi) {
   ec.col0 = n0 + wn * G::WN;
   ec.lane = lane;
   ec.split = tc.split;
-  ec.scratch = (float*)((char*)lds + wave * (G::kLdsBytes / 4));
+  ec.scratch = (float*)((char*)lds + wave * (G::kLdsBytes / WAVES));
   epi.template apply<FM, FN>(acc, ec);
 #endif
 }

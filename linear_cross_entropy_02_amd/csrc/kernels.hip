@@ -133,14 +133,19 @@ struct StoreEpi {
   __device__ __forceinline__ void apply(f4 (&acc)[FM][FN], const EpiCoord& ec) const {
     TO* const base = out + (int64_t)ec.split * split_stride + (int64_t)ec.row0 * ldo + ec.col0;
     const int rows = M - ec.row0, cols = N - ec.col0;  // N % 4 == 0
-    const bool acc_in = accumulate;
-    staged_rows(acc, ec.lane, ec.scratch, [&](int rr, int cc, f4 v) {
-      if (rr < rows && cc < cols) {
-        TO* p = base + (int64_t)rr * ldo + cc;
-        if (acc_in) v += load4(p);
-        store4(p, v);
-      }
-    });
+    if (accumulate) {
+      // read-modify-write: the previous values of a 32-row pass are loaded
+      // before the pass is staged, so their latency overlaps the LDS work
+      staged_rows_rmw(acc, ec.lane, ec.scratch, [&](int rr, int cc) -> f4 {
+        return (rr < rows && cc < cols) ? load4(base + (int64_t)rr * ldo + cc) : (f4){0, 0, 0, 0};
+      }, [&](int rr, int cc, f4 v) {
+        if (rr < rows && cc < cols) store4(base + (int64_t)rr * ldo + cc, v);
+      });
+    } else {
+      staged_rows(acc, ec.lane, ec.scratch, [&](int rr, int cc, f4 v) {
+        if (rr < rows && cc < cols) store4(base + (int64_t)rr * ldo + cc, v);
+      });
+    }
   }
 };
 
@@ -148,9 +153,9 @@ struct StoreEpi {
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-template <typename T, int BM, int BN, class Epi>
+template <typename T, int BM, int BN, int WAVES, class Epi>
 static hipError_t run_gemm(const GemmShape& g0, const Epi& epi, hipStream_t s) {
-  using G = TileGeom<BM, BN>;
+  using G = TileGeom<BM, BN, WAVES>;
   GemmShape g = g0;
   g.tiles_m = cdiv(g.M, BM);
   g.tiles_n = cdiv(g.N, BN);
@@ -159,27 +164,27 @@ static hipError_t run_gemm(const GemmShape& g0, const Epi& epi, hipStream_t s) {
   if (g.group_m < 1) g.group_m = 1;
   if (g.group_m > g.tiles_m) g.group_m = g.tiles_m;
   const int nblk = g.tiles_m * g.tiles_n * g.splits;
-  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, Epi>), dim3(nblk), dim3(G::kThreads),
+  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, WAVES, Epi>), dim3(nblk), dim3(G::kThreads),
                      G::kLdsBytes, s, g, epi);
   return hipGetLastError();
 }
 
 // The GEMM kernels use more than the default 64 KB of dynamic LDS.
-template <typename T, int BM, int BN, class Epi>
+template <typename T, int BM, int BN, int WAVES, class Epi>
 static hipError_t set_lds_attr() {
-  using G = TileGeom<BM, BN>;
-  return hipFuncSetAttribute((const void*)gemm_nt_kernel<T, BM, BN, Epi>,
+  using G = TileGeom<BM, BN, WAVES>;
+  return hipFuncSetAttribute((const void*)gemm_nt_kernel<T, BM, BN, WAVES, Epi>,
                              hipFuncAttributeMaxDynamicSharedMemorySize, G::kLdsBytes);
 }
 
 template <typename T>
 static hipError_t setup_t() {
   hipError_t e;
-  if ((e = set_lds_attr<T, 256, 256, LogitsEpi<T>>()) != hipSuccess) return e;
-  if ((e = set_lds_attr<T, 256, 256, StoreEpi<T>>()) != hipSuccess) return e;
-  if ((e = set_lds_attr<T, 256, 256, StoreEpi<float>>()) != hipSuccess) return e;
-  if ((e = set_lds_attr<T, 128, 128, StoreEpi<T>>()) != hipSuccess) return e;
-  if ((e = set_lds_attr<T, 128, 128, StoreEpi<float>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 256, 256, 4, LogitsEpi<T>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<T>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<float>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<T>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<float>>()) != hipSuccess) return e;
   return hipSuccess;
 }
 
@@ -200,7 +205,10 @@ static hipError_t logits_t(const LogitsArgs& a, hipStream_t s) {
   g.N = a.V;
   g.K = a.H;
   g.splits = 1;
-  g.group_m = 1 << 30;  // all row tiles of the chunk share each W tile
+  // Four row tiles per group: the 32 blocks an XCD runs at once form a 4 x 8
+  // patch, which keeps both the X chunk and W tiles resident in its L2
+  // (walking all 16 row tiles per W tile re-streams X from beyond L2).
+  g.group_m = 4;
   LogitsEpi<T> epi;
   epi.P = (T*)a.P;
   epi.ldp = a.ldp;
@@ -213,7 +221,7 @@ static hipError_t logits_t(const LogitsArgs& a, hipStream_t s) {
   epi.ignore_index = a.ignore_index;
   epi.M = a.M;
   epi.V = a.V;
-  return run_gemm<T, 256, 256>(g, epi, s);
+  return run_gemm<T, 256, 256, 4>(g, epi, s);
 }
 
 hipError_t launch_logits(Dt dt, const LogitsArgs& a, hipStream_t s) {
@@ -244,8 +252,8 @@ static hipError_t store_t2(TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
   epi.N = a.N;
   epi.split_stride = a.split_stride;
   epi.accumulate = a.accumulate;
-  if (tc == TileCfg::T256) return run_gemm<T, 256, 256>(g, epi, s);
-  return run_gemm<T, 128, 128>(g, epi, s);
+  if (tc == TileCfg::T256) return run_gemm<T, 256, 256, 4>(g, epi, s);
+  return run_gemm<T, 128, 128, 4>(g, epi, s);
 }
 
 template <typename T>
@@ -357,92 +365,100 @@ hipError_t launch_transpose(Dt dt, const void* src, int rows, int cols, int64_t 
 }
 
 // ------------------------------------------------------------- finalize ---
-// Merge rule for two online-softmax states (m, sum, argmax): the larger max
-// wins and the other sum is rescaled by exp(m_other - m); the rescale factor
-// is 1 when the max does not change.  Empty states (sum == 0) are skipped so
-// that two empty states never form (-inf) - (-inf).
-__device__ __forceinline__ void merge_state(float& m, float& s, int& a, float m2, float s2, int a2) {
-  if (s2 == 0.f) return;
-  if (s == 0.f) {
-    m = m2;
-    s = s2;
-    a = a2;
-    return;
-  }
-  if (m2 > m) {
-    s = s * exp_fast(m - m2) + s2;
-    m = m2;
-    a = a2;
-  } else if (m2 == m) {
-    s += s2;
-    a = min(a, a2);
-  } else {
-    s += s2 * exp_fast(m2 - m);
-  }
-}
-
-// Block of 32 rows x 8 slices of the partial tiles: each thread merges the
-// tiles j = slice, slice + 8, ... of its row (coalesced across rows in the
-// tile-major layout), the 8 slice states merge through LDS, then every
-// thread rescales its tiles' maxima into alpha.
-constexpr int kFinRows = 32, kFinSlices = 8;
-__global__ void __launch_bounds__(256) finalize_kernel(FinalizeArgs a) {
-  __shared__ float s_m[kFinSlices][kFinRows], s_s[kFinSlices][kFinRows], s_lse[kFinRows];
-  __shared__ int s_a[kFinSlices][kFinRows];
+// Block of 32 rows x 32 slices of the partial tiles (tile-major layout:
+// the 32 rows of a slice read 128 contiguous bytes).  Three passes over the
+// row's partials, each a parallel reduction over the slices:
+//   1. m = max_j m_j and the argmax of the first tile reaching it (tiles
+//      are in column order, so this is the lowest column index);
+//   2. sum = sum_j s_j exp(m_j - m), lse = m + ln sum (the merge of
+//      online-softmax states: each partial sum rescaled to the common max);
+//   3. alpha_j = s valid exp(m_j - lse), overwriting m_j.
+constexpr int kFinRows = 32, kFinSlices = 32;
+__global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
+  __shared__ float s_f[kFinSlices][kFinRows + 1];
+  __shared__ int s_i[kFinSlices][kFinRows + 1];
+  __shared__ float s_m[kFinRows], s_lse[kFinRows], s_sc[kFinRows];
   __shared__ double s_nll[kFinRows];
   const int rl = threadIdx.x % kFinRows, sl = threadIdx.x / kFinRows;
   const int row = blockIdx.x * kFinRows + rl;
   const bool live = row < a.M;
-  float m = kNegInf, sm = 0.f;
+  // pass 1: max and argmax
+  float m = kNegInf;
   int am = 0x7fffffff;
   if (live)
     for (int j = sl; j < a.nt; j += kFinSlices) {
       const int64_t o = (int64_t)j * a.ldr + row;
-      merge_state(m, sm, am, a.pm[o], a.ps[o], a.pa[o]);
+      const float mj = a.pm[o];
+      if (a.ps[o] > 0.f && (mj > m || (mj == m && a.pa[o] < am))) {
+        m = mj;
+        am = a.pa[o];
+      }
     }
-  s_m[sl][rl] = m;
-  s_s[sl][rl] = sm;
-  s_a[sl][rl] = am;
+  s_f[sl][rl] = m;
+  s_i[sl][rl] = am;
+  __syncthreads();
+  if (sl == 0) {
+    for (int k = 1; k < kFinSlices; ++k) {
+      const float mk = s_f[k][rl];
+      const int ak = s_i[k][rl];
+      if (mk > m || (mk == m && ak < am)) {
+        m = mk;
+        am = ak;
+      }
+    }
+    s_m[rl] = m;
+    if (live && a.argmax_out) a.argmax_out[row] = am;
+  }
+  __syncthreads();
+  // pass 2: rescaled sum
+  m = s_m[rl];
+  float sum = 0.f;
+  if (live)
+    for (int j = sl; j < a.nt; j += kFinSlices) {
+      const int64_t o = (int64_t)j * a.ldr + row;
+      const float sj = a.ps[o];
+      if (sj > 0.f) sum += sj * exp_fast(a.pm[o] - m);
+    }
+  s_f[sl][rl] = sum;
   __syncthreads();
   if (sl == 0) {
     double nll = 0.0;
+    float lse = 0.f, sc = 0.f;
     if (live) {
-#pragma unroll
-      for (int k = 1; k < kFinSlices; ++k) merge_state(m, sm, am, s_m[k][rl], s_s[k][rl], s_a[k][rl]);
-      const float lse = m + log_fast(sm);
+      for (int k = 1; k < kFinSlices; ++k) sum += s_f[k][rl];
+      lse = m + log_fast(sum);
       const int64_t yt = a.y[row];
       const bool valid = target_valid(yt, a.ignore_index, a.V);
-      const float sc = valid ? *a.scale : 0.f;
+      sc = valid ? *a.scale : 0.f;
       const float zt = valid ? a.ztgt[row] : 0.f;
       a.dzt[row] = valid ? sc * (exp_fast(zt - lse) - 1.f) : 0.f;
       if (a.lse_out) a.lse_out[row] = lse;
-      if (a.argmax_out) a.argmax_out[row] = am;
       nll = valid ? (double)lse - (double)zt : 0.0;
-      s_lse[rl] = lse;
-      s_s[0][rl] = sc;
     }
+    s_lse[rl] = lse;
+    s_sc[rl] = sc;
     s_nll[rl] = nll;
   }
   __syncthreads();
+  // pass 3: alpha
   if (live) {
-    // alpha_j = s valid exp(m_j - lse): rescales the stored exp(z - m_j)
-    // into s valid softmax(z).
-    const float lse = s_lse[rl], sc = s_s[0][rl];
+    const float lse = s_lse[rl], sc = s_sc[rl];
     for (int j = sl; j < a.nt; j += kFinSlices) {
       const int64_t o = (int64_t)j * a.ldr + row;
       a.pm[o] = (a.ps[o] > 0.f) ? sc * exp_fast(a.pm[o] - lse) : 0.f;
     }
   }
   if (threadIdx.x == 0) {
-    double sum = 0.0;
-    for (int k = 0; k < kFinRows; ++k) sum += s_nll[k];
-    a.loss_part[blockIdx.x] = a.first_chunk ? sum : a.loss_part[blockIdx.x] + sum;
+    double total = 0.0;
+    for (int k = 0; k < kFinRows; ++k) total += s_nll[k];
+    a.loss_part[blockIdx.x] = a.first_chunk ? total : a.loss_part[blockIdx.x] + total;
   }
 }
 
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(finalize_kernel, dim3(cdiv(a.M, kFinRows)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(finalize_kernel, dim3(cdiv(a.M, kFinRows)), dim3(kFinRows * kFinSlices), 0, s,
+                     a);
   return hipGetLastError();
 }
 
