@@ -23,7 +23,12 @@
 //   fp32:  v_mfma_f32_16x16x4_f32 issued four times on the four floats of
 //          one 16-byte read, element q of lane l pairing A and B on the same
 //          k, so the four issues together contract 16 consecutive k.
-//   D:     lane l, register r holds row 4*(l/16) + r, column l%16.
+//   D:     lane l, register r holds row 4*(l/16) + r, column l%16 of the
+//          product of its first operand with the second; the engine passes
+//          the B fragment first, so a fragment holds the C block transposed
+//          (lane l: row l%16, columns 4*(l/16) .. +3).  Epilogues then store
+//          16 (fp32) or 8 (bf16) contiguous bytes per lane and reduce a row
+//          over four lanes instead of sixteen.
 // Grid order is XCD-aware: consecutive logical tiles land on one XCD (its
 // own L2), walking M fastest inside groups of `group_m` rows of tiles so
 // that blocks sharing a B tile run together.
@@ -124,50 +129,24 @@ struct TileGeom {
 __device__ __forceinline__ int swz(int row, int kv) { return row * 8 + (kv ^ (row & 7)); }
 
 // What every epilogue receives: the wave's accumulator fragments and where
-// they sit.  acc[i][j][r] is C[row0 + 16 i + 4 (lane/16) + r][col0 + 16 j + lane%16].
-// `scratch` is this wave's private part of the (then idle) LDS: kLdsBytes /
-// WAVES bytes.
+// they sit.  The MFMAs take the B fragment as their first operand, so each
+// fragment holds a 16 x 16 block of C transposed: acc[i][j][r] is
+// C[row0 + 16 i + lane%16][col0 + 16 j + 4 (lane/16) + r], i.e. a lane owns
+// four consecutive columns of one row per fragment, and the four lanes
+// lane%16 + {0, 16, 32, 48} together own 16 consecutive columns.
 struct EpiCoord {
   int row0, col0;  // first row / column of this wave's tile
   int lane;
   int split;
-  float* scratch;
 };
 
-// Writes the wave's (16 FM) x (16 FN) fp32 tile out as 16-byte row segments:
-// 32 rows at a time are transposed through the wave's LDS scratch, then each
-// lane hands `sink(row, col, float4)` four consecutive columns of one row
-// (a wave covers whole rows, 64 lanes x 16 bytes per step), with `row` and
-// `col` relative to the wave tile.  The padded row stride keeps both the
-// 4-byte writes and the 16-byte reads free of bank conflicts.
-template <int FM, int FN, class Sink>
-__device__ __forceinline__ void staged_rows(const f4 (&acc)[FM][FN], int lane, float* scratch,
-                                            Sink&& sink) {
-  constexpr int WN = FN * 16;
-  constexpr int STRIDE = WN + 4;  // floats; 4 * STRIDE = 16 (mod 64) banks
-  constexpr int CH = 2;           // fragment rows (32 tile rows) per pass
-  constexpr int VPR = WN / 4;     // 16-byte vectors per row
-  constexpr int RPI = 64 / VPR;   // rows per wave-wide read
-  constexpr int NRD = 16 * CH / RPI;
-  static_assert(FM % CH == 0 && 64 % VPR == 0, "tile shape");
-  const int g = lane >> 4, c = lane & 15;
+// Accumulators starting at zero (the `init` of most epilogues).
+template <int FM, int FN>
+__device__ __forceinline__ void zero_init(f4 (&acc)[FM][FN]) {
 #pragma unroll
-  for (int i0 = 0; i0 < FM; i0 += CH) {
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int ii = 0; ii < CH; ++ii)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) scratch[(16 * ii + 4 * g + r) * STRIDE + 16 * j + c] = acc[i0 + ii][j][r];
-    wave_lds_fence();
-#pragma unroll
-    for (int k = 0; k < NRD; ++k) {
-      const int rr = k * RPI + lane / VPR, cv = lane % VPR;
-      const f4 v = *(const f4*)&scratch[rr * STRIDE + 4 * cv];
-      sink(16 * i0 + rr, 4 * cv, v);
-    }
-    wave_lds_fence();
-  }
+    for (int j = 0; j < FN; ++j) acc[i][j] = (f4){0.f, 0.f, 0.f, 0.f};
 }
 
 // Buffer resource (4 SGPRs) for raw loads of `bytes` bytes from `base`: an
@@ -200,6 +179,18 @@ __device__ __forceinline__ void dma16(i4v rsrc, uint32_t lds_addr, uint32_t voff
 #endif
 }
 
+// 16 bytes per lane from a buffer resource straight into an accumulator
+// fragment.  Issued as asm, like dma16, so the compiler's wait-count model
+// never sees it: it must be issued before the first stage's DMAs, whose
+// vmcnt wait in the prologue then covers it too.
+__device__ __forceinline__ void load16_acc(f4& dst, i4v rsrc, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const i4v r = {__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
+                 __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=a"(dst) : "v"(voff), "s"(r) : "memory");
+#endif
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // K-loop schedule, one 128-byte K-stage per iteration, two LDS stages:
@@ -212,41 +203,6 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 //       threaded through them.
 // The wave never waits on LDS after the barrier: the fragments its MFMAs
 // need were read before it.
-// staged_rows for a read-modify-write: `load(row, col)` fetches the old
-// four values of every segment of a pass before the pass goes through LDS,
-// `sink(row, col, old + new)` stores them.
-template <int FM, int FN, class Load, class Sink>
-__device__ __forceinline__ void staged_rows_rmw(const f4 (&acc)[FM][FN], int lane, float* scratch,
-                                                Load&& load, Sink&& sink) {
-  constexpr int WN = FN * 16;
-  constexpr int STRIDE = WN + 4;
-  constexpr int CH = 2;
-  constexpr int VPR = WN / 4;
-  constexpr int RPI = 64 / VPR;
-  constexpr int NRD = 16 * CH / RPI;
-  const int g = lane >> 4, c = lane & 15;
-#pragma unroll
-  for (int i0 = 0; i0 < FM; i0 += CH) {
-    f4 old[NRD];
-#pragma unroll
-    for (int k = 0; k < NRD; ++k) old[k] = load(16 * i0 + k * RPI + lane / VPR, 4 * (lane % VPR));
-#pragma unroll
-    for (int ii = 0; ii < CH; ++ii)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) scratch[(16 * ii + 4 * g + r) * STRIDE + 16 * j + c] = acc[i0 + ii][j][r];
-    wave_lds_fence();
-#pragma unroll
-    for (int k = 0; k < NRD; ++k) {
-      const int rr = k * RPI + lane / VPR, cv = lane % VPR;
-      const f4 v = *(const f4*)&scratch[rr * STRIDE + 4 * cv];
-      sink(16 * i0 + rr, 4 * cv, v + old[k]);
-    }
-    wave_lds_fence();
-  }
-}
-
 template <typename T, int BM, int BN, int WAVES, class Epi>
 __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi epi) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the launch stub
@@ -301,11 +257,17 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
   const uint32_t lds_a = lds_base + wave * (BM * 8 / WAVES) * 16;
   const uint32_t lds_b = lds_base + BM * 8 * 16 + wave * (BN * 8 / WAVES) * 16;
 
+  EpiCoord ec;
+  ec.row0 = m0 + wm * G::WM;
+  ec.col0 = n0 + wn * G::WN;
+  ec.lane = lane;
+  ec.split = tc.split;
+
+  // The epilogue chooses the starting accumulators: zero, or (to accumulate
+  // into an existing output) its old values, loaded with load16_acc here,
+  // before any DMA, so that the prologue's wait for stage 0 covers them.
   f4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = (f4){0.f, 0.f, 0.f, 0.f};
+  epi.template init<FM, FN>(acc, ec);
 
   // DMA j of stage `st` (0/1) for K-offset k0: j < A_INS loads A, else B.
   // Past the end of K every offset is out of range and the stage fills
@@ -345,7 +307,7 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
     for (int j = 0; j < NDMA; ++j) issue_one(0, k_begin, j);
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) issue_one(1, k_begin + BK, j);
-    __builtin_amdgcn_s_waitcnt(kWaitStage0);  // stage 0 landed
+    __builtin_amdgcn_s_waitcnt(kWaitStage0);  // initial accumulators and stage 0 landed
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int r = 0; r < NR; ++r) read_one(0, 0, r, fa0, fb0);
@@ -354,7 +316,7 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
       // [A]
 #pragma unroll
       for (int q = 0; q < NM; ++q) {
-        acc[q / FN][q % FN] = mma16<T>(fa0[q / FN], fb0[q % FN], acc[q / FN][q % FN]);
+        acc[q / FN][q % FN] = mma16<T>(fb0[q % FN], fa0[q / FN], acc[q / FN][q % FN]);
         if (q % SPA == SPA - 1 && q / SPA < NR) read_one(cur, 1, q / SPA, fa1, fb1);
       }
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
@@ -363,7 +325,7 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
       const int k2 = k_begin + (kt + 2) * BK;  // past the end: zero fill, unused
 #pragma unroll
       for (int q = 0; q < NM; ++q) {
-        acc[q / FN][q % FN] = mma16<T>(fa1[q / FN], fb1[q % FN], acc[q / FN][q % FN]);
+        acc[q / FN][q % FN] = mma16<T>(fb1[q % FN], fa1[q / FN], acc[q / FN][q % FN]);
         // DMAs alternate with the fragment reads (bursts of DMA issue from
         // all waves at once stall on the address unit); reads go B
         // fragments first: [A] consumes all B fragments in its first FN
@@ -385,14 +347,6 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
   __builtin_amdgcn_s_waitcnt(0x0F70);
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   drain_fence(acc);
-
-  __syncthreads();  // every wave is done with the stages: LDS becomes scratch
-  EpiCoord ec;
-  ec.row0 = m0 + wm * G::WM;
-  ec.col0 = n0 + wn * G::WN;
-  ec.lane = lane;
-  ec.split = tc.split;
-  ec.scratch = (float*)((char*)lds + wave * (G::kLdsBytes / WAVES));
   epi.template apply<FM, FN>(acc, ec);
 #endif
 }

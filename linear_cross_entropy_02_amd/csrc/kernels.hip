@@ -18,6 +18,8 @@
 //   dW GEMM       dW  += dZ^T X_c (K = chunk tokens), first chunk stores.
 #include "kernels.h"
 
+#include <type_traits>
+
 #include "common.h"
 #include "gemm.h"
 
@@ -41,10 +43,11 @@ __device__ __forceinline__ f4 load4(const bf16* p) {
 }
 
 // Logits epilogue: online-logsumexp partials per (row, 128-column wave tile).
-// Row reductions run in the MFMA layout (a row's 128 columns sit in 16
-// lanes x 8 fragments) with DPP moves; the partials are written tile-major
-// ([tile][row], 16 consecutive rows per store); exp(z - tile max) goes out
-// through the LDS-staged row store.
+// A lane owns one row of each fragment row-block and 32 of the wave tile's
+// 128 columns; the other 96 sit in lanes lane ^ 16, ^ 32, ^ 48, so a row
+// reduction is a 32-value in-lane pass plus two cross-lane steps.  The
+// partials are written tile-major ([tile][row], 16 consecutive rows per
+// store) and exp(z - tile max) goes straight out as 4-element row segments.
 template <typename T>
 struct LogitsEpi {
   T* P;
@@ -59,68 +62,108 @@ struct LogitsEpi {
   int M, V;
 
   template <int FM, int FN>
-  __device__ __forceinline__ void apply(f4 (&acc)[FM][FN], const EpiCoord& ec) const {
+  __device__ __forceinline__ void init(f4 (&acc)[FM][FN], const EpiCoord&) const {
+    zero_init(acc);
+  }
+
+  // FULL: every column of the wave tile is < V (no per-column test).
+  template <bool FULL, int FM, int FN>
+  __device__ __forceinline__ void rows(f4 (&acc)[FM][FN], const EpiCoord& ec) const {
     const int g = ec.lane >> 4, c = ec.lane & 15;
     const int ptile = ec.col0 / (FN * 16);
-    const bool tile_live = ec.col0 < V;
+    const int lc0 = ec.col0 + 4 * g;  // this lane's first column
+    // column of the row's target relative to this lane's first column, or
+    // -1 when the target is ignored or outside the lane's columns
+    int toff[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      float mxr[4], smr[4];
-      int air[4];
+      const int row = ec.row0 + 16 * i + c;
+      const int64_t yt = row < M ? y[row] : ignore_index;
+      const int64_t off = yt - lc0;
+      toff[i] = (target_valid(yt, ignore_index, V) && off >= 0 && off < 16 * FN && (off & 12) == 0)
+                    ? (int)off : -1;
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = ec.row0 + 16 * i + 4 * g + r;
-        const int64_t yt = row < M ? y[row] : -1;
-        const bool yv = row < M && target_valid(yt, ignore_index, V);
-        float mx = kNegInf;
-        int ai = 0x7fffffff;
+    for (int i = 0; i < FM; ++i) {
+      const int row = ec.row0 + 16 * i + c;
+      // max and lowest-index argmax; the lane visits its columns in increasing
+      // order, so a strict comparison keeps the first of equal values
+      float mx = kNegInf;
+      int ai = 0x7fffffff;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = ec.col0 + 16 * j + c;
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
           const float z = acc[i][j][r];
-          if (col < V && z > mx) {
+          if ((FULL || lc0 + 16 * j + r < V) && z > mx) {
             mx = z;
-            ai = col;
+            ai = lc0 + 16 * j + r;
           }
         }
-        row16_argmax(mx, ai);
-        const float mb = (mx == kNegInf) ? 0.f : mx * kLog2e;
-        float sum = 0.f;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = ec.col0 + 16 * j + c;
-          const float z = acc[i][j][r];
-          if (yv && (int64_t)col == yt) ztgt[row] = z;
-          const float e = (col < V) ? __builtin_amdgcn_exp2f(__builtin_fmaf(z, kLog2e, -mb)) : 0.f;
+      for (int m = 16; m <= 32; m *= 2) {
+        const float om = shfl_xor_f(mx, m);
+        const int oa = shfl_xor_i(ai, m);
+        const bool take = om > mx || (om == mx && oa < ai);
+        mx = take ? om : mx;
+        ai = take ? oa : ai;
+      }
+      // target logit: held by the one lane whose columns contain y (rare
+      // branch: a row's target falls in one of V / 128 wave tiles)
+      {
+        if (toff[i] >= 0) {
+          const int tk = 4 * (toff[i] >> 4) + (toff[i] & 3);
+          float zt = 0.f;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) zt = (4 * j + r == tk) ? acc[i][j][r] : zt;
+          ztgt[row] = zt;
+        }
+      }
+      const float mb = (mx == kNegInf) ? 0.f : mx * kLog2e;
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = (FULL || lc0 + 16 * j + r < V)
+                              ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][r], kLog2e, -mb))
+                              : 0.f;
           sum += e;
           acc[i][j][r] = e;
         }
-        mxr[r] = mx;
-        air[r] = ai;
-        smr[r] = row16_sum(sum);
-      }
-      // lane (g, c < 4) writes row 16 i + 4 g + c: 16 consecutive rows per store
-      const int row = ec.row0 + 16 * i + 4 * g + c;
-      if (c < 4 && tile_live && row < M) {
-        const float m = c == 0 ? mxr[0] : c == 1 ? mxr[1] : c == 2 ? mxr[2] : mxr[3];
-        const float sm = c == 0 ? smr[0] : c == 1 ? smr[1] : c == 2 ? smr[2] : smr[3];
-        const int am = c == 0 ? air[0] : c == 1 ? air[1] : c == 2 ? air[2] : air[3];
-        const int64_t o = (int64_t)ptile * ldr + row;
-        pm[o] = m;
-        ps[o] = sm;
-        pa[o] = am;
+      sum += shfl_xor_f(sum, 16);
+      sum += shfl_xor_f(sum, 32);
+      if (row < M) {
+        if (g == 0 && ec.col0 < V) {
+          const int64_t o = (int64_t)ptile * ldr + row;
+          pm[o] = mx;
+          ps[o] = sum;
+          pa[o] = ai;
+        }
+        // columns up to the padded row length are allocated; those >= V get 0
+        T* const prow = P + (int64_t)row * ldp + lc0;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) store4(prow + 16 * j, acc[i][j]);
       }
     }
-    T* const base = P + (int64_t)ec.row0 * ldp + ec.col0;
-    const int rows = M - ec.row0;
-    staged_rows(acc, ec.lane, ec.scratch, [&](int rr, int cc, f4 v) {
-      if (rr < rows) store4(base + (int64_t)rr * ldp + cc, v);
-    });
+  }
+
+  template <int FM, int FN>
+  __device__ __forceinline__ void apply(f4 (&acc)[FM][FN], const EpiCoord& ec) const {
+    if (ec.col0 + 16 * FN <= V)
+      rows<true>(acc, ec);
+    else
+      rows<false>(acc, ec);
   }
 };
 
-// Plain store epilogue (dX, dW, split-K partials): 16-byte row segments,
-// optionally accumulating into the fp32 output.
+// Plain store epilogue (dX, dW, split-K partials): each lane stores four
+// consecutive columns of one row per fragment.  To accumulate into the fp32
+// output (dW over token chunks) the accumulators start from the old values,
+// loaded before the K loop, so the epilogue is a plain store either way.
+// N % 4 == 0, so a 4-column segment is either whole or outside.
 template <typename TO>
 struct StoreEpi {
   TO* out;
@@ -130,21 +173,43 @@ struct StoreEpi {
   bool accumulate;
 
   template <int FM, int FN>
-  __device__ __forceinline__ void apply(f4 (&acc)[FM][FN], const EpiCoord& ec) const {
-    TO* const base = out + (int64_t)ec.split * split_stride + (int64_t)ec.row0 * ldo + ec.col0;
-    const int rows = M - ec.row0, cols = N - ec.col0;  // N % 4 == 0
-    if (accumulate) {
-      // read-modify-write: the previous values of a 32-row pass are loaded
-      // before the pass is staged, so their latency overlaps the LDS work
-      staged_rows_rmw(acc, ec.lane, ec.scratch, [&](int rr, int cc) -> f4 {
-        return (rr < rows && cc < cols) ? load4(base + (int64_t)rr * ldo + cc) : (f4){0, 0, 0, 0};
-      }, [&](int rr, int cc, f4 v) {
-        if (rr < rows && cc < cols) store4(base + (int64_t)rr * ldo + cc, v);
-      });
+  __device__ __forceinline__ void init(f4 (&acc)[FM][FN], const EpiCoord& ec) const {
+    if constexpr (!std::is_same<TO, float>::value) {
+      zero_init(acc);  // accumulation is fp32 only
     } else {
-      staged_rows(acc, ec.lane, ec.scratch, [&](int rr, int cc, f4 v) {
-        if (rr < rows && cc < cols) store4(base + (int64_t)rr * ldo + cc, v);
-      });
+      // One unconditional path (no merge of a zero and a loaded value for
+      // the register allocator to reconcile with copies): every fragment is
+      // loaded through a buffer resource covering the wave's rows below M.
+      // Rows past M read zero; columns past N, and everything when not
+      // accumulating, get an out-of-range offset, which also reads zero.
+      const int g = ec.lane >> 4, c = ec.lane & 15;
+      const int rows = M - ec.row0 < 16 * FM ? M - ec.row0 : 16 * FM;
+      const float* const base =
+          out + (int64_t)ec.split * split_stride + (int64_t)ec.row0 * ldo + ec.col0;
+      const i4v rs = make_rsrc(base, rows > 0 && accumulate ? (uint32_t)((int64_t)rows * ldo * 4) : 0u);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = 4 * g + 16 * j;
+          const uint32_t off = (uint32_t)(((16 * i + c) * ldo + col) * 4);
+          load16_acc(acc[i][j], rs, accumulate && ec.col0 + col < N ? off : kOobOffset);
+        }
+    }
+  }
+
+  template <int FM, int FN>
+  __device__ __forceinline__ void apply(f4 (&acc)[FM][FN], const EpiCoord& ec) const {
+    const int g = ec.lane >> 4, c = ec.lane & 15;
+    TO* const base = out + (int64_t)ec.split * split_stride;
+    const int lc0 = ec.col0 + 4 * g;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = ec.row0 + 16 * i + c;
+      TO* const p = base + (int64_t)row * ldo + lc0;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        if (row < M && lc0 + 16 * j < N) store4(p + 16 * j, acc[i][j]);
     }
   }
 };
