@@ -1,6 +1,7 @@
 """Benchmark: fused linear cross-entropy forward+backward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--chunk 4096]
+                    [--dw-chunks 2]
 
 A step is one flce_fwd_bwd call over one batch: logits GEMM with the
 online-logsumexp epilogue, dZ formation, dX and dW GEMMs, loss -- the whole
@@ -51,6 +52,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", type=int, default=4)
     p.add_argument("--chunk", type=int, default=4096)
+    p.add_argument("--dw-chunks", type=int, default=2,
+                   help="token chunks per dW GEMM (the dZ^T of that many chunks is kept)")
     p.add_argument("--cpu-sample", type=int, default=256,
                    help="tokens of the workload the CPU oracle is timed on (0 = skip)")
     p.add_argument("--no-timing", action="store_true",
@@ -95,7 +98,7 @@ def summarize_profiles(d: str):
 
     stats = rows("prof_kt", "run_kernel_stats.csv")
     lines = ["# Kernel time, fused linear-CE fwd+bwd, llama3-8b head (T=16384, H=4096, V=128256, "
-             "bf16, chunk 4096)", "",
+             "bf16, chunk 4096, dW over 2 chunks)", "",
              "Command (repo root, MI355X):", "", "    " + PROFILE_CMDS["kt"], "",
              "3 timed + 1 warm-up steps (4 calls of flce_fwd_bwd), per-kernel HIP event timing on.",
              "", "| kernel | calls | total ms | avg ms | % time |", "|---|---|---|---|---|"]
@@ -125,7 +128,7 @@ def summarize_profiles(d: str):
     traffic = {"source_hash": kernel_source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
                "kernels": {}}
     lines = ["# HBM traffic per launch, fused linear-CE fwd+bwd, llama3-8b head "
-             "(T=16384, H=4096, V=128256, bf16, chunk 4096)", "",
+             "(T=16384, H=4096, V=128256, bf16, chunk 4096, dW over 2 chunks)", "",
              "Commands (repo root, MI355X), one counter pass each:", ""]
     lines += ["    " + PROFILE_CMDS[k] for k in ("fetch", "write", "cal_fetch", "cal_write")]
     lines += ["", f"Calibration: a 1 GiB device-to-device copy reads FETCH_SIZE x {f_scale:.3f} and "
@@ -199,7 +202,8 @@ def main():
     X, W, y = workloads.to_torch(inp, "cuda")
     print(f"[bench] inputs for {wl.name} ready in {time.time() - t_gen:.1f}s", file=sys.stderr,
           flush=True)
-    op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=args.chunk)
+    op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=args.chunk,
+                                      dw_chunks=args.dw_chunks)
     out = op.alloc_outputs(wl.T, "cuda")
     stream = torch.cuda.current_stream()
 
@@ -240,11 +244,10 @@ def main():
                                  "avg_ms": tot / n}
         flce.flce_timing_enable(op.handle, False)
         dom = max(kernels, key=lambda k: kernels[k]["total_ms"])
-        C = op.chunk_tokens
-        n_chunks = -(-T // C)
         if dom in ("logits_gemm", "dx_gemm", "dw_gemm"):
-            # each GEMM launch contracts one chunk: 2 * C_chunk * H * V flops
-            flop_per_launch = 2.0 * T * H * V / n_chunks
+            # each of the three contractions does 2 T H V flops per step, split
+            # over its launches (one per chunk; one per dW group for dW)
+            flop_per_launch = 2.0 * T * H * V / kernels[dom]["launches_per_step"]
             achieved = flop_per_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
             roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                         "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
@@ -271,6 +274,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "H": H, "V": V, "chunk_tokens": op.chunk_tokens,
+                   "dw_chunks": op.dw_chunks,
                    "reduction": wl.reduction, "ignore_frac": wl.ignore_frac,
                    "targets": wl.targets},
         "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / peak, 4),

@@ -63,18 +63,24 @@ typedef struct {
   int64_t hidden;       /* H: > 0, multiple of 8 (bf16) or 4 (fp32)          */
   int64_t vocab;        /* V: > 0                                              */
   int32_t dtype;        /* flce_dtype_t                                        */
-  int32_t reserved;     /* must be 0                                           */
+  int32_t dw_chunks;    /* G: chunks whose dZ^T is kept for one dW GEMM of
+                           depth K = G*C; 0 = default (1), at most 8.  The dW
+                           tiles are then read and written once per G chunks
+                           instead of once per chunk, for (G-1)*C*V more
+                           workspace elements.                                  */
   int64_t chunk_tokens; /* C: tokens per chunk; 0 = default (4096).  Rounded up
-                           to a multiple of 256.  The workspace is O(C*V + V*H)
-                           and does not depend on the number of tokens T.     */
+                           to a multiple of 256.  The workspace is
+                           O((1+G)*C*V + V*H) and does not depend on the number
+                           of tokens T.                                         */
 } flce_config_t;
 
 typedef struct flce_handle* flce_handle_t;
 
-/* Create a handle for fixed (H, V, dtype, C) on the current HIP device and
- * allocate its workspace.  Returns INVALID_ARGUMENT for a bad config (no
- * device call is made), OUT_OF_MEMORY / HIP if allocation fails. *out is
- * set to NULL on failure. */
+/* Create a handle for fixed (H, V, dtype, C, G) on the current HIP device
+ * and allocate its workspace.  Returns INVALID_ARGUMENT for a bad config and
+ * UNSUPPORTED when H, V rounded up to a multiple of 256, or G*C exceeds 2^20
+ * (no device call is made in either case), OUT_OF_MEMORY / HIP if
+ * allocation fails.  *out is set to NULL on failure. */
 flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out);
 
 /* Bytes of device workspace the handle owns (independent of T). */
@@ -82,6 +88,9 @@ size_t flce_workspace_bytes(flce_handle_t h);
 
 /* Tokens per chunk after rounding (C). */
 int64_t flce_chunk_tokens(flce_handle_t h);
+
+/* Chunks per dW GEMM (G), after applying the default. */
+int32_t flce_dw_chunks(flce_handle_t h);
 
 /*
  * Fused forward + backward of the linear cross-entropy head.

@@ -31,7 +31,7 @@ FLCE_MEAN = 1
 FLCE_SUM = 2
 
 EXPORTED = (
-    "flce_create", "flce_workspace_bytes", "flce_chunk_tokens", "flce_fwd_bwd",
+    "flce_create", "flce_workspace_bytes", "flce_chunk_tokens", "flce_dw_chunks", "flce_fwd_bwd",
     "flce_query_error", "flce_timing_enable", "flce_timing_kinds", "flce_timing_kind_name",
     "flce_timing_read", "flce_destroy", "flce_status_string", "flce_last_error",
 )
@@ -39,7 +39,7 @@ EXPORTED = (
 
 class flce_config_t(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int64), ("vocab", ctypes.c_int64),
-                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("dw_chunks", ctypes.c_int32),
                 ("chunk_tokens", ctypes.c_int64)]
 
 
@@ -69,6 +69,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.flce_workspace_bytes.restype = ctypes.c_size_t
     lib.flce_chunk_tokens.argtypes = [P]
     lib.flce_chunk_tokens.restype = i64
+    lib.flce_dw_chunks.argtypes = [P]
+    lib.flce_dw_chunks.restype = i32
     lib.flce_fwd_bwd.argtypes = [P, P, P, P, i64, i64, i32, P, P, P, P, P, P, P]
     lib.flce_fwd_bwd.restype = st
     lib.flce_query_error.argtypes = [P, P, ctypes.POINTER(i64)]
@@ -100,9 +102,9 @@ def last_error() -> str:
 
 
 # ------------------------------------------------------------ C-name calls ---
-def flce_create(hidden: int, vocab: int, dtype: int, chunk_tokens: int = 0, reserved: int = 0):
+def flce_create(hidden: int, vocab: int, dtype: int, chunk_tokens: int = 0, dw_chunks: int = 0):
     """Returns (status, handle)."""
-    cfg = flce_config_t(hidden, vocab, dtype, reserved, chunk_tokens)
+    cfg = flce_config_t(hidden, vocab, dtype, dw_chunks, chunk_tokens)
     h = ctypes.c_void_p()
     st = load().flce_create(ctypes.byref(cfg), ctypes.byref(h))
     return st, h
@@ -118,6 +120,10 @@ def flce_workspace_bytes(handle) -> int:
 
 def flce_chunk_tokens(handle) -> int:
     return load().flce_chunk_tokens(handle)
+
+
+def flce_dw_chunks(handle) -> int:
+    return load().flce_dw_chunks(handle)
 
 
 def _ptr(t) -> Optional[int]:
@@ -172,21 +178,22 @@ def flce_timing_read(handle, kind: int):
 
 # ------------------------------------------------------------ torch facade ---
 class FusedLinearCrossEntropy:
-    """A handle for fixed (H, V, dtype, chunk) plus output allocation.
+    """A handle for fixed (H, V, dtype, chunk, dW group) plus output allocation.
 
     fwd_bwd(X, W, y) returns a dict of device tensors: loss (float32 scalar),
     dX (X's dtype), dW (float32), lse (float32 [T]), argmax (int32 [T]) and
     n_valid (int64 scalar).  Gradients are for a loss gradient seed of 1.
     """
 
-    def __init__(self, hidden: int, vocab: int, dtype="bf16", chunk_tokens: int = 0):
+    def __init__(self, hidden: int, vocab: int, dtype="bf16", chunk_tokens: int = 0,
+                 dw_chunks: int = 0):
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("FusedLinearCrossEntropy needs a HIP device")
         self.torch_dtype = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
         self.dtype = FLCE_BF16 if dtype == "bf16" else FLCE_F32
         self.hidden, self.vocab = hidden, vocab
-        st, h = flce_create(hidden, vocab, self.dtype, chunk_tokens)
+        st, h = flce_create(hidden, vocab, self.dtype, chunk_tokens, dw_chunks)
         if st != FLCE_OK:
             raise FlceError(st, "flce_create")
         self.handle = h
@@ -198,6 +205,10 @@ class FusedLinearCrossEntropy:
     @property
     def chunk_tokens(self) -> int:
         return flce_chunk_tokens(self.handle)
+
+    @property
+    def dw_chunks(self) -> int:
+        return flce_dw_chunks(self.handle)
 
     def close(self):
         if getattr(self, "handle", None):

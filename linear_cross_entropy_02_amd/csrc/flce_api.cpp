@@ -40,6 +40,7 @@ const char* kKindNames[K_NUM] = {"count_valid",   "transpose_w", "transpose_x", 
                                  "dw_gemm",       "loss",        "zero_fill"};
 
 constexpr int64_t kDefaultChunk = 4096;
+constexpr int kMaxDwChunks = 8;
 
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -56,13 +57,14 @@ struct flce_handle {
   int device = 0;
   Dt dt = Dt::BF16;
   int64_t H = 0, V = 0, C = 0, Vpad = 0, nt = 0;
+  int G = 1;               // chunks per dW GEMM
   int splitk_alloc = 1;  // split-K planes the workspace holds for a full chunk
   size_t ws_bytes = 0;
   char* ws = nullptr;
   void* Wt = nullptr;      // W^T           [H x Vpad]
   void* P = nullptr;       // exp / dZ      [C x Vpad]
-  void* Pt = nullptr;      // dZ^T          [Vpad x C]
-  void* Xt = nullptr;      // X_c^T         [H x C]
+  void* Pt = nullptr;      // dZ^T of G chunks [Vpad x G*C]
+  void* Xt = nullptr;      // X^T of G chunks  [H x G*C]
   float* pm = nullptr;     // tile max / alpha [nt x C], tile-major
   float* ps = nullptr;     // tile sum      [nt x C]
   int* pa = nullptr;       // tile argmax   [nt x C]
@@ -185,17 +187,20 @@ flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out) {
   *out = nullptr;
   if (!cfg) return FLCE_ERR_INVALID_ARGUMENT;
   if (cfg->dtype != FLCE_F32 && cfg->dtype != FLCE_BF16) return FLCE_ERR_INVALID_ARGUMENT;
-  if (cfg->reserved != 0) return FLCE_ERR_INVALID_ARGUMENT;
+  if (cfg->dw_chunks < 0 || cfg->dw_chunks > kMaxDwChunks) return FLCE_ERR_INVALID_ARGUMENT;
   const Dt dt = cfg->dtype == FLCE_BF16 ? Dt::BF16 : Dt::F32;
   const int64_t H = cfg->hidden, V = cfg->vocab;
   if (H <= 0 || V <= 0) return FLCE_ERR_INVALID_ARGUMENT;
   if (H % elems_per_vec(dt) != 0) return FLCE_ERR_INVALID_ARGUMENT;
   if (cfg->chunk_tokens < 0) return FLCE_ERR_INVALID_ARGUMENT;
-  // 32-bit tile indexing inside the kernels
-  if (H > (1 << 20) || V > (int64_t)1 << 30) return FLCE_ERR_UNSUPPORTED;
+  // The GEMM kernels address a 256-row operand tile with 32-bit byte
+  // offsets (row x leading dimension x element size < 2^31): leading
+  // dimensions H, the padded vocabulary and G x C stay at or below 2^20.
+  if (H > (1 << 20) || round_up(V, 256) > (1 << 20)) return FLCE_ERR_UNSUPPORTED;
   int64_t C = cfg->chunk_tokens ? cfg->chunk_tokens : kDefaultChunk;
   C = round_up(C, 256);
-  if (C > (1 << 20)) return FLCE_ERR_UNSUPPORTED;
+  const int64_t G = cfg->dw_chunks ? cfg->dw_chunks : 1;
+  if (C * G > (1 << 20)) return FLCE_ERR_UNSUPPORTED;
 
   flce_handle* h = new (std::nothrow) flce_handle();
   if (!h) return FLCE_ERR_OUT_OF_MEMORY;
@@ -213,6 +218,7 @@ flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out) {
   h->H = H;
   h->V = V;
   h->C = C;
+  h->G = (int)G;
   h->Vpad = round_up(V, 256);
   h->nt = cdiv64(V, kPartialWidth);
   {
@@ -230,8 +236,8 @@ flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out) {
   };
   const size_t oWt = carve((size_t)H * h->Vpad * es);
   const size_t oP = carve((size_t)C * h->Vpad * es);
-  const size_t oPt = carve((size_t)h->Vpad * C * es);
-  const size_t oXt = carve((size_t)H * C * es);
+  const size_t oPt = carve((size_t)h->Vpad * h->G * C * es);
+  const size_t oXt = carve((size_t)H * h->G * C * es);
   const size_t opm = carve((size_t)C * h->nt * 4);
   const size_t ops = carve((size_t)C * h->nt * 4);
   const size_t opa = carve((size_t)C * h->nt * 4);
@@ -276,6 +282,8 @@ size_t flce_workspace_bytes(flce_handle_t h) { return h ? h->ws_bytes : 0; }
 
 int64_t flce_chunk_tokens(flce_handle_t h) { return h ? h->C : 0; }
 
+int32_t flce_dw_chunks(flce_handle_t h) { return h ? h->G : 0; }
+
 flce_status_t flce_destroy(flce_handle_t h) {
   if (!h) return FLCE_OK;
   drain_timing(h);
@@ -311,6 +319,7 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const 
   const Dt dt = h->dt;
   const size_t es = elem_size(dt);
   const int64_t H = h->H, V = h->V, C = h->C, Vpad = h->Vpad, nt = h->nt;
+  const int64_t G = h->G, GC = G * C;  // dZ^T / X^T of G chunks side by side
   const int rsum = reduction == FLCE_SUM ? 1 : 0;
 
 #define FLCE_LAUNCH(kind, expr)                                      \
@@ -338,9 +347,13 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const 
     const int64_t Ck = round_up(Cc, 64);
     const char* Xc = (const char*)X + (size_t)t0 * H * es;
     const int64_t* yc = targets + t0;
+    // slot of this chunk in the G-chunk dZ^T / X^T buffers; every chunk but
+    // the batch's last is full, so the slots of a group are contiguous in K
+    const int64_t gs = c % G;
+    const bool last = t0 + Cc >= T;
 
-    FLCE_LAUNCH(K_TRANSPOSE_X,
-                launch_transpose(dt, Xc, (int)Cc, (int)H, H, h->Xt, C, (int)Ck, s));
+    FLCE_LAUNCH(K_TRANSPOSE_X, launch_transpose(dt, Xc, (int)Cc, (int)H, H,
+                                                (char*)h->Xt + (size_t)gs * C * es, GC, (int)Ck, s));
 
     LogitsArgs la{};
     la.X = Xc;
@@ -381,8 +394,8 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const 
     FixupArgs xa{};
     xa.P = h->P;
     xa.ldp = Vpad;
-    xa.Pt = h->Pt;
-    xa.ldpt = C;
+    xa.Pt = (char*)h->Pt + (size_t)gs * C * es;
+    xa.ldpt = GC;
     xa.M = (int)Cc;
     xa.rows_out = (int)Ck;
     xa.V = (int)V;
@@ -430,23 +443,25 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const 
                                                    (int)H, dXc, H, s));
       }
     }
-    // dW (+)= dZ^T X_c   (M = V, N = H, K = Ck); the first chunk stores.
-    {
+    // dW (+)= dZ^T X over the chunks of a group (M = V, N = H, K = gs C + Ck)
+    // once its last chunk is in; the first group stores.
+    if (gs == G - 1 || last) {
+      const int64_t Kg = gs * C + Ck;
       TileCfg tc;
       int splits;
-      plan_gemm(V, H, Ck, 1, &tc, &splits);
+      plan_gemm(V, H, Kg, 1, &tc, &splits);
       GemmOutArgs ga{};
       ga.A = h->Pt;
-      ga.lda = C;
+      ga.lda = GC;
       ga.B = h->Xt;
-      ga.ldb = C;
+      ga.ldb = GC;
       ga.M = (int)V;
       ga.N = (int)H;
-      ga.K = (int)Ck;
+      ga.K = (int)Kg;
       ga.out = dW;
       ga.ldo = H;
       ga.out_f32 = true;
-      ga.accumulate = c > 0;
+      ga.accumulate = c >= G;
       ga.splits = 1;
       ga.split_stride = 0;
       FLCE_LAUNCH(K_DW, launch_gemm_store(dt, tc, ga, s));

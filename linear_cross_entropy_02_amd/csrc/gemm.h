@@ -7,15 +7,25 @@
 //   dX         = dZ * W        A = dZ  (C x V),   B = W^T (H x V)
 //   dW        += dZ^T * X      A = dZ^T(V x C),   B = X^T (H x C)
 //
-// Block tile BM x BN, 4 waves in a 2 x 2 layout or 8 waves in a 2 x 4
-// layout; each wave owns a (BM/2) x (BN/(WAVES/2)) accumulator tile made of
-// 16 x 16 MFMA fragments.  One
+// Block tile BM x BN, 4 waves in a 2 x 2 layout; each wave owns a
+// (BM/2) x (BN/2) accumulator tile made of 16 x 16 MFMA fragments.  One
 // K-stage covers 128 bytes per row (64 bf16 or 32 fp32), staged through LDS
-// with a double buffer; rows are stored as eight 16-byte vectors whose
-// positions are XOR-swizzled by the row index so that both the direct-to-LDS
-// writes and the fragment reads are free of bank conflicts.  (Full 128-byte
-// row segments per load matter: a deeper ring of 64-byte stages in the same
-// LDS was measured slower.)
+// by direct-to-LDS loads; rows are stored as eight 16-byte vectors whose
+// positions are XOR-swizzled by the row index so that both the DMA writes
+// and the fragment reads are free of bank conflicts.  (Full 128-byte row
+// segments per load matter: a deeper ring of 64-byte stages in the same LDS
+// was measured slower.)
+//
+// Pipeline: each K-stage is split in two substeps around one barrier.  The
+// LDS holds three A buffers and two B buffers (160 KB for 256 x 256), so the
+// A half of stage kt + 2 can be loaded while stage kt is still being read:
+//   [A] substep-0 MFMAs of stage kt | substep-1 reads of stage kt,
+//       A DMAs of stage kt + 2 (into the A buffer of stage kt - 1)
+//   wait: everything but those A DMAs; barrier
+//   [B] substep-1 MFMAs of stage kt | substep-0 reads of stage kt + 1,
+//       B DMAs of stage kt + 2 (into the B buffer of stage kt)
+// The address unit thus sees half the DMAs in each phase instead of all of
+// them in one.
 //
 // MFMA layouts used (16 x 16 output fragments):
 //   bf16:  v_mfma_f32_16x16x32_bf16, lane l holds A[l%16][8 consecutive k]
@@ -112,8 +122,7 @@ __device__ __forceinline__ void drain_fence(f4 (&acc)[FM][FN]) {
 #endif
 }
 
-// WAVES = 4 (2 x 2 waves, one per SIMD) or 8 (2 x 4 waves, two per SIMD:
-// while one wave waits to issue a load the other keeps the MFMA pipe busy).
+// WAVES = 4: 2 x 2 waves, one per SIMD.
 template <int BM, int BN, int WAVES = 4>
 struct TileGeom {
   static constexpr int kWaves = WAVES;
@@ -121,8 +130,9 @@ struct TileGeom {
   static constexpr int kThreads = 64 * WAVES;
   static constexpr int WM = BM / 2, WN = BN / kWavesN;  // wave tile
   static constexpr int FM = WM / 16, FN = WN / 16;
-  static constexpr int kStageVecs = (BM + BN) * 8;  // 16-byte vectors per stage
-  static constexpr int kLdsBytes = 2 * kStageVecs * 16;
+  // LDS: three A stage buffers and two B stage buffers of 128-byte rows
+  static constexpr int kABufBytes = BM * 128, kBBufBytes = BN * 128;
+  static constexpr int kLdsBytes = 3 * kABufBytes + 2 * kBBufBytes;
 };
 
 // Position of k-vector `kv` (0..7) of LDS row `row` within a stage.
@@ -213,8 +223,7 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
   constexpr int A_INS = BM / (8 * WAVES);  // 16-byte loads per lane per stage (A)
   constexpr int B_INS = BN / (8 * WAVES);
   constexpr int FM = G::FM, FN = G::FN;
-  constexpr uint32_t kStageBytes = G::kStageVecs * 16;
-  extern __shared__ uint4 lds[];  // 2 * kStageVecs, sized at launch
+  extern __shared__ uint4 lds[];  // G::kLdsBytes, sized at launch
 
   const TileCoord tc = map_tile(g);
   const int tid = threadIdx.x;
@@ -255,7 +264,7 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
   }
   const uint32_t lds_base = (uint32_t)(size_t)((lds_ptr_t)lds);
   const uint32_t lds_a = lds_base + wave * (BM * 8 / WAVES) * 16;
-  const uint32_t lds_b = lds_base + BM * 8 * 16 + wave * (BN * 8 / WAVES) * 16;
+  const uint32_t lds_b = lds_base + 3 * G::kABufBytes + wave * (BN * 8 / WAVES) * 16;
 
   EpiCoord ec;
   ec.row0 = m0 + wm * G::WM;
@@ -269,75 +278,97 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
   f4 acc[FM][FN];
   epi.template init<FM, FN>(acc, ec);
 
-  // DMA j of stage `st` (0/1) for K-offset k0: j < A_INS loads A, else B.
-  // Past the end of K every offset is out of range and the stage fills
-  // with zeros.
-  auto issue_one = [&](int st, int k0, int j) {
+  // DMA j of one operand for K-offset k0 into A buffer `ab` (0..2) or B
+  // buffer `bb` (0..1).  Past the end of K every offset is out of range and
+  // the buffer fills with zeros.
+  auto issue_a = [&](int ab, int k0, int j) {
     const bool kin = kv_lane * EPV < k_end - k0;
-    const uint32_t so = (uint32_t)st * kStageBytes;
-    if (j < A_INS)
-      dma16(rA, lds_a + so + 1024 * j, kin ? a_off[j] : kOobOffset, k0 * ES);
-    else
-      dma16(rB, lds_b + so + 1024 * (j - A_INS), kin ? b_off[j - A_INS] : kOobOffset, k0 * ES);
+    dma16(rA, lds_a + (uint32_t)ab * G::kABufBytes + 1024 * j, kin ? a_off[j] : kOobOffset, k0 * ES);
   };
-  // Fragment read r of substep s of stage st: r < FM reads A fragment r,
-  // else B fragment r - FM.
-  auto read_one = [&](int st, int s, int r, uint4 (&fa)[FM], uint4 (&fb)[FN]) {
-    const uint4* stage = lds + st * G::kStageVecs;
+  auto issue_b = [&](int bb, int k0, int j) {
+    const bool kin = kv_lane * EPV < k_end - k0;
+    dma16(rB, lds_b + (uint32_t)bb * G::kBBufBytes + 1024 * j, kin ? b_off[j] : kOobOffset, k0 * ES);
+  };
+  // Fragment read r of substep s from A buffer ab / B buffer bb: r < FM
+  // reads A fragment r, else B fragment r - FM.
+  auto read_one = [&](int ab, int bb, int s, int r, uint4 (&fa)[FM], uint4 (&fb)[FN]) {
     const int kv = 4 * s + (lane >> 4);
     if (r < FM)
-      fa[r] = stage[swz(wm * G::WM + 16 * r + (lane & 15), kv)];
+      fa[r] = lds[ab * (G::kABufBytes / 16) + swz(wm * G::WM + 16 * r + (lane & 15), kv)];
     else
-      fb[r - FM] = stage[BM * 8 + swz(wn * G::WN + 16 * (r - FM) + (lane & 15), kv)];
+      fb[r - FM] = lds[(3 * G::kABufBytes + bb * G::kBBufBytes) / 16 +
+                       swz(wn * G::WN + 16 * (r - FM) + (lane & 15), kv)];
   };
 
   constexpr int NR = FM + FN;  // fragment reads per substep
   constexpr int NM = FM * FN;  // MFMAs per substep
   constexpr int NDMA = A_INS + B_INS;
-  constexpr int SPA = NM / NR > 0 ? NM / NR : 1;                    // [A]: reads
-  constexpr int SPB = NM / (NR + NDMA) > 0 ? NM / (NR + NDMA) : 1;  // [B]: DMA + reads
-  static_assert(NR * SPA <= NM && (NR + NDMA) * SPB <= NM, "side operations must fit");
+  // each phase carries NR reads and the DMAs of one operand
+  constexpr int NSA = NR + A_INS, NSB = NR + B_INS;
+  constexpr int SPA = NM / NSA > 0 ? NM / NSA : 1;
+  constexpr int SPB = NM / NSB > 0 ? NM / NSB : 1;
+  static_assert(NSA * SPA <= NM && NSB * SPB <= NM, "side operations must fit");
   static_assert(NDMA < 64, "vmcnt field");
   // s_waitcnt vmcnt(NDMA), expcnt/lgkmcnt not waited on
   constexpr int kWaitStage0 = (NDMA & 0xF) | ((NDMA >> 4) << 14) | 0x0F70;
+  // s_waitcnt vmcnt(A_INS) lgkmcnt(0): all but the A DMAs of this phase A
+  constexpr int kWaitMid = (A_INS & 0xF) | ((A_INS >> 4) << 14) | 0x0070;
 
   uint4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
   if (nk > 0) {
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) issue_one(0, k_begin, j);
+    for (int j = 0; j < A_INS; ++j) issue_a(0, k_begin, j);
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) issue_one(1, k_begin + BK, j);
+    for (int j = 0; j < B_INS; ++j) issue_b(0, k_begin, j);
+#pragma unroll
+    for (int j = 0; j < A_INS; ++j) issue_a(1, k_begin + BK, j);
+#pragma unroll
+    for (int j = 0; j < B_INS; ++j) issue_b(1, k_begin + BK, j);
     __builtin_amdgcn_s_waitcnt(kWaitStage0);  // initial accumulators and stage 0 landed
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int r = 0; r < NR; ++r) read_one(0, 0, r, fa0, fb0);
+    for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r, fa0, fb0);
+    // stage kt sits in A buffer kt % 3 and B buffer kt % 2
+    int a_cur = 0, a_nxt = 1, a_dma = 2;
     for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1, nxt = cur ^ 1;
-      // [A]
+      const int b_cur = kt & 1, b_nxt = b_cur ^ 1;
+      const int k2 = k_begin + (kt + 2) * BK;  // past the end: zero fill, unused
+      // [A]: substep-0 MFMAs; substep-1 reads of stage kt; A half of stage
+      // kt + 2 into the A buffer stage kt - 1 used (read before the last barrier)
 #pragma unroll
       for (int q = 0; q < NM; ++q) {
         acc[q / FN][q % FN] = mma16<T>(fb0[q % FN], fa0[q / FN], acc[q / FN][q % FN]);
-        if (q % SPA == SPA - 1 && q / SPA < NR) read_one(cur, 1, q / SPA, fa1, fb1);
+        if (q % SPA == SPA - 1 && q / SPA < NSA) {
+          const int k = q / SPA;  // one DMA after every second read
+          if (k % 3 == 2 && k / 3 < A_INS)
+            issue_a(a_dma, k2, k / 3);
+          else
+            read_one(a_cur, b_cur, 1, (k - min((k + 1) / 3, A_INS) + FM) % NR, fa1, fb1);
+        }
       }
-      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+      __builtin_amdgcn_s_waitcnt(kWaitMid);  // stage kt + 1 landed, own reads done
       __builtin_amdgcn_s_barrier();
-      // [B]
-      const int k2 = k_begin + (kt + 2) * BK;  // past the end: zero fill, unused
+      // [B]: substep-1 MFMAs; substep-0 reads of stage kt + 1; B half of
+      // stage kt + 2 into the B buffer of stage kt (fully read before the barrier)
 #pragma unroll
       for (int q = 0; q < NM; ++q) {
         acc[q / FN][q % FN] = mma16<T>(fb1[q % FN], fa1[q / FN], acc[q / FN][q % FN]);
-        // DMAs alternate with the fragment reads (bursts of DMA issue from
-        // all waves at once stall on the address unit); reads go B
-        // fragments first: [A] consumes all B fragments in its first FN
-        // MFMAs but A fragment i only from MFMA i * FN on.
-        if (q % SPB == SPB - 1 && q / SPB < NR + NDMA) {
+        if (q % SPB == SPB - 1 && q / SPB < NSB) {
           const int k = q / SPB;
-          if ((k & 1) == 0 && k / 2 < NDMA)
-            issue_one(cur, k2, k / 2);
+          if (k % 3 == 2 && k / 3 < B_INS)
+            issue_b(b_cur, k2, k / 3);
           else
-            read_one(nxt, 0, ((k - min(k / 2 + 1, NDMA)) + FM) % NR, fa0, fb0);
+            read_one(a_nxt, b_nxt, 0, (k - min((k + 1) / 3, B_INS) + FM) % NR, fa0, fb0);
         }
       }
+      const int t = a_cur;
+      a_cur = a_nxt;
+      a_nxt = a_dma;
+      a_dma = t;
+      // Drain the MFMA pipe before leaving the loop: the register allocator
+      // may copy accumulators on the exit edge, and the hazard recognizer
+      // does not see the asm MFMAs whose results those copies read.
+      if (kt + 1 == nk) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     }
   }
   // The last (unused) DMAs may still be in flight; results of the asm MFMAs

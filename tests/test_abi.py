@@ -48,7 +48,7 @@ def test_status_strings(lib):
     assert flce.status_string(99) == "FLCE_ERR_UNKNOWN"
 
 
-@pytest.mark.parametrize("hidden,vocab,dtype,chunk,reserved", [
+@pytest.mark.parametrize("hidden,vocab,dtype,chunk,dw_chunks", [
     (0, 100, flce.FLCE_BF16, 0, 0),       # H <= 0
     (-8, 100, flce.FLCE_BF16, 0, 0),
     (64, 0, flce.FLCE_BF16, 0, 0),        # V <= 0
@@ -56,11 +56,23 @@ def test_status_strings(lib):
     (6, 100, flce.FLCE_F32, 0, 0),        # H not a multiple of 4 (fp32)
     (64, 100, 7, 0, 0),                   # bad dtype
     (64, 100, flce.FLCE_BF16, -1, 0),     # negative chunk
-    (64, 100, flce.FLCE_BF16, 0, 1),      # reserved != 0
+    (64, 100, flce.FLCE_BF16, 0, -1),     # negative dW group
+    (64, 100, flce.FLCE_BF16, 0, 9),      # dW group above 8
 ])
-def test_create_rejects_bad_config_without_device(lib, hidden, vocab, dtype, chunk, reserved):
-    st, h = flce.flce_create(hidden, vocab, dtype, chunk, reserved)
+def test_create_rejects_bad_config_without_device(lib, hidden, vocab, dtype, chunk, dw_chunks):
+    st, h = flce.flce_create(hidden, vocab, dtype, chunk, dw_chunks)
     assert st == flce.FLCE_ERR_INVALID_ARGUMENT
+    assert not h.value
+
+
+@pytest.mark.parametrize("hidden,vocab,chunk,dw_chunks", [
+    ((1 << 20) + 8, 100, 0, 0),           # H above 2^20
+    (64, (1 << 20) + 1, 0, 0),            # padded vocabulary above 2^20
+    (64, 100, 1 << 19, 3),                # G x C above 2^20
+])
+def test_create_reports_unsupported_sizes_without_device(lib, hidden, vocab, chunk, dw_chunks):
+    st, h = flce.flce_create(hidden, vocab, flce.FLCE_BF16, chunk, dw_chunks)
+    assert st == flce.FLCE_ERR_UNSUPPORTED
     assert not h.value
 
 
@@ -79,6 +91,8 @@ def test_fwd_bwd_null_handle(lib):
 def test_misc_null_handle_calls(lib):
     assert lib.flce_destroy(None) == flce.FLCE_OK
     assert lib.flce_workspace_bytes(None) == 0
+    assert lib.flce_chunk_tokens(None) == 0
+    assert lib.flce_dw_chunks(None) == 0
     assert lib.flce_query_error(None, None, None) == flce.FLCE_ERR_INVALID_ARGUMENT
     assert lib.flce_timing_enable(None, 1) == flce.FLCE_ERR_INVALID_ARGUMENT
 

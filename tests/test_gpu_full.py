@@ -21,8 +21,9 @@ from oracle import count_valid, flce_reference, flce_rows, scale_factor
 
 pytestmark = pytest.mark.gpu
 
-# launch configuration: the chunk size the benchmark uses for workload 4
-CHUNK = {3: 4096, 4: 4096, 5: 2048}
+# launch configuration (chunk tokens, chunks per dW GEMM); workload 4 runs
+# in the configuration the benchmark times
+CHUNK = {3: (4096, 1), 4: (4096, 2), 5: (2048, 1)}
 
 
 def sample_rows(T, C, y, ignore_index, seed, n=24):
@@ -43,13 +44,15 @@ def run_full(cfg):
     print(f"[gpu-full] generating workload {cfg}: {wl.name}", flush=True)
     inp = workloads.generate(wl)
     X, W, y = workloads.to_torch(inp, "cuda")
-    op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=CHUNK[cfg])
-    print(f"[gpu-full] workload {cfg} on GPU, chunk {op.chunk_tokens}, "
+    chunk, g = CHUNK[cfg]
+    op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=chunk, dw_chunks=g)
+    print(f"[gpu-full] workload {cfg} on GPU, chunk {op.chunk_tokens}, dw_chunks {op.dw_chunks}, "
           f"workspace {op.workspace_bytes / 2**20:.0f} MiB", flush=True)
     out = op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction)
     torch.cuda.synchronize()
-    # the chunk buffers of the workspace hold C x Vpad logits-shaped values, twice
-    assert 2 * op.chunk_tokens < wl.T, "chunk buffers must stay below T x V"
+    # the workspace holds logits-shaped chunk buffers of C x Vpad (exp / dZ)
+    # and G C x Vpad (dZ^T of a dW group): together below T x V
+    assert (1 + op.dw_chunks) * op.chunk_tokens < wl.T, "chunk buffers must stay below T x V"
     res = {k: to_np(v) for k, v in out.items()}
     op.close()
     del X, W, y, out
@@ -87,7 +90,7 @@ def check_properties(wl, inp, res):
 
 
 def check_sampled_rows(wl, inp, res, n_valid, seed):
-    rows = sample_rows(wl.T, CHUNK[wl_cfg(wl)], inp.y, wl.ignore_index, seed)
+    rows = sample_rows(wl.T, CHUNK[wl_cfg(wl)][0], inp.y, wl.ignore_index, seed)
     print(f"[gpu-full] oracle on {len(rows)} sampled rows", flush=True)
     r = flce_rows(inp.X, inp.W, inp.y, rows, n_valid, wl.ignore_index, wl.reduction)
     assert np.abs(res["lse"][rows] - r["lse"]).max() <= LSE_ATOL

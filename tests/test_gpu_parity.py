@@ -14,16 +14,17 @@ from oracle import flce_reference
 pytestmark = pytest.mark.gpu
 
 
-def run(wl, chunk=0, inp=None, out=None, op=None):
+def run(wl, chunk=0, inp=None, out=None, op=None, dw_chunks=0):
     import torch
     if inp is None:
         inp = workloads.generate(wl)
     X, W, y = workloads.to_torch(inp, "cuda")
     own = op is None
     if own:
-        op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=chunk)
-    print(f"[gpu] {wl.name} T={wl.T} H={wl.H} V={wl.V} {wl.dtype} chunk={op.chunk_tokens}",
-          flush=True)
+        op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=chunk,
+                                          dw_chunks=dw_chunks)
+    print(f"[gpu] {wl.name} T={wl.T} H={wl.H} V={wl.V} {wl.dtype} chunk={op.chunk_tokens} "
+          f"dw_chunks={op.dw_chunks}", flush=True)
     res = op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction, out=out)
     torch.cuda.synchronize()
     if own:
@@ -52,6 +53,23 @@ def test_parity_vs_oracle(wl, chunk):
     inp, out = run(wl, chunk)
     ref = oracle(inp, wl)
     check_full(out, ref, inp, wl)
+
+
+# dW over groups of G chunks: full groups, a last group cut short by the
+# batch, a ragged last chunk, and G larger than the number of chunks
+DW_GROUP_CASES = [
+    (workloads.WORKLOADS[2].with_shape(T=1000, H=96, V=1000, seed=31), 256, 2),   # 2 groups, last 2nd ragged
+    (workloads.WORKLOADS[2].with_shape(T=1044, H=136, V=3001, seed=32), 256, 2),  # last group = 1 ragged chunk
+    (workloads.WORKLOADS[4].with_shape(T=900, H=512, V=20000, seed=33), 256, 3),  # 1 full + 1 partial group
+    (workloads.WORKLOADS[1].with_shape(T=200, V=777, seed=34), 64, 8),            # fp32, G > chunks
+]
+
+
+@pytest.mark.parametrize("wl,chunk,g", DW_GROUP_CASES,
+                         ids=[f"{c[0].name}-G{c[2]}" for c in DW_GROUP_CASES])
+def test_parity_dw_chunk_groups(wl, chunk, g):
+    inp, out = run(wl, chunk, dw_chunks=g)
+    check_full(out, oracle(inp, wl), inp, wl)
 
 
 def test_all_tokens_ignored():
