@@ -1,7 +1,7 @@
 """Benchmark: fused linear cross-entropy forward+backward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--chunk 4096]
-                    [--dw-chunks 2]
+                    [--dw-chunks 1]
 
 A step is one flce_fwd_bwd call over one batch: logits GEMM with the
 online-logsumexp epilogue, dZ formation, dX and dW GEMMs, loss -- the whole
@@ -22,7 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fused linear-CE fwd+bwd tokens/s and % bf16 MFMA peak, H=4096 V=128256"
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA (bf16) / fp32 vector
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA peaks, bf16 and fp32
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_JSON = os.path.join(PROFILES, "traffic.json")
 KERNEL_SOURCES = ("linear_cross_entropy_02_amd/csrc/gemm.h",
@@ -42,6 +42,12 @@ PROFILE_CMDS = {
                  "python3 bench.py --calibrate-copy 1024",
     "cal_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_cal_write -o run -- "
                  "python3 bench.py --calibrate-copy 1024",
+    "mfma": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_LDS_BANK_CONFLICT "
+            "SQ_LDS_IDX_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE --output-format csv "
+            "-d gpurun_out/prof_mfma -o run -- python3 bench.py --steps 1 --warmup 1 --cpu-sample 0 "
+            "--no-timing",
+    "mfma_util": "rocprofv3 --pmc MfmaUtil --output-format csv -d gpurun_out/prof_mfma_util -o run -- "
+                 "python3 bench.py --steps 1 --warmup 1 --cpu-sample 0 --no-timing",
 }
 
 
@@ -52,8 +58,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", type=int, default=4)
     p.add_argument("--chunk", type=int, default=4096)
-    p.add_argument("--dw-chunks", type=int, default=2,
-                   help="token chunks per dW GEMM (the dZ^T of that many chunks is kept)")
+    p.add_argument("--dw-chunks", type=int, default=1,
+                   help="token chunks per dW GEMM (the dZ^T of that many chunks is kept; "
+                        "more than 1 needs (1 + G) C V more workspace)")
     p.add_argument("--cpu-sample", type=int, default=256,
                    help="tokens of the workload the CPU oracle is timed on (0 = skip)")
     p.add_argument("--no-timing", action="store_true",
@@ -98,7 +105,7 @@ def summarize_profiles(d: str):
 
     stats = rows("prof_kt", "run_kernel_stats.csv")
     lines = ["# Kernel time, fused linear-CE fwd+bwd, llama3-8b head (T=16384, H=4096, V=128256, "
-             "bf16, chunk 4096, dW over 2 chunks)", "",
+             "bf16, chunk 4096)", "",
              "Command (repo root, MI355X):", "", "    " + PROFILE_CMDS["kt"], "",
              "3 timed + 1 warm-up steps (4 calls of flce_fwd_bwd), per-kernel HIP event timing on.",
              "", "| kernel | calls | total ms | avg ms | % time |", "|---|---|---|---|---|"]
@@ -128,7 +135,7 @@ def summarize_profiles(d: str):
     traffic = {"source_hash": kernel_source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
                "kernels": {}}
     lines = ["# HBM traffic per launch, fused linear-CE fwd+bwd, llama3-8b head "
-             "(T=16384, H=4096, V=128256, bf16, chunk 4096, dW over 2 chunks)", "",
+             "(T=16384, H=4096, V=128256, bf16, chunk 4096)", "",
              "Commands (repo root, MI355X), one counter pass each:", ""]
     lines += ["    " + PROFILE_CMDS[k] for k in ("fetch", "write", "cal_fetch", "cal_write")]
     lines += ["", f"Calibration: a 1 GiB device-to-device copy reads FETCH_SIZE x {f_scale:.3f} and "
@@ -145,6 +152,47 @@ def summarize_profiles(d: str):
         f.write("\n".join(lines) + "\n")
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(traffic, f, indent=1)
+    print("\n".join(lines))
+
+    # MFMA busy and LDS bank conflicts (both counter passes are optional)
+    def per_kernel(sub):
+        acc = collections.defaultdict(lambda: collections.defaultdict(float))
+        n = collections.defaultdict(lambda: collections.defaultdict(int))
+        for r in rows(sub, "run_counter_collection.csv"):
+            k = short_kernel_name(r["Kernel_Name"])
+            acc[k][r["Counter_Name"]] += float(r["Counter_Value"])
+            n[k][r["Counter_Name"]] += 1
+        return {k: {c: acc[k][c] / n[k][c] for c in acc[k]} for k in acc}
+    try:
+        raw = per_kernel("prof_mfma")
+    except OSError:
+        return
+    try:
+        util = per_kernel("prof_mfma_util")
+    except OSError:
+        util = {}
+    lines = ["# MFMA busy and LDS bank conflicts per launch, fused linear-CE fwd+bwd, llama3-8b "
+             "head (T=16384, H=4096, V=128256, bf16, chunk 4096)", "",
+             "Commands (repo root, MI355X), one counter pass each:", "",
+             "    " + PROFILE_CMDS["mfma"], "    " + PROFILE_CMDS["mfma_util"], "",
+             "MfmaUtil is rocprofv3's derived metric (percent of the MFMA units' cycles busy over "
+             "the launch); bf16 FLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; bank conflicts are "
+             "SQ_LDS_BANK_CONFLICT cycles against SQ_LDS_IDX_ACTIVE cycles.", "",
+             "| kernel | MfmaUtil % | bf16 TFLOP counted | LDS bank-conflict cycles | "
+             "LDS active cycles | conflict % |", "|---|---|---|---|---|---|"]
+    for k, c in sorted(raw.items(), key=lambda kv: -kv[1].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0)):
+        mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        if mops <= 0:
+            continue
+        bc, act = c.get("SQ_LDS_BANK_CONFLICT", 0.0), c.get("SQ_LDS_IDX_ACTIVE", 0.0)
+        mu = util.get(k, {}).get("MfmaUtil")
+        lines.append(f"| {k} | {mu:.1f} | {mops * 512 / 1e12:.3f} | {bc:.3e} | {act:.3e} | "
+                     f"{100.0 * bc / act if act else 0.0:.2f} |" if mu is not None else
+                     f"| {k} | n/a | {mops * 512 / 1e12:.3f} | {bc:.3e} | {act:.3e} | "
+                     f"{100.0 * bc / act if act else 0.0:.2f} |")
+    lines += ["", f"Kernel sources hash at measurement: {kernel_source_hash()}"]
+    with open(os.path.join(PROFILES, "mfma_lds_counters_llama3_8b_head.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
@@ -217,13 +265,21 @@ def main():
         flce.flce_timing_enable(op.handle, True)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
+    free_before = torch.cuda.mem_get_info()[0]
     start.record(stream)
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction, out=out)
+        marks[i + 1].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
+    free_after = torch.cuda.mem_get_info()[0]
     ms = start.elapsed_time(stop) / args.steps
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    ms_median = per_step[len(per_step) // 2] if len(per_step) % 2 else \
+        0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
     loss = float(out["loss"].item())
     assert np.isfinite(loss), loss
 
@@ -279,7 +335,12 @@ def main():
                    "targets": wl.targets},
         "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / peak, 4),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+        "ms_per_step_median": round(ms_median, 3),
         "workspace_bytes": op.workspace_bytes,
+        # the no-T x V-buffer check: workspace against a bf16 T x V buffer,
+        # and device memory taken during the timed calls (none is allocated)
+        "workspace_vs_TxV_bf16": round(op.workspace_bytes / (2.0 * T * V), 4),
+        "device_alloc_in_calls_bytes": max(0, free_before - free_after),
     }
     op.close()
     print(json.dumps(line), flush=True)
