@@ -1,0 +1,113 @@
+"""PyTorch autograd wrapper around the fused head.
+
+The forward pass runs the whole fused computation (loss, dX and dW for a
+loss gradient of 1) in one flce_fwd_bwd call and keeps dX and dW; the
+backward pass only scales them by the incoming gradient of the scalar loss,
+since the gradients are already finished when the loss is returned
+(efficient-llm-anatomy README, Selected insights: fused cross-entropy
+computes backward during forward).  Autograd then accumulates them into
+`.grad`.
+
+A custom Function is invisible to autocast unless it opts in (same README
+and section: autocast does not see Function.apply()), so the forward is
+decorated with custom_fwd and casts its floating inputs to bf16 when autocast
+is on; dW, computed in fp32, is handed back in W's dtype.
+"""
+from __future__ import annotations
+
+import threading
+
+import torch
+
+from . import FusedLinearCrossEntropy
+
+_handles: dict = {}
+_lock = threading.Lock()
+
+
+def _handle(device: torch.device, stream: torch.cuda.Stream, H: int, V: int, dtype: str,
+            chunk_tokens: int, dw_chunks: int) -> FusedLinearCrossEntropy:
+    """One handle per (device, stream, shape, dtype, chunking): a handle owns
+    its workspace and must not be used by two streams at once."""
+    key = (device.index, stream.cuda_stream, H, V, dtype, chunk_tokens, dw_chunks)
+    with _lock:
+        op = _handles.get(key)
+        if op is None:
+            with torch.cuda.device(device):
+                op = FusedLinearCrossEntropy(H, V, dtype, chunk_tokens=chunk_tokens,
+                                             dw_chunks=dw_chunks)
+            _handles[key] = op
+        return op
+
+
+def clear_handle_cache():
+    """Free every cached handle's workspace."""
+    with _lock:
+        for op in _handles.values():
+            op.close()
+        _handles.clear()
+
+
+class LinearCrossEntropyFunction(torch.autograd.Function):
+    @staticmethod
+    @torch.amp.custom_fwd(device_type="cuda", cast_inputs=torch.bfloat16)
+    def forward(ctx, X, W, targets, ignore_index: int = -100, reduction: str = "mean",
+                chunk_tokens: int = 0, dw_chunks: int = 0):
+        if X.dim() != 2 or W.dim() != 2 or X.shape[1] != W.shape[1]:
+            raise ValueError("X must be [T, H] and W [V, H]")
+        if X.dtype != W.dtype or X.dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("X and W must share a dtype, bf16 or fp32")
+        if reduction not in ("mean", "sum"):
+            raise ValueError("reduction must be 'mean' or 'sum'")
+        dtype = "bf16" if X.dtype == torch.bfloat16 else "f32"
+        X = X.contiguous()
+        W = W.contiguous()
+        targets = targets.contiguous()
+        stream = torch.cuda.current_stream(X.device)
+        op = _handle(X.device, stream, X.shape[1], W.shape[0], dtype, chunk_tokens, dw_chunks)
+        out = op.fwd_bwd(X, W, targets, ignore_index, reduction)
+        ctx.save_for_backward(out["dX"], out["dW"])
+        ctx.w_dtype = W.dtype
+        ctx.mark_non_differentiable(out["lse"])
+        return out["loss"], out["lse"]
+
+    @staticmethod
+    @torch.amp.custom_bwd(device_type="cuda")
+    def backward(ctx, grad_loss, grad_lse):
+        dX, dW = ctx.saved_tensors
+        g = grad_loss.to(torch.float32)
+        gX = (dX.to(torch.float32) * g).to(dX.dtype) if ctx.needs_input_grad[0] else None
+        gW = (dW * g).to(ctx.w_dtype) if ctx.needs_input_grad[1] else None
+        return gX, gW, None, None, None, None, None
+
+
+def linear_cross_entropy(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+                         ignore_index: int = -100, reduction: str = "mean",
+                         chunk_tokens: int = 0, dw_chunks: int = 0,
+                         return_lse: bool = False):
+    """Cross-entropy of softmax(X W^T) against `targets`, fused: the T x V
+    logits are never formed.  Returns the scalar loss (and the per-token
+    log-sum-exp when `return_lse`); gradients reach X and W through
+    autograd."""
+    loss, lse = LinearCrossEntropyFunction.apply(X, W, targets, ignore_index, reduction,
+                                                 chunk_tokens, dw_chunks)
+    return (loss, lse) if return_lse else loss
+
+
+class LinearCrossEntropy(torch.nn.Module):
+    """An lm_head with a fused cross-entropy loss: holds W ([V, H]) and maps
+    hidden states and targets to the loss."""
+
+    def __init__(self, hidden: int, vocab: int, dtype=torch.bfloat16, device="cuda",
+                 ignore_index: int = -100, reduction: str = "mean", chunk_tokens: int = 0):
+        super().__init__()
+        self.weight = torch.nn.Parameter(torch.empty(vocab, hidden, dtype=dtype, device=device))
+        torch.nn.init.normal_(self.weight, std=hidden ** -0.5)
+        self.ignore_index = ignore_index
+        self.reduction = reduction
+        self.chunk_tokens = chunk_tokens
+
+    def forward(self, hidden_states: torch.Tensor, targets: torch.Tensor) -> torch.Tensor:
+        X = hidden_states.reshape(-1, hidden_states.shape[-1])
+        return linear_cross_entropy(X, self.weight, targets.reshape(-1), self.ignore_index,
+                                    self.reduction, self.chunk_tokens)

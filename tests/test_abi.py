@@ -116,3 +116,15 @@ def test_library_has_no_undefined_internal_symbols(lib):
                          text=True, check=True).stdout
     bad = [l for l in out.splitlines() if "flce" in l]
     assert not bad, bad
+
+
+def test_autograd_wrapper_refuses_host_tensors():
+    """The wrapper has no CPU path: without a HIP device (or given host
+    tensors) it raises instead of computing anything on the host."""
+    import torch
+    from linear_cross_entropy_02_amd.autograd import linear_cross_entropy
+    X = torch.zeros(4, 8, dtype=torch.bfloat16, requires_grad=True)
+    W = torch.zeros(16, 8, dtype=torch.bfloat16, requires_grad=True)
+    y = torch.zeros(4, dtype=torch.int64)
+    with pytest.raises((RuntimeError, ValueError, AssertionError)):
+        linear_cross_entropy(X, W, y)

@@ -1,0 +1,120 @@
+"""GPU parity of the autograd wrapper: loss and the gradients autograd
+delivers to X and W, against the float64 oracle, including a scaled loss
+gradient, accumulation into existing .grad, autocast and the nn.Module."""
+import numpy as np
+import pytest
+
+import workloads
+from flce_check import GRAD_RTOL, LOSS_RTOL, LSE_ATOL, rel_frob, to_np
+from oracle import flce_reference
+
+pytestmark = pytest.mark.gpu
+
+WL = workloads.WORKLOADS[2].with_shape(T=700, H=256, V=3000, seed=41)
+
+
+def leaves(inp, dtype):
+    import torch
+    X, W, y = workloads.to_torch(inp, "cuda")
+    X = X.to(dtype).detach().requires_grad_(True)
+    W = W.to(dtype).detach().requires_grad_(True)
+    return X, W, y
+
+
+def check_grads(X, W, ref, scale, dtype_name):
+    # W.grad comes back in W's dtype (bf16 rounds dW to 8 mantissa bits)
+    assert rel_frob(to_np(X.grad), scale * ref["dX"]) <= GRAD_RTOL[dtype_name]
+    assert rel_frob(to_np(W.grad), scale * ref["dW"]) <= GRAD_RTOL[dtype_name]
+
+
+def test_backward_matches_oracle():
+    import torch
+    from linear_cross_entropy_02_amd.autograd import linear_cross_entropy
+    inp = workloads.generate(WL)
+    X, W, y = leaves(inp, torch.bfloat16)
+    print(f"[gpu-autograd] {WL.name} T={WL.T} H={WL.H} V={WL.V}", flush=True)
+    loss, lse = linear_cross_entropy(X, W, y, WL.ignore_index, WL.reduction, chunk_tokens=256,
+                                     return_lse=True)
+    loss.backward()
+    torch.cuda.synchronize()
+    ref = flce_reference(inp.X, inp.W, inp.y, WL.ignore_index, WL.reduction)
+    assert abs(float(loss.detach()) - ref["loss"]) <= LOSS_RTOL * abs(ref["loss"])
+    assert np.abs(to_np(lse) - ref["lse"]).max() <= LSE_ATOL
+    assert X.grad.dtype == torch.bfloat16 and W.grad.dtype == torch.bfloat16
+    check_grads(X, W, ref, 1.0, "bf16")
+
+
+def test_scaled_loss_and_accumulation():
+    import torch
+    from linear_cross_entropy_02_amd.autograd import linear_cross_entropy
+    inp = workloads.generate(WL)
+    X, W, y = leaves(inp, torch.bfloat16)
+    ref = flce_reference(inp.X, inp.W, inp.y, WL.ignore_index, WL.reduction)
+    (2.5 * linear_cross_entropy(X, W, y, WL.ignore_index, WL.reduction)).backward()
+    check_grads(X, W, ref, 2.5, "bf16")
+    # a second backward accumulates into .grad
+    (-1.0 * linear_cross_entropy(X, W, y, WL.ignore_index, WL.reduction)).backward()
+    torch.cuda.synchronize()
+    check_grads(X, W, ref, 1.5, "bf16")
+
+
+def test_only_weight_requires_grad():
+    import torch
+    from linear_cross_entropy_02_amd.autograd import linear_cross_entropy
+    inp = workloads.generate(WL)
+    X, W, y = leaves(inp, torch.bfloat16)
+    X.requires_grad_(False)
+    linear_cross_entropy(X, W, y, WL.ignore_index, WL.reduction).backward()
+    ref = flce_reference(inp.X, inp.W, inp.y, WL.ignore_index, WL.reduction)
+    assert X.grad is None
+    assert rel_frob(to_np(W.grad), ref["dW"]) <= GRAD_RTOL["bf16"]
+
+
+def test_autocast_runs_the_bf16_path():
+    """fp32 leaves under autocast: the forward sees bf16 copies (the oracle
+    is fed the same rounded values) and the gradients flow back in fp32."""
+    import torch
+    from linear_cross_entropy_02_amd.autograd import linear_cross_entropy
+    inp = workloads.generate(WL)
+    X, W, y = leaves(inp, torch.float32)
+    with torch.autocast("cuda", dtype=torch.bfloat16):
+        loss = linear_cross_entropy(X, W, y, WL.ignore_index, WL.reduction)
+    loss.backward()
+    torch.cuda.synchronize()
+    assert X.grad.dtype == torch.float32 and W.grad.dtype == torch.float32
+    ref = flce_reference(inp.X, inp.W, inp.y, WL.ignore_index, WL.reduction)
+    assert abs(float(loss.detach()) - ref["loss"]) <= LOSS_RTOL * abs(ref["loss"])
+    check_grads(X, W, ref, 1.0, "bf16")
+
+
+def test_fp32_without_autocast():
+    import torch
+    from linear_cross_entropy_02_amd.autograd import linear_cross_entropy
+    wl = workloads.WORKLOADS[1]
+    inp = workloads.generate(wl)
+    X, W, y = leaves(inp, torch.float32)
+    loss = linear_cross_entropy(X, W, y, wl.ignore_index, wl.reduction)
+    loss.backward()
+    torch.cuda.synchronize()
+    ref = flce_reference(inp.X, inp.W, inp.y, wl.ignore_index, wl.reduction)
+    assert abs(float(loss.detach()) - ref["loss"]) <= LOSS_RTOL * abs(ref["loss"])
+    check_grads(X, W, ref, 1.0, "f32")
+
+
+def test_module_on_batched_hidden_states():
+    import torch
+    from linear_cross_entropy_02_amd.autograd import LinearCrossEntropy
+    inp = workloads.generate(WL)
+    X, W, y = workloads.to_torch(inp, "cuda")
+    head = LinearCrossEntropy(WL.H, WL.V, chunk_tokens=256)
+    with torch.no_grad():
+        head.weight.copy_(W)
+    hs = X.reshape(7, 100, WL.H).detach().requires_grad_(True)
+    loss = head(hs, y.reshape(7, 100))
+    loss.backward()
+    torch.cuda.synchronize()
+    ref = flce_reference(inp.X, inp.W, inp.y, WL.ignore_index, WL.reduction)
+    assert abs(float(loss.detach()) - ref["loss"]) <= LOSS_RTOL * abs(ref["loss"])
+    assert hs.grad.shape == (7, 100, WL.H)
+    assert rel_frob(to_np(hs.grad.reshape(-1, WL.H)), ref["dX"]) <= GRAD_RTOL["bf16"]
+    assert rel_frob(to_np(head.weight.grad), ref["dW"]) <= GRAD_RTOL["bf16"]
