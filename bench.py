@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fused linear-CE fwd+bwd tokens/s and % bf16 MFMA peak, H=4096 V=128256"
+METRIC_FWD = "forward-only per-token log-probs tokens/s and % bf16 MFMA peak, H=4096 V=128256"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA peaks, bf16 and fp32
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_JSON = os.path.join(PROFILES, "traffic.json")
@@ -63,6 +64,8 @@ def parse():
                         "more than 1 needs (1 + G) C V more workspace)")
     p.add_argument("--cpu-sample", type=int, default=256,
                    help="tokens of the workload the CPU oracle is timed on (0 = skip)")
+    p.add_argument("--forward-only", action="store_true",
+                   help="time flce_forward (per-token log-probs and loss, no gradients)")
     p.add_argument("--no-timing", action="store_true",
                    help="time without per-kernel events (no roofline)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -252,11 +255,21 @@ def main():
           flush=True)
     op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=args.chunk,
                                       dw_chunks=args.dw_chunks)
-    out = op.alloc_outputs(wl.T, "cuda")
+    fwd_only = args.forward_only
+    if fwd_only:
+        out = op.forward(X, W, y, wl.ignore_index, wl.reduction)
+
+        def step():
+            op.forward(X, W, y, wl.ignore_index, wl.reduction, out=out)
+    else:
+        out = op.alloc_outputs(wl.T, "cuda")
+
+        def step():
+            op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction, out=out)
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
-        op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction, out=out)
+        step()
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
@@ -271,7 +284,7 @@ def main():
     start.record(stream)
     marks[0].record(stream)
     for i in range(args.steps):
-        op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction, out=out)
+        step()
         marks[i + 1].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
@@ -284,7 +297,8 @@ def main():
     assert np.isfinite(loss), loss
 
     T, H, V = wl.T, wl.H, wl.V
-    flops = 6.0 * T * H * V
+    # fwd+bwd: three contractions of 2 T H V flops; forward only: the logits
+    flops = (2.0 if fwd_only else 6.0) * T * H * V
     tokens_per_s = T / (ms * 1e-3)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
@@ -307,7 +321,7 @@ def main():
             achieved = flop_per_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
             roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                         "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                        "traffic": measured_traffic(dom)}
+                        "traffic": None if fwd_only else measured_traffic(dom)}
         else:
             roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": 8000.0,
                         "unit": "GB/s", "frac": None, "traffic": None}
@@ -318,14 +332,15 @@ def main():
         ns = min(args.cpu_sample, T)
         threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
         t0 = time.time()
-        flce_reference(inp.X[:ns], inp.W, inp.y[:ns], wl.ignore_index, wl.reduction, chunk=256)
+        flce_reference(inp.X[:ns], inp.W, inp.y[:ns], wl.ignore_index, wl.reduction, chunk=256,
+                       want_grads=not fwd_only)
         dt = time.time() - t0
         cpu = {"value": round(ns / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"first {ns} of {T} tokens of {wl.name} (full W), float64 numpy oracle, "
                          f"{dt:.1f}s"}
 
     line = {
-        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC_FWD if fwd_only else METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic",

@@ -122,8 +122,33 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W,
                            float* lse, int32_t* argmax, int64_t* n_valid,
                            void* stream);
 
+/*
+ * Forward only: per-token log-probabilities of the targets and the reduced
+ * loss, without gradients (evaluation; the token log-prob ratios of
+ * policy-gradient methods).  "Alisa's book of LLMs", Mathy things >
+ * Information theory > implementing the loss: the per-token log-prob is the
+ * log-softmax at the target, z_target - lse, and the loss averages (or sums)
+ * its negation over the non-ignored tokens.
+ *
+ * Inputs as for flce_fwd_bwd.  Outputs (device, overwritten, each nullable):
+ *   loss           [1]  float32  reduced loss (reduction as for flce_fwd_bwd)
+ *   token_logprob  [T]  float32  z_target - lse; 0 for ignored tokens
+ *   lse            [T]  float32  per-token logsumexp
+ *   argmax         [T]  int32    per-token argmax of z, lowest index on ties
+ *   n_valid        [1]  int64    number of non-ignored tokens
+ * Only the logits GEMM and the merge of its partials run: no T x V or
+ * C x V values are written.  The handle's workspace is reused, so a handle
+ * must not run flce_forward and flce_fwd_bwd concurrently.  Out-of-range
+ * targets are treated as ignored and counted for flce_query_error.
+ * Returns without enqueuing anything on an argument error.
+ */
+flce_status_t flce_forward(flce_handle_t h, const void* X, const void* W, const int64_t* targets,
+                           int64_t T, int64_t ignore_index, int32_t reduction, float* loss,
+                           float* token_logprob, float* lse, int32_t* argmax, int64_t* n_valid,
+                           void* stream);
+
 /* Synchronise `stream` and read the number of out-of-range targets seen by
- * the last flce_fwd_bwd on this handle.  Returns FLCE_ERR_BAD_TARGET when it
+ * the last flce_fwd_bwd or flce_forward on this handle.  Returns FLCE_ERR_BAD_TARGET when it
  * is > 0, FLCE_OK otherwise.  bad_targets may be NULL. */
 flce_status_t flce_query_error(flce_handle_t h, void* stream, int64_t* bad_targets);
 

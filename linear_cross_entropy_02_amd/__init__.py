@@ -31,7 +31,7 @@ FLCE_MEAN = 1
 FLCE_SUM = 2
 
 EXPORTED = (
-    "flce_create", "flce_workspace_bytes", "flce_chunk_tokens", "flce_dw_chunks", "flce_fwd_bwd",
+    "flce_create", "flce_workspace_bytes", "flce_chunk_tokens", "flce_dw_chunks", "flce_fwd_bwd", "flce_forward",
     "flce_query_error", "flce_timing_enable", "flce_timing_kinds", "flce_timing_kind_name",
     "flce_timing_read", "flce_destroy", "flce_status_string", "flce_last_error",
 )
@@ -73,6 +73,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.flce_dw_chunks.restype = i32
     lib.flce_fwd_bwd.argtypes = [P, P, P, P, i64, i64, i32, P, P, P, P, P, P, P]
     lib.flce_fwd_bwd.restype = st
+    lib.flce_forward.argtypes = [P, P, P, P, i64, i64, i32, P, P, P, P, P, P]
+    lib.flce_forward.restype = st
     lib.flce_query_error.argtypes = [P, P, ctypes.POINTER(i64)]
     lib.flce_query_error.restype = st
     lib.flce_timing_enable.argtypes = [P, i32]
@@ -144,6 +146,18 @@ def flce_fwd_bwd(handle, X, W, targets, T: int, ignore_index: int, reduction: in
         stream = torch.cuda.current_stream().cuda_stream
     return load().flce_fwd_bwd(handle, _ptr(X), _ptr(W), _ptr(targets), T, ignore_index,
                                reduction, _ptr(loss), _ptr(dX), _ptr(dW), _ptr(lse),
+                               _ptr(argmax), _ptr(n_valid), stream)
+
+
+def flce_forward(handle, X, W, targets, T: int, ignore_index: int, reduction: int,
+                 loss=None, token_logprob=None, lse=None, argmax=None, n_valid=None,
+                 stream=None) -> int:
+    """Direct call of the forward-only entry point (see flce_fwd_bwd)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    return load().flce_forward(handle, _ptr(X), _ptr(W), _ptr(targets), T, ignore_index,
+                               reduction, _ptr(loss), _ptr(token_logprob), _ptr(lse),
                                _ptr(argmax), _ptr(n_valid), stream)
 
 
@@ -242,6 +256,29 @@ class FusedLinearCrossEntropy:
                           out["dW"], out.get("lse"), out.get("argmax"), out.get("n_valid"))
         if st != FLCE_OK:
             raise FlceError(st, "flce_fwd_bwd")
+        return out
+
+    def forward(self, X, W, y, ignore_index: int = -100, reduction: str = "mean", out=None):
+        """Forward only: loss, per-token log-prob of the target (0 where
+        ignored), lse, argmax and n_valid, without gradients."""
+        import torch
+        T = X.shape[0] if X is not None else 0
+        self._check(X, W, y, T)
+        if out is None:
+            dev = W.device
+            out = dict(
+                loss=torch.empty((), dtype=torch.float32, device=dev),
+                token_logprob=torch.empty((T,), dtype=torch.float32, device=dev),
+                lse=torch.empty((T,), dtype=torch.float32, device=dev),
+                argmax=torch.empty((T,), dtype=torch.int32, device=dev),
+                n_valid=torch.empty((), dtype=torch.int64, device=dev),
+            )
+        red = FLCE_MEAN if reduction == "mean" else FLCE_SUM if reduction == "sum" else -1
+        st = flce_forward(self.handle, X, W, y, T, ignore_index, red, out.get("loss"),
+                          out.get("token_logprob"), out.get("lse"), out.get("argmax"),
+                          out.get("n_valid"))
+        if st != FLCE_OK:
+            raise FlceError(st, "flce_forward")
         return out
 
     def _check(self, X, W, y, T):

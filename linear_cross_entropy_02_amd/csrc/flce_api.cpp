@@ -387,6 +387,8 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const 
     fa.scale = h->scale;
     fa.lse_out = lse ? lse + t0 : nullptr;
     fa.argmax_out = argmax ? argmax + t0 : nullptr;
+    fa.logprob_out = nullptr;
+    fa.backward = true;
     fa.loss_part = h->loss_part;
     fa.first_chunk = c == 0;
     FLCE_LAUNCH(K_FINALIZE, launch_finalize(fa, s));
@@ -469,6 +471,98 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const 
   }
   const int nparts = (int)cdiv64(T < C ? T : C, 32);  // finalize blocks of the first chunk
   FLCE_LAUNCH(K_LOSS, launch_loss(h->loss_part, nparts, h->nvalid, rsum, loss, s));
+#undef FLCE_LAUNCH
+  return FLCE_OK;
+}
+
+flce_status_t flce_forward(flce_handle_t h, const void* X, const void* W, const int64_t* targets,
+                           int64_t T, int64_t ignore_index, int32_t reduction, float* loss,
+                           float* token_logprob, float* lse, int32_t* argmax, int64_t* n_valid,
+                           void* stream) {
+  if (!h) return FLCE_ERR_INVALID_ARGUMENT;
+  if (T < 0) return FLCE_ERR_INVALID_ARGUMENT;
+  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!W) return FLCE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!X || !targets)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(W) || (T > 0 && !aligned16(X))) return FLCE_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)loss & 3u) || ((uintptr_t)token_logprob & 3u) || ((uintptr_t)lse & 3u) ||
+      ((uintptr_t)argmax & 3u) || ((uintptr_t)n_valid & 7u) || ((uintptr_t)targets & 7u))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != h->device) {
+    g_last_error = "flce_forward: current device differs from the handle's device";
+    return FLCE_ERR_INVALID_ARGUMENT;
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  const Dt dt = h->dt;
+  const size_t es = elem_size(dt);
+  const int64_t H = h->H, V = h->V, C = h->C, nt = h->nt;
+  const int rsum = reduction == FLCE_SUM ? 1 : 0;
+
+#define FLCE_LAUNCH(kind, expr)                                      \
+  do {                                                               \
+    hipError_t _e = timed(h, kind, s, [&] { return (expr); });       \
+    if (_e != hipSuccess) return hip_fail(_e, kKindNames[kind]);     \
+  } while (0)
+
+  FLCE_LAUNCH(K_COUNT, launch_count(targets, T, ignore_index, V, rsum, h->nvalid, h->scale, h->bad,
+                                    n_valid, s));
+  if (T == 0) {
+    if (loss) {
+      FLCE_LAUNCH(K_ZERO, launch_zero(h->loss_part, 8, s));
+      FLCE_LAUNCH(K_LOSS, launch_loss(h->loss_part, 1, h->nvalid, rsum, loss, s));
+    }
+    return FLCE_OK;
+  }
+  // Only the logits GEMM (its epilogue keeps the online-softmax partials
+  // and the target logit, nothing T x V-shaped) and the merge run.
+  for (int64_t t0 = 0, c = 0; t0 < T; t0 += C, ++c) {
+    const int64_t Cc = (T - t0 < C) ? (T - t0) : C;
+    LogitsArgs la{};
+    la.X = (const char*)X + (size_t)t0 * H * es;
+    la.W = W;
+    la.M = (int)Cc;
+    la.V = (int)V;
+    la.H = (int)H;
+    la.P = nullptr;
+    la.ldp = 0;
+    la.pm = h->pm;
+    la.ps = h->ps;
+    la.pa = h->pa;
+    la.ldr = C;
+    la.ztgt = h->ztgt;
+    la.y = targets + t0;
+    la.ignore_index = ignore_index;
+    FLCE_LAUNCH(K_LOGITS, launch_logits(dt, la, s));
+
+    FinalizeArgs fa{};
+    fa.M = (int)Cc;
+    fa.nt = (int)nt;
+    fa.V = (int)V;
+    fa.pm = h->pm;
+    fa.ps = h->ps;
+    fa.pa = h->pa;
+    fa.ldr = C;
+    fa.ztgt = h->ztgt;
+    fa.dzt = h->dzt;
+    fa.y = targets + t0;
+    fa.ignore_index = ignore_index;
+    fa.scale = h->scale;
+    fa.lse_out = lse ? lse + t0 : nullptr;
+    fa.argmax_out = argmax ? argmax + t0 : nullptr;
+    fa.logprob_out = token_logprob ? token_logprob + t0 : nullptr;
+    fa.backward = false;
+    fa.loss_part = h->loss_part;
+    fa.first_chunk = c == 0;
+    FLCE_LAUNCH(K_FINALIZE, launch_finalize(fa, s));
+  }
+  if (loss) {
+    const int nparts = (int)cdiv64(T < C ? T : C, 32);
+    FLCE_LAUNCH(K_LOSS, launch_loss(h->loss_part, nparts, h->nvalid, rsum, loss, s));
+  }
 #undef FLCE_LAUNCH
   return FLCE_OK;
 }

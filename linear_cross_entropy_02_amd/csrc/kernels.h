@@ -18,7 +18,7 @@ struct LogitsArgs {
   const void* X;        // chunk rows, [M x H]
   const void* W;        // [V x H]
   int M, V, H;
-  void* P;              // exp(z - m_tile), [M x ldp] in the input dtype
+  void* P;              // exp(z - m_tile), [M x ldp] in the input dtype; null: not stored
   int64_t ldp;
   float* pm;            // partial tile max         [nt x ldr], tile-major
   float* ps;            // partial tile sum of exp  [nt x ldr]
@@ -64,6 +64,8 @@ struct FinalizeArgs {
   const float* scale;
   float* lse_out;        // nullable, chunk-relative
   int32_t* argmax_out;   // nullable, chunk-relative
+  float* logprob_out;    // nullable, chunk-relative: z_target - lse (0 if ignored)
+  bool backward;         // also form dzt and turn pm into alpha
   double* loss_part;     // one slot per 32 rows
   int first_chunk;
 };

@@ -60,6 +60,7 @@ struct LogitsEpi {
   const int64_t* y;
   int64_t ignore_index;
   int M, V;
+  bool store_p;  // false: partials and target logit only (forward-only calls)
 
   template <int FM, int FN>
   __device__ __forceinline__ void init(f4 (&acc)[FM][FN], const EpiCoord&) const {
@@ -143,9 +144,11 @@ struct LogitsEpi {
           pa[o] = ai;
         }
         // columns up to the padded row length are allocated; those >= V get 0
-        T* const prow = P + (int64_t)row * ldp + lc0;
+        if (store_p) {
+          T* const prow = P + (int64_t)row * ldp + lc0;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) store4(prow + 16 * j, acc[i][j]);
+          for (int j = 0; j < FN; ++j) store4(prow + 16 * j, acc[i][j]);
+        }
       }
     }
   }
@@ -286,6 +289,7 @@ static hipError_t logits_t(const LogitsArgs& a, hipStream_t s) {
   epi.ignore_index = a.ignore_index;
   epi.M = a.M;
   epi.V = a.V;
+  epi.store_p = a.P != nullptr;
   return run_gemm<T, 256, 256, 4>(g, epi, s);
 }
 
@@ -496,8 +500,9 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
       const bool valid = target_valid(yt, a.ignore_index, a.V);
       sc = valid ? *a.scale : 0.f;
       const float zt = valid ? a.ztgt[row] : 0.f;
-      a.dzt[row] = valid ? sc * (exp_fast(zt - lse) - 1.f) : 0.f;
+      if (a.backward) a.dzt[row] = valid ? sc * (exp_fast(zt - lse) - 1.f) : 0.f;
       if (a.lse_out) a.lse_out[row] = lse;
+      if (a.logprob_out) a.logprob_out[row] = valid ? zt - lse : 0.f;
       nll = valid ? (double)lse - (double)zt : 0.0;
     }
     s_lse[rl] = lse;
@@ -505,8 +510,8 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
     s_nll[rl] = nll;
   }
   __syncthreads();
-  // pass 3: alpha
-  if (live) {
+  // pass 3: alpha (only when the gradient follows)
+  if (live && a.backward) {
     const float lse = s_lse[rl], sc = s_sc[rl];
     for (int j = sl; j < a.nt; j += kFinSlices) {
       const int64_t o = (int64_t)j * a.ldr + row;
