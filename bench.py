@@ -23,6 +23,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused linear-CE fwd+bwd tokens/s and % bf16 MFMA peak, H=4096 V=128256"
 METRIC_FWD = "forward-only per-token log-probs tokens/s and % bf16 MFMA peak, H=4096 V=128256"
+METRIC_SHARD = ("vocabulary-parallel shard (1 of {n}) fwd+bwd tokens/s and % bf16 MFMA peak, "
+                "H=4096 V=128256")
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA peaks, bf16 and fp32
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_JSON = os.path.join(PROFILES, "traffic.json")
@@ -64,6 +66,10 @@ def parse():
                         "more than 1 needs (1 + G) C V more workspace)")
     p.add_argument("--cpu-sample", type=int, default=256,
                    help="tokens of the workload the CPU oracle is timed on (0 = skip)")
+    p.add_argument("--vocab-shards", type=int, default=1, metavar="N",
+                   help="time one device's share of an N-way vocabulary-parallel head: "
+                        "flce_vocab_shard_forward + flce_vocab_shard_backward on V/N rows "
+                        "(the collectives between them are not part of the step)")
     p.add_argument("--forward-only", action="store_true",
                    help="time flce_forward (per-token log-probs and loss, no gradients)")
     p.add_argument("--no-timing", action="store_true",
@@ -253,10 +259,36 @@ def main():
     X, W, y = workloads.to_torch(inp, "cuda")
     print(f"[bench] inputs for {wl.name} ready in {time.time() - t_gen:.1f}s", file=sys.stderr,
           flush=True)
-    op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=args.chunk,
-                                      dw_chunks=args.dw_chunks)
+    n_shards = max(1, args.vocab_shards)
     fwd_only = args.forward_only
-    if fwd_only:
+    if n_shards > 1:
+        # the whole vocabulary's lse, as the collectives after step 1 would give it
+        full = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=args.chunk)
+        lse_g = full.forward(X, W, y, wl.ignore_index, wl.reduction)["lse"]
+        full.close()
+        Vs = wl.V // n_shards
+        Ws = W[:Vs].contiguous()
+        op = flce.FusedLinearCrossEntropy(wl.H, Vs, wl.dtype, chunk_tokens=args.chunk,
+                                          dw_chunks=args.dw_chunks)
+        red = flce.FLCE_MEAN if wl.reduction == "mean" else flce.FLCE_SUM
+        parts = [torch.empty(wl.T, device="cuda") for _ in range(3)]
+        amax = torch.empty(wl.T, dtype=torch.int32, device="cuda")
+        dXp = torch.empty(wl.T, wl.H, dtype=X.dtype, device="cuda")
+        dWs = torch.empty(Vs, wl.H, dtype=torch.float32, device="cuda")
+        out = {"loss": lse_g[:1]}
+
+        def step():
+            st1 = flce.flce_vocab_shard_forward(op.handle, X, Ws, y, wl.T, wl.ignore_index, 0,
+                                                wl.V, parts[0], parts[1], amax, parts[2])
+            st2 = flce.flce_vocab_shard_backward(op.handle, X, Ws, y, wl.T, wl.ignore_index, 0,
+                                                 wl.V, red, lse_g, dXp, dWs)
+            assert st1 == flce.FLCE_OK and st2 == flce.FLCE_OK, (st1, st2)
+    else:
+        op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=args.chunk,
+                                          dw_chunks=args.dw_chunks)
+    if n_shards > 1:
+        pass  # step() is set above
+    elif fwd_only:
         out = op.forward(X, W, y, wl.ignore_index, wl.reduction)
 
         def step():
@@ -297,8 +329,12 @@ def main():
     assert np.isfinite(loss), loss
 
     T, H, V = wl.T, wl.H, wl.V
-    # fwd+bwd: three contractions of 2 T H V flops; forward only: the logits
-    flops = (2.0 if fwd_only else 6.0) * T * H * V
+    # fwd+bwd: three contractions of 2 T H V flops; forward only: the logits;
+    # a vocabulary shard: its logits twice (step 1 and the recompute in
+    # step 2) and its dX and dW contributions, over V / N columns
+    if n_shards > 1:
+        V = V // n_shards
+    flops = (8.0 if n_shards > 1 else 2.0 if fwd_only else 6.0) * T * H * V
     tokens_per_s = T / (ms * 1e-3)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
@@ -315,19 +351,22 @@ def main():
         flce.flce_timing_enable(op.handle, False)
         dom = max(kernels, key=lambda k: kernels[k]["total_ms"])
         if dom in ("logits_gemm", "dx_gemm", "dw_gemm"):
-            # each of the three contractions does 2 T H V flops per step, split
-            # over its launches (one per chunk; one per dW group for dW)
-            flop_per_launch = 2.0 * T * H * V / kernels[dom]["launches_per_step"]
+            # each of the contractions does 2 T H V flops per step, split over
+            # its launches (one per chunk; one per dW group for dW); a
+            # vocabulary shard runs its logits GEMM twice per step
+            nrep = 2.0 if (n_shards > 1 and dom == "logits_gemm") else 1.0
+            flop_per_launch = nrep * 2.0 * T * H * V / kernels[dom]["launches_per_step"]
             achieved = flop_per_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
             roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                         "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                        "traffic": None if fwd_only else measured_traffic(dom)}
+                        "traffic": None if (fwd_only or n_shards > 1) else
+                        measured_traffic(dom)}
         else:
             roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": 8000.0,
                         "unit": "GB/s", "frac": None, "traffic": None}
 
     cpu = None
-    if args.cpu_sample > 0:
+    if args.cpu_sample > 0 and n_shards == 1:
         from oracle import flce_reference
         ns = min(args.cpu_sample, T)
         threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
@@ -340,12 +379,13 @@ def main():
                          f"{dt:.1f}s"}
 
     line = {
-        "metric": METRIC_FWD if fwd_only else METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": (METRIC_SHARD.format(n=n_shards) if n_shards > 1 else
+                   METRIC_FWD if fwd_only else METRIC), "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "H": H, "V": V, "chunk_tokens": op.chunk_tokens,
-                   "dw_chunks": op.dw_chunks,
+                   "dw_chunks": op.dw_chunks, "vocab_shards": n_shards, "V_total": wl.V,
                    "reduction": wl.reduction, "ignore_frac": wl.ignore_frac,
                    "targets": wl.targets},
         "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / peak, 4),

@@ -147,6 +147,49 @@ flce_status_t flce_forward(flce_handle_t h, const void* X, const void* W, const 
                            float* token_logprob, float* lse, int32_t* argmax, int64_t* n_valid,
                            void* stream);
 
+/*
+ * Vocabulary-parallel building blocks.  With W split by rows over G devices
+ * (a column-parallel lm_head), each device holds W_shard = W[vocab_offset :
+ * vocab_offset + V] (V as given to flce_create) and runs two calls around the
+ * caller's collectives.  The per-shard (max, sum of exp) pairs merge exactly
+ * like the online-softmax partials of "Alisa's book of LLMs", Numerical
+ * stability and other tricks: the global lse is M + ln sum_s sumexp_s
+ * exp(m_s - M) with M = max_s m_s.  Targets are replicated: a target is valid
+ * when it is not ignore_index and lies in [0, vocab_total); the shard holding
+ * it "owns" it.
+ *
+ * Step 1, flce_vocab_shard_forward: per token of this shard's columns
+ *   m        [T] float32  max logit (required)
+ *   sumexp   [T] float32  sum of exp(z - m) (required)
+ *   argmax   [T] int32    global id of the first max (nullable)
+ *   ztarget  [T] float32  the target's logit if this shard owns the target,
+ *                         else 0 -- a sum over shards gives z_target (required)
+ * The caller then all-reduces: M = max m, sumexp * exp(m - M) summed, ztarget
+ * summed; lse = M + ln(sum), loss = s * sum_t valid_t (lse_t - ztarget_t).
+ *
+ * Step 2, flce_vocab_shard_backward, given that global lse [T]:
+ *   dX_partial [T x H] dtype   this shard's dZ W_shard; summed over shards
+ *                              by the caller, it is dX
+ *   dW_shard   [V x H] float32 this shard's rows of dW (complete)
+ * with dZ = s valid (exp(z - lse) - onehot) as for flce_fwd_bwd and s from
+ * `reduction` over the valid targets.  Step 2 recomputes the shard's logits
+ * (the call keeps nothing of step 1), so a vocabulary-parallel step costs
+ * 8 T H V_shard flops per device instead of 6.
+ *
+ * Both return INVALID_ARGUMENT, with nothing enqueued, for a shard outside
+ * [0, vocab_total) or vocab_total >= 2^31, and as flce_fwd_bwd otherwise.
+ */
+flce_status_t flce_vocab_shard_forward(flce_handle_t h, const void* X, const void* W_shard,
+                                       const int64_t* targets, int64_t T, int64_t ignore_index,
+                                       int64_t vocab_offset, int64_t vocab_total, float* m,
+                                       float* sumexp, int32_t* argmax, float* ztarget,
+                                       void* stream);
+flce_status_t flce_vocab_shard_backward(flce_handle_t h, const void* X, const void* W_shard,
+                                        const int64_t* targets, int64_t T, int64_t ignore_index,
+                                        int64_t vocab_offset, int64_t vocab_total,
+                                        int32_t reduction, const float* lse, void* dX_partial,
+                                        float* dW_shard, void* stream);
+
 /* Synchronise `stream` and read the number of out-of-range targets seen by
  * the last flce_fwd_bwd or flce_forward on this handle.  Returns FLCE_ERR_BAD_TARGET when it
  * is > 0, FLCE_OK otherwise.  bad_targets may be NULL. */

@@ -32,6 +32,7 @@ FLCE_SUM = 2
 
 EXPORTED = (
     "flce_create", "flce_workspace_bytes", "flce_chunk_tokens", "flce_dw_chunks", "flce_fwd_bwd", "flce_forward",
+    "flce_vocab_shard_forward", "flce_vocab_shard_backward",
     "flce_query_error", "flce_timing_enable", "flce_timing_kinds", "flce_timing_kind_name",
     "flce_timing_read", "flce_destroy", "flce_status_string", "flce_last_error",
 )
@@ -75,6 +76,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.flce_fwd_bwd.restype = st
     lib.flce_forward.argtypes = [P, P, P, P, i64, i64, i32, P, P, P, P, P, P]
     lib.flce_forward.restype = st
+    lib.flce_vocab_shard_forward.argtypes = [P, P, P, P, i64, i64, i64, i64, P, P, P, P, P]
+    lib.flce_vocab_shard_forward.restype = st
+    lib.flce_vocab_shard_backward.argtypes = [P, P, P, P, i64, i64, i64, i64, i32, P, P, P, P]
+    lib.flce_vocab_shard_backward.restype = st
     lib.flce_query_error.argtypes = [P, P, ctypes.POINTER(i64)]
     lib.flce_query_error.restype = st
     lib.flce_timing_enable.argtypes = [P, i32]
@@ -159,6 +164,28 @@ def flce_forward(handle, X, W, targets, T: int, ignore_index: int, reduction: in
     return load().flce_forward(handle, _ptr(X), _ptr(W), _ptr(targets), T, ignore_index,
                                reduction, _ptr(loss), _ptr(token_logprob), _ptr(lse),
                                _ptr(argmax), _ptr(n_valid), stream)
+
+
+def flce_vocab_shard_forward(handle, X, W_shard, targets, T: int, ignore_index: int,
+                             vocab_offset: int, vocab_total: int, m, sumexp, argmax, ztarget,
+                             stream=None) -> int:
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    return load().flce_vocab_shard_forward(handle, _ptr(X), _ptr(W_shard), _ptr(targets), T,
+                                           ignore_index, vocab_offset, vocab_total, _ptr(m),
+                                           _ptr(sumexp), _ptr(argmax), _ptr(ztarget), stream)
+
+
+def flce_vocab_shard_backward(handle, X, W_shard, targets, T: int, ignore_index: int,
+                              vocab_offset: int, vocab_total: int, reduction: int, lse,
+                              dX_partial, dW_shard, stream=None) -> int:
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    return load().flce_vocab_shard_backward(handle, _ptr(X), _ptr(W_shard), _ptr(targets), T,
+                                            ignore_index, vocab_offset, vocab_total, reduction,
+                                            _ptr(lse), _ptr(dX_partial), _ptr(dW_shard), stream)
 
 
 def flce_query_error(handle, stream=None):
@@ -280,6 +307,40 @@ class FusedLinearCrossEntropy:
         if st != FLCE_OK:
             raise FlceError(st, "flce_forward")
         return out
+
+    def shard_forward(self, X, W_shard, y, vocab_offset: int, vocab_total: int,
+                      ignore_index: int = -100):
+        """Vocabulary shard, step 1: per-token (m, sumexp, global argmax,
+        ztarget) of this shard's columns."""
+        import torch
+        T = X.shape[0]
+        self._check(X, W_shard, y, T)
+        dev = W_shard.device
+        out = {k: torch.empty((T,), dtype=torch.float32, device=dev)
+               for k in ("m", "sumexp", "ztarget")}
+        out["argmax"] = torch.empty((T,), dtype=torch.int32, device=dev)
+        st = flce_vocab_shard_forward(self.handle, X, W_shard, y, T, ignore_index, vocab_offset,
+                                      vocab_total, out["m"], out["sumexp"], out["argmax"],
+                                      out["ztarget"])
+        if st != FLCE_OK:
+            raise FlceError(st, "flce_vocab_shard_forward")
+        return out
+
+    def shard_backward(self, X, W_shard, y, lse, vocab_offset: int, vocab_total: int,
+                       ignore_index: int = -100, reduction: str = "mean"):
+        """Vocabulary shard, step 2: this shard's dX contribution and its rows
+        of dW, given the whole vocabulary's lse."""
+        import torch
+        T = X.shape[0]
+        self._check(X, W_shard, y, T)
+        dX = torch.empty((T, self.hidden), dtype=self.torch_dtype, device=X.device)
+        dW = torch.empty((self.vocab, self.hidden), dtype=torch.float32, device=X.device)
+        red = FLCE_MEAN if reduction == "mean" else FLCE_SUM if reduction == "sum" else -1
+        st = flce_vocab_shard_backward(self.handle, X, W_shard, y, T, ignore_index, vocab_offset,
+                                       vocab_total, red, lse, dX, dW)
+        if st != FLCE_OK:
+            raise FlceError(st, "flce_vocab_shard_backward")
+        return dX, dW
 
     def _check(self, X, W, y, T):
         if W.dtype != self.torch_dtype or tuple(W.shape) != (self.vocab, self.hidden):

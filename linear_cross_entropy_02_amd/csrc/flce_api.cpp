@@ -293,28 +293,35 @@ flce_status_t flce_destroy(flce_handle_t h) {
   return FLCE_OK;
 }
 
-flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const int64_t* targets,
-                           int64_t T, int64_t ignore_index, int32_t reduction, float* loss,
-                           void* dX, float* dW, float* lse, int32_t* argmax, int64_t* n_valid,
-                           void* stream) {
-  if (!h) return FLCE_ERR_INVALID_ARGUMENT;
-  if (T < 0) return FLCE_ERR_INVALID_ARGUMENT;
-  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARGUMENT;
-  if (!W || !loss || !dW) return FLCE_ERR_INVALID_ARGUMENT;
-  if (T > 0 && (!X || !targets || !dX)) return FLCE_ERR_INVALID_ARGUMENT;
-  if (!aligned16(W) || !aligned16(dW) || (T > 0 && (!aligned16(X) || !aligned16(dX))))
-    return FLCE_ERR_INVALID_ARGUMENT;
-  if (((uintptr_t)loss & 3u) || ((uintptr_t)lse & 3u) || ((uintptr_t)argmax & 3u) ||
-      ((uintptr_t)n_valid & 7u) || ((uintptr_t)targets & 7u))
-    return FLCE_ERR_INVALID_ARGUMENT;
+namespace {
+
+// Columns this call sees: W's rows are vocabulary ids [y_shift, y_shift + V)
+// of a vocabulary of v_total ids (y_shift = 0, v_total = V unless W is a
+// vocabulary shard).  lse_in, when given, replaces the lse of these columns
+// by the whole vocabulary's.
+struct Cols {
+  int64_t y_shift;
+  int64_t v_total;
+  const float* lse_in;
+};
+
+flce_status_t check_device(flce_handle_t h, const char* who) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (dev != h->device) {
-    g_last_error = "flce_fwd_bwd: current device differs from the handle's device";
+    g_last_error = std::string(who) + ": current device differs from the handle's device";
     return FLCE_ERR_INVALID_ARGUMENT;
   }
+  return FLCE_OK;
+}
 
+bool misaligned(const void* p, uintptr_t mask) { return ((uintptr_t)p & mask) != 0; }
+
+flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const int64_t* targets,
+                          int64_t T, int64_t ignore_index, int32_t reduction, float* loss,
+                          void* dX, float* dW, float* lse, int32_t* argmax, int64_t* n_valid,
+                          const Cols& cols, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const Dt dt = h->dt;
   const size_t es = elem_size(dt);
@@ -328,12 +335,14 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const 
     if (_e != hipSuccess) return hip_fail(_e, kKindNames[kind]);     \
   } while (0)
 
-  FLCE_LAUNCH(K_COUNT, launch_count(targets, T, ignore_index, V, rsum, h->nvalid, h->scale, h->bad,
-                                    n_valid, s));
+  FLCE_LAUNCH(K_COUNT, launch_count(targets, T, ignore_index, cols.v_total, rsum, h->nvalid,
+                                    h->scale, h->bad, n_valid, s));
   if (T == 0) {
     FLCE_LAUNCH(K_ZERO, launch_zero(dW, (size_t)V * H * 4, s));
-    FLCE_LAUNCH(K_ZERO, launch_zero(h->loss_part, 8, s));
-    FLCE_LAUNCH(K_LOSS, launch_loss(h->loss_part, 1, h->nvalid, rsum, loss, s));
+    if (loss) {
+      FLCE_LAUNCH(K_ZERO, launch_zero(h->loss_part, 8, s));
+      FLCE_LAUNCH(K_LOSS, launch_loss(h->loss_part, 1, h->nvalid, rsum, loss, s));
+    }
     return FLCE_OK;
   }
 
@@ -370,6 +379,7 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const 
     la.ztgt = h->ztgt;
     la.y = yc;
     la.ignore_index = ignore_index;
+    la.y_shift = cols.y_shift;
     FLCE_LAUNCH(K_LOGITS, launch_logits(dt, la, s));
 
     FinalizeArgs fa{};
@@ -388,6 +398,9 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const 
     fa.lse_out = lse ? lse + t0 : nullptr;
     fa.argmax_out = argmax ? argmax + t0 : nullptr;
     fa.logprob_out = nullptr;
+    fa.y_shift = cols.y_shift;
+    fa.v_total = cols.v_total;
+    fa.lse_in = cols.lse_in ? cols.lse_in + t0 : nullptr;
     fa.backward = true;
     fa.loss_part = h->loss_part;
     fa.first_chunk = c == 0;
@@ -408,6 +421,7 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const 
     xa.dzt = h->dzt;
     xa.y = yc;
     xa.ignore_index = ignore_index;
+    xa.y_shift = cols.y_shift;
     FLCE_LAUNCH(K_FIXUP, launch_fixup(dt, xa, s));
 
     // dX_c = dZ W   (M = Cc, N = H, K = vocabulary)
@@ -469,33 +483,19 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const 
       FLCE_LAUNCH(K_DW, launch_gemm_store(dt, tc, ga, s));
     }
   }
-  const int nparts = (int)cdiv64(T < C ? T : C, 32);  // finalize blocks of the first chunk
-  FLCE_LAUNCH(K_LOSS, launch_loss(h->loss_part, nparts, h->nvalid, rsum, loss, s));
+  if (loss) {
+    const int nparts = (int)cdiv64(T < C ? T : C, 32);  // finalize blocks of the first chunk
+    FLCE_LAUNCH(K_LOSS, launch_loss(h->loss_part, nparts, h->nvalid, rsum, loss, s));
+  }
 #undef FLCE_LAUNCH
   return FLCE_OK;
 }
 
-flce_status_t flce_forward(flce_handle_t h, const void* X, const void* W, const int64_t* targets,
-                           int64_t T, int64_t ignore_index, int32_t reduction, float* loss,
-                           float* token_logprob, float* lse, int32_t* argmax, int64_t* n_valid,
-                           void* stream) {
-  if (!h) return FLCE_ERR_INVALID_ARGUMENT;
-  if (T < 0) return FLCE_ERR_INVALID_ARGUMENT;
-  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARGUMENT;
-  if (!W) return FLCE_ERR_INVALID_ARGUMENT;
-  if (T > 0 && (!X || !targets)) return FLCE_ERR_INVALID_ARGUMENT;
-  if (!aligned16(W) || (T > 0 && !aligned16(X))) return FLCE_ERR_INVALID_ARGUMENT;
-  if (((uintptr_t)loss & 3u) || ((uintptr_t)token_logprob & 3u) || ((uintptr_t)lse & 3u) ||
-      ((uintptr_t)argmax & 3u) || ((uintptr_t)n_valid & 7u) || ((uintptr_t)targets & 7u))
-    return FLCE_ERR_INVALID_ARGUMENT;
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (dev != h->device) {
-    g_last_error = "flce_forward: current device differs from the handle's device";
-    return FLCE_ERR_INVALID_ARGUMENT;
-  }
-
+flce_status_t run_forward(flce_handle_t h, const void* X, const void* W, const int64_t* targets,
+                          int64_t T, int64_t ignore_index, int32_t reduction, float* loss,
+                          float* token_logprob, float* lse, int32_t* argmax, int64_t* n_valid,
+                          float* m_out, float* sum_out, float* zt_out, const Cols& cols,
+                          void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const Dt dt = h->dt;
   const size_t es = elem_size(dt);
@@ -508,8 +508,8 @@ flce_status_t flce_forward(flce_handle_t h, const void* X, const void* W, const 
     if (_e != hipSuccess) return hip_fail(_e, kKindNames[kind]);     \
   } while (0)
 
-  FLCE_LAUNCH(K_COUNT, launch_count(targets, T, ignore_index, V, rsum, h->nvalid, h->scale, h->bad,
-                                    n_valid, s));
+  FLCE_LAUNCH(K_COUNT, launch_count(targets, T, ignore_index, cols.v_total, rsum, h->nvalid,
+                                    h->scale, h->bad, n_valid, s));
   if (T == 0) {
     if (loss) {
       FLCE_LAUNCH(K_ZERO, launch_zero(h->loss_part, 8, s));
@@ -536,6 +536,7 @@ flce_status_t flce_forward(flce_handle_t h, const void* X, const void* W, const 
     la.ztgt = h->ztgt;
     la.y = targets + t0;
     la.ignore_index = ignore_index;
+    la.y_shift = cols.y_shift;
     FLCE_LAUNCH(K_LOGITS, launch_logits(dt, la, s));
 
     FinalizeArgs fa{};
@@ -554,6 +555,12 @@ flce_status_t flce_forward(flce_handle_t h, const void* X, const void* W, const 
     fa.lse_out = lse ? lse + t0 : nullptr;
     fa.argmax_out = argmax ? argmax + t0 : nullptr;
     fa.logprob_out = token_logprob ? token_logprob + t0 : nullptr;
+    fa.y_shift = cols.y_shift;
+    fa.v_total = cols.v_total;
+    fa.lse_in = nullptr;
+    fa.m_out = m_out ? m_out + t0 : nullptr;
+    fa.sum_out = sum_out ? sum_out + t0 : nullptr;
+    fa.zt_out = zt_out ? zt_out + t0 : nullptr;
     fa.backward = false;
     fa.loss_part = h->loss_part;
     fa.first_chunk = c == 0;
@@ -565,6 +572,94 @@ flce_status_t flce_forward(flce_handle_t h, const void* X, const void* W, const 
   }
 #undef FLCE_LAUNCH
   return FLCE_OK;
+}
+
+}  // namespace
+
+flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const int64_t* targets,
+                           int64_t T, int64_t ignore_index, int32_t reduction, float* loss,
+                           void* dX, float* dW, float* lse, int32_t* argmax, int64_t* n_valid,
+                           void* stream) {
+  if (!h) return FLCE_ERR_INVALID_ARGUMENT;
+  if (T < 0) return FLCE_ERR_INVALID_ARGUMENT;
+  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!W || !loss || !dW) return FLCE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!X || !targets || !dX)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(W) || !aligned16(dW) || (T > 0 && (!aligned16(X) || !aligned16(dX))))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  if (misaligned(loss, 3) || misaligned(lse, 3) || misaligned(argmax, 3) ||
+      misaligned(n_valid, 7) || misaligned(targets, 7))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  const flce_status_t st = check_device(h, "flce_fwd_bwd");
+  if (st != FLCE_OK) return st;
+  return run_fwd_bwd(h, X, W, targets, T, ignore_index, reduction, loss, dX, dW, lse, argmax,
+                     n_valid, Cols{0, h->V, nullptr}, stream);
+}
+
+flce_status_t flce_forward(flce_handle_t h, const void* X, const void* W, const int64_t* targets,
+                           int64_t T, int64_t ignore_index, int32_t reduction, float* loss,
+                           float* token_logprob, float* lse, int32_t* argmax, int64_t* n_valid,
+                           void* stream) {
+  if (!h) return FLCE_ERR_INVALID_ARGUMENT;
+  if (T < 0) return FLCE_ERR_INVALID_ARGUMENT;
+  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!W) return FLCE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!X || !targets)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(W) || (T > 0 && !aligned16(X))) return FLCE_ERR_INVALID_ARGUMENT;
+  if (misaligned(loss, 3) || misaligned(token_logprob, 3) || misaligned(lse, 3) ||
+      misaligned(argmax, 3) || misaligned(n_valid, 7) || misaligned(targets, 7))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  const flce_status_t st = check_device(h, "flce_forward");
+  if (st != FLCE_OK) return st;
+  return run_forward(h, X, W, targets, T, ignore_index, reduction, loss, token_logprob, lse,
+                     argmax, n_valid, nullptr, nullptr, nullptr, Cols{0, h->V, nullptr}, stream);
+}
+
+// A shard's columns must lie inside the vocabulary.
+static bool bad_shard(flce_handle_t h, int64_t vocab_offset, int64_t vocab_total) {
+  return vocab_offset < 0 || vocab_total < h->V || vocab_offset > vocab_total - h->V ||
+         vocab_total > ((int64_t)1 << 31) - 1;
+}
+
+flce_status_t flce_vocab_shard_forward(flce_handle_t h, const void* X, const void* W_shard,
+                                       const int64_t* targets, int64_t T, int64_t ignore_index,
+                                       int64_t vocab_offset, int64_t vocab_total, float* m,
+                                       float* sumexp, int32_t* argmax, float* ztarget,
+                                       void* stream) {
+  if (!h) return FLCE_ERR_INVALID_ARGUMENT;
+  if (T < 0 || bad_shard(h, vocab_offset, vocab_total)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!W_shard) return FLCE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!X || !targets || !m || !sumexp || !ztarget)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(W_shard) || (T > 0 && !aligned16(X))) return FLCE_ERR_INVALID_ARGUMENT;
+  if (misaligned(m, 3) || misaligned(sumexp, 3) || misaligned(argmax, 3) ||
+      misaligned(ztarget, 3) || misaligned(targets, 7))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  const flce_status_t st = check_device(h, "flce_vocab_shard_forward");
+  if (st != FLCE_OK) return st;
+  return run_forward(h, X, W_shard, targets, T, ignore_index, FLCE_SUM, nullptr, nullptr, nullptr,
+                     argmax, nullptr, m, sumexp, ztarget, Cols{vocab_offset, vocab_total, nullptr},
+                     stream);
+}
+
+flce_status_t flce_vocab_shard_backward(flce_handle_t h, const void* X, const void* W_shard,
+                                        const int64_t* targets, int64_t T, int64_t ignore_index,
+                                        int64_t vocab_offset, int64_t vocab_total,
+                                        int32_t reduction, const float* lse, void* dX_partial,
+                                        float* dW_shard, void* stream) {
+  if (!h) return FLCE_ERR_INVALID_ARGUMENT;
+  if (T < 0 || bad_shard(h, vocab_offset, vocab_total)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!W_shard || !dW_shard) return FLCE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!X || !targets || !lse || !dX_partial)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(W_shard) || !aligned16(dW_shard) ||
+      (T > 0 && (!aligned16(X) || !aligned16(dX_partial))))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  if (misaligned(lse, 3) || misaligned(targets, 7)) return FLCE_ERR_INVALID_ARGUMENT;
+  const flce_status_t st = check_device(h, "flce_vocab_shard_backward");
+  if (st != FLCE_OK) return st;
+  return run_fwd_bwd(h, X, W_shard, targets, T, ignore_index, reduction, nullptr, dX_partial,
+                     dW_shard, nullptr, nullptr, nullptr, Cols{vocab_offset, vocab_total, lse},
+                     stream);
 }
 
 flce_status_t flce_query_error(flce_handle_t h, void* stream, int64_t* bad_targets) {

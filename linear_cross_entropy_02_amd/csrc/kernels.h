@@ -27,6 +27,7 @@ struct LogitsArgs {
   float* ztgt;          // logit of the target, [M]
   const int64_t* y;     // chunk targets, [M]
   int64_t ignore_index;
+  int64_t y_shift;      // vocabulary id of W's row 0 (0 unless W is a vocabulary shard)
 };
 // Width in columns of one online-logsumexp partial (the wave tile width of
 // the 256 x 256 logits GEMM).
@@ -61,6 +62,12 @@ struct FinalizeArgs {
   const float* ztgt;
   float* dzt;
   const int64_t* y; int64_t ignore_index;
+  int64_t y_shift;       // vocabulary id of column 0 (shard offset; argmax_out adds it)
+  int64_t v_total;       // whole vocabulary, for target validity
+  const float* lse_in;   // nullable: the whole vocabulary's lse, given (shard backward)
+  float* m_out;          // nullable: max over these columns
+  float* sum_out;        // nullable: sum of exp(z - max) over these columns
+  float* zt_out;         // nullable: target logit if these columns hold it, else 0
   const float* scale;
   float* lse_out;        // nullable, chunk-relative
   int32_t* argmax_out;   // nullable, chunk-relative
@@ -81,6 +88,7 @@ struct FixupArgs {
   const float* alpha;            // [nt x ldr], tile-major
   const float* dzt;              // [M]
   const int64_t* y; int64_t ignore_index;
+  int64_t y_shift;               // vocabulary id of column 0 (shard offset)
 };
 hipError_t launch_fixup(Dt dt, const FixupArgs& a, hipStream_t s);
 

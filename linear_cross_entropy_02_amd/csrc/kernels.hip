@@ -59,6 +59,7 @@ struct LogitsEpi {
   float* ztgt;
   const int64_t* y;
   int64_t ignore_index;
+  int64_t y_shift;  // vocabulary id of column 0 (a vocabulary shard's offset)
   int M, V;
   bool store_p;  // false: partials and target logit only (forward-only calls)
 
@@ -80,8 +81,9 @@ struct LogitsEpi {
     for (int i = 0; i < FM; ++i) {
       const int row = ec.row0 + 16 * i + c;
       const int64_t yt = row < M ? y[row] : ignore_index;
-      const int64_t off = yt - lc0;
-      toff[i] = (target_valid(yt, ignore_index, V) && off >= 0 && off < 16 * FN && (off & 12) == 0)
+      const int64_t off = yt - y_shift - lc0;
+      toff[i] = (yt != ignore_index && off >= 0 && off < 16 * FN && (off & 12) == 0 &&
+                 lc0 + off < V)
                     ? (int)off : -1;
     }
 #pragma unroll
@@ -287,6 +289,7 @@ static hipError_t logits_t(const LogitsArgs& a, hipStream_t s) {
   epi.ztgt = a.ztgt;
   epi.y = a.y;
   epi.ignore_index = a.ignore_index;
+  epi.y_shift = a.y_shift;
   epi.M = a.M;
   epi.V = a.V;
   epi.store_p = a.P != nullptr;
@@ -476,7 +479,7 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
       }
     }
     s_m[rl] = m;
-    if (live && a.argmax_out) a.argmax_out[row] = am;
+    if (live && a.argmax_out) a.argmax_out[row] = am == 0x7fffffff ? am : am + (int)a.y_shift;
   }
   __syncthreads();
   // pass 2: rescaled sum
@@ -495,14 +498,21 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
     float lse = 0.f, sc = 0.f;
     if (live) {
       for (int k = 1; k < kFinSlices; ++k) sum += s_f[k][rl];
-      lse = m + log_fast(sum);
+      // validity against the whole vocabulary; ownership of the target by
+      // these columns (all of them unless this is a vocabulary shard)
       const int64_t yt = a.y[row];
-      const bool valid = target_valid(yt, a.ignore_index, a.V);
+      const bool valid = target_valid(yt, a.ignore_index, a.v_total);
+      const int64_t yl = yt - a.y_shift;
+      const bool owned = valid && yl >= 0 && yl < a.V;
+      lse = a.lse_in ? a.lse_in[row] : m + log_fast(sum);
       sc = valid ? *a.scale : 0.f;
-      const float zt = valid ? a.ztgt[row] : 0.f;
-      if (a.backward) a.dzt[row] = valid ? sc * (exp_fast(zt - lse) - 1.f) : 0.f;
+      const float zt = owned ? a.ztgt[row] : 0.f;
+      if (a.backward) a.dzt[row] = owned ? sc * (exp_fast(zt - lse) - 1.f) : 0.f;
       if (a.lse_out) a.lse_out[row] = lse;
       if (a.logprob_out) a.logprob_out[row] = valid ? zt - lse : 0.f;
+      if (a.m_out) a.m_out[row] = m;
+      if (a.sum_out) a.sum_out[row] = sum;
+      if (a.zt_out) a.zt_out[row] = zt;
       nll = valid ? (double)lse - (double)zt : 0.0;
     }
     s_lse[rl] = lse;
@@ -560,10 +570,11 @@ __global__ void __launch_bounds__(256) fixup_kernel(FixupArgs a) {
       const T* pe = (const T*)&pv;
       const float al = (v < a.V) ? a.alpha[(int64_t)(v / kPartialWidth) * a.ldr + t] : 0.f;
       const int64_t yt = a.y[t];
-      const bool valid = target_valid(yt, a.ignore_index, a.V);
+      const int64_t yl = yt - a.y_shift;  // target's column among these V
+      const bool owned = yt != a.ignore_index && yl >= 0 && yl < a.V;
 #pragma unroll
       for (int k = 0; k < EPV; ++k) d[k] = (v + k < a.V) ? al * Elem<T>::to_f32(pe[k]) : 0.f;
-      if (valid && yt >= v && yt < v + EPV) d[yt - v] = a.dzt[t];
+      if (owned && yl >= v && yl < v + EPV) d[yl - v] = a.dzt[t];
       uint4 ov;
       T* oe = (T*)&ov;
 #pragma unroll
