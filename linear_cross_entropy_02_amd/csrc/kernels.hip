@@ -602,13 +602,89 @@ __global__ void __launch_bounds__(256) fixup_kernel(FixupArgs a) {
   }
 }
 
+// bf16 fixup with a wider tile: 64 tokens x 256 columns per block.  Each
+// thread forms eight 8-column vectors of dZ (written back in place and into
+// LDS), then transposes one 8 x 8 block (8 tokens x 8 columns) in registers
+// and writes eight 16-byte dZ^T segments; the 8 threads with the same column
+// octet write one 128-byte run of a dZ^T row.  LDS rows are 512 bytes with
+// the 16-byte slot XOR-swizzled by the row's token group (row / 8), which
+// keeps both the row-wise writes and the transposing reads free of bank
+// conflicts.
+constexpr int kFixT = 64, kFixV = 256;
+__global__ void __launch_bounds__(256) fixup_bf16_kernel(FixupArgs a) {
+  __shared__ uint4 tile[kFixT * (kFixV / 8)];  // 32 KB
+  const int v0 = blockIdx.x * kFixV, t0 = blockIdx.y * kFixT;
+  const int tid = threadIdx.x;
+  uint16_t* const P = (uint16_t*)a.P;
+  uint16_t* const Pt = (uint16_t*)a.Pt;
+  // phase 1: row r = tid / 32 + 8 p, column octet cv = tid % 32
+  const int cv = tid & 31;
+  const int v = v0 + cv * 8;
+  const bool vlive = v < a.V;
+  const int64_t aoff = (int64_t)(v / kPartialWidth) * a.ldr;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int r = (tid >> 5) + 8 * p;
+    const int t = t0 + r;
+    uint4 ov = make_uint4(0u, 0u, 0u, 0u);
+    if (t < a.M) {
+      uint16_t* const src = P + (int64_t)t * a.ldp + v;
+      const uint4 pv = *(const uint4*)src;
+      float d[8];
+      unpack8_bf16(pv, d);
+      const float al = vlive ? a.alpha[aoff + t] : 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) d[k] = (v + k < a.V) ? al * d[k] : 0.f;
+      const int64_t yt = a.y[t];
+      const int64_t yl = yt - a.y_shift;
+      if (yt != a.ignore_index && yl >= v && yl < v + 8 && yl < a.V) {
+        const float dz = a.dzt[t];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) d[k] = (yl == v + k) ? dz : d[k];
+      }
+      ov = pack8_bf16(d);
+      *(uint4*)src = ov;
+    }
+    tile[r * 32 + (cv ^ ((r >> 3) & 7))] = ov;
+  }
+  __syncthreads();
+  // phase 2: token group tg = tid % 8, column octet vo = tid / 8
+  const int tg = tid & 7, vo = tid >> 3;
+  uint4 rd[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) rd[k] = tile[(8 * tg + k) * 32 + (vo ^ tg)];
+  const int t = t0 + 8 * tg;
+  if (t < a.rows_out) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // element j of each token's vector: dword j / 2, half j % 2
+      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t w[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint4 x = rd[k];
+        w[k] = (j >> 1) == 0 ? x.x : (j >> 1) == 1 ? x.y : (j >> 1) == 2 ? x.z : x.w;
+      }
+      uint4 o;
+      o.x = __builtin_amdgcn_perm(w[1], w[0], sel);
+      o.y = __builtin_amdgcn_perm(w[3], w[2], sel);
+      o.z = __builtin_amdgcn_perm(w[5], w[4], sel);
+      o.w = __builtin_amdgcn_perm(w[7], w[6], sel);
+      *(uint4*)(Pt + (int64_t)(v0 + 8 * vo + j) * a.ldpt + t) = o;
+    }
+  }
+}
+
 hipError_t launch_fixup(Dt dt, const FixupArgs& a, hipStream_t s) {
   if (a.rows_out <= 0) return hipSuccess;
-  dim3 grid(cdiv(a.Vpad, 64), cdiv(a.rows_out, 64));
-  if (dt == Dt::BF16)
-    hipLaunchKernelGGL(fixup_kernel<bf16>, grid, dim3(256), 0, s, a);
-  else
+  if (dt == Dt::BF16) {
+    // Vpad is a multiple of 256 and rows_out of 64: the grid covers them exactly
+    dim3 grid(cdiv(a.Vpad, kFixV), cdiv(a.rows_out, kFixT));
+    hipLaunchKernelGGL(fixup_bf16_kernel, grid, dim3(256), 0, s, a);
+  } else {
+    dim3 grid(cdiv(a.Vpad, 64), cdiv(a.rows_out, 64));
     hipLaunchKernelGGL(fixup_kernel<float>, grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
