@@ -423,9 +423,63 @@ __global__ void __launch_bounds__(256) transpose_kernel(const T* __restrict__ sr
   }
 }
 
+// bf16 with 8-element alignment everywhere: 64 source rows x 256 source
+// columns per block, the layout and 8 x 8 register transpose of the bf16
+// fixup (swizzled 512-byte LDS rows, 16-byte accesses on both sides, eight
+// neighbouring threads per 128-byte destination run).
+__global__ void __launch_bounds__(256) transpose_bf16_kernel(const uint16_t* __restrict__ src,
+                                                             int rows, int cols, int64_t ld_src,
+                                                             uint16_t* __restrict__ dst,
+                                                             int64_t ld_dst, int rows_out) {
+  __shared__ uint4 tile[64 * 32];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 256;
+  const int tid = threadIdx.x;
+  const int cv = tid & 31;
+  const int gc = c0 + 8 * cv;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int r = (tid >> 5) + 8 * p;
+    const int gr = r0 + r;
+    uint4 val = make_uint4(0u, 0u, 0u, 0u);
+    if (gr < rows && gc < cols) val = *(const uint4*)(src + (int64_t)gr * ld_src + gc);
+    tile[r * 32 + (cv ^ ((r >> 3) & 7))] = val;
+  }
+  __syncthreads();
+  const int tg = tid & 7, vo = tid >> 3;
+  uint4 rd[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) rd[k] = tile[(8 * tg + k) * 32 + (vo ^ tg)];
+  const int gr = r0 + 8 * tg;
+  if (gr >= rows_out) return;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int dc = c0 + 8 * vo + j;  // destination row
+    if (dc >= cols) break;
+    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint4 x = rd[k];
+      w[k] = (j >> 1) == 0 ? x.x : (j >> 1) == 1 ? x.y : (j >> 1) == 2 ? x.z : x.w;
+    }
+    uint4 o;
+    o.x = __builtin_amdgcn_perm(w[1], w[0], sel);
+    o.y = __builtin_amdgcn_perm(w[3], w[2], sel);
+    o.z = __builtin_amdgcn_perm(w[5], w[4], sel);
+    o.w = __builtin_amdgcn_perm(w[7], w[6], sel);
+    *(uint4*)(dst + (int64_t)dc * ld_dst + gr) = o;
+  }
+}
+
 hipError_t launch_transpose(Dt dt, const void* src, int rows, int cols, int64_t ld_src, void* dst,
                             int64_t ld_dst, int rows_out, hipStream_t s) {
   if (rows_out <= 0 || cols <= 0) return hipSuccess;
+  if (dt == Dt::BF16 && cols % 8 == 0 && rows_out % 8 == 0 && ld_src % 8 == 0 && ld_dst % 8 == 0) {
+    dim3 grid(cdiv(rows_out, 64), cdiv(cols, 256));
+    hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, (const uint16_t*)src, rows,
+                       cols, ld_src, (uint16_t*)dst, ld_dst, rows_out);
+    return hipGetLastError();
+  }
   dim3 grid(cdiv(rows_out, 64), cdiv(cols, 64));
   if (dt == Dt::BF16)
     hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)src, rows, cols,
