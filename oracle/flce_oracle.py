@@ -38,7 +38,7 @@ from typing import Dict, Iterable, Optional
 import numpy as np
 
 __all__ = ["flce_reference", "flce_bruteforce", "flce_rows", "validity",
-           "count_valid", "scale_factor"]
+           "count_valid", "scale_factor", "distill_reference", "distill_bruteforce"]
 
 
 def validity(y: np.ndarray, ignore_index: int) -> np.ndarray:
@@ -235,3 +235,111 @@ def flce_bruteforce(X, W, y, ignore_index: int = -100, reduction: str = "mean") 
 def loss_only(X, W, y, ignore_index: int = -100, reduction: str = "mean") -> float:
     """Scalar loss alone (used by finite-difference checks)."""
     return flce_reference(X, W, y, ignore_index, reduction, want_grads=False)["loss"]
+
+
+# ---------------------------------------------------------------------------
+# Soft-target (distillation) cross-entropy with a temperature.
+#
+#   z^S = X W^T (student),  z^T = X_T W_T^T (teacher, its own hidden size)
+#   p_t = softmax(z^S_t / tau),  q_t = softmax(z^T_t / tau)
+#   l_t = valid_t * H(q_t, p_t) = -valid_t sum_v q_tv ln p_tv
+#   loss = s sum_t l_t,  dZ^S_tv = s valid_t (p_tv - q_tv) / tau
+#   dX = dZ^S W,  dW = dZ^S^T X        (the teacher receives no gradient)
+#
+# Alisa's book of LLMs, Mathy things > Information theory: cross entropy of
+# a target distribution against the model's is the KL divergence plus the
+# target's own entropy, and for a one-hot target it is the NLL above;
+# Neural net basics (softmax with temperature): logits are divided by the
+# temperature before the softmax.  Readings: the targets array serves only
+# as the mask (valid_t = [y_t != ignore_index]); no factor tau^2 is applied
+# (a caller wanting the usual distillation scaling multiplies the loss and
+# the gradients by tau^2); the gradient is the softmax + CE gradient of the
+# same book (d/dz of -sum q ln softmax(z) = softmax(z) - q, since q sums to
+# one) taken through the division by tau.
+# ---------------------------------------------------------------------------
+def distill_reference(X: np.ndarray, W: np.ndarray, X_teacher: np.ndarray,
+                      W_teacher: np.ndarray, y: np.ndarray, ignore_index: int = -100,
+                      temperature: float = 1.0, reduction: str = "mean",
+                      chunk: int = 512, want_grads: bool = True) -> Dict[str, np.ndarray]:
+    """Loss (and dX, dW of the student) of the soft-target CE above, float64."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    Xt = np.asarray(X_teacher, dtype=np.float64)
+    Wt = np.asarray(W_teacher, dtype=np.float64)
+    y = np.asarray(y)
+    T, H = X.shape
+    V = W.shape[0]
+    if Xt.shape[0] != T or Wt.shape[0] != V or Xt.shape[1] != Wt.shape[1]:
+        raise ValueError("teacher shapes")
+    tau = float(temperature)
+    if not tau > 0.0:
+        raise ValueError("temperature must be positive")
+    valid = validity(y, ignore_index)
+    n_valid = int(valid.sum())
+    s = scale_factor(n_valid, reduction)
+    lse_s = np.zeros(T)
+    lse_t = np.zeros(T)
+    per_token = np.zeros(T)
+    dX = np.zeros((T, H)) if want_grads else None
+    dW = np.zeros((V, H)) if want_grads else None
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        a = (X[t0:t1] @ W.T) / tau                     # student logits / tau
+        b = (Xt[t0:t1] @ Wt.T) / tau                   # teacher logits / tau
+        ma = a.max(axis=1)
+        la = ma + np.log(np.exp(a - ma[:, None]).sum(axis=1))
+        mb = b.max(axis=1)
+        lb = mb + np.log(np.exp(b - mb[:, None]).sum(axis=1))
+        lse_s[t0:t1] = la
+        lse_t[t0:t1] = lb
+        logp = a - la[:, None]                         # log-softmax, student
+        q = np.exp(b - lb[:, None])                    # softmax, teacher
+        vc = valid[t0:t1]
+        per_token[t0:t1] = np.where(vc, -(q * logp).sum(axis=1), 0.0)
+        if want_grads:
+            g = (np.exp(logp) - q) * (s * vc.astype(np.float64) / tau)[:, None]
+            dX[t0:t1] = g @ W
+            dW += g.T @ X[t0:t1]
+    total = float(per_token.sum())
+    loss = total * s if reduction == "mean" else total
+    out = dict(loss=loss, per_token=per_token, lse_student=lse_s, lse_teacher=lse_t,
+               n_valid=n_valid, scale=s)
+    if want_grads:
+        out.update(dX=dX, dW=dW)
+    return out
+
+
+def distill_bruteforce(X, W, X_teacher, W_teacher, y, ignore_index: int = -100,
+                       temperature: float = 1.0, reduction: str = "mean") -> Dict[str, object]:
+    """Pure-Python loops over the same definitions, for tiny inputs."""
+    X = [[float(v) for v in row] for row in np.asarray(X)]
+    W = [[float(v) for v in row] for row in np.asarray(W)]
+    Xt = [[float(v) for v in row] for row in np.asarray(X_teacher)]
+    Wt = [[float(v) for v in row] for row in np.asarray(W_teacher)]
+    y = [int(v) for v in np.asarray(y)]
+    T, V, H = len(X), len(W), len(X[0])
+    Ht = len(Xt[0])
+    tau = float(temperature)
+    valid = [yt != ignore_index for yt in y]
+    n_valid = sum(valid)
+    s = 1.0 if reduction == "sum" else (0.0 if n_valid == 0 else 1.0 / n_valid)
+    dX = [[0.0] * H for _ in range(T)]
+    dW = [[0.0] * H for _ in range(V)]
+    total = 0.0
+    for t in range(T):
+        if not valid[t]:
+            continue
+        a = [sum(X[t][h] * W[v][h] for h in range(H)) / tau for v in range(V)]
+        b = [sum(Xt[t][h] * Wt[v][h] for h in range(Ht)) / tau for v in range(V)]
+        za = sum(math.exp(x - max(a)) for x in a)
+        zb = sum(math.exp(x - max(b)) for x in b)
+        p = [math.exp(x - max(a)) / za for x in a]
+        q = [math.exp(x - max(b)) / zb for x in b]
+        total += -sum(q[v] * math.log(p[v]) for v in range(V))
+        for v in range(V):
+            g = s * (p[v] - q[v]) / tau
+            for h in range(H):
+                dX[t][h] += g * W[v][h]
+                dW[v][h] += g * X[t][h]
+    loss = total * s if reduction == "mean" else total
+    return dict(loss=loss, dX=dX, dW=dW, n_valid=n_valid)
