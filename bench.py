@@ -23,6 +23,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused linear-CE fwd+bwd tokens/s and % bf16 MFMA peak, H=4096 V=128256"
 METRIC_FWD = "forward-only per-token log-probs tokens/s and % bf16 MFMA peak, H=4096 V=128256"
+METRIC_DISTILL = ("soft-target (distillation) fwd+bwd tokens/s and % bf16 MFMA peak, "
+                  "H=4096 V=128256, teacher on the fly")
 METRIC_SHARD = ("vocabulary-parallel shard (1 of {n}) fwd+bwd tokens/s and % bf16 MFMA peak, "
                 "H=4096 V=128256")
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA peaks, bf16 and fp32
@@ -70,6 +72,9 @@ def parse():
                    help="time one device's share of an N-way vocabulary-parallel head: "
                         "flce_vocab_shard_forward + flce_vocab_shard_backward on V/N rows "
                         "(the collectives between them are not part of the step)")
+    p.add_argument("--distill-teacher-hidden", type=int, default=0, metavar="HT",
+                   help="time flce_distill_fwd_bwd with a teacher head of hidden size HT "
+                        "(temperature 2) instead of the hard-label path")
     p.add_argument("--forward-only", action="store_true",
                    help="time flce_forward (per-token log-probs and loss, no gradients)")
     p.add_argument("--no-timing", action="store_true",
@@ -261,7 +266,18 @@ def main():
           flush=True)
     n_shards = max(1, args.vocab_shards)
     fwd_only = args.forward_only
-    if n_shards > 1:
+    Ht = args.distill_teacher_hidden
+    if Ht > 0:
+        tinp = workloads.generate(wl.with_shape(H=Ht, seed=wl.seed + 500))
+        Xq, Wq, _ = workloads.to_torch(tinp, "cuda")
+        del tinp
+        op = flce.FusedDistillationCrossEntropy(wl.H, wl.V, Ht, wl.dtype, chunk_tokens=args.chunk,
+                                                dw_chunks=args.dw_chunks)
+        out = op.distill(X, W, Xq, Wq, y, 2.0, wl.ignore_index, wl.reduction)
+
+        def step():
+            op.distill(X, W, Xq, Wq, y, 2.0, wl.ignore_index, wl.reduction, out=out)
+    elif n_shards > 1:
         # the whole vocabulary's lse, as the collectives after step 1 would give it
         full = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=args.chunk)
         lse_g = full.forward(X, W, y, wl.ignore_index, wl.reduction)["lse"]
@@ -286,7 +302,7 @@ def main():
     else:
         op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=args.chunk,
                                           dw_chunks=args.dw_chunks)
-    if n_shards > 1:
+    if n_shards > 1 or Ht > 0:
         pass  # step() is set above
     elif fwd_only:
         out = op.forward(X, W, y, wl.ignore_index, wl.reduction)
@@ -335,6 +351,8 @@ def main():
     if n_shards > 1:
         V = V // n_shards
     flops = (8.0 if n_shards > 1 else 2.0 if fwd_only else 6.0) * T * H * V
+    if Ht > 0:  # the teacher's logits on top of the student's three contractions
+        flops = 6.0 * T * H * V + 2.0 * T * Ht * V
     tokens_per_s = T / (ms * 1e-3)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
@@ -355,18 +373,20 @@ def main():
             # its launches (one per chunk; one per dW group for dW); a
             # vocabulary shard runs its logits GEMM twice per step
             nrep = 2.0 if (n_shards > 1 and dom == "logits_gemm") else 1.0
+            if Ht > 0 and dom == "logits_gemm":  # student and teacher logits
+                nrep = (H + Ht) / H
             flop_per_launch = nrep * 2.0 * T * H * V / kernels[dom]["launches_per_step"]
             achieved = flop_per_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
             roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                         "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                        "traffic": None if (fwd_only or n_shards > 1) else
+                        "traffic": None if (fwd_only or n_shards > 1 or Ht > 0) else
                         measured_traffic(dom)}
         else:
             roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": 8000.0,
                         "unit": "GB/s", "frac": None, "traffic": None}
 
     cpu = None
-    if args.cpu_sample > 0 and n_shards == 1:
+    if args.cpu_sample > 0 and n_shards == 1 and Ht == 0:
         from oracle import flce_reference
         ns = min(args.cpu_sample, T)
         threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
@@ -379,13 +399,14 @@ def main():
                          f"{dt:.1f}s"}
 
     line = {
-        "metric": (METRIC_SHARD.format(n=n_shards) if n_shards > 1 else
+        "metric": (METRIC_DISTILL if Ht > 0 else METRIC_SHARD.format(n=n_shards) if n_shards > 1 else
                    METRIC_FWD if fwd_only else METRIC), "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "H": H, "V": V, "chunk_tokens": op.chunk_tokens,
                    "dw_chunks": op.dw_chunks, "vocab_shards": n_shards, "V_total": wl.V,
+                   "teacher_hidden": Ht,
                    "reduction": wl.reduction, "ignore_frac": wl.ignore_frac,
                    "targets": wl.targets},
         "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / peak, 4),

@@ -190,6 +190,41 @@ flce_status_t flce_vocab_shard_backward(flce_handle_t h, const void* X, const vo
                                         int32_t reduction, const float* lse, void* dX_partial,
                                         float* dW_shard, void* stream);
 
+/*
+ * Soft targets (distillation) with a temperature.  "Alisa's book of LLMs",
+ * Mathy things > Information theory: the cross-entropy of a target
+ * distribution q against the model's p is KL(q || p) plus the entropy of q,
+ * and reduces to the NLL of the target for a one-hot q; Neural net basics:
+ * the softmax with a temperature divides the logits by it first.  Here q
+ * comes from a teacher head evaluated on the fly, so neither model's T x V
+ * logits are held:
+ *
+ *   p_t = softmax(X_t W^T / tau),  q_t = softmax(X_teacher_t W_teacher^T / tau)
+ *   loss = s sum_t valid_t H(q_t, p_t),   dZ = s valid (p - q) / tau
+ *   dX = dZ W (X's dtype),  dW = dZ^T X (fp32); the teacher gets no gradient
+ *
+ * with valid_t and s from `targets`, ignore_index and `reduction` as for
+ * flce_fwd_bwd (the targets serve only as the mask; out-of-range ids count
+ * as ignored and are reported by flce_query_error).  No tau^2 factor is
+ * applied: multiply loss and gradients by tau^2 for the usual distillation
+ * scaling.
+ *
+ * flce_distill_create: as flce_create, plus the teacher's hidden size
+ * (> 0, a multiple of 8 for bf16 or 4 for fp32, at most 2^20) and a second
+ * C x V workspace buffer for the teacher's exponentials.
+ * flce_distill_fwd_bwd: X [T x H], W [V x H], X_teacher [T x Ht],
+ * W_teacher [V x Ht], all in the handle's dtype; temperature > 0 and
+ * finite.  INVALID_ARGUMENT, with nothing enqueued, for a handle made by
+ * flce_create or a bad argument.
+ */
+flce_status_t flce_distill_create(const flce_config_t* cfg, int64_t teacher_hidden,
+                                  flce_handle_t* out);
+flce_status_t flce_distill_fwd_bwd(flce_handle_t h, const void* X, const void* W,
+                                   const void* X_teacher, const void* W_teacher,
+                                   const int64_t* targets, int64_t T, int64_t ignore_index,
+                                   float temperature, int32_t reduction, float* loss, void* dX,
+                                   float* dW, int64_t* n_valid, void* stream);
+
 /* Synchronise `stream` and read the number of out-of-range targets seen by
  * the last flce_fwd_bwd or flce_forward on this handle.  Returns FLCE_ERR_BAD_TARGET when it
  * is > 0, FLCE_OK otherwise.  bad_targets may be NULL. */

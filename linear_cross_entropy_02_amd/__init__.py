@@ -32,7 +32,8 @@ FLCE_SUM = 2
 
 EXPORTED = (
     "flce_create", "flce_workspace_bytes", "flce_chunk_tokens", "flce_dw_chunks", "flce_fwd_bwd", "flce_forward",
-    "flce_vocab_shard_forward", "flce_vocab_shard_backward",
+    "flce_vocab_shard_forward", "flce_vocab_shard_backward", "flce_distill_create",
+    "flce_distill_fwd_bwd",
     "flce_query_error", "flce_timing_enable", "flce_timing_kinds", "flce_timing_kind_name",
     "flce_timing_read", "flce_destroy", "flce_status_string", "flce_last_error",
 )
@@ -80,6 +81,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.flce_vocab_shard_forward.restype = st
     lib.flce_vocab_shard_backward.argtypes = [P, P, P, P, i64, i64, i64, i64, i32, P, P, P, P]
     lib.flce_vocab_shard_backward.restype = st
+    lib.flce_distill_create.argtypes = [ctypes.POINTER(flce_config_t), i64, ctypes.POINTER(P)]
+    lib.flce_distill_create.restype = st
+    lib.flce_distill_fwd_bwd.argtypes = [P, P, P, P, P, P, i64, i64, ctypes.c_float, i32, P, P, P,
+                                         P, P]
+    lib.flce_distill_fwd_bwd.restype = st
     lib.flce_query_error.argtypes = [P, P, ctypes.POINTER(i64)]
     lib.flce_query_error.restype = st
     lib.flce_timing_enable.argtypes = [P, i32]
@@ -186,6 +192,26 @@ def flce_vocab_shard_backward(handle, X, W_shard, targets, T: int, ignore_index:
     return load().flce_vocab_shard_backward(handle, _ptr(X), _ptr(W_shard), _ptr(targets), T,
                                             ignore_index, vocab_offset, vocab_total, reduction,
                                             _ptr(lse), _ptr(dX_partial), _ptr(dW_shard), stream)
+
+
+def flce_distill_create(hidden: int, vocab: int, dtype: int, teacher_hidden: int,
+                        chunk_tokens: int = 0, dw_chunks: int = 0):
+    """Returns (status, handle) of a soft-target handle."""
+    cfg = flce_config_t(hidden, vocab, dtype, dw_chunks, chunk_tokens)
+    h = ctypes.c_void_p()
+    st = load().flce_distill_create(ctypes.byref(cfg), teacher_hidden, ctypes.byref(h))
+    return st, h
+
+
+def flce_distill_fwd_bwd(handle, X, W, X_teacher, W_teacher, targets, T: int, ignore_index: int,
+                         temperature: float, reduction: int, loss, dX, dW, n_valid=None,
+                         stream=None) -> int:
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    return load().flce_distill_fwd_bwd(handle, _ptr(X), _ptr(W), _ptr(X_teacher), _ptr(W_teacher),
+                                       _ptr(targets), T, ignore_index, temperature, reduction,
+                                       _ptr(loss), _ptr(dX), _ptr(dW), _ptr(n_valid), stream)
 
 
 def flce_query_error(handle, stream=None):
@@ -352,3 +378,47 @@ class FusedLinearCrossEntropy:
                 raise ValueError("X must be a contiguous [T, H] tensor in the handle's dtype")
             if y.dtype.is_floating_point or y.element_size() != 8 or y.shape != (T,):
                 raise ValueError("targets must be int64 [T]")
+
+
+class FusedDistillationCrossEntropy(FusedLinearCrossEntropy):
+    """Soft-target handle: the student head's tempered softmax against a
+    teacher head's, both evaluated on the fly (see flce_distill_fwd_bwd)."""
+
+    def __init__(self, hidden: int, vocab: int, teacher_hidden: int, dtype="bf16",
+                 chunk_tokens: int = 0, dw_chunks: int = 0):
+        import torch
+        if not torch.cuda.is_available():
+            raise RuntimeError("FusedDistillationCrossEntropy needs a HIP device")
+        self.torch_dtype = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+        self.dtype = FLCE_BF16 if dtype == "bf16" else FLCE_F32
+        self.hidden, self.vocab, self.teacher_hidden = hidden, vocab, teacher_hidden
+        st, h = flce_distill_create(hidden, vocab, self.dtype, teacher_hidden, chunk_tokens,
+                                    dw_chunks)
+        if st != FLCE_OK:
+            raise FlceError(st, "flce_distill_create")
+        self.handle = h
+
+    def distill(self, X, W, X_teacher, W_teacher, y, temperature: float = 1.0,
+                ignore_index: int = -100, reduction: str = "mean", out=None):
+        import torch
+        T = X.shape[0]
+        self._check(X, W, y, T)
+        if (X_teacher.dtype != self.torch_dtype or tuple(X_teacher.shape) != (T, self.teacher_hidden)
+                or tuple(W_teacher.shape) != (self.vocab, self.teacher_hidden)
+                or W_teacher.dtype != self.torch_dtype or not X_teacher.is_contiguous()
+                or not W_teacher.is_contiguous()):
+            raise ValueError("teacher tensors must be contiguous [T, Ht] and [V, Ht] "
+                             "in the handle's dtype")
+        if out is None:
+            dev = W.device
+            out = dict(loss=torch.empty((), dtype=torch.float32, device=dev),
+                       dX=torch.empty((T, self.hidden), dtype=self.torch_dtype, device=dev),
+                       dW=torch.empty((self.vocab, self.hidden), dtype=torch.float32, device=dev),
+                       n_valid=torch.empty((), dtype=torch.int64, device=dev))
+        red = FLCE_MEAN if reduction == "mean" else FLCE_SUM if reduction == "sum" else -1
+        st = flce_distill_fwd_bwd(self.handle, X, W, X_teacher, W_teacher, y, T, ignore_index,
+                                  float(temperature), red, out["loss"], out["dX"], out["dW"],
+                                  out.get("n_valid"))
+        if st != FLCE_OK:
+            raise FlceError(st, "flce_distill_fwd_bwd")
+        return out

@@ -58,6 +58,7 @@ struct flce_handle {
   Dt dt = Dt::BF16;
   int64_t H = 0, V = 0, C = 0, Vpad = 0, nt = 0;
   int G = 1;               // chunks per dW GEMM
+  int64_t Ht = 0;          // teacher hidden size (soft-target handles only)
   int splitk_alloc = 1;  // split-K planes the workspace holds for a full chunk
   size_t ws_bytes = 0;
   char* ws = nullptr;
@@ -72,6 +73,11 @@ struct flce_handle {
   float* dzt = nullptr;    // [C]
   double* loss_part = nullptr;  // [C / 32]
   float* splitk = nullptr;      // [splitk_alloc x C x H]
+  void* Pq = nullptr;           // teacher exp(z_T / tau - m_tile) [C x Vpad]
+  float* pmq = nullptr;         // teacher partials / alpha [nt x C]
+  float* psq = nullptr;
+  int* paq = nullptr;
+  float* pc = nullptr;          // cross partials [nt x C]
   int64_t* nvalid = nullptr;
   float* scale = nullptr;
   int64_t* bad = nullptr;
@@ -182,7 +188,7 @@ const char* flce_timing_kind_name(int32_t kind) {
   return kKindNames[kind];
 }
 
-flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out) {
+static flce_status_t create_impl(const flce_config_t* cfg, int64_t Ht, flce_handle_t* out) {
   if (!out) return FLCE_ERR_INVALID_ARGUMENT;
   *out = nullptr;
   if (!cfg) return FLCE_ERR_INVALID_ARGUMENT;
@@ -246,6 +252,13 @@ flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out) {
   const size_t olp = carve((size_t)(C / 32) * 8);
   const size_t osk = h->splitk_alloc > 1 ? carve((size_t)h->splitk_alloc * C * H * 4) : 0;
   const size_t osc = carve(64);
+  // soft targets: the teacher's exponentials and partials, and the cross partials
+  const size_t oPq = Ht ? carve((size_t)C * h->Vpad * es) : 0;
+  const size_t opmq = Ht ? carve((size_t)C * h->nt * 4) : 0;
+  const size_t opsq = Ht ? carve((size_t)C * h->nt * 4) : 0;
+  const size_t opaq = Ht ? carve((size_t)C * h->nt * 4) : 0;
+  const size_t opc = Ht ? carve((size_t)C * h->nt * 4) : 0;
+  h->Ht = Ht;
   h->ws_bytes = off;
   e = hipMalloc((void**)&h->ws, h->ws_bytes);
   if (e != hipSuccess) {
@@ -268,6 +281,13 @@ flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out) {
   h->nvalid = (int64_t*)(h->ws + osc);
   h->scale = (float*)(h->ws + osc + 16);
   h->bad = (int64_t*)(h->ws + osc + 32);
+  if (Ht) {
+    h->Pq = h->ws + oPq;
+    h->pmq = (float*)(h->ws + opmq);
+    h->psq = (float*)(h->ws + opsq);
+    h->paq = (int*)(h->ws + opaq);
+    h->pc = (float*)(h->ws + opc);
+  }
   e = hipMemset(h->ws + osc, 0, 64);
   if (e != hipSuccess) {
     (void)hipFree(h->ws);
@@ -276,6 +296,20 @@ flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out) {
   }
   *out = h;
   return FLCE_OK;
+}
+
+flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out) {
+  return create_impl(cfg, 0, out);
+}
+
+flce_status_t flce_distill_create(const flce_config_t* cfg, int64_t teacher_hidden,
+                                  flce_handle_t* out) {
+  if (out) *out = nullptr;
+  if (!cfg || teacher_hidden <= 0) return FLCE_ERR_INVALID_ARGUMENT;
+  const Dt dt = cfg->dtype == FLCE_BF16 ? Dt::BF16 : Dt::F32;
+  if (teacher_hidden % elems_per_vec(dt) != 0) return FLCE_ERR_INVALID_ARGUMENT;
+  if (teacher_hidden > (1 << 20)) return FLCE_ERR_UNSUPPORTED;
+  return create_impl(cfg, teacher_hidden, out);
 }
 
 size_t flce_workspace_bytes(flce_handle_t h) { return h ? h->ws_bytes : 0; }
@@ -305,6 +339,14 @@ struct Cols {
   const float* lse_in;
 };
 
+// Soft targets: a teacher head (its hidden states and weight, hidden size
+// h->Ht) whose tempered softmax replaces the one-hot target.
+struct Soft {
+  const void* Xq;
+  const void* Wq;
+  float inv_temp;
+};
+
 flce_status_t check_device(flce_handle_t h, const char* who) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
@@ -321,7 +363,7 @@ bool misaligned(const void* p, uintptr_t mask) { return ((uintptr_t)p & mask) !=
 flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const int64_t* targets,
                           int64_t T, int64_t ignore_index, int32_t reduction, float* loss,
                           void* dX, float* dW, float* lse, int32_t* argmax, int64_t* n_valid,
-                          const Cols& cols, void* stream) {
+                          const Cols& cols, void* stream, const Soft* soft = nullptr) {
   hipStream_t s = (hipStream_t)stream;
   const Dt dt = h->dt;
   const size_t es = elem_size(dt);
@@ -364,6 +406,49 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
     FLCE_LAUNCH(K_TRANSPOSE_X, launch_transpose(dt, Xc, (int)Cc, (int)H, H,
                                                 (char*)h->Xt + (size_t)gs * C * es, GC, (int)Ck, s));
 
+    if (soft) {
+      // teacher: tempered logits, their exponentials and partials, then its
+      // alpha = exp(m_tile - lse) (no reduction scale, no one-hot column)
+      LogitsArgs qa{};
+      qa.X = (const char*)soft->Xq + (size_t)t0 * h->Ht * es;
+      qa.W = soft->Wq;
+      qa.M = (int)Cc;
+      qa.V = (int)V;
+      qa.H = (int)h->Ht;
+      qa.P = h->Pq;
+      qa.ldp = Vpad;
+      qa.pm = h->pmq;
+      qa.ps = h->psq;
+      qa.pa = h->paq;
+      qa.ldr = C;
+      qa.ztgt = h->ztgt;
+      qa.y = yc;
+      qa.ignore_index = ignore_index;
+      qa.y_shift = 0;
+      qa.inv_temp = soft->inv_temp;
+      FLCE_LAUNCH(K_LOGITS, launch_logits(dt, qa, s));
+      FinalizeArgs qf{};
+      qf.M = (int)Cc;
+      qf.nt = (int)nt;
+      qf.V = (int)V;
+      qf.pm = h->pmq;
+      qf.ps = h->psq;
+      qf.pa = h->paq;
+      qf.ldr = C;
+      qf.ztgt = h->ztgt;
+      qf.dzt = h->dzt;
+      qf.y = yc;
+      qf.ignore_index = ignore_index;
+      qf.scale = h->scale;
+      qf.y_shift = 0;
+      qf.v_total = V;
+      qf.unit_scale = true;
+      qf.no_target = true;
+      qf.backward = true;
+      qf.loss_part = nullptr;
+      FLCE_LAUNCH(K_FINALIZE, launch_finalize(qf, s));
+    }
+
     LogitsArgs la{};
     la.X = Xc;
     la.W = W;
@@ -380,6 +465,11 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
     la.y = yc;
     la.ignore_index = ignore_index;
     la.y_shift = cols.y_shift;
+    if (soft) {
+      la.inv_temp = soft->inv_temp;
+      la.Pq = h->Pq;
+      la.pc = h->pc;
+    }
     FLCE_LAUNCH(K_LOGITS, launch_logits(dt, la, s));
 
     FinalizeArgs fa{};
@@ -401,6 +491,12 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
     fa.y_shift = cols.y_shift;
     fa.v_total = cols.v_total;
     fa.lse_in = cols.lse_in ? cols.lse_in + t0 : nullptr;
+    if (soft) {
+      fa.cross_pc = h->pc;
+      fa.alpha_q = h->pmq;
+      fa.alpha_mul = soft->inv_temp;
+      fa.no_target = true;
+    }
     fa.backward = true;
     fa.loss_part = h->loss_part;
     fa.first_chunk = c == 0;
@@ -422,6 +518,11 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
     xa.y = yc;
     xa.ignore_index = ignore_index;
     xa.y_shift = cols.y_shift;
+    if (soft) {
+      xa.no_target = true;
+      xa.Pq = h->Pq;
+      xa.alpha_q = h->pmq;
+    }
     FLCE_LAUNCH(K_FIXUP, launch_fixup(dt, xa, s));
 
     // dX_c = dZ W   (M = Cc, N = H, K = vocabulary)
@@ -660,6 +761,29 @@ flce_status_t flce_vocab_shard_backward(flce_handle_t h, const void* X, const vo
   return run_fwd_bwd(h, X, W_shard, targets, T, ignore_index, reduction, nullptr, dX_partial,
                      dW_shard, nullptr, nullptr, nullptr, Cols{vocab_offset, vocab_total, lse},
                      stream);
+}
+
+flce_status_t flce_distill_fwd_bwd(flce_handle_t h, const void* X, const void* W,
+                                   const void* X_teacher, const void* W_teacher,
+                                   const int64_t* targets, int64_t T, int64_t ignore_index,
+                                   float temperature, int32_t reduction, float* loss, void* dX,
+                                   float* dW, int64_t* n_valid, void* stream) {
+  if (!h || h->Ht <= 0) return FLCE_ERR_INVALID_ARGUMENT;
+  if (T < 0) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!(temperature > 0.f) || !(temperature < 3.0e38f)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!W || !W_teacher || !loss || !dW) return FLCE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!X || !X_teacher || !targets || !dX)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(W) || !aligned16(W_teacher) || !aligned16(dW) ||
+      (T > 0 && (!aligned16(X) || !aligned16(X_teacher) || !aligned16(dX))))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  if (misaligned(loss, 3) || misaligned(n_valid, 7) || misaligned(targets, 7))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  const flce_status_t st = check_device(h, "flce_distill_fwd_bwd");
+  if (st != FLCE_OK) return st;
+  const Soft soft{X_teacher, W_teacher, 1.f / temperature};
+  return run_fwd_bwd(h, X, W, targets, T, ignore_index, reduction, loss, dX, dW, nullptr, nullptr,
+                     n_valid, Cols{0, h->V, nullptr}, stream, &soft);
 }
 
 flce_status_t flce_query_error(flce_handle_t h, void* stream, int64_t* bad_targets) {

@@ -28,6 +28,11 @@ struct LogitsArgs {
   const int64_t* y;     // chunk targets, [M]
   int64_t ignore_index;
   int64_t y_shift;      // vocabulary id of W's row 0 (0 unless W is a vocabulary shard)
+  float inv_temp = 1.f; // logits are divided by the softmax temperature
+  // Soft targets: the teacher's exp(z_T / tau - m_tile) of the same chunk
+  // ([M x ldp], input dtype) and, per (tile, row), sum_v P_T z / tau out.
+  const void* Pq = nullptr;
+  float* pc = nullptr;
 };
 // Width in columns of one online-logsumexp partial (the wave tile width of
 // the 256 x 256 logits GEMM).
@@ -68,12 +73,21 @@ struct FinalizeArgs {
   float* m_out;          // nullable: max over these columns
   float* sum_out;        // nullable: sum of exp(z - max) over these columns
   float* zt_out;         // nullable: target logit if these columns hold it, else 0
+  // Soft targets: per (tile, row) cross partials of the student's logits
+  // with the teacher's exponentials, and the teacher's alpha (its
+  // exp(m_tile - lse), read for the cross term, then scaled like the
+  // student's alpha for the dZ pass).
+  const float* cross_pc = nullptr;
+  float* alpha_q = nullptr;
+  float alpha_mul = 1.f;     // extra factor of alpha (1 / temperature)
+  bool unit_scale = false;   // alpha without the reduction's 1/n_valid (teacher)
+  bool no_target = false;    // no one-hot term (soft targets, teacher)
   const float* scale;
   float* lse_out;        // nullable, chunk-relative
   int32_t* argmax_out;   // nullable, chunk-relative
   float* logprob_out;    // nullable, chunk-relative: z_target - lse (0 if ignored)
   bool backward;         // also form dzt and turn pm into alpha
-  double* loss_part;     // one slot per 32 rows
+  double* loss_part;     // one slot per 32 rows; nullable
   int first_chunk;
 };
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
@@ -89,6 +103,9 @@ struct FixupArgs {
   const float* dzt;              // [M]
   const int64_t* y; int64_t ignore_index;
   int64_t y_shift;               // vocabulary id of column 0 (shard offset)
+  bool no_target = false;        // soft targets: no one-hot column
+  const void* Pq = nullptr;      // soft targets: teacher exponentials, subtracted
+  const float* alpha_q = nullptr;  //   with this scale, [nt x ldr]
 };
 hipError_t launch_fixup(Dt dt, const FixupArgs& a, hipStream_t s);
 

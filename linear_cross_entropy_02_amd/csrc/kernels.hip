@@ -48,10 +48,18 @@ __device__ __forceinline__ f4 load4(const bf16* p) {
 // reduction is a 32-value in-lane pass plus two cross-lane steps.  The
 // partials are written tile-major ([tile][row], 16 consecutive rows per
 // store) and exp(z - tile max) goes straight out as 4-element row segments.
-template <typename T>
+//
+// With a temperature tau the partials are those of z / tau (max m / tau,
+// sum of exp(z / tau - m / tau)); with CROSS (soft targets) each (row, tile)
+// also gets sum_v P_T z / tau, P_T being the teacher's stored
+// exp(z_T / tau - m_T) of the same columns.
+template <typename T, bool CROSS = false>
 struct LogitsEpi {
   T* P;
   int64_t ldp;
+  float inv_temp;
+  const T* Pq;  // CROSS: teacher exponentials, [M x ldp]
+  float* pc;    // CROSS: cross partials, [nt x ldr]
   float* pm;
   float* ps;
   int* pa;
@@ -124,14 +132,30 @@ struct LogitsEpi {
           ztgt[row] = zt;
         }
       }
-      const float mb = (mx == kNegInf) ? 0.f : mx * kLog2e;
+      float cross = 0.f;
+      if constexpr (CROSS) {
+        // columns >= V hold a zero teacher exponential and a zero logit
+        if (row < M) {
+          const T* const qrow = Pq + (int64_t)row * ldp + lc0;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const f4 q = load4(qrow + 16 * j);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) cross = __builtin_fmaf(q[r], acc[i][j][r], cross);
+          }
+        }
+        cross += shfl_xor_f(cross, 16);
+        cross += shfl_xor_f(cross, 32);
+      }
+      const float kl = kLog2e * inv_temp;
+      const float mb = (mx == kNegInf) ? 0.f : mx * kl;
       float sum = 0.f;
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float e = (FULL || lc0 + 16 * j + r < V)
-                              ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][r], kLog2e, -mb))
+                              ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][r], kl, -mb))
                               : 0.f;
           sum += e;
           acc[i][j][r] = e;
@@ -141,9 +165,10 @@ struct LogitsEpi {
       if (row < M) {
         if (g == 0 && ec.col0 < V) {
           const int64_t o = (int64_t)ptile * ldr + row;
-          pm[o] = mx;
+          pm[o] = mx * inv_temp;
           ps[o] = sum;
           pa[o] = ai;
+          if constexpr (CROSS) pc[o] = cross * inv_temp;
         }
         // columns up to the padded row length are allocated; those >= V get 0
         if (store_p) {
@@ -250,7 +275,8 @@ static hipError_t set_lds_attr() {
 template <typename T>
 static hipError_t setup_t() {
   hipError_t e;
-  if ((e = set_lds_attr<T, 256, 256, 4, LogitsEpi<T>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 256, 256, 4, LogitsEpi<T, false>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 256, 256, 4, LogitsEpi<T, true>>()) != hipSuccess) return e;
   if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<T>>()) != hipSuccess) return e;
   if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<float>>()) != hipSuccess) return e;
   if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<T>>()) != hipSuccess) return e;
@@ -262,6 +288,28 @@ hipError_t gemm_setup() {
   hipError_t e = setup_t<bf16>();
   if (e != hipSuccess) return e;
   return setup_t<float>();
+}
+
+template <typename T, bool CROSS>
+static hipError_t logits_run(const LogitsArgs& a, const GemmShape& g, hipStream_t s) {
+  LogitsEpi<T, CROSS> epi;
+  epi.P = (T*)a.P;
+  epi.ldp = a.ldp;
+  epi.inv_temp = a.inv_temp;
+  epi.Pq = (const T*)a.Pq;
+  epi.pc = a.pc;
+  epi.pm = a.pm;
+  epi.ps = a.ps;
+  epi.pa = a.pa;
+  epi.ldr = a.ldr;
+  epi.ztgt = a.ztgt;
+  epi.y = a.y;
+  epi.ignore_index = a.ignore_index;
+  epi.y_shift = a.y_shift;
+  epi.M = a.M;
+  epi.V = a.V;
+  epi.store_p = a.P != nullptr;
+  return run_gemm<T, 256, 256, 4>(g, epi, s);
 }
 
 template <typename T>
@@ -279,21 +327,7 @@ static hipError_t logits_t(const LogitsArgs& a, hipStream_t s) {
   // patch, which keeps both the X chunk and W tiles resident in its L2
   // (walking all 16 row tiles per W tile re-streams X from beyond L2).
   g.group_m = 4;
-  LogitsEpi<T> epi;
-  epi.P = (T*)a.P;
-  epi.ldp = a.ldp;
-  epi.pm = a.pm;
-  epi.ps = a.ps;
-  epi.pa = a.pa;
-  epi.ldr = a.ldr;
-  epi.ztgt = a.ztgt;
-  epi.y = a.y;
-  epi.ignore_index = a.ignore_index;
-  epi.y_shift = a.y_shift;
-  epi.M = a.M;
-  epi.V = a.V;
-  epi.store_p = a.P != nullptr;
-  return run_gemm<T, 256, 256, 4>(g, epi, s);
+  return a.Pq ? logits_run<T, true>(a, g, s) : logits_run<T, false>(a, g, s);
 }
 
 hipError_t launch_logits(Dt dt, const LogitsArgs& a, hipStream_t s) {
@@ -502,6 +536,7 @@ hipError_t launch_transpose(Dt dt, const void* src, int rows, int cols, int64_t 
 constexpr int kFinRows = 32, kFinSlices = 32;
 __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   __shared__ float s_f[kFinSlices][kFinRows + 1];
+  __shared__ float s_c[kFinSlices][kFinRows + 1];
   __shared__ int s_i[kFinSlices][kFinRows + 1];
   __shared__ float s_m[kFinRows], s_lse[kFinRows], s_sc[kFinRows];
   __shared__ double s_nll[kFinRows];
@@ -537,29 +572,35 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   }
   __syncthreads();
   // pass 2: rescaled sum
+  // (soft targets: also sum_j alpha_q_j pc_j = sum_v q_v z_v / tau)
   m = s_m[rl];
-  float sum = 0.f;
+  float sum = 0.f, cr = 0.f;
   if (live)
     for (int j = sl; j < a.nt; j += kFinSlices) {
       const int64_t o = (int64_t)j * a.ldr + row;
       const float sj = a.ps[o];
       if (sj > 0.f) sum += sj * exp_fast(a.pm[o] - m);
+      if (a.cross_pc) cr += a.cross_pc[o] * a.alpha_q[o];
     }
   s_f[sl][rl] = sum;
+  s_c[sl][rl] = cr;
   __syncthreads();
   if (sl == 0) {
     double nll = 0.0;
     float lse = 0.f, sc = 0.f;
     if (live) {
-      for (int k = 1; k < kFinSlices; ++k) sum += s_f[k][rl];
+      for (int k = 1; k < kFinSlices; ++k) {
+        sum += s_f[k][rl];
+        cr += s_c[k][rl];
+      }
       // validity against the whole vocabulary; ownership of the target by
       // these columns (all of them unless this is a vocabulary shard)
       const int64_t yt = a.y[row];
       const bool valid = target_valid(yt, a.ignore_index, a.v_total);
       const int64_t yl = yt - a.y_shift;
-      const bool owned = valid && yl >= 0 && yl < a.V;
+      const bool owned = valid && !a.no_target && yl >= 0 && yl < a.V;
       lse = a.lse_in ? a.lse_in[row] : m + log_fast(sum);
-      sc = valid ? *a.scale : 0.f;
+      sc = valid ? (a.unit_scale ? 1.f : *a.scale) * a.alpha_mul : 0.f;
       const float zt = owned ? a.ztgt[row] : 0.f;
       if (a.backward) a.dzt[row] = owned ? sc * (exp_fast(zt - lse) - 1.f) : 0.f;
       if (a.lse_out) a.lse_out[row] = lse;
@@ -567,7 +608,8 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
       if (a.m_out) a.m_out[row] = m;
       if (a.sum_out) a.sum_out[row] = sum;
       if (a.zt_out) a.zt_out[row] = zt;
-      nll = valid ? (double)lse - (double)zt : 0.0;
+      // hard target: lse - z_y; soft targets: lse - sum_v q_v z_v / tau
+      nll = valid ? (double)lse - (double)(a.cross_pc ? cr : zt) : 0.0;
     }
     s_lse[rl] = lse;
     s_sc[rl] = sc;
@@ -580,9 +622,10 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
     for (int j = sl; j < a.nt; j += kFinSlices) {
       const int64_t o = (int64_t)j * a.ldr + row;
       a.pm[o] = (a.ps[o] > 0.f) ? sc * exp_fast(a.pm[o] - lse) : 0.f;
+      if (a.alpha_q) a.alpha_q[o] *= sc;
     }
   }
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0 && a.loss_part) {
     double total = 0.0;
     for (int k = 0; k < kFinRows; ++k) total += s_nll[k];
     a.loss_part[blockIdx.x] = a.first_chunk ? total : a.loss_part[blockIdx.x] + total;
@@ -628,7 +671,15 @@ __global__ void __launch_bounds__(256) fixup_kernel(FixupArgs a) {
       const bool owned = yt != a.ignore_index && yl >= 0 && yl < a.V;
 #pragma unroll
       for (int k = 0; k < EPV; ++k) d[k] = (v + k < a.V) ? al * Elem<T>::to_f32(pe[k]) : 0.f;
-      if (owned && yl >= v && yl < v + EPV) d[yl - v] = a.dzt[t];
+      if (a.Pq) {  // soft targets: minus the teacher's probability, same scale
+        uint4 qv = *(const uint4*)((const T*)a.Pq + (int64_t)t * a.ldp + v);
+        const T* qe = (const T*)&qv;
+        const float aq = (v < a.V) ? a.alpha_q[(int64_t)(v / kPartialWidth) * a.ldr + t] : 0.f;
+#pragma unroll
+        for (int k = 0; k < EPV; ++k)
+          d[k] = (v + k < a.V) ? d[k] - aq * Elem<T>::to_f32(qe[k]) : 0.f;
+      }
+      if (owned && !a.no_target && yl >= v && yl < v + EPV) d[yl - v] = a.dzt[t];
       uint4 ov;
       T* oe = (T*)&ov;
 #pragma unroll
@@ -689,9 +740,16 @@ __global__ void __launch_bounds__(256) fixup_bf16_kernel(FixupArgs a) {
       const float al = vlive ? a.alpha[aoff + t] : 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) d[k] = (v + k < a.V) ? al * d[k] : 0.f;
+      if (a.Pq) {  // soft targets: minus the teacher's probability, same scale
+        float q[8];
+        unpack8_bf16(*(const uint4*)((const uint16_t*)a.Pq + (int64_t)t * a.ldp + v), q);
+        const float aq = vlive ? a.alpha_q[aoff + t] : 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) d[k] = (v + k < a.V) ? __builtin_fmaf(-aq, q[k], d[k]) : 0.f;
+      }
       const int64_t yt = a.y[t];
       const int64_t yl = yt - a.y_shift;
-      if (yt != a.ignore_index && yl >= v && yl < v + 8 && yl < a.V) {
+      if (!a.no_target && yt != a.ignore_index && yl >= v && yl < v + 8 && yl < a.V) {
         const float dz = a.dzt[t];
 #pragma unroll
         for (int k = 0; k < 8; ++k) d[k] = (yl == v + k) ? dz : d[k];

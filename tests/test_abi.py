@@ -128,3 +128,20 @@ def test_autograd_wrapper_refuses_host_tensors():
     y = torch.zeros(4, dtype=torch.int64)
     with pytest.raises((RuntimeError, ValueError, AssertionError)):
         linear_cross_entropy(X, W, y)
+
+
+@pytest.mark.parametrize("teacher_hidden,status", [
+    (0, flce.FLCE_ERR_INVALID_ARGUMENT),
+    (-8, flce.FLCE_ERR_INVALID_ARGUMENT),
+    (12, flce.FLCE_ERR_INVALID_ARGUMENT),          # not a multiple of 8 (bf16)
+    ((1 << 20) + 8, flce.FLCE_ERR_UNSUPPORTED),
+])
+def test_distill_create_rejects_bad_teacher_without_device(lib, teacher_hidden, status):
+    st, h = flce.flce_distill_create(64, 100, flce.FLCE_BF16, teacher_hidden)
+    assert st == status and not h.value
+
+
+def test_distill_null_handle(lib):
+    st = lib.flce_distill_fwd_bwd(None, 16, 16, 16, 16, 16, 4, -100, 1.0, flce.FLCE_MEAN, 16, 16,
+                                  16, None, None)
+    assert st == flce.FLCE_ERR_INVALID_ARGUMENT
