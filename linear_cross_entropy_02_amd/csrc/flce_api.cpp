@@ -71,7 +71,7 @@ struct flce_handle {
   int* pa = nullptr;       // tile argmax   [nt x C]
   float* ztgt = nullptr;   // [C]
   float* dzt = nullptr;    // [C]
-  double* loss_part = nullptr;  // [C / 32]
+  double* loss_part = nullptr;  // [C / kFinalizeRows]
   float* splitk = nullptr;      // [splitk_alloc x C x H]
   void* Pq = nullptr;           // teacher exp(z_T / tau - m_tile) [C x Vpad]
   float* pmq = nullptr;         // teacher partials / alpha [nt x C]
@@ -249,7 +249,7 @@ static flce_status_t create_impl(const flce_config_t* cfg, int64_t Ht, flce_hand
   const size_t opa = carve((size_t)C * h->nt * 4);
   const size_t ozt = carve((size_t)C * 4);
   const size_t odz = carve((size_t)C * 4);
-  const size_t olp = carve((size_t)(C / 32) * 8);
+  const size_t olp = carve((size_t)cdiv64(C, kFinalizeRows) * 8);
   const size_t osk = h->splitk_alloc > 1 ? carve((size_t)h->splitk_alloc * C * H * 4) : 0;
   const size_t osc = carve(64);
   // soft targets: the teacher's exponentials and partials, and the cross partials
@@ -585,7 +585,7 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
     }
   }
   if (loss) {
-    const int nparts = (int)cdiv64(T < C ? T : C, 32);  // finalize blocks of the first chunk
+    const int nparts = (int)cdiv64(T < C ? T : C, kFinalizeRows);  // finalize blocks of the first chunk
     FLCE_LAUNCH(K_LOSS, launch_loss(h->loss_part, nparts, h->nvalid, rsum, loss, s));
   }
 #undef FLCE_LAUNCH
@@ -668,7 +668,7 @@ flce_status_t run_forward(flce_handle_t h, const void* X, const void* W, const i
     FLCE_LAUNCH(K_FINALIZE, launch_finalize(fa, s));
   }
   if (loss) {
-    const int nparts = (int)cdiv64(T < C ? T : C, 32);
+    const int nparts = (int)cdiv64(T < C ? T : C, kFinalizeRows);
     FLCE_LAUNCH(K_LOSS, launch_loss(h->loss_part, nparts, h->nvalid, rsum, loss, s));
   }
 #undef FLCE_LAUNCH

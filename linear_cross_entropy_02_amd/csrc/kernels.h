@@ -87,9 +87,11 @@ struct FinalizeArgs {
   int32_t* argmax_out;   // nullable, chunk-relative
   float* logprob_out;    // nullable, chunk-relative: z_target - lse (0 if ignored)
   bool backward;         // also form dzt and turn pm into alpha
-  double* loss_part;     // one slot per 32 rows; nullable
+  double* loss_part;     // one slot per kFinalizeRows rows; nullable
   int first_chunk;
 };
+// Rows per finalize block, hence rows per loss partial.
+constexpr int kFinalizeRows = 16;
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
 
 struct FixupArgs {

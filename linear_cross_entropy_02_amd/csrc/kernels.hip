@@ -525,15 +525,16 @@ hipError_t launch_transpose(Dt dt, const void* src, int rows, int cols, int64_t 
 }
 
 // ------------------------------------------------------------- finalize ---
-// Block of 32 rows x 32 slices of the partial tiles (tile-major layout:
-// the 32 rows of a slice read 128 contiguous bytes).  Three passes over the
+// Block of 16 rows x 64 slices of the partial tiles (tile-major layout:
+// the 16 rows of a slice read 64 contiguous bytes); 16 rows per block puts
+// a 4096-row chunk on 256 blocks, one per compute unit.  Three passes over the
 // row's partials, each a parallel reduction over the slices:
 //   1. m = max_j m_j and the argmax of the first tile reaching it (tiles
 //      are in column order, so this is the lowest column index);
 //   2. sum = sum_j s_j exp(m_j - m), lse = m + ln sum (the merge of
 //      online-softmax states: each partial sum rescaled to the common max);
 //   3. alpha_j = s valid exp(m_j - lse), overwriting m_j.
-constexpr int kFinRows = 32, kFinSlices = 32;
+constexpr int kFinRows = kFinalizeRows, kFinSlices = 1024 / kFinRows;
 __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   __shared__ float s_f[kFinSlices][kFinRows + 1];
   __shared__ float s_c[kFinSlices][kFinRows + 1];
