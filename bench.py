@@ -1,7 +1,6 @@
 """Benchmark: fused linear cross-entropy forward+backward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--chunk 4096]
-                    [--dw-chunks 1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--chunk C] [--dw-chunks G]
 
 A step is one flce_fwd_bwd call over one batch: logits GEMM with the
 online-logsumexp epilogue, dZ formation, dX and dW GEMMs, loss -- the whole
@@ -62,10 +61,12 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", type=int, default=4)
-    p.add_argument("--chunk", type=int, default=4096)
-    p.add_argument("--dw-chunks", type=int, default=1,
+    p.add_argument("--chunk", type=int, default=0,
+                   help="tokens per chunk (0 = the workload's launch configuration)")
+    p.add_argument("--dw-chunks", type=int, default=0,
                    help="token chunks per dW GEMM (the dZ^T of that many chunks is kept; "
-                        "more than 1 needs (1 + G) C V more workspace)")
+                        "more than 1 needs (G - 1) C V more workspace; 0 = the workload's "
+                        "launch configuration)")
     p.add_argument("--cpu-sample", type=int, default=256,
                    help="tokens of the workload the CPU oracle is timed on (0 = skip)")
     p.add_argument("--vocab-shards", type=int, default=1, metavar="N",
@@ -119,7 +120,7 @@ def summarize_profiles(d: str):
 
     stats = rows("prof_kt", "run_kernel_stats.csv")
     lines = ["# Kernel time, fused linear-CE fwd+bwd, llama3-8b head (T=16384, H=4096, V=128256, "
-             "bf16, chunk 4096)", "",
+             "bf16, chunk 2048, 4 chunks per dW GEMM)", "",
              "Command (repo root, MI355X):", "", "    " + PROFILE_CMDS["kt"], "",
              "3 timed + 1 warm-up steps (4 calls of flce_fwd_bwd), per-kernel HIP event timing on.",
              "", "| kernel | calls | total ms | avg ms | % time |", "|---|---|---|---|---|"]
@@ -146,10 +147,12 @@ def summarize_profiles(d: str):
     w_scale = cal_bytes / (cw[copy[0]] * 1024)
     fetch = per_kernel("prof_fetch", "FETCH_SIZE")
     write = per_kernel("prof_write", "WRITE_SIZE")
-    traffic = {"source_hash": kernel_source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
+    import workloads
+    traffic = {"source_hash": kernel_source_hash(), "launch": list(workloads.launch_config(4)),
+               "fetch_scale": f_scale, "write_scale": w_scale,
                "kernels": {}}
     lines = ["# HBM traffic per launch, fused linear-CE fwd+bwd, llama3-8b head "
-             "(T=16384, H=4096, V=128256, bf16, chunk 4096)", "",
+             "(T=16384, H=4096, V=128256, bf16, chunk 2048, 4 chunks per dW GEMM)", "",
              "Commands (repo root, MI355X), one counter pass each:", ""]
     lines += ["    " + PROFILE_CMDS[k] for k in ("fetch", "write", "cal_fetch", "cal_write")]
     lines += ["", f"Calibration: a 1 GiB device-to-device copy reads FETCH_SIZE x {f_scale:.3f} and "
@@ -186,7 +189,7 @@ def summarize_profiles(d: str):
     except OSError:
         util = {}
     lines = ["# MFMA busy and LDS bank conflicts per launch, fused linear-CE fwd+bwd, llama3-8b "
-             "head (T=16384, H=4096, V=128256, bf16, chunk 4096)", "",
+             "head (T=16384, H=4096, V=128256, bf16, chunk 2048, 4 chunks per dW GEMM)", "",
              "Commands (repo root, MI355X), one counter pass each:", "",
              "    " + PROFILE_CMDS["mfma"], "    " + PROFILE_CMDS["mfma_util"], "",
              "MfmaUtil is rocprofv3's derived metric (percent of the MFMA units' cycles busy over "
@@ -210,19 +213,20 @@ def summarize_profiles(d: str):
     print("\n".join(lines))
 
 
-def measured_traffic(kernel_kind: str):
+def measured_traffic(kernel_kind: str, launch):
     """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None when the kernel sources changed since it was taken."""
+    summary, or None when the kernel sources or the launch configuration
+    (chunk, chunks per dW GEMM) differ from those it was taken with."""
     try:
         with open(TRAFFIC_JSON) as f:
             t = json.load(f)
     except OSError:
         return None
-    if t.get("source_hash") != kernel_source_hash():
+    if t.get("source_hash") != kernel_source_hash() or t.get("launch") != list(launch):
         return None
-    # logits: LogitsEpi; dX: stores the input dtype; dW: stores fp32
-    tag = {"logits_gemm": "LogitsEpi", "dx_gemm": "StoreEpi<bf16>",
-           "dw_gemm": "StoreEpi<float>"}.get(kernel_kind)
+    # logits: LogitsEpi; dX: stores the input dtype; dW: the accumulating fp32 store
+    tag = {"logits_gemm": "LogitsEpi", "dx_gemm": "StoreEpi<bf16, false>",
+           "dw_gemm": "StoreEpi<float, true>"}.get(kernel_kind)
     for k, v in t["kernels"].items():
         if tag and tag in k:
             return round(v["read_bytes"] + v["write_bytes"])
@@ -259,6 +263,9 @@ def main():
     import workloads
 
     wl = workloads.WORKLOADS[args.workload]
+    chunk, dwc = workloads.launch_config(args.workload)
+    args.chunk = args.chunk or chunk
+    args.dw_chunks = args.dw_chunks or dwc
     t_gen = time.time()
     inp = workloads.generate(wl, keep_f32=args.cpu_sample > 0)
     X, W, y = workloads.to_torch(inp, "cuda")
@@ -379,8 +386,9 @@ def main():
             achieved = flop_per_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
             roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                         "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                        "traffic": None if (fwd_only or n_shards > 1 or Ht > 0) else
-                        measured_traffic(dom)}
+                        "traffic": None if (fwd_only or n_shards > 1 or Ht > 0 or
+                                            args.workload != 4) else
+                        measured_traffic(dom, (op.chunk_tokens, op.dw_chunks))}
         else:
             roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": 8000.0,
                         "unit": "GB/s", "frac": None, "traffic": None}

@@ -150,10 +150,21 @@ void plan_gemm(int64_t M, int64_t N, int64_t K, int max_splits, TileCfg* tc, int
     *tc = TileCfg::T256;
     return;
   }
+  const int64_t ksteps = cdiv64(K, 64);
+  // A grid of 64 to 239 256-wide tiles with a long K loop: split K two to
+  // four ways to fill the chip rather than fall back to 128-wide tiles,
+  // whose 64 x 64 wave tiles read twice the LDS bytes per MFMA.
+  if (t256 >= 64) {
+    const int64_t s = cdiv64(240, t256);
+    if (s <= max_splits && ksteps / s >= 64) {
+      *tc = TileCfg::T256;
+      *splits = (int)s;
+      return;
+    }
+  }
   *tc = TileCfg::T128;
   if (t128 >= 256 || max_splits <= 1) return;
   int64_t s = cdiv64(512, t128);
-  const int64_t ksteps = cdiv64(K, 64);
   if (s > ksteps / 4) s = ksteps / 4;
   if (s > max_splits) s = max_splits;
   if (s < 1) s = 1;
@@ -578,6 +589,7 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       ga.out = dW;
       ga.ldo = H;
       ga.out_f32 = true;
+      ga.may_accumulate = true;
       ga.accumulate = c >= G;
       ga.splits = 1;
       ga.split_stride = 0;

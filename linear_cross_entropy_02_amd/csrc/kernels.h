@@ -46,7 +46,9 @@ struct GemmOutArgs {
   int M, N, K;
   void* out; int64_t ldo;
   bool out_f32;           // store fp32 (dW, split-K partials) or the input dtype
-  bool accumulate;        // out += result (fp32 only)
+  bool may_accumulate;    // fp32 only: the instantiation that can start from the
+                          // output's old values (dW); `accumulate` picks per launch
+  bool accumulate;        // out += result (requires may_accumulate)
   int splits;             // split-K factor; partial planes `split_stride` apart
   int64_t split_stride;
 };

@@ -193,9 +193,11 @@ struct LogitsEpi {
 // consecutive columns of one row per fragment.  To accumulate into the fp32
 // output (dW over token chunks) the accumulators start from the old values,
 // loaded before the K loop, so the epilogue is a plain store either way.
+// ACC = false (dX, split-K partials) starts from zero with no loads.
 // N % 4 == 0, so a 4-column segment is either whole or outside.
-template <typename TO>
+template <typename TO, bool ACC>
 struct StoreEpi {
+  static_assert(!ACC || std::is_same<TO, float>::value, "accumulation is fp32 only");
   TO* out;
   int64_t ldo;
   int M, N;
@@ -204,8 +206,8 @@ struct StoreEpi {
 
   template <int FM, int FN>
   __device__ __forceinline__ void init(f4 (&acc)[FM][FN], const EpiCoord& ec) const {
-    if constexpr (!std::is_same<TO, float>::value) {
-      zero_init(acc);  // accumulation is fp32 only
+    if constexpr (!ACC) {
+      zero_init(acc);
     } else {
       // One unconditional path (no merge of a zero and a loaded value for
       // the register allocator to reconcile with copies): every fragment is
@@ -277,10 +279,12 @@ static hipError_t setup_t() {
   hipError_t e;
   if ((e = set_lds_attr<T, 256, 256, 4, LogitsEpi<T, false>>()) != hipSuccess) return e;
   if ((e = set_lds_attr<T, 256, 256, 4, LogitsEpi<T, true>>()) != hipSuccess) return e;
-  if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<T>>()) != hipSuccess) return e;
-  if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<float>>()) != hipSuccess) return e;
-  if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<T>>()) != hipSuccess) return e;
-  if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<float>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<T, false>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<float, false>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<float, true>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<T, false>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<float, false>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<float, true>>()) != hipSuccess) return e;
   return hipSuccess;
 }
 
@@ -334,7 +338,7 @@ hipError_t launch_logits(Dt dt, const LogitsArgs& a, hipStream_t s) {
   return dt == Dt::BF16 ? logits_t<bf16>(a, s) : logits_t<float>(a, s);
 }
 
-template <typename T, typename TO>
+template <typename T, typename TO, bool ACC>
 static hipError_t store_t2(TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
   GemmShape g{};
   g.A = a.A;
@@ -351,20 +355,22 @@ static hipError_t store_t2(TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
     g.k_per_split = cdiv(ksteps, g.splits) * BK;
   }
   g.group_m = 4;
-  StoreEpi<TO> epi;
+  StoreEpi<TO, ACC> epi;
   epi.out = (TO*)a.out;
   epi.ldo = a.ldo;
   epi.M = a.M;
   epi.N = a.N;
   epi.split_stride = a.split_stride;
-  epi.accumulate = a.accumulate;
+  epi.accumulate = ACC && a.accumulate;
   if (tc == TileCfg::T256) return run_gemm<T, 256, 256, 4>(g, epi, s);
   return run_gemm<T, 128, 128, 4>(g, epi, s);
 }
 
 template <typename T>
 static hipError_t store_t(TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
-  return a.out_f32 ? store_t2<T, float>(tc, a, s) : store_t2<T, T>(tc, a, s);
+  if (a.accumulate && !(a.out_f32 && a.may_accumulate)) return hipErrorInvalidValue;
+  if (!a.out_f32) return store_t2<T, T, false>(tc, a, s);
+  return a.may_accumulate ? store_t2<T, float, true>(tc, a, s) : store_t2<T, float, false>(tc, a, s);
 }
 
 hipError_t launch_gemm_store(Dt dt, TileCfg tc, const GemmOutArgs& a, hipStream_t s) {

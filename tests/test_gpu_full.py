@@ -21,9 +21,8 @@ from oracle import count_valid, flce_reference, flce_rows, scale_factor
 
 pytestmark = pytest.mark.gpu
 
-# launch configuration (chunk tokens, chunks per dW GEMM); workload 4 runs
-# in the configuration the benchmark times
-CHUNK = {3: (4096, 1), 4: (4096, 2), 5: (2048, 1)}
+# each workload in the launch configuration the benchmark times
+CHUNK = {n: workloads.launch_config(n) for n in (3, 4, 5)}
 
 
 def sample_rows(T, C, y, ignore_index, seed, n=24):

@@ -45,6 +45,9 @@ CASES = [
     (workloads.WORKLOADS[2].with_shape(T=777, H=264, V=2049, seed=12), 512),  # H % 64 != 0
     (workloads.WORKLOADS[4].with_shape(T=600, H=1024, V=20000, seed=13), 256),  # zipf head
     (workloads.WORKLOADS[5].with_shape(T=700, H=512, V=12345, seed=14), 256),   # outliers, runs, sum
+    # dX of a 2048-token chunk at H = 2048 is 64 tiles of 256 x 256: K split
+    # four ways over the vocabulary, then the partials summed
+    (workloads.WORKLOADS[4].with_shape(T=2100, H=2048, V=16500, seed=15), 2048),
 ]
 
 

@@ -23,7 +23,8 @@ The five named workloads are the fused-CE head shapes: a tiny fp32 case,
 the efficient-llm-anatomy layer shape (B=4, S=1024, H=512, V=16000), its
 full-model shape (B=16, S=4096), a Llama-3-8B-shaped head (H=4096,
 V=128256) and a large ragged head (H=8192, V=128256, outlier rows, 25 %
-ignored in runs, sum reduction).
+ignored in runs, sum reduction).  LAUNCH records the chunking each of them
+is timed and parity-tested in (a launch setting, not an input).
 """
 from __future__ import annotations
 
@@ -74,6 +75,17 @@ WORKLOADS = {
                 w_std=0.01, targets="zipf", ignore_frac=0.25, ignore_mode="runs",
                 outlier_frac=0.001, reduction="sum", seed=1005),
 }
+
+# Launch configuration per workload: (tokens per chunk C, chunks per dW GEMM G).
+# The two chunk-sized buffers (exponentials of one chunk, dZ^T of G chunks)
+# take (1 + G) C V elements, kept below T V.  At H = 4096, C = 2048 with G = 4
+# makes each dW GEMM 8192 tokens deep (the dW tiles are read and written
+# twice per call instead of four times) and is the fastest that fits.
+LAUNCH = {4: (2048, 4), 5: (2048, 1)}
+
+
+def launch_config(n: int) -> tuple[int, int]:
+    return LAUNCH.get(n, (4096, 1))
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
