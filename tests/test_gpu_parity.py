@@ -41,6 +41,7 @@ CASES = [
     (workloads.WORKLOADS[1], 0),                                            # tiny fp32, full
     (workloads.WORKLOADS[1].with_shape(T=200, V=777, seed=7), 64),          # fp32 ragged, 4 chunks
     (workloads.WORKLOADS[2], 0),                                            # page-1 layer shape, full
+    (workloads.WORKLOADS[2], workloads.launch_config(2)[0]),                # same, as benchmarked
     (workloads.WORKLOADS[2].with_shape(T=1000, H=96, V=1000, seed=11), 256),  # ragged T/H/V
     (workloads.WORKLOADS[2].with_shape(T=777, H=264, V=2049, seed=12), 512),  # H % 64 != 0
     (workloads.WORKLOADS[4].with_shape(T=600, H=1024, V=20000, seed=13), 256),  # zipf head
