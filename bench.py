@@ -263,7 +263,9 @@ def main():
     import workloads
 
     wl = workloads.WORKLOADS[args.workload]
-    chunk, dwc = workloads.launch_config(args.workload)
+    mode = ("forward" if args.forward_only else "shard" if args.vocab_shards > 1 else
+            "distill" if args.distill_teacher_hidden > 0 else "fwd_bwd")
+    chunk, dwc = workloads.launch_config(args.workload, mode)
     args.chunk = args.chunk or chunk
     args.dw_chunks = args.dw_chunks or dwc
     t_gen = time.time()

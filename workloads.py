@@ -84,9 +84,15 @@ WORKLOADS = {
 # four times.  Workload 5 cannot stay below T x V (W^T alone is H V = T V
 # elements there); it takes the fastest setting.
 LAUNCH = {2: (1024, 1), 3: (8192, 1), 4: (2048, 4), 5: (2048, 2)}
+# The other entry points at workload 4's shape, chosen the same way: the
+# forward-only call has no dW GEMM; a vocabulary shard's head is V / N wide;
+# the soft-target head also holds the teacher's chunk of exponentials.
+LAUNCH_MODES = {"forward": (4096, 1), "shard": (4096, 1), "distill": (2048, 1)}
 
 
-def launch_config(n: int) -> tuple[int, int]:
+def launch_config(n: int, mode: str = "fwd_bwd") -> tuple[int, int]:
+    if mode != "fwd_bwd":
+        return LAUNCH_MODES[mode]
     return LAUNCH.get(n, (4096, 1))
 
 
