@@ -93,7 +93,7 @@ struct FinalizeArgs {
   int first_chunk;
 };
 // Rows per finalize block, hence rows per loss partial.
-constexpr int kFinalizeRows = 16;
+constexpr int kFinalizeRows = 8;
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
 
 struct FixupArgs {

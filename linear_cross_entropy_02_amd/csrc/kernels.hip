@@ -531,9 +531,9 @@ hipError_t launch_transpose(Dt dt, const void* src, int rows, int cols, int64_t 
 }
 
 // ------------------------------------------------------------- finalize ---
-// Block of 16 rows x 64 slices of the partial tiles (tile-major layout:
-// the 16 rows of a slice read 64 contiguous bytes); 16 rows per block puts
-// a 4096-row chunk on 256 blocks, one per compute unit.  Three passes over the
+// Block of 8 rows x 128 slices of the partial tiles (tile-major layout:
+// the 8 rows of a slice read 32 contiguous bytes); 8 rows per block puts a
+// 2048-row chunk on 256 blocks, one per compute unit.  Three passes over the
 // row's partials, each a parallel reduction over the slices:
 //   1. m = max_j m_j and the argmax of the first tile reaching it (tiles
 //      are in column order, so this is the lowest column index);
@@ -565,15 +565,22 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   s_f[sl][rl] = m;
   s_i[sl][rl] = am;
   __syncthreads();
-  if (sl == 0) {
-    for (int k = 1; k < kFinSlices; ++k) {
-      const float mk = s_f[k][rl];
-      const int ak = s_i[k][rl];
+  // tree over the slices: slice sl takes in slice sl + w (the combine is
+  // commutative: larger max, then lower index), then writes its own slot
+  for (int w = kFinSlices / 2; w > 0; w >>= 1) {
+    if (sl < w) {
+      const float mk = s_f[sl + w][rl];
+      const int ak = s_i[sl + w][rl];
       if (mk > m || (mk == m && ak < am)) {
         m = mk;
         am = ak;
       }
+      s_f[sl][rl] = m;
+      s_i[sl][rl] = am;
     }
+    __syncthreads();
+  }
+  if (sl == 0) {
     s_m[rl] = m;
     if (live && a.argmax_out) a.argmax_out[row] = am == 0x7fffffff ? am : am + (int)a.y_shift;
   }
@@ -592,14 +599,19 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   s_f[sl][rl] = sum;
   s_c[sl][rl] = cr;
   __syncthreads();
+  for (int w = kFinSlices / 2; w > 0; w >>= 1) {  // fixed-order tree sum
+    if (sl < w) {
+      sum += s_f[sl + w][rl];
+      cr += s_c[sl + w][rl];
+      s_f[sl][rl] = sum;
+      s_c[sl][rl] = cr;
+    }
+    __syncthreads();
+  }
   if (sl == 0) {
     double nll = 0.0;
     float lse = 0.f, sc = 0.f;
     if (live) {
-      for (int k = 1; k < kFinSlices; ++k) {
-        sum += s_f[k][rl];
-        cr += s_c[k][rl];
-      }
       // validity against the whole vocabulary; ownership of the target by
       // these columns (all of them unless this is a vocabulary shard)
       const int64_t yt = a.y[row];
