@@ -67,7 +67,7 @@ def parse():
                    help="token chunks per dW GEMM (the dZ^T of that many chunks is kept; "
                         "more than 1 needs (G - 1) C V more workspace; 0 = the workload's "
                         "launch configuration)")
-    p.add_argument("--cpu-sample", type=int, default=256,
+    p.add_argument("--cpu-sample", type=int, default=2048,
                    help="tokens of the workload the CPU oracle is timed on (0 = skip)")
     p.add_argument("--vocab-shards", type=int, default=1, metavar="N",
                    help="time one device's share of an N-way vocabulary-parallel head: "
