@@ -49,6 +49,10 @@ CASES = [
     # dX of a 2048-token chunk at H = 2048 is 64 tiles of 256 x 256: K split
     # four ways over the vocabulary, then the partials summed
     (workloads.WORKLOADS[4].with_shape(T=2100, H=2048, V=16500, seed=15), 2048),
+    # degenerate sizes: one K-step shorter than a stage, a vocabulary smaller
+    # than one 128-column partial tile
+    (workloads.WORKLOADS[2].with_shape(T=300, H=8, V=50, seed=16), 256),
+    (workloads.WORKLOADS[1].with_shape(T=70, H=4, V=3, seed=17), 64),
 ]
 
 
