@@ -106,7 +106,7 @@ def test_timing_kinds(lib):
 def test_library_has_no_undefined_internal_symbols(lib):
     """Every kernel launch stub must be defined in the library itself (a
     kernel template that fails to instantiate in the host pass leaves an
-    undefined stub that only shows up at load time on the GPU machine)."""
+    undefined stub that only shows up when the library is loaded on a GPU)."""
     import shutil
     import subprocess
     nm = shutil.which("nm")

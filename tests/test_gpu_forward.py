@@ -129,7 +129,8 @@ def test_forward_out_of_range_targets_and_arguments():
 
 
 def test_forward_full_size_llama_head():
-    """Workload 4 at full size in the benchmark's chunking: sampled rows
+    """The Llama-3-8B head (T=16384, H=4096, V=128256) at full size in the
+    benchmark's chunking: sampled rows
     against the oracle's per-row outputs, and the loss against the mean of
     the per-token log-probs."""
     import torch

@@ -283,7 +283,8 @@ def test_p6_torch_cross_entropy(reduction):
 
 @pytest.mark.parametrize("cfg", [1, 2])
 def test_p6_torch_on_workloads(cfg):
-    """Workload 1 in full and a token slice of workload 2, vs torch float64."""
+    """The tiny fp32 head in full and a token slice of the 4096 x 512 x 16000
+    layer shape, vs torch float64."""
     torch = pytest.importorskip("torch")
     F = torch.nn.functional
     wl = workloads.WORKLOADS[cfg]
