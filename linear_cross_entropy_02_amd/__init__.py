@@ -304,6 +304,11 @@ class FusedLinearCrossEntropy:
         self._check(X, W, y, T)
         if out is None:
             out = self.alloc_outputs(T, W.device)
+        else:
+            for k in ("loss", "dX", "dW"):
+                if out.get(k) is None:
+                    raise ValueError(f"out[{k!r}] is required")
+            self._check_out(out, self._out_spec(T), W.device)
         red = FLCE_MEAN if reduction == "mean" else FLCE_SUM if reduction == "sum" else -1
         st = flce_fwd_bwd(self.handle, X, W, y, T, ignore_index, red, out["loss"], out["dX"],
                           out["dW"], out.get("lse"), out.get("argmax"), out.get("n_valid"))
@@ -326,6 +331,8 @@ class FusedLinearCrossEntropy:
                 argmax=torch.empty((T,), dtype=torch.int32, device=dev),
                 n_valid=torch.empty((), dtype=torch.int64, device=dev),
             )
+        else:
+            self._check_out(out, self._out_spec(T), W.device)
         red = FLCE_MEAN if reduction == "mean" else FLCE_SUM if reduction == "sum" else -1
         st = flce_forward(self.handle, X, W, y, T, ignore_index, red, out.get("loss"),
                           out.get("token_logprob"), out.get("lse"), out.get("argmax"),
@@ -359,6 +366,7 @@ class FusedLinearCrossEntropy:
         import torch
         T = X.shape[0]
         self._check(X, W_shard, y, T)
+        self._check_out({"lse": lse}, self._out_spec(T), W_shard.device)
         dX = torch.empty((T, self.hidden), dtype=self.torch_dtype, device=X.device)
         dW = torch.empty((self.vocab, self.hidden), dtype=torch.float32, device=X.device)
         red = FLCE_MEAN if reduction == "mean" else FLCE_SUM if reduction == "sum" else -1
@@ -374,10 +382,35 @@ class FusedLinearCrossEntropy:
         if not W.is_contiguous():
             raise ValueError("W must be contiguous")
         if T:
-            if X.dtype != self.torch_dtype or X.shape[1] != self.hidden or not X.is_contiguous():
+            if (X.dtype != self.torch_dtype or X.dim() != 2 or X.shape[1] != self.hidden
+                    or not X.is_contiguous()):
                 raise ValueError("X must be a contiguous [T, H] tensor in the handle's dtype")
-            if y.dtype.is_floating_point or y.element_size() != 8 or y.shape != (T,):
-                raise ValueError("targets must be int64 [T]")
+            if (y.dtype.is_floating_point or y.element_size() != 8 or tuple(y.shape) != (T,)
+                    or not y.is_contiguous()):
+                raise ValueError("targets must be a contiguous int64 [T] tensor")
+            if X.device != W.device or y.device != W.device:
+                raise ValueError("X, W and the targets must be on one device")
+
+    @staticmethod
+    def _check_out(out, spec, device):
+        """Caller-supplied output buffers: each present entry must have the
+        shape and dtype the call writes, be contiguous and sit on `device`
+        (the library writes the full extent without further checks)."""
+        for name, (shape, dtype) in spec.items():
+            t = out.get(name)
+            if t is None:
+                continue
+            if (tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous()
+                    or t.device != device):
+                raise ValueError(f"out[{name!r}] must be a contiguous {dtype} tensor of shape "
+                                 f"{tuple(shape)} on {device}")
+
+    def _out_spec(self, T):
+        import torch
+        return dict(loss=((), torch.float32), dX=((T, self.hidden), self.torch_dtype),
+                    dW=((self.vocab, self.hidden), torch.float32), lse=((T,), torch.float32),
+                    argmax=((T,), torch.int32), n_valid=((), torch.int64),
+                    token_logprob=((T,), torch.float32))
 
 
 class FusedDistillationCrossEntropy(FusedLinearCrossEntropy):
@@ -415,6 +448,13 @@ class FusedDistillationCrossEntropy(FusedLinearCrossEntropy):
                        dX=torch.empty((T, self.hidden), dtype=self.torch_dtype, device=dev),
                        dW=torch.empty((self.vocab, self.hidden), dtype=torch.float32, device=dev),
                        n_valid=torch.empty((), dtype=torch.int64, device=dev))
+        else:
+            for k in ("loss", "dX", "dW"):
+                if out.get(k) is None:
+                    raise ValueError(f"out[{k!r}] is required")
+            self._check_out(out, self._out_spec(T), W.device)
+        if X_teacher.device != W.device or W_teacher.device != W.device:
+            raise ValueError("teacher tensors must be on the student's device")
         red = FLCE_MEAN if reduction == "mean" else FLCE_SUM if reduction == "sum" else -1
         st = flce_distill_fwd_bwd(self.handle, X, W, X_teacher, W_teacher, y, T, ignore_index,
                                   float(temperature), red, out["loss"], out["dX"], out["dW"],

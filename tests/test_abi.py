@@ -145,3 +145,50 @@ def test_distill_null_handle(lib):
     st = lib.flce_distill_fwd_bwd(None, 16, 16, 16, 16, 16, 4, -100, 1.0, flce.FLCE_MEAN, 16, 16,
                                   16, None, None)
     assert st == flce.FLCE_ERR_INVALID_ARGUMENT
+
+
+def _bare_op(hidden=16, vocab=40):
+    """A FusedLinearCrossEntropy without a handle: enough to exercise the
+    binding's argument checks, which run before any library call."""
+    import torch
+    op = object.__new__(flce.FusedLinearCrossEntropy)
+    op.hidden, op.vocab, op.torch_dtype, op.handle = hidden, vocab, torch.float32, None
+    return op
+
+
+def test_binding_checks_inputs_before_any_call():
+    import torch
+    op = _bare_op()
+    X, W = torch.zeros(5, 16), torch.zeros(40, 16)
+    y = torch.zeros(5, dtype=torch.int64)
+    op._check(X, W, y, 5)  # well-formed
+    with pytest.raises(ValueError, match="targets"):
+        op._check(X, W, torch.zeros(10, dtype=torch.int64)[::2], 5)  # strided view
+    with pytest.raises(ValueError, match="targets"):
+        op._check(X, W, torch.zeros(5, dtype=torch.int32), 5)
+    with pytest.raises(ValueError, match="X must"):
+        op._check(torch.zeros(16, 5).t(), W, y, 5)  # not contiguous
+    with pytest.raises(ValueError, match="W must"):
+        op._check(X, torch.zeros(41, 16), y, 5)
+    with pytest.raises(ValueError, match="W must"):
+        op._check(X, W.to(torch.float64), y, 5)
+
+
+def test_binding_checks_output_buffers():
+    """A wrongly shaped, typed or strided `out` buffer is refused before the
+    library would write its full extent."""
+    import torch
+    op = _bare_op()
+    spec, dev = op._out_spec(5), torch.device("cpu")
+    good = dict(loss=torch.zeros(()), dX=torch.zeros(5, 16), dW=torch.zeros(40, 16),
+                lse=torch.zeros(5), argmax=torch.zeros(5, dtype=torch.int32),
+                n_valid=torch.zeros((), dtype=torch.int64))
+    op._check_out(good, spec, dev)
+    op._check_out({"loss": good["loss"], "dX": good["dX"], "dW": good["dW"]}, spec, dev)
+    for name, bad in (("dW", torch.zeros(39, 16)), ("dX", torch.zeros(5, 16, dtype=torch.float64)),
+                      ("lse", torch.zeros(10)[::2]), ("argmax", torch.zeros(5)),
+                      ("n_valid", torch.zeros(1, dtype=torch.int64))):
+        with pytest.raises(ValueError, match=name):
+            op._check_out(dict(good, **{name: bad}), spec, dev)
+    with pytest.raises(ValueError, match="on meta"):  # buffers on another device
+        op._check_out(good, spec, torch.device("meta"))
