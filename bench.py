@@ -233,6 +233,34 @@ def measured_traffic(kernel_kind: str, launch):
     return None
 
 
+def per_kernel_rooflines(kernels, T, H, V, dtype, mfma_peak):
+    """Achieved rate of each timed kernel of one fwd+bwd step against its own
+    bound, from algorithmic work only: 2 T H V flops for each contraction;
+    for the bandwidth passes the bytes they must move (the fixup reads the
+    exponentials and writes dZ and dZ^T; a transpose reads and writes its
+    matrix once; the merge reads the (max, sum, argmax) partials and writes
+    alpha, 16 bytes per (token, 128-column tile))."""
+    es = 2 if dtype == "bf16" else 4
+    nt = -(-V // 128)
+    work = {"logits_gemm": ("mfma", 2.0 * T * H * V), "dx_gemm": ("mfma", 2.0 * T * H * V),
+            "dw_gemm": ("mfma", 2.0 * T * H * V), "fixup_dz": ("hbm", 3.0 * T * V * es),
+            "transpose_w": ("hbm", 2.0 * V * H * es), "transpose_x": ("hbm", 2.0 * T * H * es),
+            "finalize": ("hbm", 16.0 * nt * T)}
+    out = {}
+    for name, (bound, per_step) in work.items():
+        k = kernels.get(name)
+        if not k or not k["total_ms"]:
+            continue
+        rate = per_step / (k["total_ms"] * 1e-3)
+        if bound == "mfma":
+            out[name] = {"bound": "mfma", "achieved": round(rate / 1e12, 1), "unit": "TFLOP/s",
+                         "frac": round(rate / 1e12 / mfma_peak, 4)}
+        else:
+            out[name] = {"bound": "hbm", "achieved": round(rate / 1e9, 1), "unit": "GB/s",
+                         "frac": round(rate / 1e9 / 8000.0, 4)}
+    return out
+
+
 def calibrate_copy(mib: int):
     import torch
     n = mib * 2 ** 20 // 4
@@ -368,6 +396,7 @@ def main():
 
     roofline = None
     kernels = {}
+    kernel_rooflines = None
     if timing:
         names = flce.flce_timing_kinds()
         for k, name in enumerate(names):
@@ -394,6 +423,8 @@ def main():
         else:
             roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": 8000.0,
                         "unit": "GB/s", "frac": None, "traffic": None}
+        if not (fwd_only or n_shards > 1 or Ht > 0):
+            kernel_rooflines = per_kernel_rooflines(kernels, T, H, V, wl.dtype, peak)
 
     cpu = None
     if args.cpu_sample > 0 and n_shards == 1 and Ht == 0:
@@ -421,6 +452,7 @@ def main():
                    "targets": wl.targets},
         "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / peak, 4),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+        "kernel_rooflines": kernel_rooflines,
         "ms_per_step_median": round(ms_median, 3),
         "workspace_bytes": op.workspace_bytes,
         # the no-T x V-buffer check: workspace against a bf16 T x V buffer,

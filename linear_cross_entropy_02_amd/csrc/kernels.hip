@@ -540,7 +540,7 @@ hipError_t launch_transpose(Dt dt, const void* src, int rows, int cols, int64_t 
 //   2. sum = sum_j s_j exp(m_j - m), lse = m + ln sum (the merge of
 //      online-softmax states: each partial sum rescaled to the common max);
 //   3. alpha_j = s valid exp(m_j - lse), overwriting m_j.
-constexpr int kFinRows = kFinalizeRows, kFinSlices = 1024 / kFinRows;
+constexpr int kFinRows = kFinalizeRows, kFinSlices = 1024 / kFinRows, kFinCache = 8;
 __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   __shared__ float s_f[kFinSlices][kFinRows + 1];
   __shared__ float s_c[kFinSlices][kFinRows + 1];
@@ -550,11 +550,36 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   const int rl = threadIdx.x % kFinRows, sl = threadIdx.x / kFinRows;
   const int row = blockIdx.x * kFinRows + rl;
   const bool live = row < a.M;
+  // The first kFinCache tiles of this slice (all of them up to
+  // kFinCache * kFinSlices = 1024 tiles, a 131072-column vocabulary) are
+  // read once, all loads in flight together, and kept in registers for the
+  // three passes; tiles beyond are read again by each pass.
+  float cm[kFinCache], cs[kFinCache];
+  int ca[kFinCache];
+#pragma unroll
+  for (int q = 0; q < kFinCache; ++q) {
+    const int j = sl + q * kFinSlices;
+    cm[q] = kNegInf;
+    cs[q] = 0.f;
+    ca[q] = 0x7fffffff;
+    if (live && j < a.nt) {
+      const int64_t o = (int64_t)j * a.ldr + row;
+      cm[q] = a.pm[o];
+      cs[q] = a.ps[o];
+      ca[q] = a.pa[o];
+    }
+  }
   // pass 1: max and argmax
   float m = kNegInf;
   int am = 0x7fffffff;
+#pragma unroll
+  for (int q = 0; q < kFinCache; ++q)
+    if (cs[q] > 0.f && (cm[q] > m || (cm[q] == m && ca[q] < am))) {
+      m = cm[q];
+      am = ca[q];
+    }
   if (live)
-    for (int j = sl; j < a.nt; j += kFinSlices) {
+    for (int j = sl + kFinCache * kFinSlices; j < a.nt; j += kFinSlices) {
       const int64_t o = (int64_t)j * a.ldr + row;
       const float mj = a.pm[o];
       if (a.ps[o] > 0.f && (mj > m || (mj == m && a.pa[o] < am))) {
@@ -589,8 +614,17 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   // (soft targets: also sum_j alpha_q_j pc_j = sum_v q_v z_v / tau)
   m = s_m[rl];
   float sum = 0.f, cr = 0.f;
+#pragma unroll
+  for (int q = 0; q < kFinCache; ++q) {
+    const int j = sl + q * kFinSlices;
+    if (cs[q] > 0.f) sum += cs[q] * exp_fast(cm[q] - m);
+    if (a.cross_pc && live && j < a.nt) {
+      const int64_t o = (int64_t)j * a.ldr + row;
+      cr += a.cross_pc[o] * a.alpha_q[o];
+    }
+  }
   if (live)
-    for (int j = sl; j < a.nt; j += kFinSlices) {
+    for (int j = sl + kFinCache * kFinSlices; j < a.nt; j += kFinSlices) {
       const int64_t o = (int64_t)j * a.ldr + row;
       const float sj = a.ps[o];
       if (sj > 0.f) sum += sj * exp_fast(a.pm[o] - m);
@@ -638,7 +672,16 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   // pass 3: alpha (only when the gradient follows)
   if (live && a.backward) {
     const float lse = s_lse[rl], sc = s_sc[rl];
-    for (int j = sl; j < a.nt; j += kFinSlices) {
+#pragma unroll
+    for (int q = 0; q < kFinCache; ++q) {
+      const int j = sl + q * kFinSlices;
+      if (j < a.nt) {
+        const int64_t o = (int64_t)j * a.ldr + row;
+        a.pm[o] = (cs[q] > 0.f) ? sc * exp_fast(cm[q] - lse) : 0.f;
+        if (a.alpha_q) a.alpha_q[o] *= sc;
+      }
+    }
+    for (int j = sl + kFinCache * kFinSlices; j < a.nt; j += kFinSlices) {
       const int64_t o = (int64_t)j * a.ldr + row;
       a.pm[o] = (a.ps[o] > 0.f) ? sc * exp_fast(a.pm[o] - lse) : 0.f;
       if (a.alpha_q) a.alpha_q[o] *= sc;
