@@ -593,6 +593,9 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       ga.accumulate = c >= G;
       ga.splits = 1;
       ga.split_stride = 0;
+      // the dX split-K planes are free again here (summed before this launch)
+      ga.tail_part = h->splitk;
+      ga.tail_part_bytes = h->splitk ? (size_t)h->splitk_alloc * C * H * sizeof(float) : 0;
       FLCE_LAUNCH(K_DW, launch_gemm_store(dt, tc, ga, s));
     }
   }

@@ -57,11 +57,27 @@ struct GemmShape {
   int splits;        // split-K factor (1 = none)
   int k_per_split;   // multiple of the stage depth, unused when splits == 1
   int group_m;       // rows of tiles walked together (>= 1)
+  // Logical tiles this launch covers: [tile_first, tile_first + tile_count)
+  // of the grid's walk order (set by the launcher; all tiles by default).
+  int tile_first, tile_count;
 };
 
 struct TileCoord {
   int tm, tn, split;
+  int slot;  // index of the tile within the launch's range
 };
+
+// Logical tile -> (row tile, column tile): M fastest inside groups of
+// `group_m` rows of tiles.
+__device__ __forceinline__ void tile_rc(const GemmShape& g, int tile, int& tm, int& tn) {
+  const int per_group = g.group_m * g.tiles_n;
+  const int gid = tile / per_group;
+  const int first_m = gid * g.group_m;
+  const int gsize = min(g.tiles_m - first_m, g.group_m);
+  const int in_group = tile - gid * per_group;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
 
 // Block id -> tile.  Hardware dispatches consecutive block ids to the 8 XCDs
 // round-robin; give each XCD a contiguous range of logical tiles.
@@ -71,17 +87,10 @@ __device__ __forceinline__ TileCoord map_tile(const GemmShape& g) {
   const int q = nblk >> 3, r = nblk & 7;
   const int xcd = bid & 7, slot = bid >> 3;
   const int logical = xcd * q + min(xcd, r) + slot;
-  const int per_split = g.tiles_m * g.tiles_n;
   TileCoord c;
-  c.split = logical / per_split;
-  const int tile = logical - c.split * per_split;
-  const int per_group = g.group_m * g.tiles_n;
-  const int gid = tile / per_group;
-  const int first_m = gid * g.group_m;
-  const int gsize = min(g.tiles_m - first_m, g.group_m);
-  const int in_group = tile - gid * per_group;
-  c.tm = first_m + in_group % gsize;
-  c.tn = in_group / gsize;
+  c.split = logical / g.tile_count;
+  c.slot = logical - c.split * g.tile_count;
+  tile_rc(g, g.tile_first + c.slot, c.tm, c.tn);
   return c;
 }
 
@@ -148,6 +157,7 @@ struct EpiCoord {
   int row0, col0;  // first row / column of this wave's tile
   int lane;
   int split;
+  int slot;        // the block tile's index within the launch's tile range
 };
 
 // Accumulators starting at zero (the `init` of most epilogues).
@@ -271,6 +281,7 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
   ec.col0 = n0 + wn * G::WN;
   ec.lane = lane;
   ec.split = tc.split;
+  ec.slot = tc.slot;
 
   // The epilogue chooses the starting accumulators: zero, or (to accumulate
   // into an existing output) its old values, loaded with load16_acc here,

@@ -51,6 +51,11 @@ struct GemmOutArgs {
   bool accumulate;        // out += result (requires may_accumulate)
   int splits;             // split-K factor; partial planes `split_stride` apart
   int64_t split_stride;
+  // Optional scratch for the last partial round of a large accumulating
+  // grid (dW): those tiles are split in K into fp32 partial tiles here and
+  // summed, with the old output, by a second pass.  nullptr: never split.
+  float* tail_part = nullptr;
+  size_t tail_part_bytes = 0;
 };
 hipError_t launch_gemm_store(Dt dt, TileCfg tc, const GemmOutArgs& a, hipStream_t s);
 

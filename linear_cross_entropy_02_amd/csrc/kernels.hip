@@ -246,6 +246,55 @@ struct StoreEpi {
   }
 };
 
+// Split-K partial of one block tile, stored compactly: plane
+// (split, slot) of `part` holds the BM x BN block tile row-major, slot being
+// the tile's index within the launch's tile range.  Rows and columns past
+// the matrix edge hold zeros (their operand rows read as zero).
+template <int BM, int BN>
+struct TilePartialEpi {
+  float* part;
+  int tile_count;
+
+  template <int FM, int FN>
+  __device__ __forceinline__ void init(f4 (&acc)[FM][FN], const EpiCoord&) const {
+    zero_init(acc);
+  }
+
+  template <int FM, int FN>
+  __device__ __forceinline__ void apply(f4 (&acc)[FM][FN], const EpiCoord& ec) const {
+    const int g = ec.lane >> 4, c = ec.lane & 15;
+    float* const base = part + ((int64_t)ec.split * tile_count + ec.slot) * (BM * BN);
+    const int r0 = ec.row0 % BM, c0 = ec.col0 % BN;  // wave tile within the block tile
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        *(f4*)(base + (r0 + 16 * i + c) * BN + c0 + 16 * j + 4 * g) = acc[i][j];
+  }
+};
+
+// out[tile] = (accumulate ? out[tile] : 0) + part[0][slot] + ... +
+// part[splits-1][slot], in that order, for the tiles [tile_first,
+// tile_first + tile_count) of the grid walk `g`; 256 threads x 4 values per
+// block, (BM x BN) / 1024 blocks per tile.
+template <int BM, int BN>
+__global__ void __launch_bounds__(256) tile_reduce_kernel(GemmShape g, const float* part,
+                                                          int splits, float* out, int64_t ldo,
+                                                          bool accumulate) {
+  constexpr int kPerTile = BM * BN / 1024;
+  const int slot = blockIdx.x / kPerTile;
+  const int e = ((blockIdx.x % kPerTile) * 256 + (int)threadIdx.x) * 4;
+  int tm, tn;
+  tile_rc(g, g.tile_first + slot, tm, tn);
+  const int row = tm * BM + e / BN, col = tn * BN + e % BN;
+  if (row >= g.M || col >= g.N) return;  // N % 4 == 0: a 4-column group is whole
+  f4* const o = (f4*)(out + (int64_t)row * ldo + col);
+  f4 acc = accumulate ? *o : (f4){0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < splits; ++sp)
+    acc += *(const f4*)(part + ((int64_t)sp * g.tile_count + slot) * (BM * BN) + e);
+  *o = acc;
+}
+
 // ------------------------------------------------------------ launchers ---
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -260,7 +309,13 @@ static hipError_t run_gemm(const GemmShape& g0, const Epi& epi, hipStream_t s) {
   if (g.splits < 1) g.splits = 1;
   if (g.group_m < 1) g.group_m = 1;
   if (g.group_m > g.tiles_m) g.group_m = g.tiles_m;
-  const int nblk = g.tiles_m * g.tiles_n * g.splits;
+  if (g.tile_count <= 0) {
+    g.tile_first = 0;
+    g.tile_count = g.tiles_m * g.tiles_n;
+  }
+  if (g.tile_first < 0 || g.tile_first + g.tile_count > g.tiles_m * g.tiles_n)
+    return hipErrorInvalidValue;
+  const int nblk = g.tile_count * g.splits;
   hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, WAVES, Epi>), dim3(nblk), dim3(G::kThreads),
                      G::kLdsBytes, s, g, epi);
   return hipGetLastError();
@@ -282,16 +337,28 @@ static hipError_t setup_t() {
   if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<T, false>>()) != hipSuccess) return e;
   if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<float, false>>()) != hipSuccess) return e;
   if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<float, true>>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 256, 256, 4, TilePartialEpi<256, 256>>()) != hipSuccess) return e;
   if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<T, false>>()) != hipSuccess) return e;
   if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<float, false>>()) != hipSuccess) return e;
   if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<float, true>>()) != hipSuccess) return e;
   return hipSuccess;
 }
 
+// Compute units of the device set up last (all devices of a process are
+// taken to be alike): the blocks one round of 256 x 256 tiles occupies.
+static int g_num_cus = 256;
+
 hipError_t gemm_setup() {
   hipError_t e = setup_t<bf16>();
   if (e != hipSuccess) return e;
-  return setup_t<float>();
+  e = setup_t<float>();
+  if (e != hipSuccess) return e;
+  int dev = 0, cus = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+    return e;
+  if (cus > 0) g_num_cus = cus;
+  return hipSuccess;
 }
 
 template <typename T, bool CROSS>
@@ -362,8 +429,44 @@ static hipError_t store_t2(TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
   epi.N = a.N;
   epi.split_stride = a.split_stride;
   epi.accumulate = ACC && a.accumulate;
-  if (tc == TileCfg::T256) return run_gemm<T, 256, 256, 4>(g, epi, s);
-  return run_gemm<T, 128, 128, 4>(g, epi, s);
+  if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4>(g, epi, s);
+  if constexpr (ACC) {
+    // The grid's last partial round (rem tiles, under half the CUs busy for
+    // a whole tile) is split 2-4 ways in K instead: the full rounds run as
+    // usual, the rem tiles' K-slices write fp32 partial tiles, and a pass
+    // sums them (with the old output) in a fixed order.
+    constexpr int BK = 8 * Elem<T>::kVec;
+    const int tiles = cdiv(a.M, 256) * cdiv(a.N, 256);
+    const int nfull = tiles / g_num_cus * g_num_cus, rem = tiles - nfull;
+    const int sp = rem > 0 ? min(4, g_num_cus / rem) : 0;
+    if (a.tail_part && g.splits == 1 && nfull >= g_num_cus && rem > 0 && 2 * rem <= g_num_cus &&
+        cdiv(a.K, BK) >= 8 * sp &&
+        (size_t)sp * rem * 256 * 256 * sizeof(float) <= a.tail_part_bytes) {
+      GemmShape gm = g;
+      gm.tile_first = 0;
+      gm.tile_count = nfull;
+      hipError_t e = run_gemm<T, 256, 256, 4>(gm, epi, s);
+      if (e != hipSuccess) return e;
+      GemmShape gt = g;
+      gt.tile_first = nfull;
+      gt.tile_count = rem;
+      gt.splits = sp;
+      gt.k_per_split = cdiv(cdiv(a.K, BK), sp) * BK;
+      TilePartialEpi<256, 256> pe;
+      pe.part = a.tail_part;
+      pe.tile_count = rem;
+      if ((e = run_gemm<T, 256, 256, 4>(gt, pe, s)) != hipSuccess) return e;
+      // the walk the GEMM used (run_gemm's own view of the grid)
+      gt.tiles_m = cdiv(a.M, 256);
+      gt.tiles_n = cdiv(a.N, 256);
+      gt.group_m = min(max(gt.group_m, 1), gt.tiles_m);
+      hipLaunchKernelGGL((tile_reduce_kernel<256, 256>), dim3(rem * (256 * 256 / 1024)),
+                         dim3(256), 0, s, gt, (const float*)a.tail_part, sp, (float*)a.out,
+                         a.ldo, (bool)(ACC && a.accumulate));
+      return hipGetLastError();
+    }
+  }
+  return run_gemm<T, 256, 256, 4>(g, epi, s);
 }
 
 template <typename T>

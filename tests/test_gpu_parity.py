@@ -49,6 +49,10 @@ CASES = [
     # dX of a 2048-token chunk at H = 2048 is 64 tiles of 256 x 256: K split
     # four ways over the vocabulary, then the partials summed
     (workloads.WORKLOADS[4].with_shape(T=2100, H=2048, V=16500, seed=15), 2048),
+    # its dW grid (65 x 8 = 520 tiles on 256 CUs) splits the last 8 tiles four
+    # ways in K and sums them in a second pass, both when the first chunk
+    # stores dW and when the second accumulates into it
+    (workloads.WORKLOADS[4].with_shape(T=4200, H=2048, V=16500, seed=18), 2048),
     # degenerate sizes: one K-step shorter than a stage, a vocabulary smaller
     # than one 128-column partial tile
     (workloads.WORKLOADS[2].with_shape(T=300, H=8, V=50, seed=16), 256),
