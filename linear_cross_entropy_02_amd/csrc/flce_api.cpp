@@ -414,8 +414,14 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
     const int64_t gs = c % G;
     const bool last = t0 + Cc >= T;
 
-    FLCE_LAUNCH(K_TRANSPOSE_X, launch_transpose(dt, Xc, (int)Cc, (int)H, H,
-                                                (char*)h->Xt + (size_t)gs * C * es, GC, (int)Ck, s));
+    // X^T of the whole group at its first chunk (X is an input, all of it
+    // available): one transpose per dW GEMM; the previous group's dW GEMM,
+    // earlier in the stream, has finished reading the buffer
+    if (gs == 0) {
+      const int64_t Cg = (T - t0 < GC) ? (T - t0) : GC;
+      FLCE_LAUNCH(K_TRANSPOSE_X, launch_transpose(dt, Xc, (int)Cg, (int)H, H, h->Xt, GC,
+                                                  (int)round_up(Cg, 64), s));
+    }
 
     if (soft) {
       // teacher: tempered logits, their exponentials and partials, then its
