@@ -53,6 +53,8 @@ CASES = [
     # ways in K and sums them in a second pass, both when the first chunk
     # stores dW and when the second accumulates into it
     (workloads.WORKLOADS[4].with_shape(T=4200, H=2048, V=16500, seed=18), 2048),
+    # 38 x 16 = 608 dW tiles: the last 96 split two ways
+    (workloads.WORKLOADS[4].with_shape(T=4200, H=4096, V=9700, seed=19), 2048),
     # degenerate sizes: one K-step shorter than a stage, a vocabulary smaller
     # than one 128-column partial tile
     (workloads.WORKLOADS[2].with_shape(T=300, H=8, V=50, seed=16), 256),
