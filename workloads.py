@@ -88,7 +88,7 @@ LAUNCH = {2: (1024, 1), 3: (8192, 1), 4: (2048, 4), 5: (2048, 2)}
 # way: the forward-only call has no dW GEMM; a vocabulary shard's head is
 # V / N wide; the soft-target head also holds the teacher's chunk of
 # exponentials.
-LAUNCH_MODES = {"forward": (4096, 1), "shard": (4096, 1), "distill": (2048, 1)}
+LAUNCH_MODES = {"forward": (4096, 1), "shard": (4096, 1), "distill": (2048, 3)}
 
 
 def launch_config(n: int, mode: str = "fwd_bwd") -> tuple[int, int]:
