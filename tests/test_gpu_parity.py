@@ -55,6 +55,9 @@ CASES = [
     (workloads.WORKLOADS[4].with_shape(T=4200, H=2048, V=16500, seed=18), 2048),
     # 38 x 16 = 608 dW tiles: the last 96 split two ways
     (workloads.WORKLOADS[4].with_shape(T=4200, H=4096, V=9700, seed=19), 2048),
+    # a vocabulary of more than 1024 partial tiles: the merge keeps 1024 of
+    # them per row block in registers and reads the rest in each pass
+    (workloads.WORKLOADS[4].with_shape(T=100, H=64, V=140000, seed=20), 256),
     # degenerate sizes: one K-step shorter than a stage, a vocabulary smaller
     # than one 128-column partial tile
     (workloads.WORKLOADS[2].with_shape(T=300, H=8, V=50, seed=16), 256),
