@@ -55,6 +55,8 @@ CASES = [
     (workloads.WORKLOADS[4].with_shape(T=4200, H=2048, V=16500, seed=18), 2048),
     # 38 x 16 = 608 dW tiles: the last 96 split two ways
     (workloads.WORKLOADS[4].with_shape(T=4200, H=4096, V=9700, seed=19), 2048),
+    # the same split of the dW grid on fp32 operands
+    (workloads.WORKLOADS[1].with_shape(T=2100, H=2048, V=16500, seed=21), 2048),
     # a vocabulary of more than 1024 partial tiles: the merge keeps 1024 of
     # them per row block in registers and reads the rest in each pass
     (workloads.WORKLOADS[4].with_shape(T=100, H=64, V=140000, seed=20), 256),
