@@ -58,7 +58,7 @@ PROFILE_CMDS = {
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", type=int, default=4)
     p.add_argument("--chunk", type=int, default=0,
