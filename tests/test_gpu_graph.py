@@ -1,4 +1,5 @@
-"""A whole flce_fwd_bwd call captured into a HIP graph and replayed.
+"""A whole flce_fwd_bwd call captured into a HIP graph and replayed; and two
+handles used from two streams at once.
 
 The call enqueues kernels only (no allocation, no memset, no host sync), so
 it can be captured; every reduction has a fixed order, so each replay must
@@ -60,3 +61,31 @@ def test_graph_replays_match_eager(dtype_wl):
         assert same(out, ref), f"replay {r} differs from the eager call"
         assert same(other, eager2)
     op.close()
+
+
+def test_two_handles_on_two_streams():
+    """Two handles own separate workspaces: calls enqueued on two streams at
+    once give the same bits as the same calls run one after the other."""
+    import torch
+    wl = workloads.WORKLOADS[2].with_shape(T=900, H=256, V=5000, seed=83)
+    a_in = workloads.generate(wl)
+    b_in = workloads.generate(wl.with_shape(seed=84))
+    Xa, Wa, ya = workloads.to_torch(a_in, "cuda")
+    Xb, Wb, yb = workloads.to_torch(b_in, "cuda")
+    op_a = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=256)
+    op_b = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=256)
+    ref_a = op_a.fwd_bwd(Xa, Wa, ya, wl.ignore_index, wl.reduction)
+    ref_b = op_b.fwd_bwd(Xb, Wb, yb, wl.ignore_index, wl.reduction)
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    sa.wait_stream(torch.cuda.current_stream())
+    sb.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        with torch.cuda.stream(sa):
+            out_a = op_a.fwd_bwd(Xa, Wa, ya, wl.ignore_index, wl.reduction)
+        with torch.cuda.stream(sb):
+            out_b = op_b.fwd_bwd(Xb, Wb, yb, wl.ignore_index, wl.reduction)
+        torch.cuda.synchronize()
+        assert same(out_a, ref_a) and same(out_b, ref_b)
+    op_a.close()
+    op_b.close()
