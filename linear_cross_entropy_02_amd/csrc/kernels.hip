@@ -491,6 +491,8 @@ __global__ void __launch_bounds__(1024) count_kernel(const int64_t* __restrict__
                                                      int64_t* n_valid_out) {
   __shared__ long long s_nv[1024], s_nb[1024];
   long long nv = 0, nb = 0;
+  // unrolled so that eight independent target loads are in flight per thread
+#pragma unroll 8
   for (int64_t t = threadIdx.x; t < T; t += 1024) {
     const int64_t v = y[t];
     if (v != ignore_index) {
