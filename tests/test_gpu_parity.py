@@ -49,6 +49,9 @@ CASES = [
     # dX of a 2048-token chunk at H = 2048 is 64 tiles of 256 x 256: K split
     # four ways over the vocabulary, then the partials summed
     (workloads.WORKLOADS[4].with_shape(T=2100, H=2048, V=16500, seed=15), 2048),
+    # the same 64 dX tiles over a 9000-word vocabulary: 35 K-steps per split,
+    # the short splits that the 65536 x 512 x 16000 workload runs on
+    (workloads.WORKLOADS[4].with_shape(T=2100, H=2048, V=9000, seed=22), 2048),
     # its dW grid (65 x 8 = 520 tiles on 256 CUs) splits the last 8 tiles four
     # ways in K and sums them in a second pass, both when the first chunk
     # stores dW and when the second accumulates into it
