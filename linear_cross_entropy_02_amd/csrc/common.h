@@ -117,6 +117,17 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Block id -> logical block index such that consecutive logical blocks run
+// on one XCD.  The hardware hands consecutive block ids to the 8 XCDs in
+// turn, each with its own L2; blocks whose rows share cache lines should sit
+// on the same one.  A bijection on [0, gridDim.x).
+__device__ __forceinline__ int xcd_local_block() {
+  const int nblk = (int)gridDim.x, bid = (int)blockIdx.x;
+  const int q = nblk >> 3, r = nblk & 7;
+  const int xcd = bid & 7, slot = bid >> 3;
+  return xcd * q + min(xcd, r) + slot;
+}
+
 // Valid target: not the ignore index and inside [0, V).  The equality test
 // comes first, so the ignore index may be a real vocabulary id.
 __device__ __forceinline__ bool target_valid(int64_t y, int64_t ignore_index, int64_t V) {

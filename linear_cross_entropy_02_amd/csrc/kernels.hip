@@ -653,7 +653,10 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   __shared__ float s_m[kFinRows], s_lse[kFinRows], s_sc[kFinRows];
   __shared__ double s_nll[kFinRows];
   const int rl = threadIdx.x % kFinRows, sl = threadIdx.x / kFinRows;
-  const int row = blockIdx.x * kFinRows + rl;
+  // a partial array row of 32 tokens (one 128-byte line) spans four row
+  // blocks: keep them on one XCD so the line is fetched into one L2
+  const int rb = xcd_local_block();
+  const int row = rb * kFinRows + rl;
   const bool live = row < a.M;
   // The first kFinCache tiles of this slice (all of them up to
   // kFinCache * kFinSlices = 1024 tiles, a 131072-column vocabulary) are
@@ -795,7 +798,7 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   if (threadIdx.x == 0 && a.loss_part) {
     double total = 0.0;
     for (int k = 0; k < kFinRows; ++k) total += s_nll[k];
-    a.loss_part[blockIdx.x] = a.first_chunk ? total : a.loss_part[blockIdx.x] + total;
+    a.loss_part[rb] = a.first_chunk ? total : a.loss_part[rb] + total;
   }
 }
 
