@@ -67,6 +67,10 @@ def parse():
                    help="token chunks per dW GEMM (the dZ^T of that many chunks is kept; "
                         "more than 1 needs (G - 1) C V more workspace; 0 = the workload's "
                         "launch configuration)")
+    p.add_argument("--weight-copy", choices=("auto", "on", "off"), default="auto",
+                   help="dX through a transposed copy of W made per call (on) or reading W "
+                        "as stored (off; bf16, no copy in the workspace); auto = the "
+                        "workload's launch configuration")
     p.add_argument("--cpu-sample", type=int, default=2048,
                    help="tokens of the workload the CPU oracle is timed on (0 = skip)")
     p.add_argument("--vocab-shards", type=int, default=1, metavar="N",
@@ -296,6 +300,8 @@ def main():
     chunk, dwc = workloads.launch_config(args.workload, mode)
     args.chunk = args.chunk or chunk
     args.dw_chunks = args.dw_chunks or dwc
+    wcopy = (workloads.weight_copy(args.workload, mode) if args.weight_copy == "auto"
+             else args.weight_copy == "on")
     t_gen = time.time()
     inp = workloads.generate(wl, keep_f32=args.cpu_sample > 0)
     X, W, y = workloads.to_torch(inp, "cuda")
@@ -309,7 +315,7 @@ def main():
         Xq, Wq, _ = workloads.to_torch(tinp, "cuda")
         del tinp
         op = flce.FusedDistillationCrossEntropy(wl.H, wl.V, Ht, wl.dtype, chunk_tokens=args.chunk,
-                                                dw_chunks=args.dw_chunks)
+                                                dw_chunks=args.dw_chunks, weight_copy=wcopy)
         out = op.distill(X, W, Xq, Wq, y, 2.0, wl.ignore_index, wl.reduction)
 
         def step():
@@ -322,7 +328,7 @@ def main():
         Vs = wl.V // n_shards
         Ws = W[:Vs].contiguous()
         op = flce.FusedLinearCrossEntropy(wl.H, Vs, wl.dtype, chunk_tokens=args.chunk,
-                                          dw_chunks=args.dw_chunks)
+                                          dw_chunks=args.dw_chunks, weight_copy=wcopy)
         red = flce.FLCE_MEAN if wl.reduction == "mean" else flce.FLCE_SUM
         parts = [torch.empty(wl.T, device="cuda") for _ in range(3)]
         amax = torch.empty(wl.T, dtype=torch.int32, device="cuda")
@@ -338,7 +344,7 @@ def main():
             assert st1 == flce.FLCE_OK and st2 == flce.FLCE_OK, (st1, st2)
     else:
         op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=args.chunk,
-                                          dw_chunks=args.dw_chunks)
+                                          dw_chunks=args.dw_chunks, weight_copy=wcopy)
     if n_shards > 1 or Ht > 0:
         pass  # step() is set above
     elif fwd_only:
@@ -446,7 +452,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "H": H, "V": V, "chunk_tokens": op.chunk_tokens,
-                   "dw_chunks": op.dw_chunks, "vocab_shards": n_shards, "V_total": wl.V,
+                   "dw_chunks": op.dw_chunks, "weight_copy": wcopy, "vocab_shards": n_shards,
+                   "V_total": wl.V,
                    "teacher_hidden": Ht,
                    "reduction": wl.reduction, "ignore_frac": wl.ignore_frac,
                    "targets": wl.targets},

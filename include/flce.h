@@ -72,15 +72,25 @@ typedef struct {
                            to a multiple of 256.  The workspace is
                            O((1+G)*C*V + V*H) and does not depend on the number
                            of tokens T.                                         */
+  int32_t flags;        /* 0 or FLCE_FLAG_NO_WEIGHT_COPY                       */
 } flce_config_t;
+
+/* The dX GEMM reads W in its stored [V x H] layout instead of a transposed
+ * copy made at every call: the workspace shrinks by H*V*2 bytes and the
+ * per-call transpose goes away, for a dX GEMM that runs about 8 % slower
+ * (its LDS reads of W are transposing 8-byte reads).  bf16 only, and
+ * V*H*2 must stay below 2^31 bytes; FLCE_ERR_UNSUPPORTED otherwise. */
+#define FLCE_FLAG_NO_WEIGHT_COPY 1
 
 typedef struct flce_handle* flce_handle_t;
 
-/* Create a handle for fixed (H, V, dtype, C, G) on the current HIP device
- * and allocate its workspace.  Returns INVALID_ARGUMENT for a bad config and
- * UNSUPPORTED when H, V rounded up to a multiple of 256, or G*C exceeds 2^20
- * (no device call is made in either case), OUT_OF_MEMORY / HIP if
- * allocation fails.  *out is set to NULL on failure. */
+/* Create a handle for fixed (H, V, dtype, C, G, flags) on the current HIP
+ * device and allocate its workspace.  Returns INVALID_ARGUMENT for a bad
+ * config (unknown flag bits included) and UNSUPPORTED when H, V rounded up to
+ * a multiple of 256, or G*C exceeds 2^20, or FLCE_FLAG_NO_WEIGHT_COPY is
+ * asked for fp32 or for V*H*2 >= 2^31 bytes (no device call is made in any
+ * of these cases), OUT_OF_MEMORY / HIP if allocation fails.  *out is set to
+ * NULL on failure. */
 flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out);
 
 /* Bytes of device workspace the handle owns (independent of T). */

@@ -42,7 +42,10 @@ EXPORTED = (
 class flce_config_t(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int64), ("vocab", ctypes.c_int64),
                 ("dtype", ctypes.c_int32), ("dw_chunks", ctypes.c_int32),
-                ("chunk_tokens", ctypes.c_int64)]
+                ("chunk_tokens", ctypes.c_int64), ("flags", ctypes.c_int32)]
+
+
+FLCE_FLAG_NO_WEIGHT_COPY = 1
 
 
 class FlceError(RuntimeError):
@@ -115,9 +118,10 @@ def last_error() -> str:
 
 
 # ------------------------------------------------------------ C-name calls ---
-def flce_create(hidden: int, vocab: int, dtype: int, chunk_tokens: int = 0, dw_chunks: int = 0):
+def flce_create(hidden: int, vocab: int, dtype: int, chunk_tokens: int = 0, dw_chunks: int = 0,
+                flags: int = 0):
     """Returns (status, handle)."""
-    cfg = flce_config_t(hidden, vocab, dtype, dw_chunks, chunk_tokens)
+    cfg = flce_config_t(hidden, vocab, dtype, dw_chunks, chunk_tokens, flags)
     h = ctypes.c_void_p()
     st = load().flce_create(ctypes.byref(cfg), ctypes.byref(h))
     return st, h
@@ -195,9 +199,9 @@ def flce_vocab_shard_backward(handle, X, W_shard, targets, T: int, ignore_index:
 
 
 def flce_distill_create(hidden: int, vocab: int, dtype: int, teacher_hidden: int,
-                        chunk_tokens: int = 0, dw_chunks: int = 0):
+                        chunk_tokens: int = 0, dw_chunks: int = 0, flags: int = 0):
     """Returns (status, handle) of a soft-target handle."""
-    cfg = flce_config_t(hidden, vocab, dtype, dw_chunks, chunk_tokens)
+    cfg = flce_config_t(hidden, vocab, dtype, dw_chunks, chunk_tokens, flags)
     h = ctypes.c_void_p()
     st = load().flce_distill_create(ctypes.byref(cfg), teacher_hidden, ctypes.byref(h))
     return st, h
@@ -253,14 +257,15 @@ class FusedLinearCrossEntropy:
     """
 
     def __init__(self, hidden: int, vocab: int, dtype="bf16", chunk_tokens: int = 0,
-                 dw_chunks: int = 0):
+                 dw_chunks: int = 0, weight_copy: bool = True):
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("FusedLinearCrossEntropy needs a HIP device")
         self.torch_dtype = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
         self.dtype = FLCE_BF16 if dtype == "bf16" else FLCE_F32
         self.hidden, self.vocab = hidden, vocab
-        st, h = flce_create(hidden, vocab, self.dtype, chunk_tokens, dw_chunks)
+        flags = 0 if weight_copy else FLCE_FLAG_NO_WEIGHT_COPY
+        st, h = flce_create(hidden, vocab, self.dtype, chunk_tokens, dw_chunks, flags)
         if st != FLCE_OK:
             raise FlceError(st, "flce_create")
         self.handle = h
@@ -418,15 +423,16 @@ class FusedDistillationCrossEntropy(FusedLinearCrossEntropy):
     teacher head's, both evaluated on the fly (see flce_distill_fwd_bwd)."""
 
     def __init__(self, hidden: int, vocab: int, teacher_hidden: int, dtype="bf16",
-                 chunk_tokens: int = 0, dw_chunks: int = 0):
+                 chunk_tokens: int = 0, dw_chunks: int = 0, weight_copy: bool = True):
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("FusedDistillationCrossEntropy needs a HIP device")
         self.torch_dtype = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
         self.dtype = FLCE_BF16 if dtype == "bf16" else FLCE_F32
         self.hidden, self.vocab, self.teacher_hidden = hidden, vocab, teacher_hidden
+        flags = 0 if weight_copy else FLCE_FLAG_NO_WEIGHT_COPY
         st, h = flce_distill_create(hidden, vocab, self.dtype, teacher_hidden, chunk_tokens,
-                                    dw_chunks)
+                                    dw_chunks, flags)
         if st != FLCE_OK:
             raise FlceError(st, "flce_distill_create")
         self.handle = h

@@ -60,6 +60,7 @@ struct flce_handle {
   int G = 1;               // chunks per dW GEMM
   int64_t Ht = 0;          // teacher hidden size (soft-target handles only)
   int splitk_alloc = 1;  // split-K planes the workspace holds for a full chunk
+  bool w_copy = true;      // dX reads W^T (a copy made per call) or W as stored
   size_t ws_bytes = 0;
   char* ws = nullptr;
   void* Wt = nullptr;      // W^T           [H x Vpad]
@@ -220,6 +221,11 @@ static flce_status_t create_impl(const flce_config_t* cfg, int64_t Ht, flce_hand
   C = round_up(C, 256);
   const int64_t G = cfg->dw_chunks ? cfg->dw_chunks : 1;
   if (C * G > (1 << 20)) return FLCE_ERR_UNSUPPORTED;
+  if (cfg->flags & ~FLCE_FLAG_NO_WEIGHT_COPY) return FLCE_ERR_INVALID_ARGUMENT;
+  const bool no_wcopy = (cfg->flags & FLCE_FLAG_NO_WEIGHT_COPY) != 0;
+  // W as stored: bf16 transposing LDS reads; one buffer descriptor spans W,
+  // whose size must stay below the out-of-range offset (2^31) that reads 0
+  if (no_wcopy && (dt != Dt::BF16 || V * H * 2 >= ((int64_t)1 << 31))) return FLCE_ERR_UNSUPPORTED;
 
   flce_handle* h = new (std::nothrow) flce_handle();
   if (!h) return FLCE_ERR_OUT_OF_MEMORY;
@@ -238,6 +244,7 @@ static flce_status_t create_impl(const flce_config_t* cfg, int64_t Ht, flce_hand
   h->V = V;
   h->C = C;
   h->G = (int)G;
+  h->w_copy = !no_wcopy;
   h->Vpad = round_up(V, 256);
   h->nt = cdiv64(V, kPartialWidth);
   {
@@ -253,7 +260,7 @@ static flce_status_t create_impl(const flce_config_t* cfg, int64_t Ht, flce_hand
     off += round_up((int64_t)bytes, 256);
     return o;
   };
-  const size_t oWt = carve((size_t)H * h->Vpad * es);
+  const size_t oWt = h->w_copy ? carve((size_t)H * h->Vpad * es) : 0;
   const size_t oP = carve((size_t)C * h->Vpad * es);
   const size_t oPt = carve((size_t)h->Vpad * h->G * C * es);
   const size_t oXt = carve((size_t)H * h->G * C * es);
@@ -280,7 +287,7 @@ static flce_status_t create_impl(const flce_config_t* cfg, int64_t Ht, flce_hand
     (void)hipGetLastError();
     return st == FLCE_ERR_HIP ? FLCE_ERR_OUT_OF_MEMORY : st;
   }
-  h->Wt = h->ws + oWt;
+  h->Wt = h->w_copy ? h->ws + oWt : nullptr;
   h->P = h->ws + oP;
   h->Pt = h->ws + oPt;
   h->Xt = h->ws + oXt;
@@ -401,9 +408,11 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
     return FLCE_OK;
   }
 
-  // W^T (zero-padded to Vpad columns): K-contiguous operand of dX = dZ W.
-  FLCE_LAUNCH(K_TRANSPOSE_W,
-              launch_transpose(dt, W, (int)V, (int)H, H, h->Wt, Vpad, (int)Vpad, s));
+  // W^T (zero-padded to Vpad columns): K-contiguous operand of dX = dZ W,
+  // unless the handle reads W as stored.
+  if (h->w_copy)
+    FLCE_LAUNCH(K_TRANSPOSE_W,
+                launch_transpose(dt, W, (int)V, (int)H, H, h->Wt, Vpad, (int)Vpad, s));
 
   const int64_t KV = round_up(V, 64);  // K-depth of the dX GEMM
   for (int64_t t0 = 0, c = 0; t0 < T; t0 += C, ++c) {
@@ -554,11 +563,19 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       GemmOutArgs ga{};
       ga.A = h->P;
       ga.lda = Vpad;
-      ga.B = h->Wt;
-      ga.ldb = Vpad;
+      if (h->w_copy) {
+        ga.B = h->Wt;
+        ga.ldb = Vpad;
+        ga.K = (int)KV;
+      } else {
+        // W's V rows as stored; dZ's columns from V on are zero
+        ga.B = W;
+        ga.ldb = H;
+        ga.K = (int)V;
+        ga.b_stored = true;
+      }
       ga.M = (int)Cc;
       ga.N = (int)H;
-      ga.K = (int)KV;
       ga.accumulate = false;
       char* dXc = (char*)dX + (size_t)t0 * H * es;
       if (splits == 1) {

@@ -42,6 +42,18 @@
 // Grid order is XCD-aware: consecutive logical tiles land on one XCD (its
 // own L2), walking M fastest inside groups of `group_m` rows of tiles so
 // that blocks sharing a B tile run together.
+//
+// BT (bf16 only): B is given as stored, K rows of N contiguous elements
+// (dX = dZ W reading W itself rather than a transposed copy).  A B stage is
+// then 64 k-rows of BN elements; its fragments come from ds_read_b64_tr_b16,
+// which in each group of 16 lanes hands slot i of lane d the element d % 4
+// of what lane 4 i + d / 4 read.  Two such reads (k-rows k and k + 4) give
+// lane l its column l % 16 at 8 consecutive k when lane s reads k-row
+// 8 (s / 16) + (s % 16) / 4, columns 4 (s % 4) .. +3.  The 16-byte units of
+// k-row r sit at unit ^ tr_swz(r), which keeps those reads free of bank
+// conflicts.  The reads move 8 bytes per lane instead of 16, so this engine
+// runs ~8 % slower than with a transposed copy of B; it saves the copy's
+// memory.
 #pragma once
 
 #include "common.h"
@@ -147,6 +159,25 @@ struct TileGeom {
 // Position of k-vector `kv` (0..7) of LDS row `row` within a stage.
 __device__ __forceinline__ int swz(int row, int kv) { return row * 8 + (kv ^ (row & 7)); }
 
+// BT stages: position of 16-byte unit u of k-row r is u ^ tr_swz(r).  The
+// four k-rows one lane group reads land in four different 32-byte windows,
+// and the groups served in the same cycle (k-rows 8 apart) in different
+// 128-byte halves of the banks.
+__device__ __forceinline__ int tr_swz(int r) { return (2 * (r & 3)) ^ (8 * ((r >> 3) & 1)); }
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+// 8 bytes per lane from LDS, transposed within each group of 16 lanes.
+__device__ __forceinline__ uint2 lds_read_tr16(uint32_t byte_addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const v4s_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s_t*)(size_t)byte_addr);
+  return __builtin_bit_cast(uint2, v);
+#else
+  (void)byte_addr;
+  return make_uint2(0u, 0u);
+#endif
+}
+
 // What every epilogue receives: the wave's accumulator fragments and where
 // they sit.  The MFMAs take the B fragment as their first operand, so each
 // fragment holds a 16 x 16 block of C transposed: acc[i][j][r] is
@@ -223,7 +254,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 //       threaded through them.
 // The wave never waits on LDS after the barrier: the fragments its MFMAs
 // need were read before it.
-template <typename T, int BM, int BN, int WAVES, class Epi>
+template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false>
 __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi epi) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the launch stub
   using G = TileGeom<BM, BN, WAVES>;
@@ -233,6 +264,8 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
   constexpr int A_INS = BM / (8 * WAVES);  // 16-byte loads per lane per stage (A)
   constexpr int B_INS = BN / (8 * WAVES);
   constexpr int FM = G::FM, FN = G::FN;
+  static_assert(!BT || (sizeof(T) == 2 && WAVES == 4), "stored-layout B: bf16, 4 waves");
+  constexpr int UPR = BN / 8;  // BT: 16-byte units per k-row of a B stage
   extern __shared__ uint4 lds[];  // G::kLdsBytes, sized at launch
 
   const TileCoord tc = map_tile(g);
@@ -252,8 +285,11 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
   const int a_rows = min(BM, g.M - m0), b_rows = min(BN, g.N - n0);
   const i4v rA =
       make_rsrc((const T*)g.A + (int64_t)m0 * g.lda, (uint32_t)((int64_t)a_rows * g.lda * ES));
-  const i4v rB =
-      make_rsrc((const T*)g.B + (int64_t)n0 * g.ldb, (uint32_t)((int64_t)b_rows * g.ldb * ES));
+  // BT: from B's column n0 over all K rows (the host keeps K ldb ES < 2^31,
+  // below the out-of-range offset)
+  const i4v rB = BT ? make_rsrc((const T*)g.B + n0, (uint32_t)((int64_t)g.K * g.ldb * ES))
+                    : make_rsrc((const T*)g.B + (int64_t)n0 * g.ldb,
+                                (uint32_t)((int64_t)b_rows * g.ldb * ES));
 
   // Direct-to-LDS loads write lane i of a wave's load to the LDS slot
   // base + 16 i.  Slot p of a stage holds row p / 8 and logical k-vector
@@ -267,10 +303,24 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
     const int row = wave * (BM / WAVES) + 8 * j + (lane >> 3);
     a_off[j] = (uint32_t)(((int64_t)row * g.lda + kv_lane * EPV) * ES);
   }
+  // BT: slot p of a B stage holds k-row p / UPR, unit (p % UPR) ^ tr_swz(row);
+  // b_krow is that k-row, b_nin whether the unit's columns lie inside N.
+  int b_krow[B_INS];
+  bool b_nin[B_INS];
 #pragma unroll
   for (int j = 0; j < B_INS; ++j) {
-    const int row = wave * (BN / WAVES) + 8 * j + (lane >> 3);
-    b_off[j] = (uint32_t)(((int64_t)row * g.ldb + kv_lane * EPV) * ES);
+    if constexpr (!BT) {
+      const int row = wave * (BN / WAVES) + 8 * j + (lane >> 3);
+      b_off[j] = (uint32_t)(((int64_t)row * g.ldb + kv_lane * EPV) * ES);
+      b_krow[j] = 0;
+      b_nin[j] = true;
+    } else {
+      const int p = wave * (16 * UPR) + 64 * j + lane;
+      const int r = p / UPR, u = (p % UPR) ^ tr_swz(p / UPR);
+      b_off[j] = (uint32_t)(((int64_t)r * g.ldb + 8 * u) * ES);
+      b_krow[j] = r;
+      b_nin[j] = n0 + 8 * u < g.N;
+    }
   }
   const uint32_t lds_base = (uint32_t)(size_t)((lds_ptr_t)lds);
   const uint32_t lds_a = lds_base + wave * (BM * 8 / WAVES) * 16;
@@ -297,8 +347,26 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
     dma16(rA, lds_a + (uint32_t)ab * G::kABufBytes + 1024 * j, kin ? a_off[j] : kOobOffset, k0 * ES);
   };
   auto issue_b = [&](int bb, int k0, int j) {
-    const bool kin = kv_lane * EPV < k_end - k0;
-    dma16(rB, lds_b + (uint32_t)bb * G::kBBufBytes + 1024 * j, kin ? b_off[j] : kOobOffset, k0 * ES);
+    if constexpr (!BT) {
+      const bool kin = kv_lane * EPV < k_end - k0;
+      dma16(rB, lds_b + (uint32_t)bb * G::kBBufBytes + 1024 * j, kin ? b_off[j] : kOobOffset,
+            k0 * ES);
+    } else {
+      const bool in = b_nin[j] && b_krow[j] < k_end - k0;
+      dma16(rB, lds_b + (uint32_t)bb * G::kBBufBytes + 1024 * j, in ? b_off[j] : kOobOffset,
+            (uint32_t)((int64_t)k0 * g.ldb * ES));
+    }
+  };
+  // BT fragment: columns n16 .. n16 + 15 of the stage in B buffer bb, substep s
+  const int tr_g = lane >> 4, tr_i = (lane >> 2) & 3, tr_q = lane & 3;
+  auto read_b_tr = [&](int bb, int n16, int s) -> uint4 {
+    const uint32_t buf = lds_base + 3 * G::kABufBytes + (uint32_t)bb * G::kBBufBytes;
+    const int u = (n16 >> 3) + (tr_q >> 1);
+    const int k0r = 32 * s + 8 * tr_g + tr_i;
+    const uint2 lo = lds_read_tr16(buf + k0r * (BN * 2) + ((u ^ tr_swz(k0r)) << 4) + (tr_q & 1) * 8);
+    const uint2 hi =
+        lds_read_tr16(buf + (k0r + 4) * (BN * 2) + ((u ^ tr_swz(k0r + 4)) << 4) + (tr_q & 1) * 8);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
   };
   // Fragment read r of substep s from A buffer ab / B buffer bb: r < FM
   // reads A fragment r, else B fragment r - FM.
@@ -306,9 +374,11 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
     const int kv = 4 * s + (lane >> 4);
     if (r < FM)
       fa[r] = lds[ab * (G::kABufBytes / 16) + swz(wm * G::WM + 16 * r + (lane & 15), kv)];
-    else
+    else if constexpr (!BT)
       fb[r - FM] = lds[(3 * G::kABufBytes + bb * G::kBBufBytes) / 16 +
                        swz(wn * G::WN + 16 * (r - FM) + (lane & 15), kv)];
+    else
+      fb[r - FM] = read_b_tr(bb, wn * G::WN + 16 * (r - FM), s);
   };
 
   constexpr int NR = FM + FN;  // fragment reads per substep

@@ -56,6 +56,9 @@ struct GemmOutArgs {
   // summed, with the old output, by a second pass.  nullptr: never split.
   float* tail_part = nullptr;
   size_t tail_part_bytes = 0;
+  // B as stored, K rows of N contiguous elements (ldb >= N), rather than
+  // N x K: bf16 only, not accumulating, K * ldb * 2 < 2^31 bytes.
+  bool b_stored = false;
 };
 hipError_t launch_gemm_store(Dt dt, TileCfg tc, const GemmOutArgs& a, hipStream_t s);
 

@@ -299,7 +299,7 @@ __global__ void __launch_bounds__(256) tile_reduce_kernel(GemmShape g, const flo
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-template <typename T, int BM, int BN, int WAVES, class Epi>
+template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false>
 static hipError_t run_gemm(const GemmShape& g0, const Epi& epi, hipStream_t s) {
   using G = TileGeom<BM, BN, WAVES>;
   GemmShape g = g0;
@@ -316,16 +316,16 @@ static hipError_t run_gemm(const GemmShape& g0, const Epi& epi, hipStream_t s) {
   if (g.tile_first < 0 || g.tile_first + g.tile_count > g.tiles_m * g.tiles_n)
     return hipErrorInvalidValue;
   const int nblk = g.tile_count * g.splits;
-  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, WAVES, Epi>), dim3(nblk), dim3(G::kThreads),
+  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, WAVES, Epi, BT>), dim3(nblk), dim3(G::kThreads),
                      G::kLdsBytes, s, g, epi);
   return hipGetLastError();
 }
 
 // The GEMM kernels use more than the default 64 KB of dynamic LDS.
-template <typename T, int BM, int BN, int WAVES, class Epi>
+template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false>
 static hipError_t set_lds_attr() {
   using G = TileGeom<BM, BN, WAVES>;
-  return hipFuncSetAttribute((const void*)gemm_nt_kernel<T, BM, BN, WAVES, Epi>,
+  return hipFuncSetAttribute((const void*)gemm_nt_kernel<T, BM, BN, WAVES, Epi, BT>,
                              hipFuncAttributeMaxDynamicSharedMemorySize, G::kLdsBytes);
 }
 
@@ -341,6 +341,12 @@ static hipError_t setup_t() {
   if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<T, false>>()) != hipSuccess) return e;
   if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<float, false>>()) != hipSuccess) return e;
   if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<float, true>>()) != hipSuccess) return e;
+  if constexpr (std::is_same<T, bf16>::value) {  // dX reading W as stored
+    if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<T, false>, true>()) != hipSuccess) return e;
+    if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<float, false>, true>()) != hipSuccess) return e;
+    if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<T, false>, true>()) != hipSuccess) return e;
+    if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<float, false>, true>()) != hipSuccess) return e;
+  }
   return hipSuccess;
 }
 
@@ -429,6 +435,13 @@ static hipError_t store_t2(TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
   epi.N = a.N;
   epi.split_stride = a.split_stride;
   epi.accumulate = ACC && a.accumulate;
+  if (a.b_stored) {
+    if constexpr (std::is_same<T, bf16>::value && !ACC) {
+      if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4, StoreEpi<TO, ACC>, true>(g, epi, s);
+      return run_gemm<T, 256, 256, 4, StoreEpi<TO, ACC>, true>(g, epi, s);
+    }
+    return hipErrorInvalidValue;
+  }
   if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4>(g, epi, s);
   if constexpr (ACC) {
     // The grid's last partial round (rem tiles, under half the CUs busy for

@@ -76,6 +76,29 @@ def test_create_reports_unsupported_sizes_without_device(lib, hidden, vocab, chu
     assert not h.value
 
 
+@pytest.mark.parametrize("hidden,vocab,dtype,flags,status", [
+    (64, 100, flce.FLCE_BF16, 2, flce.FLCE_ERR_INVALID_ARGUMENT),          # unknown flag bit
+    (64, 100, flce.FLCE_BF16, -1, flce.FLCE_ERR_INVALID_ARGUMENT),
+    (64, 100, flce.FLCE_F32, flce.FLCE_FLAG_NO_WEIGHT_COPY, flce.FLCE_ERR_UNSUPPORTED),  # fp32
+    # W of 2^31 bytes or more: one buffer descriptor no longer spans it below
+    # the out-of-range offset
+    (8192, 131072, flce.FLCE_BF16, flce.FLCE_FLAG_NO_WEIGHT_COPY, flce.FLCE_ERR_UNSUPPORTED),
+])
+def test_create_checks_flags_without_device(lib, hidden, vocab, dtype, flags, status):
+    st, h = flce.flce_create(hidden, vocab, dtype, 0, 0, flags)
+    assert st == status
+    assert not h.value
+
+
+def test_config_layout_matches_header():
+    # the ctypes mirror of flce_config_t: field offsets as C lays them out
+    c = flce.flce_config_t
+    assert [(n, getattr(c, n).offset) for n, _ in c._fields_] == [
+        ("hidden", 0), ("vocab", 8), ("dtype", 16), ("dw_chunks", 20), ("chunk_tokens", 24),
+        ("flags", 32)]
+    assert ctypes.sizeof(c) == 40
+
+
 def test_create_null_arguments(lib):
     assert lib.flce_create(None, None) == flce.FLCE_ERR_INVALID_ARGUMENT
     h = ctypes.c_void_p()

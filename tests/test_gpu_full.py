@@ -45,7 +45,8 @@ def run_full(cfg):
     inp = workloads.generate(wl)
     X, W, y = workloads.to_torch(inp, "cuda")
     chunk, g = CHUNK[cfg]
-    op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=chunk, dw_chunks=g)
+    op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=chunk, dw_chunks=g,
+                                      weight_copy=workloads.weight_copy(cfg))
     print(f"[gpu-full] workload {cfg} on GPU, chunk {op.chunk_tokens}, dw_chunks {op.dw_chunks}, "
           f"workspace {op.workspace_bytes / 2**20:.0f} MiB", flush=True)
     out = op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction)
@@ -53,6 +54,8 @@ def run_full(cfg):
     # the workspace holds logits-shaped chunk buffers of C x Vpad (exp / dZ)
     # and G C x Vpad (dZ^T of a dW group): together below T x V
     assert (1 + op.dw_chunks) * op.chunk_tokens < wl.T, "chunk buffers must stay below T x V"
+    # and the whole workspace below a bf16 T x V buffer
+    assert op.workspace_bytes < wl.T * wl.V * 2, (op.workspace_bytes, wl.T * wl.V * 2)
     res = {k: to_np(v) for k, v in out.items()}
     op.close()
     del X, W, y, out

@@ -14,7 +14,7 @@ from oracle import flce_reference
 pytestmark = pytest.mark.gpu
 
 
-def run(wl, chunk=0, inp=None, out=None, op=None, dw_chunks=0):
+def run(wl, chunk=0, inp=None, out=None, op=None, dw_chunks=0, weight_copy=True):
     import torch
     if inp is None:
         inp = workloads.generate(wl)
@@ -22,9 +22,9 @@ def run(wl, chunk=0, inp=None, out=None, op=None, dw_chunks=0):
     own = op is None
     if own:
         op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=chunk,
-                                          dw_chunks=dw_chunks)
+                                          dw_chunks=dw_chunks, weight_copy=weight_copy)
     print(f"[gpu] {wl.name} T={wl.T} H={wl.H} V={wl.V} {wl.dtype} chunk={op.chunk_tokens} "
-          f"dw_chunks={op.dw_chunks}", flush=True)
+          f"dw_chunks={op.dw_chunks} weight_copy={weight_copy}", flush=True)
     res = op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction, out=out)
     torch.cuda.synchronize()
     if own:
@@ -92,6 +92,42 @@ DW_GROUP_CASES = [
 def test_parity_dw_chunk_groups(wl, chunk, g):
     inp, out = run(wl, chunk, dw_chunks=g)
     check_full(out, oracle(inp, wl), inp, wl)
+
+
+# dX reading W as stored (transposing LDS reads, no W^T copy): 128-wide
+# tiles with ragged T/H/V, H % 64 != 0, 256-wide tiles split four ways in K,
+# a full 256-wide grid on the outlier-row head, degenerate sizes
+NO_WCOPY_CASES = [
+    (workloads.WORKLOADS[2].with_shape(T=1000, H=96, V=1000, seed=41), 256),
+    (workloads.WORKLOADS[2].with_shape(T=777, H=264, V=2049, seed=42), 512),
+    (workloads.WORKLOADS[4].with_shape(T=2100, H=2048, V=9000, seed=43), 2048),
+    (workloads.WORKLOADS[5].with_shape(T=2100, H=8192, V=3000, seed=44), 2048),
+    (workloads.WORKLOADS[2].with_shape(T=300, H=8, V=50, seed=45), 256),
+]
+
+
+@pytest.mark.parametrize("wl,chunk", NO_WCOPY_CASES, ids=[c[0].name for c in NO_WCOPY_CASES])
+def test_parity_no_weight_copy(wl, chunk):
+    import torch
+    inp = workloads.generate(wl)
+    inp, out = run(wl, chunk, inp=inp, weight_copy=False)
+    check_full(out, oracle(inp, wl), inp, wl)
+    # the same products in the same order as through the copy: bit for bit
+    _, ref = run(wl, chunk, inp=inp)
+    for k in ("loss", "dX", "dW", "lse", "argmax", "n_valid"):
+        assert torch.equal(out[k], ref[k]), k
+
+
+def test_no_weight_copy_workspace_and_dtype():
+    wl = workloads.WORKLOADS[2].with_shape(T=300, H=256, V=3000, seed=46)
+    a = flce.FusedLinearCrossEntropy(wl.H, wl.V, "bf16", chunk_tokens=256)
+    b = flce.FusedLinearCrossEntropy(wl.H, wl.V, "bf16", chunk_tokens=256, weight_copy=False)
+    vpad = -(-wl.V // 256) * 256
+    assert a.workspace_bytes - b.workspace_bytes == wl.H * vpad * 2
+    a.close()
+    b.close()
+    with pytest.raises(flce.FlceError):
+        flce.FusedLinearCrossEntropy(64, 300, "f32", weight_copy=False)
 
 
 def test_all_tokens_ignored():

@@ -91,6 +91,16 @@ LAUNCH = {1: (256, 1), 2: (1024, 1), 3: (8192, 1), 4: (2048, 4), 5: (2048, 2)}
 LAUNCH_MODES = {"forward": (4096, 1), "shard": (4096, 1), "distill": (2048, 3)}
 
 
+# Workloads whose handle reads W as stored in the dX GEMM instead of a
+# transposed copy made per call: the 8192 x 8192 x 128256 head, where that
+# copy alone is as large as a bf16 T x V buffer.
+NO_WEIGHT_COPY = {5}
+
+
+def weight_copy(n: int, mode: str = "fwd_bwd") -> bool:
+    return not (mode == "fwd_bwd" and n in NO_WEIGHT_COPY)
+
+
 def launch_config(n: int, mode: str = "fwd_bwd") -> tuple[int, int]:
     if mode != "fwd_bwd":
         return LAUNCH_MODES[mode]
