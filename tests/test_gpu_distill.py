@@ -11,7 +11,7 @@ from oracle import distill_reference, flce_reference
 pytestmark = pytest.mark.gpu
 
 
-def run(wl, Ht, tau, chunk, teacher_seed, same_teacher=False):
+def run(wl, Ht, tau, chunk, teacher_seed, same_teacher=False, weight_copy=True):
     import torch
     inp = workloads.generate(wl)
     if same_teacher:
@@ -24,7 +24,8 @@ def run(wl, Ht, tau, chunk, teacher_seed, same_teacher=False):
         Xq_np, Wq_np = tinp.X, tinp.W
         X, W, y = workloads.to_torch(inp, "cuda")
         Xq, Wq, _ = workloads.to_torch(tinp, "cuda")
-    op = flce.FusedDistillationCrossEntropy(wl.H, wl.V, Ht, wl.dtype, chunk_tokens=chunk)
+    op = flce.FusedDistillationCrossEntropy(wl.H, wl.V, Ht, wl.dtype, chunk_tokens=chunk,
+                                            weight_copy=weight_copy)
     print(f"[gpu-distill] {wl.name} T={wl.T} H={wl.H} Ht={Ht} V={wl.V} tau={tau} "
           f"chunk={op.chunk_tokens}", flush=True)
     out = op.distill(X, W, Xq, Wq, y, tau, wl.ignore_index, wl.reduction)
@@ -42,12 +43,17 @@ CASES = [
     (workloads.WORKLOADS[1], 32, 0.7, 0),
     (workloads.WORKLOADS[1].with_shape(T=200, V=777, seed=74), 48, 3.0, 64),
 ]
+CASES = [c + (True,) for c in CASES] + [
+    # the student's dX reading W as stored
+    (workloads.WORKLOADS[4].with_shape(T=600, H=512, V=20000, seed=76), 512, 1.0, 256, False),
+]
 
 
-@pytest.mark.parametrize("wl,Ht,tau,chunk", CASES,
-                         ids=[f"{c[0].name}-Ht{c[1]}-tau{c[2]}" for c in CASES])
-def test_distill_vs_oracle(wl, Ht, tau, chunk):
-    inp, res, ref = run(wl, Ht, tau, chunk, teacher_seed=wl.seed + 500)
+@pytest.mark.parametrize("wl,Ht,tau,chunk,wcopy", CASES,
+                         ids=[f"{c[0].name}-Ht{c[1]}-tau{c[2]}" + ("" if c[4] else "-no-wcopy")
+                              for c in CASES])
+def test_distill_vs_oracle(wl, Ht, tau, chunk, wcopy):
+    inp, res, ref = run(wl, Ht, tau, chunk, teacher_seed=wl.seed + 500, weight_copy=wcopy)
     assert abs(float(res["loss"]) - ref["loss"]) <= LOSS_RTOL * abs(ref["loss"]), \
         (float(res["loss"]), ref["loss"])
     assert int(res["n_valid"]) == ref["n_valid"]

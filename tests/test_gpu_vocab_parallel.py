@@ -18,7 +18,7 @@ from oracle import count_valid, flce_reference, scale_factor
 pytestmark = pytest.mark.gpu
 
 
-def run_sharded(wl, cuts, chunk=256):
+def run_sharded(wl, cuts, chunk=256, weight_copy=True):
     import torch
     inp = workloads.generate(wl)
     X, W, y = workloads.to_torch(inp, "cuda")
@@ -26,7 +26,8 @@ def run_sharded(wl, cuts, chunk=256):
     print(f"[gpu-vocab-parallel] {wl.name} T={wl.T} H={wl.H} V={wl.V} shards {bounds}", flush=True)
     shards = []
     for v0, v1 in zip(bounds[:-1], bounds[1:]):
-        op = flce.FusedLinearCrossEntropy(wl.H, v1 - v0, wl.dtype, chunk_tokens=chunk)
+        op = flce.FusedLinearCrossEntropy(wl.H, v1 - v0, wl.dtype, chunk_tokens=chunk,
+                                          weight_copy=weight_copy)
         Ws = W[v0:v1].contiguous()
         part = op.shard_forward(X, Ws, y, v0, wl.V, wl.ignore_index)
         shards.append((op, v0, Ws, {k: to_np(v) for k, v in part.items()}))
@@ -56,16 +57,23 @@ def run_sharded(wl, cuts, chunk=256):
 
 
 CASES = [
+    # (workload, shard boundaries, dX through a W^T copy)
     (workloads.WORKLOADS[4].with_shape(T=600, H=512, V=20000, seed=61), (7000, 13001)),
     (workloads.WORKLOADS[5].with_shape(T=700, H=256, V=12345, seed=62), (6000,)),
     (workloads.WORKLOADS[2].with_shape(T=1000, H=96, V=1000, seed=63), (100, 300, 999)),
     (workloads.WORKLOADS[1].with_shape(T=200, V=777, seed=64), (300,)),
 ]
+CASES = [c + (True,) for c in CASES] + [
+    # shards whose dX reads W_shard as stored
+    (workloads.WORKLOADS[4].with_shape(T=600, H=512, V=20000, seed=65), (7000, 13001), False),
+]
 
 
-@pytest.mark.parametrize("wl,cuts", CASES, ids=[f"{c[0].name}-{len(c[1]) + 1}shards" for c in CASES])
-def test_vocab_parallel_vs_oracle(wl, cuts):
-    inp, got = run_sharded(wl, cuts)
+@pytest.mark.parametrize("wl,cuts,wcopy", CASES,
+                         ids=[f"{c[0].name}-{len(c[1]) + 1}shards" + ("" if c[2] else "-no-wcopy")
+                              for c in CASES])
+def test_vocab_parallel_vs_oracle(wl, cuts, wcopy):
+    inp, got = run_sharded(wl, cuts, weight_copy=wcopy)
     ref = flce_reference(inp.X, inp.W, inp.y, wl.ignore_index, wl.reduction)
     assert abs(got["loss"] - ref["loss"]) <= LOSS_RTOL * abs(ref["loss"])
     assert np.abs(got["lse"] - ref["lse"]).max() <= LSE_ATOL
