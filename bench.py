@@ -71,7 +71,7 @@ def parse():
                    help="dX through a transposed copy of W made per call (on) or reading W "
                         "as stored (off; bf16, no copy in the workspace); auto = the "
                         "workload's launch configuration")
-    p.add_argument("--cpu-sample", type=int, default=2048,
+    p.add_argument("--cpu-sample", type=int, default=3072,
                    help="tokens of the workload the CPU oracle is timed on (0 = skip)")
     p.add_argument("--vocab-shards", type=int, default=1, metavar="N",
                    help="time one device's share of an N-way vocabulary-parallel head: "
