@@ -77,7 +77,7 @@ typedef struct {
 
 /* The dX GEMM reads W in its stored [V x H] layout instead of a transposed
  * copy made at every call: the workspace shrinks by H*V*2 bytes and the
- * per-call transpose goes away, for a dX GEMM that runs about 8 % slower
+ * per-call transpose goes away, for a dX GEMM that runs 8-12 % slower
  * (its LDS reads of W are transposing 8-byte reads).  bf16 only, and
  * V*H*2 must stay below 2^31 bytes; FLCE_ERR_UNSUPPORTED otherwise. */
 #define FLCE_FLAG_NO_WEIGHT_COPY 1

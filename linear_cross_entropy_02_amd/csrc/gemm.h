@@ -52,7 +52,7 @@
 // 8 (s / 16) + (s % 16) / 4, columns 4 (s % 4) .. +3.  The 16-byte units of
 // k-row r sit at unit ^ tr_swz(r), which keeps those reads free of bank
 // conflicts.  The reads move 8 bytes per lane instead of 16, so this engine
-// runs ~8 % slower than with a transposed copy of B; it saves the copy's
+// runs 8-12 % slower than with a transposed copy of B; it saves the copy's
 // memory.
 #pragma once
 
