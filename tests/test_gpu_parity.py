@@ -41,7 +41,6 @@ CASES = [
     (workloads.WORKLOADS[1], 0),                                            # tiny fp32, full
     (workloads.WORKLOADS[1].with_shape(T=200, V=777, seed=7), 64),          # fp32 ragged, 4 chunks
     (workloads.WORKLOADS[2], 0),                                            # page-1 layer shape, full
-    (workloads.WORKLOADS[2], workloads.launch_config(2)[0]),                # same, as benchmarked
     (workloads.WORKLOADS[2].with_shape(T=1000, H=96, V=1000, seed=11), 256),  # ragged T/H/V
     (workloads.WORKLOADS[2].with_shape(T=777, H=264, V=2049, seed=12), 512),  # H % 64 != 0
     (workloads.WORKLOADS[4].with_shape(T=600, H=1024, V=20000, seed=13), 256),  # zipf head
@@ -75,6 +74,16 @@ def test_parity_vs_oracle(wl, chunk):
     inp, out = run(wl, chunk)
     ref = oracle(inp, wl)
     check_full(out, ref, inp, wl)
+
+
+@pytest.mark.parametrize("n", [1, 2])
+def test_parity_as_benchmarked(n):
+    # the two small workloads in full, in the launch configuration bench.py
+    # times (the large ones: test_gpu_full.py)
+    wl = workloads.WORKLOADS[n]
+    chunk, g = workloads.launch_config(n)
+    inp, out = run(wl, chunk, dw_chunks=g, weight_copy=workloads.weight_copy(n))
+    check_full(out, oracle(inp, wl), inp, wl)
 
 
 # dW over groups of G chunks: full groups, a last group cut short by the
