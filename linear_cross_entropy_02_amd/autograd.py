@@ -26,16 +26,16 @@ _lock = threading.Lock()
 
 
 def _handle(device: torch.device, stream: torch.cuda.Stream, H: int, V: int, dtype: str,
-            chunk_tokens: int, dw_chunks: int) -> FusedLinearCrossEntropy:
+            chunk_tokens: int, dw_chunks: int, weight_copy: bool = True) -> FusedLinearCrossEntropy:
     """One handle per (device, stream, shape, dtype, chunking): a handle owns
     its workspace and must not be used by two streams at once."""
-    key = (device.index, stream.cuda_stream, H, V, dtype, chunk_tokens, dw_chunks)
+    key = (device.index, stream.cuda_stream, H, V, dtype, chunk_tokens, dw_chunks, weight_copy)
     with _lock:
         op = _handles.get(key)
         if op is None:
             with torch.cuda.device(device):
                 op = FusedLinearCrossEntropy(H, V, dtype, chunk_tokens=chunk_tokens,
-                                             dw_chunks=dw_chunks)
+                                             dw_chunks=dw_chunks, weight_copy=weight_copy)
             _handles[key] = op
         return op
 
@@ -52,7 +52,7 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
     @staticmethod
     @torch.amp.custom_fwd(device_type="cuda", cast_inputs=torch.bfloat16)
     def forward(ctx, X, W, targets, ignore_index: int = -100, reduction: str = "mean",
-                chunk_tokens: int = 0, dw_chunks: int = 0):
+                chunk_tokens: int = 0, dw_chunks: int = 0, weight_copy: bool = True):
         if X.dim() != 2 or W.dim() != 2 or X.shape[1] != W.shape[1]:
             raise ValueError("X must be [T, H] and W [V, H]")
         if X.dtype != W.dtype or X.dtype not in (torch.bfloat16, torch.float32):
@@ -64,7 +64,8 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
         W = W.contiguous()
         targets = targets.contiguous()
         stream = torch.cuda.current_stream(X.device)
-        op = _handle(X.device, stream, X.shape[1], W.shape[0], dtype, chunk_tokens, dw_chunks)
+        op = _handle(X.device, stream, X.shape[1], W.shape[0], dtype, chunk_tokens, dw_chunks,
+                     weight_copy)
         out = op.fwd_bwd(X, W, targets, ignore_index, reduction)
         ctx.save_for_backward(out["dX"], out["dW"])
         ctx.w_dtype = W.dtype
@@ -78,19 +79,20 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
         g = grad_loss.to(torch.float32)
         gX = (dX.to(torch.float32) * g).to(dX.dtype) if ctx.needs_input_grad[0] else None
         gW = (dW * g).to(ctx.w_dtype) if ctx.needs_input_grad[1] else None
-        return gX, gW, None, None, None, None, None
+        return gX, gW, None, None, None, None, None, None
 
 
 def linear_cross_entropy(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
                          ignore_index: int = -100, reduction: str = "mean",
                          chunk_tokens: int = 0, dw_chunks: int = 0,
-                         return_lse: bool = False):
+                         return_lse: bool = False, weight_copy: bool = True):
     """Cross-entropy of softmax(X W^T) against `targets`, fused: the T x V
     logits are never formed.  Returns the scalar loss (and the per-token
     log-sum-exp when `return_lse`); gradients reach X and W through
-    autograd."""
+    autograd.  weight_copy=False (bf16) has the dX contraction read W as
+    stored instead of a transposed copy made per call, for less memory."""
     loss, lse = LinearCrossEntropyFunction.apply(X, W, targets, ignore_index, reduction,
-                                                 chunk_tokens, dw_chunks)
+                                                 chunk_tokens, dw_chunks, weight_copy)
     return (loss, lse) if return_lse else loss
 
 

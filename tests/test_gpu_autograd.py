@@ -27,14 +27,16 @@ def check_grads(X, W, ref, scale, dtype_name):
     assert rel_frob(to_np(W.grad), scale * ref["dW"]) <= GRAD_RTOL[dtype_name]
 
 
-def test_backward_matches_oracle():
+@pytest.mark.parametrize("weight_copy", [True, False])
+def test_backward_matches_oracle(weight_copy):
     import torch
     from linear_cross_entropy_02_amd.autograd import linear_cross_entropy
     inp = workloads.generate(WL)
     X, W, y = leaves(inp, torch.bfloat16)
-    print(f"[gpu-autograd] {WL.name} T={WL.T} H={WL.H} V={WL.V}", flush=True)
+    print(f"[gpu-autograd] {WL.name} T={WL.T} H={WL.H} V={WL.V} weight_copy={weight_copy}",
+          flush=True)
     loss, lse = linear_cross_entropy(X, W, y, WL.ignore_index, WL.reduction, chunk_tokens=256,
-                                     return_lse=True)
+                                     return_lse=True, weight_copy=weight_copy)
     loss.backward()
     torch.cuda.synchronize()
     ref = flce_reference(inp.X, inp.W, inp.y, WL.ignore_index, WL.reduction)
