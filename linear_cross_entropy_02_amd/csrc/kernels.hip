@@ -442,24 +442,28 @@ static hipError_t store_t2(TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
     }
     return hipErrorInvalidValue;
   }
-  if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4>(g, epi, s);
   if constexpr (ACC) {
     // The grid's last partial round (rem tiles, under half the CUs busy for
     // a whole tile) is split 2-4 ways in K instead: the full rounds run as
     // usual, the rem tiles' K-slices write fp32 partial tiles, and a pass
-    // sums them (with the old output) in a fixed order.
+    // sums them (with the old output) in a fixed order.  A 256-wide grid of
+    // under half a round splits whole that way rather than fall back to
+    // 128-wide tiles.
     constexpr int BK = 8 * Elem<T>::kVec;
     const int tiles = cdiv(a.M, 256) * cdiv(a.N, 256);
     const int nfull = tiles / g_num_cus * g_num_cus, rem = tiles - nfull;
     const int sp = rem > 0 ? min(4, g_num_cus / rem) : 0;
-    if (a.tail_part && g.splits == 1 && nfull >= g_num_cus && rem > 0 && 2 * rem <= g_num_cus &&
-        cdiv(a.K, BK) >= 8 * sp &&
+    if (a.tail_part && g.splits == 1 && (nfull >= g_num_cus || (nfull == 0 && tc != TileCfg::T256)) &&
+        rem > 0 && 2 * rem <= g_num_cus && cdiv(a.K, BK) >= 8 * sp &&
         (size_t)sp * rem * 256 * 256 * sizeof(float) <= a.tail_part_bytes) {
-      GemmShape gm = g;
-      gm.tile_first = 0;
-      gm.tile_count = nfull;
-      hipError_t e = run_gemm<T, 256, 256, 4>(gm, epi, s);
-      if (e != hipSuccess) return e;
+      if (nfull > 0) {
+        GemmShape gm = g;
+        gm.tile_first = 0;
+        gm.tile_count = nfull;
+        hipError_t e = run_gemm<T, 256, 256, 4>(gm, epi, s);
+        if (e != hipSuccess) return e;
+      }
+      hipError_t e;
       GemmShape gt = g;
       gt.tile_first = nfull;
       gt.tile_count = rem;
@@ -479,6 +483,7 @@ static hipError_t store_t2(TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
       return hipGetLastError();
     }
   }
+  if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4>(g, epi, s);
   return run_gemm<T, 256, 256, 4>(g, epi, s);
 }
 

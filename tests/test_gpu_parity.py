@@ -55,6 +55,10 @@ CASES = [
     # ways in K and sums them in a second pass, both when the first chunk
     # stores dW and when the second accumulates into it
     (workloads.WORKLOADS[4].with_shape(T=4200, H=2048, V=16500, seed=18), 2048),
+    # an 8192-token chunk at H = 512, V = 16000: its 126 dW tiles (under half
+    # a round) split two ways in K as a whole; the 108-token second chunk
+    # accumulates through 128-wide tiles
+    (workloads.WORKLOADS[3].with_shape(T=8300, seed=23), 8192),
     # 38 x 16 = 608 dW tiles: the last 96 split two ways
     (workloads.WORKLOADS[4].with_shape(T=4200, H=4096, V=9700, seed=19), 2048),
     # the same split of the dW grid on fp32 operands
