@@ -456,6 +456,7 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       qa.inv_temp = soft->inv_temp;
       FLCE_LAUNCH(K_LOGITS, launch_logits(dt, qa, s));
       FinalizeArgs qf{};
+      qf.block_rows = finalize_rows(nt, C);
       qf.M = (int)Cc;
       qf.nt = (int)nt;
       qf.V = (int)V;
@@ -501,6 +502,7 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
     FLCE_LAUNCH(K_LOGITS, launch_logits(dt, la, s));
 
     FinalizeArgs fa{};
+    fa.block_rows = finalize_rows(nt, C);
     fa.M = (int)Cc;
     fa.nt = (int)nt;
     fa.V = (int)V;
@@ -625,7 +627,7 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
     }
   }
   if (loss) {
-    const int nparts = (int)cdiv64(T < C ? T : C, kFinalizeRows);  // finalize blocks of the first chunk
+    const int nparts = (int)cdiv64(T < C ? T : C, finalize_rows(nt, C));  // finalize blocks of the first chunk
     FLCE_LAUNCH(K_LOSS, launch_loss(h->loss_part, nparts, h->nvalid, rsum, loss, s));
   }
 #undef FLCE_LAUNCH
@@ -681,6 +683,7 @@ flce_status_t run_forward(flce_handle_t h, const void* X, const void* W, const i
     FLCE_LAUNCH(K_LOGITS, launch_logits(dt, la, s));
 
     FinalizeArgs fa{};
+    fa.block_rows = finalize_rows(nt, C);
     fa.M = (int)Cc;
     fa.nt = (int)nt;
     fa.V = (int)V;
@@ -708,7 +711,7 @@ flce_status_t run_forward(flce_handle_t h, const void* X, const void* W, const i
     FLCE_LAUNCH(K_FINALIZE, launch_finalize(fa, s));
   }
   if (loss) {
-    const int nparts = (int)cdiv64(T < C ? T : C, kFinalizeRows);
+    const int nparts = (int)cdiv64(T < C ? T : C, finalize_rows(nt, C));
     FLCE_LAUNCH(K_LOSS, launch_loss(h->loss_part, nparts, h->nvalid, rsum, loss, s));
   }
 #undef FLCE_LAUNCH

@@ -97,11 +97,15 @@ struct FinalizeArgs {
   int32_t* argmax_out;   // nullable, chunk-relative
   float* logprob_out;    // nullable, chunk-relative: z_target - lse (0 if ignored)
   bool backward;         // also form dzt and turn pm into alpha
-  double* loss_part;     // one slot per kFinalizeRows rows; nullable
+  double* loss_part;     // one slot per block_rows rows; nullable
   int first_chunk;
+  int block_rows = 8;    // finalize_rows(nt, C): 8 or 32
 };
-// Rows per finalize block, hence rows per loss partial.
+// Rows per finalize block, hence rows per loss partial: 32 when rows hold
+// at most 256 partial tiles and a chunk of C rows still gives 256 blocks,
+// else 8.  kFinalizeRows is the smaller, which sizes the partial buffer.
 constexpr int kFinalizeRows = 8;
+inline int finalize_rows(int64_t nt, int64_t C) { return nt <= 256 && C >= 8192 ? 32 : 8; }
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
 
 struct FixupArgs {

@@ -663,21 +663,26 @@ hipError_t launch_transpose(Dt dt, const void* src, int rows, int cols, int64_t 
 //   2. sum = sum_j s_j exp(m_j - m), lse = m + ln sum (the merge of
 //      online-softmax states: each partial sum rescaled to the common max);
 //   3. alpha_j = s valid exp(m_j - lse), overwriting m_j.
-constexpr int kFinRows = kFinalizeRows, kFinSlices = 1024 / kFinRows, kFinCache = 8;
+// ROWS rows per block, 1024 / ROWS slices of each row's partials per row:
+// 8 x 128 for long rows (a 128256-word vocabulary has 1002 partial tiles),
+// 32 x 32 for rows of at most 256 tiles, which otherwise leave most slices
+// idle and spend the block's time in three 128-slice tree reductions.
+template <int ROWS>
 __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
+  constexpr int kFinRows = ROWS, kFinSlices = 1024 / ROWS, kFinCache = 8;
   __shared__ float s_f[kFinSlices][kFinRows + 1];
   __shared__ float s_c[kFinSlices][kFinRows + 1];
   __shared__ int s_i[kFinSlices][kFinRows + 1];
   __shared__ float s_m[kFinRows], s_lse[kFinRows], s_sc[kFinRows];
   __shared__ double s_nll[kFinRows];
   const int rl = threadIdx.x % kFinRows, sl = threadIdx.x / kFinRows;
-  // a partial array row of 32 tokens (one 128-byte line) spans four row
-  // blocks: keep them on one XCD so the line is fetched into one L2
+  // a partial array row of 32 tokens (one 128-byte line) spans 32 / ROWS
+  // row blocks: keep them on one XCD so the line is fetched into one L2
   const int rb = xcd_local_block();
   const int row = rb * kFinRows + rl;
   const bool live = row < a.M;
   // The first kFinCache tiles of this slice (all of them up to
-  // kFinCache * kFinSlices = 1024 tiles, a 131072-column vocabulary) are
+  // kFinCache * kFinSlices tiles: 1024 with 8 rows per block) are
   // read once, all loads in flight together, and kept in registers for the
   // three passes; tiles beyond are read again by each pass.
   float cm[kFinCache], cs[kFinCache];
@@ -822,8 +827,12 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
 
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(finalize_kernel, dim3(cdiv(a.M, kFinRows)), dim3(kFinRows * kFinSlices), 0, s,
-                     a);
+  if (a.block_rows == 32)
+    hipLaunchKernelGGL(finalize_kernel<32>, dim3(cdiv(a.M, 32)), dim3(1024), 0, s, a);
+  else if (a.block_rows == 8)
+    hipLaunchKernelGGL(finalize_kernel<8>, dim3(cdiv(a.M, 8)), dim3(1024), 0, s, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
