@@ -82,6 +82,7 @@ struct flce_handle {
   int64_t* nvalid = nullptr;
   float* scale = nullptr;
   int64_t* bad = nullptr;
+  long long* count_part = nullptr;  // per-block target counts of long batches
   // timing
   bool timing = false;
   std::vector<Pending> pending;
@@ -272,6 +273,7 @@ static flce_status_t create_impl(const flce_config_t* cfg, int64_t Ht, flce_hand
   const size_t olp = carve((size_t)cdiv64(C, kFinalizeRows) * 8);
   const size_t osk = h->splitk_alloc > 1 ? carve((size_t)h->splitk_alloc * C * H * 4) : 0;
   const size_t osc = carve(64);
+  const size_t ocp = carve(2 * kCountBlocks * sizeof(long long));
   // soft targets: the teacher's exponentials and partials, and the cross partials
   const size_t oPq = Ht ? carve((size_t)C * h->Vpad * es) : 0;
   const size_t opmq = Ht ? carve((size_t)C * h->nt * 4) : 0;
@@ -301,6 +303,7 @@ static flce_status_t create_impl(const flce_config_t* cfg, int64_t Ht, flce_hand
   h->nvalid = (int64_t*)(h->ws + osc);
   h->scale = (float*)(h->ws + osc + 16);
   h->bad = (int64_t*)(h->ws + osc + 32);
+  h->count_part = (long long*)(h->ws + ocp);
   if (Ht) {
     h->Pq = h->ws + oPq;
     h->pmq = (float*)(h->ws + opmq);
@@ -398,7 +401,7 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
   } while (0)
 
   FLCE_LAUNCH(K_COUNT, launch_count(targets, T, ignore_index, cols.v_total, rsum, h->nvalid,
-                                    h->scale, h->bad, n_valid, s));
+                                    h->scale, h->bad, n_valid, h->count_part, s));
   if (T == 0) {
     FLCE_LAUNCH(K_ZERO, launch_zero(dW, (size_t)V * H * 4, s));
     if (loss) {
@@ -652,7 +655,7 @@ flce_status_t run_forward(flce_handle_t h, const void* X, const void* W, const i
   } while (0)
 
   FLCE_LAUNCH(K_COUNT, launch_count(targets, T, ignore_index, cols.v_total, rsum, h->nvalid,
-                                    h->scale, h->bad, n_valid, s));
+                                    h->scale, h->bad, n_valid, h->count_part, s));
   if (T == 0) {
     if (loss) {
       FLCE_LAUNCH(K_ZERO, launch_zero(h->loss_part, 8, s));

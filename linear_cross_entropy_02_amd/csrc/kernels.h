@@ -62,9 +62,12 @@ struct GemmOutArgs {
 };
 hipError_t launch_gemm_store(Dt dt, TileCfg tc, const GemmOutArgs& a, hipStream_t s);
 
+// part: scratch for per-block counts, 2 * kCountBlocks values (nullable: one
+// block counts every target).
+constexpr int kCountBlocks = 64;
 hipError_t launch_count(const int64_t* y, int64_t T, int64_t ignore_index, int64_t V,
                         int reduction_sum, int64_t* n_valid, float* scale, int64_t* bad,
-                        int64_t* n_valid_out, hipStream_t s);
+                        int64_t* n_valid_out, long long* part, hipStream_t s);
 
 // dst[c][r] = src[r][c] for r < rows, 0 for rows <= r < rows_out; c < cols.
 hipError_t launch_transpose(Dt dt, const void* src, int rows, int cols, int64_t ld_src,

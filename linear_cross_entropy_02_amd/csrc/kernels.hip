@@ -502,16 +502,30 @@ hipError_t launch_gemm_store(Dt dt, TileCfg tc, const GemmOutArgs& a, hipStream_
 // n_valid = number of targets that are not the ignore index (the masked
 // mean's denominator, "Information theory > implementing the loss");
 // out-of-range targets are counted separately and treated as ignored.
+__device__ __forceinline__ void count_finish(long long n, long long nb, int reduction_sum,
+                                             int64_t* n_valid, float* scale, int64_t* bad,
+                                             int64_t* n_valid_out) {
+  *n_valid = n;
+  *bad = nb;
+  // backward seed: 1 for the sum, 1/n for the mean (0 when n = 0)
+  *scale = reduction_sum ? 1.f : (n > 0 ? 1.f / (float)n : 0.f);
+  if (n_valid_out) *n_valid_out = n;
+}
+
+// Counts over a grid-stride range of the targets: a grid of one block writes
+// the results, a larger grid writes per-block counts to part ([nblk] valid,
+// then [nblk] out of range) for count_sum_kernel.
 __global__ void __launch_bounds__(1024) count_kernel(const int64_t* __restrict__ y, int64_t T,
                                                      int64_t ignore_index, int64_t V,
                                                      int reduction_sum, int64_t* n_valid,
                                                      float* scale, int64_t* bad,
-                                                     int64_t* n_valid_out) {
+                                                     int64_t* n_valid_out, long long* part) {
   __shared__ long long s_nv[1024], s_nb[1024];
   long long nv = 0, nb = 0;
   // unrolled so that eight independent target loads are in flight per thread
 #pragma unroll 8
-  for (int64_t t = threadIdx.x; t < T; t += 1024) {
+  for (int64_t t = (int64_t)blockIdx.x * 1024 + threadIdx.x; t < T;
+       t += (int64_t)gridDim.x * 1024) {
     const int64_t v = y[t];
     if (v != ignore_index) {
       if (v >= 0 && v < V)
@@ -531,20 +545,40 @@ __global__ void __launch_bounds__(1024) count_kernel(const int64_t* __restrict__
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    const long long n = s_nv[0];
-    *n_valid = n;
-    *bad = s_nb[0];
-    // backward seed: 1 for the sum, 1/n for the mean (0 when n = 0)
-    *scale = reduction_sum ? 1.f : (n > 0 ? 1.f / (float)n : 0.f);
-    if (n_valid_out) *n_valid_out = n;
+    if (gridDim.x == 1) {
+      count_finish(s_nv[0], s_nb[0], reduction_sum, n_valid, scale, bad, n_valid_out);
+    } else {
+      part[blockIdx.x] = s_nv[0];
+      part[gridDim.x + blockIdx.x] = s_nb[0];
+    }
   }
+}
+
+// Sum of the per-block counts (integers: exact in any order).
+__global__ void count_sum_kernel(const long long* __restrict__ part, int nblk, int reduction_sum,
+                                 int64_t* n_valid, float* scale, int64_t* bad,
+                                 int64_t* n_valid_out) {
+  if (threadIdx.x != 0) return;
+  long long nv = 0, nb = 0;
+  for (int i = 0; i < nblk; ++i) {
+    nv += part[i];
+    nb += part[nblk + i];
+  }
+  count_finish(nv, nb, reduction_sum, n_valid, scale, bad, n_valid_out);
 }
 
 hipError_t launch_count(const int64_t* y, int64_t T, int64_t ignore_index, int64_t V,
                         int reduction_sum, int64_t* n_valid, float* scale, int64_t* bad,
-                        int64_t* n_valid_out, hipStream_t s) {
-  hipLaunchKernelGGL(count_kernel, dim3(1), dim3(1024), 0, s, y, T, ignore_index, V, reduction_sum,
-                     n_valid, scale, bad, n_valid_out);
+                        int64_t* n_valid_out, long long* part, hipStream_t s) {
+  // one block up to 32768 targets; beyond, a block per 8192 of them, at most
+  // kCountBlocks, and a second pass over their counts
+  const int64_t want = (T + 8191) / 8192;
+  const int nblk = (part && T >= 32768) ? (int)(want < kCountBlocks ? want : kCountBlocks) : 1;
+  hipLaunchKernelGGL(count_kernel, dim3(nblk), dim3(1024), 0, s, y, T, ignore_index, V,
+                     reduction_sum, n_valid, scale, bad, n_valid_out, part);
+  if (nblk > 1)
+    hipLaunchKernelGGL(count_sum_kernel, dim3(1), dim3(64), 0, s, (const long long*)part, nblk,
+                       reduction_sum, n_valid, scale, bad, n_valid_out);
   return hipGetLastError();
 }
 

@@ -218,6 +218,29 @@ def test_out_of_range_targets_are_counted_and_ignored():
     op.close()
 
 
+@pytest.mark.parametrize("T", [32767, 40000, 700000])
+def test_target_counts_of_long_batches(T):
+    # from 32768 targets on, blocks count slices of the batch and a second
+    # pass sums them: n_valid and the out-of-range count stay exact
+    import dataclasses
+    import torch
+    wl = dataclasses.replace(workloads.WORKLOADS[2].with_shape(T=T, H=8, V=50, seed=26),
+                             ignore_frac=0.3)
+    inp = workloads.generate(wl)
+    y_bad = inp.y.copy()
+    bad_rows = np.random.default_rng(5).choice(T, size=37, replace=False)
+    y_bad[bad_rows] = wl.V + 3
+    X, W, _ = workloads.to_torch(inp, "cuda")
+    y = torch.from_numpy(y_bad).to("cuda")
+    op = flce.FusedLinearCrossEntropy(wl.H, wl.V, "bf16", chunk_tokens=8192)
+    out = op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction)
+    st, bad = flce.flce_query_error(op.handle)
+    assert st == flce.FLCE_ERR_BAD_TARGET and bad == 37
+    valid = (y_bad != wl.ignore_index) & (y_bad >= 0) & (y_bad < wl.V)
+    assert int(out["n_valid"].item()) == int(valid.sum())
+    op.close()
+
+
 def test_bad_arguments_rejected_without_work():
     import torch
     op = flce.FusedLinearCrossEntropy(64, 300, "bf16")
