@@ -52,6 +52,14 @@ PROFILE_CMDS = {
             "--no-timing",
     "mfma_util": "rocprofv3 --pmc MfmaUtil --output-format csv -d gpurun_out/prof_mfma_util -o run -- "
                  "python3 bench.py --steps 1 --warmup 1 --cpu-sample 0 --no-timing",
+    "stall1": "rocprofv3 --pmc SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_ANY "
+              "SQ_ACTIVE_INST_LDS SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVES --output-format csv "
+              "-d gpurun_out/prof_stall1 -o run -- python3 bench.py --steps 1 --warmup 1 --cpu-sample 0 "
+              "--no-timing",
+    "stall2": "rocprofv3 --pmc SQ_LDS_CMD_FIFO_FULL SQ_LDS_DATA_FIFO_FULL SQ_LDS_IDX_ACTIVE "
+              "SQ_ACTIVE_INST_VMEM SQ_INST_LEVEL_LDS SQ_INST_LEVEL_VMEM SQ_BUSY_CYCLES GRBM_GUI_ACTIVE "
+              "--output-format csv -d gpurun_out/prof_stall2 -o run -- python3 bench.py --steps 1 "
+              "--warmup 1 --cpu-sample 0 --no-timing",
 }
 
 
@@ -213,6 +221,38 @@ def summarize_profiles(d: str):
                      f"{100.0 * bc / act if act else 0.0:.2f} |")
     lines += ["", f"Kernel sources hash at measurement: {kernel_source_hash()}"]
     with open(os.path.join(PROFILES, "mfma_lds_counters_llama3_8b_head.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # wait and FIFO counters of the GEMMs (both passes optional)
+    try:
+        s1, s2 = per_kernel("prof_stall1"), per_kernel("prof_stall2")
+    except OSError:
+        return
+    times = {short_kernel_name(r["Name"]): float(r["AverageNs"]) * 1e-9 for r in stats}
+    lines = ["# GEMM stall counters per launch, fused linear-CE fwd+bwd, llama3-8b head (T=16384, "
+             "H=4096, V=128256, bf16, chunk 2048, 4 chunks per dW GEMM)", "",
+             "Commands (repo root, MI355X), one counter pass each:", "",
+             "    " + PROFILE_CMDS["stall1"], "    " + PROFILE_CMDS["stall2"], "",
+             "Cycles per launch = GRBM_GUI_ACTIVE / 8 XCDs; SIMD-cycles = that x 1024 SIMDs (one "
+             "wave per SIMD). MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / SIMD-cycles; the SQ_WAIT_* "
+             "counters count quad-cycles (x 4). Clock = cycles / the launch time of the kernel-time "
+             "summary.", "",
+             "| kernel | cycles / launch | clock GHz | MFMA busy | waiting on waitcnt / barrier | "
+             "waiting for LDS issue | LDS command FIFO full cycles | LDS data FIFO full cycles |",
+             "|---|---|---|---|---|---|---|---|"]
+    for k, a in sorted(s1.items(), key=lambda kv: -kv[1].get("SQ_VALU_MFMA_BUSY_CYCLES", 0)):
+        b = s2.get(k, {})
+        if a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) <= 0 or not b.get("GRBM_GUI_ACTIVE"):
+            continue
+        cyc = b["GRBM_GUI_ACTIVE"] / 8
+        simd = cyc * 1024
+        clk = f"{cyc / times[k] / 1e9:.2f}" if times.get(k) else "n/a"
+        lines.append(f"| {k} | {cyc:.3e} | {clk} | {100 * a['SQ_VALU_MFMA_BUSY_CYCLES'] / simd:.1f} % | "
+                     f"{100 * 4 * a['SQ_WAIT_ANY'] / simd:.1f} % | "
+                     f"{100 * 4 * a['SQ_WAIT_INST_LDS'] / simd:.1f} % | "
+                     f"{b.get('SQ_LDS_CMD_FIFO_FULL', 0):.2e} | {b.get('SQ_LDS_DATA_FIFO_FULL', 0):.0f} |")
+    lines += ["", f"Kernel sources hash at measurement: {kernel_source_hash()}"]
+    with open(os.path.join(PROFILES, "gemm_stall_counters_llama3_8b_head.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
