@@ -1,7 +1,8 @@
 """GPU parity on seeded random launch settings and shapes.
 
 Each case draws T, H, V, the chunk size, the chunks per dW GEMM, the dtype,
-the reduction and the share of ignored tokens from its own seed, so the
+the reduction, the share of ignored tokens and (bf16) whether dX reads a
+transposed copy of W or W as stored, from its own seed, so the
 combinations the hand-picked cases do not name (a batch shorter than one
 chunk, a hidden size that is a multiple of 8 but not of 64, a vocabulary
 below one tile, groups cut short by the batch) are compared with the
@@ -34,17 +35,21 @@ def draw(seed):
         base, name=f"random{seed}-{dtype}-T{T}-H{H}-V{V}-C{chunk}-G{g}", T=T, H=H, V=V,
         seed=5000 + seed, reduction=str(rng.choice(["mean", "sum"])),
         ignore_frac=float(rng.choice([0.0, 0.05, 0.3])))
-    return wl, chunk, g
+    # from a stream of its own, so the draws above stay what they were
+    wcopy = dtype == "f32" or bool(np.random.default_rng(seed + 7919).random() < 0.5)
+    return wl, chunk, g, wcopy
 
 
-@pytest.mark.parametrize("seed", list(range(24)))
+@pytest.mark.parametrize("seed", list(range(32)))
 def test_random_shape_vs_oracle(seed):
     import torch
-    wl, chunk, g = draw(seed)
+    wl, chunk, g, wcopy = draw(seed)
     inp = workloads.generate(wl)
     X, W, y = workloads.to_torch(inp, "cuda")
-    op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=chunk, dw_chunks=g)
-    print(f"[gpu-random] {wl.name} {wl.reduction} ignore {wl.ignore_frac}", flush=True)
+    op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=chunk, dw_chunks=g,
+                                      weight_copy=wcopy)
+    print(f"[gpu-random] {wl.name} {wl.reduction} ignore {wl.ignore_frac} weight_copy {wcopy}",
+          flush=True)
     out = op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction)
     torch.cuda.synchronize()
     op.close()
