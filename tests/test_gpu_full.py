@@ -143,3 +143,25 @@ def test_full_large_ragged_head():
     wl, inp, res = run_full(5)
     n_valid = check_properties(wl, inp, res)
     check_sampled_rows(wl, inp, res, n_valid, seed=5)
+
+
+def test_full_llama3_head_weight_as_stored_is_bitwise_equal():
+    # dX reading W as stored adds the same products in the same order as
+    # through the W^T copy, so at full size every output is the same bits
+    import torch
+    wl = workloads.WORKLOADS[4]
+    print("[gpu-full] generating workload 4 for the weight-copy comparison", flush=True)
+    inp = workloads.generate(wl, keep_f32=False)
+    X, W, y = workloads.to_torch(inp, "cuda")
+    chunk, g = CHUNK[4]
+    outs = []
+    for wcopy in (True, False):
+        op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=chunk, dw_chunks=g,
+                                          weight_copy=wcopy)
+        print(f"[gpu-full] workload 4, weight_copy {wcopy}, workspace "
+              f"{op.workspace_bytes / 2**20:.0f} MiB", flush=True)
+        outs.append(op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction))
+        torch.cuda.synchronize()
+        op.close()
+    for k in ("loss", "dX", "dW", "lse", "argmax", "n_valid"):
+        assert torch.equal(outs[0][k], outs[1][k]), k
