@@ -37,7 +37,7 @@ from typing import Dict, Iterable, Optional
 
 import numpy as np
 
-__all__ = ["flce_reference", "flce_bruteforce", "flce_rows", "validity",
+__all__ = ["flce_reference", "flce_bruteforce", "flce_rows", "flce_dw_rows", "validity",
            "count_valid", "scale_factor", "distill_reference", "distill_bruteforce"]
 
 
@@ -194,6 +194,42 @@ def flce_rows(X: np.ndarray, W: np.ndarray, y: np.ndarray, rows: Iterable[int],
             dX += dZ[:, v0:v0 + block] @ np.asarray(W[v0:v0 + block], dtype=np.float64)
         res["dX"] = dX
     return res
+
+
+def flce_dw_rows(X: np.ndarray, W: np.ndarray, y: np.ndarray, vrows: Iterable[int],
+                 lse: np.ndarray, n_valid: int, ignore_index: int = -100,
+                 reduction: str = "mean", block: int = 8192) -> np.ndarray:
+    """Rows `vrows` of dW = dZ^T X, given every token's lse.
+
+    Same definitions as flce_reference restricted to a sample of vocabulary
+    rows: dZ_tv = s valid_t (exp(z_tv - lse_t) - [v = y_t]) for the listed v
+    only (Alisa's book of LLMs, gradient of softmax + CE loss; Backpropagation
+    for the mean's 1/n), and dW_v = sum_t dZ_tv X_t (Neural net basics, batch
+    rule: the shared weight's gradient sums over the tokens).  `lse` is the
+    oracle's own per-token lse over the whole vocabulary (flce_reference with
+    want_grads=False), and n_valid the global count, so full-size problems
+    are checked on their vocabulary rows without the T x V gradient.
+    """
+    vrows = np.array(list(vrows), dtype=np.int64)
+    V, H = W.shape
+    y = np.asarray(y, dtype=np.int64)
+    lse = np.asarray(lse, dtype=np.float64)
+    s = scale_factor(n_valid, reduction)
+    valid = validity(y, ignore_index)
+    if np.any(valid & ((y < 0) | (y >= V))):
+        raise ValueError("target out of range")
+    Wv = np.asarray(W[vrows], dtype=np.float64)                # [nv x H]
+    out = np.zeros((len(vrows), H), dtype=np.float64)
+    T = len(y)
+    for t0 in range(0, T, block):
+        t1 = min(T, t0 + block)
+        Xb = np.asarray(X[t0:t1], dtype=np.float64)
+        Z = Xb @ Wv.T                                          # z_tv, sampled v
+        D = np.exp(Z - lse[t0:t1, None])
+        D -= (y[t0:t1, None] == vrows[None, :])
+        D *= (s * valid[t0:t1].astype(np.float64))[:, None]
+        out += D.T @ Xb
+    return out
 
 
 def flce_bruteforce(X, W, y, ignore_index: int = -100, reduction: str = "mean") -> Dict[str, object]:

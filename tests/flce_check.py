@@ -4,6 +4,17 @@ Tolerances are the ones the method is held to: loss within 1e-3 relative,
 lse within 1e-3 absolute, dX and dW within 2e-2 relative Frobenius error for
 bf16 inputs (1e-5 for fp32), n_valid and the ignore mask exact, argmax exact
 outside an fp32 rounding margin.
+
+The gradients are also checked row by row (each row of dX and dW against
+its own oracle norm, plus a floor of 1e-3 times the rows' root-mean-square
+norm), so a wrong set of low-magnitude rows -- rarely targeted vocabulary
+rows of dW, say -- cannot hide under the Frobenius norm of the rest.  The
+per-row bound is the whole-tensor one for bf16.  For fp32 it is 1e-4: the
+fp32 matrix instructions form each product to about 2^-17 relative (a CPU
+emulation that splits each fp32 operand into three bf16 terms and keeps the
+three leading cross products reproduces the measured lse error, 6e-6 at
+|lse| = 12, and the worst row of dW, 2-3e-5), and a dW row whose softmax
+mass sits on a few tokens inherits that relative error of their logits.
 """
 from __future__ import annotations
 
@@ -14,6 +25,7 @@ import numpy as np
 LOSS_RTOL = 1e-3
 LSE_ATOL = 1e-3
 GRAD_RTOL = {"bf16": 2e-2, "f32": 1e-5}
+GRAD_ROW_RTOL = {"bf16": 2e-2, "f32": 1e-4}
 
 
 def rel_frob(a, b) -> float:
@@ -23,6 +35,32 @@ def rel_frob(a, b) -> float:
     if nb == 0:
         return float(np.linalg.norm(a))
     return float(np.linalg.norm(a - b) / nb)
+
+
+def rel_rows(a, b, floor_frac: float = 1e-3):
+    """Per-row error ||a_i - b_i|| / (||b_i|| + floor), floor = floor_frac x
+    the rows' root-mean-square norm; returns (max, index of the max)."""
+    a = np.asarray(a, dtype=np.float64).reshape(len(a), -1)
+    b = np.asarray(b, dtype=np.float64).reshape(len(b), -1)
+    if len(b) == 0:
+        return 0.0, -1
+    nb = np.sqrt((b * b).sum(axis=1))
+    floor = floor_frac * float(np.sqrt((nb * nb).mean()))
+    if floor == 0.0:
+        floor = 1e-300
+    e = np.sqrt(((a - b) ** 2).sum(axis=1)) / (nb + floor)
+    i = int(np.argmax(e))
+    return float(e[i]), i
+
+
+def check_grad(name: str, got, want, dtype: str):
+    """Whole-tensor relative Frobenius error within GRAD_RTOL[dtype] and the
+    per-row error within GRAD_ROW_RTOL[dtype]."""
+    e = rel_frob(got, want)
+    assert e <= GRAD_RTOL[dtype], f"{name} rel err {e}"
+    er, i = rel_rows(got, want)
+    assert er <= GRAD_ROW_RTOL[dtype], f"{name} row {i}: rel err {er} (whole tensor {e})"
+    return e, er
 
 
 def to_np(t):
@@ -63,7 +101,6 @@ def check_argmax(gpu_idx, ora_idx, ora_zmax, X, W, rows, delta):
 
 def check_full(out, ref, inp, wl):
     """Element-by-element parity of every output against the full oracle."""
-    tol = GRAD_RTOL[wl.dtype]
     loss = float(out["loss"].item())
     if ref["loss"] == 0.0:
         assert loss == 0.0
@@ -78,12 +115,10 @@ def check_full(out, ref, inp, wl):
         dX = to_np(out["dX"])
         ign = inp.y == wl.ignore_index
         assert np.all(dX[ign] == 0.0), "ignored rows of dX must be exactly zero"
-        e = rel_frob(dX, ref["dX"])
-        assert e <= tol, f"dX rel err {e}"
+        check_grad("dX", dX, ref["dX"], wl.dtype)
         rows = np.arange(T)
         delta = argmax_margin(inp.X, inp.W, rows)
         check_argmax(to_np(out["argmax"]), ref["argmax"], ref["zmax"], inp.X, inp.W, rows, delta)
     dW = to_np(out["dW"])
     assert np.isfinite(dW).all()
-    e = rel_frob(dW, ref["dW"])
-    assert e <= tol, f"dW rel err {e}"
+    check_grad("dW", dW, ref["dW"], wl.dtype)

@@ -315,6 +315,35 @@ def test_rows_sampler_matches_full_oracle():
     np.testing.assert_allclose(rr["dX"], full["dX"][rows], rtol=1e-11, atol=1e-16)
 
 
+def test_dw_row_sampler_matches_full_oracle():
+    wl = workloads.WORKLOADS[4].with_shape(T=150, H=48, V=2500, seed=78)
+    inp = workloads.generate(wl)
+    full = orc.flce_reference(inp.X, inp.W, inp.y, wl.ignore_index, wl.reduction)
+    fwd = orc.flce_reference(inp.X, inp.W, inp.y, wl.ignore_index, wl.reduction,
+                             want_grads=False)
+    vs = [0, 1, 7, int(inp.y[3]), 1999, 2499]
+    got = orc.flce_dw_rows(inp.X, inp.W, inp.y, vs, fwd["lse"], full["n_valid"],
+                           wl.ignore_index, wl.reduction, block=64)
+    np.testing.assert_allclose(got, full["dW"][vs], rtol=1e-11, atol=1e-16)
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_dw_row_sampler_zero_weight_closed_form(reduction):
+    # W = 0: every softmax is uniform and lse = ln V, so
+    # dW_v = s (sum_{valid t} X_t / V - sum_{valid t, y_t = v} X_t)
+    T, H, V = 41, 6, 13
+    X, _, y = rand_problem(T, H, V, 3)
+    W = np.zeros((V, H))
+    valid = y != -100
+    n = int(valid.sum())
+    s = 1.0 / n if reduction == "mean" else 1.0
+    vs = [0, 4, 12]
+    got = orc.flce_dw_rows(X, W, y, vs, np.full(T, math.log(V)), n, -100, reduction, block=16)
+    for k, v in enumerate(vs):
+        want = s * (X[valid].sum(axis=0) / V - X[valid & (y == v)].sum(axis=0))
+        np.testing.assert_allclose(got[k], want, rtol=0, atol=1e-13)
+
+
 # ------------------------------------------------------- statistical range ---
 @pytest.mark.parametrize("cfg,T,V", [(1, None, None), (2, None, None), (4, 64, 16384)])
 def test_p11_expected_loss_range(cfg, T, V):
