@@ -12,6 +12,12 @@ A custom Function is invisible to autocast unless it opts in (same README
 and section: autocast does not see Function.apply()), so the forward is
 decorated with custom_fwd and casts its floating inputs to bf16 when autocast
 is on; dW, computed in fp32, is handed back in W's dtype.
+
+A target that is neither ignore_index nor a vocabulary id is counted on the
+device and treated as ignored (the C ABI never synchronises to raise).  With
+check_targets=True the forward reads that count back (a stream
+synchronisation) and raises ValueError when it is not zero, as PyTorch's own
+cross-entropy would.
 """
 from __future__ import annotations
 
@@ -19,7 +25,7 @@ import threading
 
 import torch
 
-from . import FusedLinearCrossEntropy
+from . import FLCE_OK, FlceError, FusedLinearCrossEntropy, flce_query_error
 
 _handles: dict = {}
 _lock = threading.Lock()
@@ -52,7 +58,8 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
     @staticmethod
     @torch.amp.custom_fwd(device_type="cuda", cast_inputs=torch.bfloat16)
     def forward(ctx, X, W, targets, ignore_index: int = -100, reduction: str = "mean",
-                chunk_tokens: int = 0, dw_chunks: int = 0, weight_copy: bool = True):
+                chunk_tokens: int = 0, dw_chunks: int = 0, weight_copy: bool = True,
+                check_targets: bool = False):
         if X.dim() != 2 or W.dim() != 2 or X.shape[1] != W.shape[1]:
             raise ValueError("X must be [T, H] and W [V, H]")
         if X.dtype != W.dtype or X.dtype not in (torch.bfloat16, torch.float32):
@@ -67,6 +74,13 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
         op = _handle(X.device, stream, X.shape[1], W.shape[0], dtype, chunk_tokens, dw_chunks,
                      weight_copy)
         out = op.fwd_bwd(X, W, targets, ignore_index, reduction)
+        if check_targets:
+            st, bad = flce_query_error(op.handle, stream.cuda_stream)
+            if bad > 0:
+                raise ValueError(f"{bad} target(s) are neither ignore_index ({ignore_index}) nor "
+                                 f"in [0, {W.shape[0]})")
+            if st != FLCE_OK:
+                raise FlceError(st, "flce_query_error")
         ctx.save_for_backward(out["dX"], out["dW"])
         ctx.w_dtype = W.dtype
         ctx.mark_non_differentiable(out["lse"])
@@ -79,20 +93,25 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
         g = grad_loss.to(torch.float32)
         gX = (dX.to(torch.float32) * g).to(dX.dtype) if ctx.needs_input_grad[0] else None
         gW = (dW * g).to(ctx.w_dtype) if ctx.needs_input_grad[1] else None
-        return gX, gW, None, None, None, None, None, None
+        return gX, gW, None, None, None, None, None, None, None
 
 
 def linear_cross_entropy(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
                          ignore_index: int = -100, reduction: str = "mean",
                          chunk_tokens: int = 0, dw_chunks: int = 0,
-                         return_lse: bool = False, weight_copy: bool = True):
+                         return_lse: bool = False, weight_copy: bool = True,
+                         check_targets: bool = False):
     """Cross-entropy of softmax(X W^T) against `targets`, fused: the T x V
     logits are never formed.  Returns the scalar loss (and the per-token
     log-sum-exp when `return_lse`); gradients reach X and W through
     autograd.  weight_copy=False (bf16) has the dX contraction read W as
-    stored instead of a transposed copy made per call, for less memory."""
+    stored instead of a transposed copy made per call, for less memory.
+    check_targets=True raises ValueError for a target outside [0, V) that
+    is not ignore_index (one stream synchronisation per call); otherwise
+    such tokens are ignored."""
     loss, lse = LinearCrossEntropyFunction.apply(X, W, targets, ignore_index, reduction,
-                                                 chunk_tokens, dw_chunks, weight_copy)
+                                                 chunk_tokens, dw_chunks, weight_copy,
+                                                 check_targets)
     return (loss, lse) if return_lse else loss
 
 
@@ -101,15 +120,18 @@ class LinearCrossEntropy(torch.nn.Module):
     hidden states and targets to the loss."""
 
     def __init__(self, hidden: int, vocab: int, dtype=torch.bfloat16, device="cuda",
-                 ignore_index: int = -100, reduction: str = "mean", chunk_tokens: int = 0):
+                 ignore_index: int = -100, reduction: str = "mean", chunk_tokens: int = 0,
+                 check_targets: bool = False):
         super().__init__()
         self.weight = torch.nn.Parameter(torch.empty(vocab, hidden, dtype=dtype, device=device))
         torch.nn.init.normal_(self.weight, std=hidden ** -0.5)
         self.ignore_index = ignore_index
         self.reduction = reduction
         self.chunk_tokens = chunk_tokens
+        self.check_targets = check_targets
 
     def forward(self, hidden_states: torch.Tensor, targets: torch.Tensor) -> torch.Tensor:
         X = hidden_states.reshape(-1, hidden_states.shape[-1])
         return linear_cross_entropy(X, self.weight, targets.reshape(-1), self.ignore_index,
-                                    self.reduction, self.chunk_tokens)
+                                    self.reduction, self.chunk_tokens,
+                                    check_targets=self.check_targets)

@@ -69,54 +69,6 @@ __device__ __forceinline__ void unpack8_bf16(uint4 p, float* v) {
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
 
-// DPP lane moves inside one 16-lane row.  The four steps below visit every
-// lane of the row once, so folding a commutative, associative combine over
-// them leaves the row's reduction in all 16 lanes:
-//   xor 1 and xor 2 inside each quad (quad_perm), then rotate the row by 4
-//   and by 8 lanes (row_ror).
-constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
-constexpr int kDppRowRor4 = 0x124;
-constexpr int kDppRowRor8 = 0x128;
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                               0xF, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_f<kDppQuadXor1>(v);
-  v += dpp_f<kDppQuadXor2>(v);
-  v += dpp_f<kDppRowRor4>(v);
-  v += dpp_f<kDppRowRor8>(v);
-  return v;
-}
-// (max, index of the max) with the lowest index winning ties.
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& m, int& a) {
-  const float om = dpp_f<CTRL>(m);
-  const int oa = dpp_i<CTRL>(a);
-  const bool take = om > m || (om == m && oa < a);
-  m = take ? om : m;
-  a = take ? oa : a;
-}
-__device__ __forceinline__ void row16_argmax(float& m, int& a) {
-  argmax_step<kDppQuadXor1>(m, a);
-  argmax_step<kDppQuadXor2>(m, a);
-  argmax_step<kDppRowRor4>(m, a);
-  argmax_step<kDppRowRor8>(m, a);
-}
-
-// Orders this wave's LDS traffic: everything issued before completes before
-// anything after it is issued or scheduled.
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_wave_barrier();
-}
-
 // Block id -> logical block index such that consecutive logical blocks run
 // on one XCD.  The hardware hands consecutive block ids to the 8 XCDs in
 // turn, each with its own L2; blocks whose rows share cache lines should sit

@@ -697,6 +697,9 @@ hipError_t launch_transpose(Dt dt, const void* src, int rows, int cols, int64_t 
 //   2. sum = sum_j s_j exp(m_j - m), lse = m + ln sum (the merge of
 //      online-softmax states: each partial sum rescaled to the common max);
 //   3. alpha_j = s valid exp(m_j - lse), overwriting m_j.
+// A tile whose sum is zero holds no column (or only -inf logits) and is
+// skipped; a NaN sum (a NaN or +inf logit in the tile) is not, so it
+// reaches the row's lse, loss and gradients as NaN.
 // ROWS rows per block, 1024 / ROWS slices of each row's partials per row:
 // 8 x 128 for long rows (a 128256-word vocabulary has 1002 partial tiles),
 // 32 x 32 for rows of at most 256 tiles, which otherwise leave most slices
@@ -739,7 +742,7 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   int am = 0x7fffffff;
 #pragma unroll
   for (int q = 0; q < kFinCache; ++q)
-    if (cs[q] > 0.f && (cm[q] > m || (cm[q] == m && ca[q] < am))) {
+    if (cs[q] != 0.f && (cm[q] > m || (cm[q] == m && ca[q] < am))) {
       m = cm[q];
       am = ca[q];
     }
@@ -747,7 +750,7 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
     for (int j = sl + kFinCache * kFinSlices; j < a.nt; j += kFinSlices) {
       const int64_t o = (int64_t)j * a.ldr + row;
       const float mj = a.pm[o];
-      if (a.ps[o] > 0.f && (mj > m || (mj == m && a.pa[o] < am))) {
+      if (a.ps[o] != 0.f && (mj > m || (mj == m && a.pa[o] < am))) {
         m = mj;
         am = a.pa[o];
       }
@@ -782,7 +785,7 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
 #pragma unroll
   for (int q = 0; q < kFinCache; ++q) {
     const int j = sl + q * kFinSlices;
-    if (cs[q] > 0.f) sum += cs[q] * exp_fast(cm[q] - m);
+    if (cs[q] != 0.f) sum += cs[q] * exp_fast(cm[q] - m);
     if (a.cross_pc && live && j < a.nt) {
       const int64_t o = (int64_t)j * a.ldr + row;
       cr += a.cross_pc[o] * a.alpha_q[o];
@@ -792,7 +795,7 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
     for (int j = sl + kFinCache * kFinSlices; j < a.nt; j += kFinSlices) {
       const int64_t o = (int64_t)j * a.ldr + row;
       const float sj = a.ps[o];
-      if (sj > 0.f) sum += sj * exp_fast(a.pm[o] - m);
+      if (sj != 0.f) sum += sj * exp_fast(a.pm[o] - m);
       if (a.cross_pc) cr += a.cross_pc[o] * a.alpha_q[o];
     }
   s_f[sl][rl] = sum;
@@ -842,13 +845,13 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
       const int j = sl + q * kFinSlices;
       if (j < a.nt) {
         const int64_t o = (int64_t)j * a.ldr + row;
-        a.pm[o] = (cs[q] > 0.f) ? sc * exp_fast(cm[q] - lse) : 0.f;
+        a.pm[o] = (cs[q] != 0.f) ? sc * exp_fast(cm[q] - lse) : 0.f;
         if (a.alpha_q) a.alpha_q[o] *= sc;
       }
     }
     for (int j = sl + kFinCache * kFinSlices; j < a.nt; j += kFinSlices) {
       const int64_t o = (int64_t)j * a.ldr + row;
-      a.pm[o] = (a.ps[o] > 0.f) ? sc * exp_fast(a.pm[o] - lse) : 0.f;
+      a.pm[o] = (a.ps[o] != 0.f) ? sc * exp_fast(a.pm[o] - lse) : 0.f;
       if (a.alpha_q) a.alpha_q[o] *= sc;
     }
   }

@@ -120,3 +120,25 @@ def test_module_on_batched_hidden_states():
     assert hs.grad.shape == (7, 100, WL.H)
     assert rel_frob(to_np(hs.grad.reshape(-1, WL.H)), ref["dX"]) <= GRAD_RTOL["bf16"]
     assert rel_frob(to_np(head.weight.grad), ref["dW"]) <= GRAD_RTOL["bf16"]
+
+
+def test_check_targets_raises_on_out_of_range_ids():
+    import torch
+    from linear_cross_entropy_02_amd.autograd import linear_cross_entropy
+    inp = workloads.generate(WL)
+    X, W, y = leaves(inp, torch.bfloat16)
+    y_bad = y.clone()
+    y_bad[[4, 9]] = WL.V + 1
+    print("[gpu-autograd] out-of-range targets with check_targets", flush=True)
+    with pytest.raises(ValueError, match="2 target"):
+        linear_cross_entropy(X, W, y_bad, WL.ignore_index, WL.reduction, check_targets=True)
+    # without the check those tokens count as ignored
+    loss = linear_cross_entropy(X, W, y_bad, WL.ignore_index, WL.reduction)
+    y_ign = inp.y.copy()
+    y_ign[[4, 9]] = WL.ignore_index
+    ref = flce_reference(inp.X, inp.W, y_ign, WL.ignore_index, WL.reduction)
+    assert abs(float(loss.detach()) - ref["loss"]) <= LOSS_RTOL * abs(ref["loss"])
+    # valid targets pass the check
+    ok = linear_cross_entropy(X, W, y, WL.ignore_index, WL.reduction, check_targets=True)
+    torch.cuda.synchronize()
+    assert np.isfinite(float(ok.detach()))

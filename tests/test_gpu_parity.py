@@ -59,6 +59,10 @@ CASES = [
     # a round) split two ways in K as a whole; the 108-token second chunk
     # accumulates through 128-wide tiles
     (workloads.WORKLOADS[3].with_shape(T=8300, seed=23), 8192),
+    # 33 x 10 = 330 dW tiles: one full round of 256, then the last 74 split
+    # three ways in K, unevenly (32 K-steps as 11/11/10 when the first chunk
+    # stores dW, 31 as 11/11/9 when the second, ragged one accumulates)
+    (workloads.WORKLOADS[4].with_shape(T=4000, H=2560, V=8300, seed=24), 2048),
     # 38 x 16 = 608 dW tiles: the last 96 split two ways
     (workloads.WORKLOADS[4].with_shape(T=4200, H=4096, V=9700, seed=19), 2048),
     # the same split of the dW grid on fp32 operands
@@ -300,3 +304,36 @@ def test_workspace_does_not_depend_on_tokens():
         assert op.workspace_bytes == ws
     assert ws < 4096 * 16000 * 2
     op.close()
+
+
+def test_non_finite_inputs_poison_like_the_oracle():
+    # A NaN row of W makes every logit of that vocabulary id NaN, so every
+    # token's lse, the loss and the gradients are NaN; a +inf entry of X
+    # makes that token's logits infinite (NaN after the max is subtracted):
+    # its lse and the loss are NaN while every other token's lse stays
+    # finite and exact.  The oracle is the reference for which is which.
+    import torch
+    wl = workloads.WORKLOADS[2].with_shape(T=300, H=128, V=1500, seed=27)
+    base = workloads.generate(wl)
+    first_valid = int(np.nonzero(base.y != wl.ignore_index)[0][0])
+    cases = {"nan_w_row": ("W", 5, None), "inf_x": ("X", first_valid, 7)}
+    for name, (which, r, c) in cases.items():
+        X = base.X.copy()
+        W = base.W.copy()
+        if which == "W":
+            W[r, :] = np.nan
+        else:
+            X[r, c] = np.inf
+        inp = workloads.Inputs(wl, X, W, base.y, workloads.f32_to_bf16_bits(X),
+                               workloads.f32_to_bf16_bits(W))
+        print(f"[gpu] non-finite case {name}", flush=True)
+        _, out = run(wl, 256, inp=inp)
+        with np.errstate(invalid="ignore", over="ignore"):
+            ref = oracle(inp, wl)
+        lse = to_np(out["lse"])
+        assert np.isnan(float(out["loss"].item())) == np.isnan(ref["loss"]), name
+        assert np.array_equal(np.isnan(lse), np.isnan(ref["lse"])), name
+        fin = ~np.isnan(ref["lse"])
+        if fin.any():
+            assert np.abs(lse[fin] - ref["lse"][fin]).max() <= 1e-3, name
+        assert np.isnan(ref["loss"]), name
