@@ -5,9 +5,11 @@
 A step is one flce_fwd_bwd call over one batch: logits GEMM with the
 online-logsumexp epilogue, dZ formation, dX and dW GEMMs, loss -- the whole
 hot path, with inputs resident in HBM.  Prints ONE JSON line with tokens/s
-(value), the roofline of the dominant kernel (per-kernel HIP events recorded
-on the call's stream inside the timed region) and the float64 CPU oracle
-timed on a bounded token sample of the same workload (cpu_baseline).
+(value) from K steps timed with nothing but two events around them, the
+GPU clock sampled during those steps, the roofline of the dominant kernel
+(from a separate pass of a few more steps with a HIP event pair around every
+launch on the call's stream) and the float64 CPU oracle timed on a bounded
+token sample of the same workload (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -91,7 +93,10 @@ def parse():
     p.add_argument("--forward-only", action="store_true",
                    help="time flce_forward (per-token log-probs and loss, no gradients)")
     p.add_argument("--no-timing", action="store_true",
-                   help="time without per-kernel events (no roofline)")
+                   help="skip the per-kernel pass after the timed steps (no roofline)")
+    p.add_argument("--kernel-steps", type=int, default=5,
+                   help="steps of the per-kernel pass (HIP events around every launch), run "
+                        "after the timed steps; at most --steps")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (3 times), "
                         "to scale HBM byte counters")
@@ -305,6 +310,96 @@ def per_kernel_rooflines(kernels, T, H, V, dtype, mfma_peak):
     return out
 
 
+class ClockSampler:
+    """GFX clock and socket power of device 0 sampled every 20 ms from a side
+    thread (amdsmi GPU metrics) while the timed steps run.  The firmware
+    refreshes that table more slowly than it is read, and its first values
+    can predate the load, so the summary is the median (and range) of the
+    samples taken in the second half of the window; None without amdsmi."""
+
+    def __init__(self, period_s: float = 0.02):
+        import threading
+        self.period_s = period_s
+        self.samples = []          # (seconds since start, MHz, watts or None)
+        self._halt = threading.Event()
+        self._thread = None
+        self._handle = None
+        self._error = None
+        self._t0 = 0.0
+
+    def _read(self):
+        import amdsmi
+        m = amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        clks = m.get("current_gfxclks")
+        clks = [c for c in clks if isinstance(c, (int, float)) and 0 < c < 10000] \
+            if isinstance(clks, (list, tuple)) else []
+        if not clks and isinstance(m.get("current_gfxclk"), (int, float)):
+            clks = [m["current_gfxclk"]]
+        p = m.get("current_socket_power")
+        p = float(p) if isinstance(p, (int, float)) and 0 < p < 5000 else None
+        if clks:
+            self.samples.append((time.time() - self._t0, sum(clks) / len(clks), p))
+
+    def _run(self):
+        while not self._halt.wait(self.period_s):
+            try:
+                self._read()
+            except Exception as e:  # metrics unavailable on this box
+                self._error = repr(e)
+                return
+
+    def start(self):
+        import threading
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._handle = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception as e:
+            self._error = repr(e)
+            self._handle = None
+            return
+        self._t0 = time.time()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        span = time.time() - self._t0
+        if self._thread is not None:
+            self._halt.set()
+            self._thread.join()
+        try:
+            if self._handle is not None:
+                import amdsmi
+                amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+        late = [s for s in self.samples if s[0] >= 0.5 * span]
+        if not late:
+            return {"gfx_clock_mhz": None, "error": self._error}
+        clk = sorted(s[1] for s in late)
+        pw = sorted(s[2] for s in late if s[2] is not None)
+        out = {"gfx_clock_mhz": clk[len(clk) // 2], "gfx_clock_mhz_min": clk[0],
+               "gfx_clock_mhz_max": clk[-1], "samples": len(clk),
+               "window_s": round(span / 2, 3), "nominal_peak_clock_mhz": 2400,
+               "source": "amdsmi gpu metrics current_gfxclks (mean of the XCDs), median of the "
+                         "samples in the second half of the timed steps"}
+        if pw:
+            out["socket_power_w"] = pw[len(pw) // 2]
+        return out
+
+
+def blas_threads():
+    """Threads of the BLAS numpy uses (threadpoolctl), or None."""
+    try:
+        import numpy  # noqa: F401  (loads the BLAS the pool query reports)
+        import threadpoolctl
+        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        return {"library": info[0].get("internal_api"), "threads": info[0].get("num_threads")} \
+            if info else None
+    except Exception:
+        return None
+
+
 def calibrate_copy(mib: int):
     import torch
     n = mib * 2 ** 20 // 4
@@ -404,14 +499,14 @@ def main():
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
-    timing = not args.no_timing
-    if timing:
-        flce.flce_timing_enable(op.handle, True)
+    # Timed region: the K steps alone, no per-kernel instrumentation.
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     free_before = torch.cuda.mem_get_info()[0]
+    sampler = ClockSampler()
+    sampler.start()
     start.record(stream)
     marks[0].record(stream)
     for i in range(args.steps):
@@ -419,6 +514,7 @@ def main():
         marks[i + 1].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
+    clock = sampler.stop()
     free_after = torch.cuda.mem_get_info()[0]
     ms = start.elapsed_time(stop) / args.steps
     per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
@@ -426,6 +522,7 @@ def main():
         0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
     loss = float(out["loss"].item())
     assert np.isfinite(loss), loss
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
     T, H, V = wl.T, wl.H, wl.V
     # fwd+bwd: three contractions of 2 T H V flops; forward only: the logits;
@@ -440,17 +537,27 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
 
+    # Per-kernel pass, after and apart from the timed region: the same steps
+    # again with a HIP event pair recorded on the call's stream around every
+    # launch; the roofline of the dominant kernel comes from these durations.
     roofline = None
     kernels = {}
     kernel_rooflines = None
-    if timing:
+    ksteps = 0 if args.no_timing else max(1, min(args.steps, args.kernel_steps))
+    if ksteps:
+        flce.flce_timing_enable(op.handle, True)
+        for _ in range(ksteps):
+            step()
+        torch.cuda.synchronize()
         names = flce.flce_timing_kinds()
         for k, name in enumerate(names):
             tot, n = flce.flce_timing_read(op.handle, k)
             if n:
-                kernels[name] = {"total_ms": tot / args.steps, "launches_per_step": n / args.steps,
+                kernels[name] = {"total_ms": tot / ksteps, "launches_per_step": n / ksteps,
                                  "avg_ms": tot / n}
         flce.flce_timing_enable(op.handle, False)
+        source = (f"HIP event pair around each launch on the call's stream, {ksteps} steps "
+                  "after the timed region")
         dom = max(kernels, key=lambda k: kernels[k]["total_ms"])
         if dom in ("logits_gemm", "dx_gemm", "dw_gemm"):
             # each of the contractions does 2 T H V flops per step, split over
@@ -465,10 +572,12 @@ def main():
                         "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                         "traffic": None if (fwd_only or n_shards > 1 or Ht > 0 or
                                             args.workload != 4) else
-                        measured_traffic(dom, (op.chunk_tokens, op.dw_chunks))}
+                        measured_traffic(dom, (op.chunk_tokens, op.dw_chunks)),
+                        "flop_per_launch": flop_per_launch,
+                        "avg_launch_ms": round(kernels[dom]["avg_ms"], 5), "source": source}
         else:
             roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": 8000.0,
-                        "unit": "GB/s", "frac": None, "traffic": None}
+                        "unit": "GB/s", "frac": None, "traffic": None, "source": source}
         if not (fwd_only or n_shards > 1 or Ht > 0):
             kernel_rooflines = per_kernel_rooflines(kernels, T, H, V, wl.dtype, peak)
 
@@ -476,12 +585,14 @@ def main():
     if args.cpu_sample > 0 and n_shards == 1 and Ht == 0:
         from oracle import flce_reference
         ns = min(args.cpu_sample, T)
-        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        blas = blas_threads()
+        threads = (blas or {}).get("threads") or len(os.sched_getaffinity(0))
         t0 = time.time()
         flce_reference(inp.X[:ns], inp.W, inp.y[:ns], wl.ignore_index, wl.reduction, chunk=256,
                        want_grads=not fwd_only)
         dt = time.time() - t0
         cpu = {"value": round(ns / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "blas": blas, "host_cpus": len(os.sched_getaffinity(0)),
                "sample": f"first {ns} of {T} tokens of {wl.name} (full W), float64 numpy oracle, "
                          f"{dt:.1f}s"}
 
@@ -498,7 +609,7 @@ def main():
                    "reduction": wl.reduction, "ignore_frac": wl.ignore_frac,
                    "targets": wl.targets},
         "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / peak, 4),
-        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+        "roofline": roofline, "cpu_baseline": cpu, "clock": clock, "kernels": kernels,
         "kernel_rooflines": kernel_rooflines,
         "ms_per_step_median": round(ms_median, 3),
         "workspace_bytes": op.workspace_bytes,
