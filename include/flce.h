@@ -235,6 +235,35 @@ flce_status_t flce_distill_fwd_bwd(flce_handle_t h, const void* X, const void* W
                                    float temperature, int32_t reduction, float* loss, void* dX,
                                    float* dW, int64_t* n_valid, void* stream);
 
+/*
+ * Allocation-free variant of flce_fwd_bwd, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It takes the configuration instead of a handle and
+ * runs the same kernels, in the same order, with the same results, as
+ * flce_fwd_bwd on a handle made by flce_create(cfg); arguments, outputs and
+ * their errors are those of flce_fwd_bwd.  The workspace lives in a static
+ * device array of FLCE_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends; the call itself allocates nothing
+ * (no hipMalloc, no allocating library routine).  Its first call on a device
+ * looks the array's address up (hipGetSymbolAddress).
+ *  - Returns FLCE_ERR_UNSUPPORTED, with nothing enqueued, when the
+ *    configuration's workspace (what flce_workspace_bytes would report for a
+ *    handle of cfg) exceeds FLCE_NOALLOC_SCRATCH_BYTES; flce_last_error then
+ *    gives the size needed.  A smaller chunk_tokens or dw_chunks, or
+ *    FLCE_FLAG_NO_WEIGHT_COPY, lowers it.
+ *  - Every call on one GPU shares that GPU's array: calls that overlap on one
+ *    GPU (other streams, other threads) race and must be ordered by the
+ *    caller.  The array keeps the last call's contents; no buffer in it needs
+ *    to start at zero.
+ *  - flce_query_error, the timing calls and the soft-target, forward-only and
+ *    vocabulary-shard calls need a handle; this call has none.
+ */
+#define FLCE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+flce_status_t flce_fwd_bwd_noalloc(const flce_config_t* cfg, const void* X, const void* W,
+                                   const int64_t* targets, int64_t T, int64_t ignore_index,
+                                   int32_t reduction, float* loss, void* dX, float* dW,
+                                   float* lse, int32_t* argmax, int64_t* n_valid, void* stream);
+
 /* Synchronise `stream` and read the number of out-of-range targets seen by
  * the last flce_fwd_bwd or flce_forward on this handle.  Returns FLCE_ERR_BAD_TARGET when it
  * is > 0, FLCE_OK otherwise.  bad_targets may be NULL. */

@@ -31,7 +31,8 @@ FLCE_MEAN = 1
 FLCE_SUM = 2
 
 EXPORTED = (
-    "flce_create", "flce_workspace_bytes", "flce_chunk_tokens", "flce_dw_chunks", "flce_fwd_bwd", "flce_forward",
+    "flce_create", "flce_workspace_bytes", "flce_chunk_tokens", "flce_dw_chunks", "flce_fwd_bwd",
+    "flce_fwd_bwd_noalloc", "flce_forward",
     "flce_vocab_shard_forward", "flce_vocab_shard_backward", "flce_distill_create",
     "flce_distill_fwd_bwd",
     "flce_query_error", "flce_timing_enable", "flce_timing_kinds", "flce_timing_kind_name",
@@ -78,6 +79,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.flce_dw_chunks.restype = i32
     lib.flce_fwd_bwd.argtypes = [P, P, P, P, i64, i64, i32, P, P, P, P, P, P, P]
     lib.flce_fwd_bwd.restype = st
+    lib.flce_fwd_bwd_noalloc.argtypes = [ctypes.POINTER(flce_config_t), P, P, P, i64, i64, i32, P,
+                                         P, P, P, P, P, P]
+    lib.flce_fwd_bwd_noalloc.restype = st
     lib.flce_forward.argtypes = [P, P, P, P, i64, i64, i32, P, P, P, P, P, P]
     lib.flce_forward.restype = st
     lib.flce_vocab_shard_forward.argtypes = [P, P, P, P, i64, i64, i64, i64, P, P, P, P, P]
@@ -162,6 +166,27 @@ def flce_fwd_bwd(handle, X, W, targets, T: int, ignore_index: int, reduction: in
     return load().flce_fwd_bwd(handle, _ptr(X), _ptr(W), _ptr(targets), T, ignore_index,
                                reduction, _ptr(loss), _ptr(dX), _ptr(dW), _ptr(lse),
                                _ptr(argmax), _ptr(n_valid), stream)
+
+
+# Bytes of the static device scratch flce_fwd_bwd_noalloc works in (one copy
+# per GPU, held by the library until the process ends).
+FLCE_NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def flce_fwd_bwd_noalloc(hidden: int, vocab: int, dtype: int, X, W, targets, T: int,
+                         ignore_index: int, reduction: int, loss, dX, dW, lse=None, argmax=None,
+                         n_valid=None, chunk_tokens: int = 0, dw_chunks: int = 0, flags: int = 0,
+                         stream=None) -> int:
+    """Direct call of the allocation-free entry point: the configuration is
+    passed with the call instead of a handle (see flce_fwd_bwd for the
+    tensors)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    cfg = flce_config_t(hidden, vocab, dtype, dw_chunks, chunk_tokens, flags)
+    return load().flce_fwd_bwd_noalloc(ctypes.byref(cfg), _ptr(X), _ptr(W), _ptr(targets), T,
+                                       ignore_index, reduction, _ptr(loss), _ptr(dX), _ptr(dW),
+                                       _ptr(lse), _ptr(argmax), _ptr(n_valid), stream)
 
 
 def flce_forward(handle, X, W, targets, T: int, ignore_index: int, reduction: int,

@@ -17,6 +17,12 @@
 
 using namespace flce;
 
+// Device scratch of flce_fwd_bwd_noalloc: a file-scope array, one copy on
+// every GPU the library runs on, held until the process ends.  Host code
+// never passes the array's name to a kernel (in host code it is only a
+// stand-in); it uses the address hipGetSymbolAddress returns per device.
+static __device__ __align__(256) unsigned char scratch[FLCE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -203,9 +209,20 @@ const char* flce_timing_kind_name(int32_t kind) {
   return kKindNames[kind];
 }
 
-static flce_status_t create_impl(const flce_config_t* cfg, int64_t Ht, flce_handle_t* out) {
-  if (!out) return FLCE_ERR_INVALID_ARGUMENT;
-  *out = nullptr;
+}  // extern "C"
+
+namespace {
+
+// Byte offsets of the workspace buffers of one handle, from (H, V, C, G,
+// dtype, weight copy, teacher) only.
+struct Layout {
+  size_t Wt, P, Pt, Xt, pm, ps, pa, zt, dz, lp, sk, sc, cp, Pq, pmq, psq, paq, pc;
+  size_t total;
+};
+
+// Validates cfg and fills the handle's sizes and the workspace layout; no
+// device call.  The workspace pointers are set by bind_workspace.
+flce_status_t configure(const flce_config_t* cfg, int64_t Ht, flce_handle* h, Layout* L) {
   if (!cfg) return FLCE_ERR_INVALID_ARGUMENT;
   if (cfg->dtype != FLCE_F32 && cfg->dtype != FLCE_BF16) return FLCE_ERR_INVALID_ARGUMENT;
   if (cfg->dw_chunks < 0 || cfg->dw_chunks > kMaxDwChunks) return FLCE_ERR_INVALID_ARGUMENT;
@@ -228,31 +245,20 @@ static flce_status_t create_impl(const flce_config_t* cfg, int64_t Ht, flce_hand
   // whose size must stay below the out-of-range offset (2^31) that reads 0
   if (no_wcopy && (dt != Dt::BF16 || V * H * 2 >= ((int64_t)1 << 31))) return FLCE_ERR_UNSUPPORTED;
 
-  flce_handle* h = new (std::nothrow) flce_handle();
-  if (!h) return FLCE_ERR_OUT_OF_MEMORY;
-  hipError_t e = hipGetDevice(&h->device);
-  if (e != hipSuccess) {
-    delete h;
-    return hip_fail(e, "hipGetDevice");
-  }
-  std::call_once(g_setup_once, [] { g_setup_err = gemm_setup(); });
-  if (g_setup_err != hipSuccess) {
-    delete h;
-    return hip_fail(g_setup_err, "gemm_setup");
-  }
   h->dt = dt;
   h->H = H;
   h->V = V;
   h->C = C;
   h->G = (int)G;
+  h->Ht = Ht;
   h->w_copy = !no_wcopy;
   h->Vpad = round_up(V, 256);
   h->nt = cdiv64(V, kPartialWidth);
   {
     TileCfg tc;
-    int s;
-    plan_gemm(C, H, round_up(V, 64), 8, &tc, &s);
-    h->splitk_alloc = s;
+    int sp;
+    plan_gemm(C, H, round_up(V, 64), 8, &tc, &sp);
+    h->splitk_alloc = sp;
   }
   const size_t es = elem_size(dt);
   size_t off = 0;
@@ -261,65 +267,105 @@ static flce_status_t create_impl(const flce_config_t* cfg, int64_t Ht, flce_hand
     off += round_up((int64_t)bytes, 256);
     return o;
   };
-  const size_t oWt = h->w_copy ? carve((size_t)H * h->Vpad * es) : 0;
-  const size_t oP = carve((size_t)C * h->Vpad * es);
-  const size_t oPt = carve((size_t)h->Vpad * h->G * C * es);
-  const size_t oXt = carve((size_t)H * h->G * C * es);
-  const size_t opm = carve((size_t)C * h->nt * 4);
-  const size_t ops = carve((size_t)C * h->nt * 4);
-  const size_t opa = carve((size_t)C * h->nt * 4);
-  const size_t ozt = carve((size_t)C * 4);
-  const size_t odz = carve((size_t)C * 4);
-  const size_t olp = carve((size_t)cdiv64(C, kFinalizeRows) * 8);
-  const size_t osk = h->splitk_alloc > 1 ? carve((size_t)h->splitk_alloc * C * H * 4) : 0;
-  const size_t osc = carve(64);
-  const size_t ocp = carve(2 * kCountBlocks * sizeof(long long));
+  L->Wt = h->w_copy ? carve((size_t)H * h->Vpad * es) : 0;
+  L->P = carve((size_t)C * h->Vpad * es);
+  L->Pt = carve((size_t)h->Vpad * h->G * C * es);
+  L->Xt = carve((size_t)H * h->G * C * es);
+  L->pm = carve((size_t)C * h->nt * 4);
+  L->ps = carve((size_t)C * h->nt * 4);
+  L->pa = carve((size_t)C * h->nt * 4);
+  L->zt = carve((size_t)C * 4);
+  L->dz = carve((size_t)C * 4);
+  L->lp = carve((size_t)cdiv64(C, kFinalizeRows) * 8);
+  L->sk = h->splitk_alloc > 1 ? carve((size_t)h->splitk_alloc * C * H * 4) : 0;
+  L->sc = carve(64);
+  L->cp = carve(2 * kCountBlocks * sizeof(long long));
   // soft targets: the teacher's exponentials and partials, and the cross partials
-  const size_t oPq = Ht ? carve((size_t)C * h->Vpad * es) : 0;
-  const size_t opmq = Ht ? carve((size_t)C * h->nt * 4) : 0;
-  const size_t opsq = Ht ? carve((size_t)C * h->nt * 4) : 0;
-  const size_t opaq = Ht ? carve((size_t)C * h->nt * 4) : 0;
-  const size_t opc = Ht ? carve((size_t)C * h->nt * 4) : 0;
-  h->Ht = Ht;
+  L->Pq = Ht ? carve((size_t)C * h->Vpad * es) : 0;
+  L->pmq = Ht ? carve((size_t)C * h->nt * 4) : 0;
+  L->psq = Ht ? carve((size_t)C * h->nt * 4) : 0;
+  L->paq = Ht ? carve((size_t)C * h->nt * 4) : 0;
+  L->pc = Ht ? carve((size_t)C * h->nt * 4) : 0;
+  L->total = off;
   h->ws_bytes = off;
-  e = hipMalloc((void**)&h->ws, h->ws_bytes);
+  return FLCE_OK;
+}
+
+// Points the handle's buffers into a workspace of L.total bytes at base.
+void bind_workspace(flce_handle* h, const Layout& L, char* base) {
+  h->ws = base;
+  h->Wt = h->w_copy ? base + L.Wt : nullptr;
+  h->P = base + L.P;
+  h->Pt = base + L.Pt;
+  h->Xt = base + L.Xt;
+  h->pm = (float*)(base + L.pm);
+  h->ps = (float*)(base + L.ps);
+  h->pa = (int*)(base + L.pa);
+  h->ztgt = (float*)(base + L.zt);
+  h->dzt = (float*)(base + L.dz);
+  h->loss_part = (double*)(base + L.lp);
+  h->splitk = h->splitk_alloc > 1 ? (float*)(base + L.sk) : nullptr;
+  h->nvalid = (int64_t*)(base + L.sc);
+  h->scale = (float*)(base + L.sc + 16);
+  h->bad = (int64_t*)(base + L.sc + 32);
+  h->count_part = (long long*)(base + L.cp);
+  if (h->Ht) {
+    h->Pq = base + L.Pq;
+    h->pmq = (float*)(base + L.pmq);
+    h->psq = (float*)(base + L.psq);
+    h->paq = (int*)(base + L.paq);
+    h->pc = (float*)(base + L.pc);
+  }
+}
+
+flce_status_t ensure_setup() {
+  std::call_once(g_setup_once, [] { g_setup_err = gemm_setup(); });
+  if (g_setup_err != hipSuccess) return hip_fail(g_setup_err, "gemm_setup");
+  return FLCE_OK;
+}
+
+flce_status_t create_impl(const flce_config_t* cfg, int64_t Ht, flce_handle_t* out) {
+  if (!out) return FLCE_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  flce_handle* h = new (std::nothrow) flce_handle();
+  if (!h) return FLCE_ERR_OUT_OF_MEMORY;
+  Layout L;
+  flce_status_t st = configure(cfg, Ht, h, &L);
+  if (st != FLCE_OK) {
+    delete h;
+    return st;
+  }
+  hipError_t e = hipGetDevice(&h->device);
   if (e != hipSuccess) {
-    flce_status_t st = hip_fail(e, "hipMalloc(workspace)");
+    delete h;
+    return hip_fail(e, "hipGetDevice");
+  }
+  if ((st = ensure_setup()) != FLCE_OK) {
+    delete h;
+    return st;
+  }
+  char* ws = nullptr;
+  e = hipMalloc((void**)&ws, L.total);
+  if (e != hipSuccess) {
+    st = hip_fail(e, "hipMalloc(workspace)");
     delete h;
     (void)hipGetLastError();
     return st == FLCE_ERR_HIP ? FLCE_ERR_OUT_OF_MEMORY : st;
   }
-  h->Wt = h->w_copy ? h->ws + oWt : nullptr;
-  h->P = h->ws + oP;
-  h->Pt = h->ws + oPt;
-  h->Xt = h->ws + oXt;
-  h->pm = (float*)(h->ws + opm);
-  h->ps = (float*)(h->ws + ops);
-  h->pa = (int*)(h->ws + opa);
-  h->ztgt = (float*)(h->ws + ozt);
-  h->dzt = (float*)(h->ws + odz);
-  h->loss_part = (double*)(h->ws + olp);
-  h->splitk = h->splitk_alloc > 1 ? (float*)(h->ws + osk) : nullptr;
-  h->nvalid = (int64_t*)(h->ws + osc);
-  h->scale = (float*)(h->ws + osc + 16);
-  h->bad = (int64_t*)(h->ws + osc + 32);
-  h->count_part = (long long*)(h->ws + ocp);
-  if (Ht) {
-    h->Pq = h->ws + oPq;
-    h->pmq = (float*)(h->ws + opmq);
-    h->psq = (float*)(h->ws + opsq);
-    h->paq = (int*)(h->ws + opaq);
-    h->pc = (float*)(h->ws + opc);
-  }
-  e = hipMemset(h->ws + osc, 0, 64);
+  bind_workspace(h, L, ws);
+  e = hipMemset(ws + L.sc, 0, 64);
   if (e != hipSuccess) {
-    (void)hipFree(h->ws);
+    (void)hipFree(ws);
     delete h;
     return hip_fail(e, "hipMemset");
   }
   *out = h;
   return FLCE_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out) {
   return create_impl(cfg, 0, out);
@@ -382,6 +428,23 @@ flce_status_t check_device(flce_handle_t h, const char* who) {
 }
 
 bool misaligned(const void* p, uintptr_t mask) { return ((uintptr_t)p & mask) != 0; }
+
+// Argument checks shared by flce_fwd_bwd and flce_fwd_bwd_noalloc.
+flce_status_t check_fwd_bwd_args(const void* X, const void* W, const int64_t* targets, int64_t T,
+                                 int32_t reduction, const float* loss, const void* dX,
+                                 const float* dW, const float* lse, const int32_t* argmax,
+                                 const int64_t* n_valid) {
+  if (T < 0) return FLCE_ERR_INVALID_ARGUMENT;
+  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!W || !loss || !dW) return FLCE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!X || !targets || !dX)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(W) || !aligned16(dW) || (T > 0 && (!aligned16(X) || !aligned16(dX))))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  if (misaligned(loss, 3) || misaligned(lse, 3) || misaligned(argmax, 3) ||
+      misaligned(n_valid, 7) || misaligned(targets, 7))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  return FLCE_OK;
+}
 
 flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const int64_t* targets,
                           int64_t T, int64_t ignore_index, int32_t reduction, float* loss,
@@ -728,16 +791,10 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const 
                            void* dX, float* dW, float* lse, int32_t* argmax, int64_t* n_valid,
                            void* stream) {
   if (!h) return FLCE_ERR_INVALID_ARGUMENT;
-  if (T < 0) return FLCE_ERR_INVALID_ARGUMENT;
-  if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARGUMENT;
-  if (!W || !loss || !dW) return FLCE_ERR_INVALID_ARGUMENT;
-  if (T > 0 && (!X || !targets || !dX)) return FLCE_ERR_INVALID_ARGUMENT;
-  if (!aligned16(W) || !aligned16(dW) || (T > 0 && (!aligned16(X) || !aligned16(dX))))
-    return FLCE_ERR_INVALID_ARGUMENT;
-  if (misaligned(loss, 3) || misaligned(lse, 3) || misaligned(argmax, 3) ||
-      misaligned(n_valid, 7) || misaligned(targets, 7))
-    return FLCE_ERR_INVALID_ARGUMENT;
-  const flce_status_t st = check_device(h, "flce_fwd_bwd");
+  flce_status_t st =
+      check_fwd_bwd_args(X, W, targets, T, reduction, loss, dX, dW, lse, argmax, n_valid);
+  if (st != FLCE_OK) return st;
+  st = check_device(h, "flce_fwd_bwd");
   if (st != FLCE_OK) return st;
   return run_fwd_bwd(h, X, W, targets, T, ignore_index, reduction, loss, dX, dW, lse, argmax,
                      n_valid, Cols{0, h->V, nullptr}, stream);
@@ -830,6 +887,70 @@ flce_status_t flce_distill_fwd_bwd(flce_handle_t h, const void* X, const void* W
   const Soft soft{X_teacher, W_teacher, 1.f / temperature};
   return run_fwd_bwd(h, X, W, targets, T, ignore_index, reduction, loss, dX, dW, nullptr, nullptr,
                      n_valid, Cols{0, h->V, nullptr}, stream, &soft);
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+char* g_scratch_ptr[kMaxDevices];
+
+// Address of this device's copy of `scratch`, looked up once per device with
+// that device current.
+flce_status_t scratch_for_device(int dev, char** out) {
+  if (dev < 0 || dev >= kMaxDevices) {
+    g_last_error = "flce_fwd_bwd_noalloc: device index beyond the library's table";
+    return FLCE_ERR_UNSUPPORTED;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? (char*)p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev])
+    return hip_fail(g_scratch_err[dev] != hipSuccess ? g_scratch_err[dev] : hipErrorInvalidSymbol,
+                    "hipGetSymbolAddress(scratch)");
+  *out = g_scratch_ptr[dev];
+  return FLCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+flce_status_t flce_fwd_bwd_noalloc(const flce_config_t* cfg, const void* X, const void* W,
+                                   const int64_t* targets, int64_t T, int64_t ignore_index,
+                                   int32_t reduction, float* loss, void* dX, float* dW, float* lse,
+                                   int32_t* argmax, int64_t* n_valid, void* stream) {
+  flce_handle h;  // not heap-allocated; its buffers are bound to the scratch
+  Layout L;
+  flce_status_t st = configure(cfg, 0, &h, &L);
+  if (st != FLCE_OK) return st;
+  st = check_fwd_bwd_args(X, W, targets, T, reduction, loss, dX, dW, lse, argmax, n_valid);
+  if (st != FLCE_OK) return st;
+  if (L.total > (size_t)FLCE_NOALLOC_SCRATCH_BYTES) {
+    char buf[200];
+    snprintf(buf, sizeof buf,
+             "flce_fwd_bwd_noalloc: this configuration needs %zu bytes of workspace, more than "
+             "the %zu-byte static scratch (smaller chunk_tokens or dw_chunks may fit)",
+             L.total, (size_t)FLCE_NOALLOC_SCRATCH_BYTES);
+    g_last_error = buf;
+    return FLCE_ERR_UNSUPPORTED;
+  }
+  hipError_t e = hipGetDevice(&h.device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if ((st = ensure_setup()) != FLCE_OK) return st;
+  char* base = nullptr;
+  if ((st = scratch_for_device(h.device, &base)) != FLCE_OK) return st;
+  bind_workspace(&h, L, base);
+  // Nothing in the workspace has to start at zero: every buffer a call reads
+  // is written earlier in the same call (the target counts, the first
+  // chunk's loss partials, the split-K partials).
+  return run_fwd_bwd(&h, X, W, targets, T, ignore_index, reduction, loss, dX, dW, lse, argmax,
+                     n_valid, Cols{0, h.V, nullptr}, stream);
 }
 
 flce_status_t flce_query_error(flce_handle_t h, void* stream, int64_t* bad_targets) {
