@@ -81,6 +81,9 @@ def parse():
                    help="dX through a transposed copy of W made per call (on) or reading W "
                         "as stored (off; bf16, no copy in the workspace); auto = the "
                         "workload's launch configuration")
+    p.add_argument("--dz-in-dx", action="store_true",
+                   help="form dZ inside the dX contraction (FLCE_FLAG_DZ_IN_DX) instead of in the "
+                        "pass that also writes dZ^T")
     p.add_argument("--cpu-sample", type=int, default=3072,
                    help="tokens of the workload the CPU oracle is timed on (0 = skip)")
     p.add_argument("--vocab-shards", type=int, default=1, metavar="N",
@@ -285,14 +288,15 @@ def measured_traffic(kernel_kind: str, launch):
 def per_kernel_rooflines(kernels, T, H, V, dtype, mfma_peak):
     """Achieved rate of each timed kernel of one fwd+bwd step against its own
     bound, from algorithmic work only: 2 T H V flops for each contraction;
-    for the bandwidth passes the bytes they must move (the fixup reads the
-    exponentials and writes dZ and dZ^T; a transpose reads and writes its
+    for the bandwidth passes the bytes they must move (the dZ pass reads the
+    exponentials and writes dZ^T, dZ itself being formed inside the dX
+    contraction; a transpose reads and writes its
     matrix once; the merge reads the (max, sum, argmax) partials and writes
     alpha, 16 bytes per (token, 128-column tile))."""
     es = 2 if dtype == "bf16" else 4
     nt = -(-V // 128)
     work = {"logits_gemm": ("mfma", 2.0 * T * H * V), "dx_gemm": ("mfma", 2.0 * T * H * V),
-            "dw_gemm": ("mfma", 2.0 * T * H * V), "fixup_dz": ("hbm", 3.0 * T * V * es),
+            "dw_gemm": ("mfma", 2.0 * T * H * V), "fixup_dz": ("hbm", 2.0 * T * V * es),
             "transpose_w": ("hbm", 2.0 * V * H * es), "transpose_x": ("hbm", 2.0 * T * H * es),
             "finalize": ("hbm", 16.0 * nt * T)}
     out = {}
@@ -479,7 +483,8 @@ def main():
             assert st1 == flce.FLCE_OK and st2 == flce.FLCE_OK, (st1, st2)
     else:
         op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=args.chunk,
-                                          dw_chunks=args.dw_chunks, weight_copy=wcopy)
+                                          dw_chunks=args.dw_chunks, weight_copy=wcopy,
+                                          dz_in_dx=args.dz_in_dx)
     if n_shards > 1 or Ht > 0:
         pass  # step() is set above
     elif fwd_only:
@@ -603,7 +608,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "H": H, "V": V, "chunk_tokens": op.chunk_tokens,
-                   "dw_chunks": op.dw_chunks, "weight_copy": wcopy, "vocab_shards": n_shards,
+                   "dw_chunks": op.dw_chunks, "weight_copy": wcopy, "dz_in_dx": args.dz_in_dx,
+                   "vocab_shards": n_shards,
                    "V_total": wl.V,
                    "teacher_hidden": Ht,
                    "reduction": wl.reduction, "ignore_frac": wl.ignore_frac,

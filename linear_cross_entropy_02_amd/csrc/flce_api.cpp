@@ -67,6 +67,7 @@ struct flce_handle {
   int64_t Ht = 0;          // teacher hidden size (soft-target handles only)
   int splitk_alloc = 1;  // split-K planes the workspace holds for a full chunk
   bool w_copy = true;      // dX reads W^T (a copy made per call) or W as stored
+  bool dz_in_dx = false;   // dZ formed inside the dX contraction (FLCE_FLAG_DZ_IN_DX)
   size_t ws_bytes = 0;
   char* ws = nullptr;
   void* Wt = nullptr;      // W^T           [H x Vpad]
@@ -78,6 +79,10 @@ struct flce_handle {
   int* pa = nullptr;       // tile argmax   [nt x C]
   float* ztgt = nullptr;   // [C]
   float* dzt = nullptr;    // [C]
+  float* ptgt = nullptr;   // [C] stored exponential at the target's column
+  float* beta = nullptr;   // [C] row scale of dZ inside the dX contraction
+  float* corr = nullptr;   // [C] target correction of the dX rows
+  uint8_t* shift = nullptr;  // [nt x C] per-(tile, row) exponent shifts
   double* loss_part = nullptr;  // [C / kFinalizeRows]
   float* splitk = nullptr;      // [splitk_alloc x C x H]
   void* Pq = nullptr;           // teacher exp(z_T / tau - m_tile) [C x Vpad]
@@ -216,7 +221,7 @@ namespace {
 // Byte offsets of the workspace buffers of one handle, from (H, V, C, G,
 // dtype, weight copy, teacher) only.
 struct Layout {
-  size_t Wt, P, Pt, Xt, pm, ps, pa, zt, dz, lp, sk, sc, cp, Pq, pmq, psq, paq, pc;
+  size_t Wt, P, Pt, Xt, pm, ps, pa, zt, dz, pt, be, co, sh, lp, sk, sc, cp, Pq, pmq, psq, paq, pc;
   size_t total;
 };
 
@@ -239,7 +244,7 @@ flce_status_t configure(const flce_config_t* cfg, int64_t Ht, flce_handle* h, La
   C = round_up(C, 256);
   const int64_t G = cfg->dw_chunks ? cfg->dw_chunks : 1;
   if (C * G > (1 << 20)) return FLCE_ERR_UNSUPPORTED;
-  if (cfg->flags & ~FLCE_FLAG_NO_WEIGHT_COPY) return FLCE_ERR_INVALID_ARGUMENT;
+  if (cfg->flags & ~(FLCE_FLAG_NO_WEIGHT_COPY | FLCE_FLAG_DZ_IN_DX)) return FLCE_ERR_INVALID_ARGUMENT;
   const bool no_wcopy = (cfg->flags & FLCE_FLAG_NO_WEIGHT_COPY) != 0;
   // W as stored: bf16 transposing LDS reads; one buffer descriptor spans W,
   // whose size must stay below the out-of-range offset (2^31) that reads 0
@@ -252,6 +257,7 @@ flce_status_t configure(const flce_config_t* cfg, int64_t Ht, flce_handle* h, La
   h->G = (int)G;
   h->Ht = Ht;
   h->w_copy = !no_wcopy;
+  h->dz_in_dx = (cfg->flags & FLCE_FLAG_DZ_IN_DX) != 0;
   h->Vpad = round_up(V, 256);
   h->nt = cdiv64(V, kPartialWidth);
   {
@@ -276,6 +282,10 @@ flce_status_t configure(const flce_config_t* cfg, int64_t Ht, flce_handle* h, La
   L->pa = carve((size_t)C * h->nt * 4);
   L->zt = carve((size_t)C * 4);
   L->dz = carve((size_t)C * 4);
+  L->pt = carve((size_t)C * 4);
+  L->be = carve((size_t)C * 4);
+  L->co = carve((size_t)C * 4);
+  L->sh = carve((size_t)C * h->nt);
   L->lp = carve((size_t)cdiv64(C, kFinalizeRows) * 8);
   L->sk = h->splitk_alloc > 1 ? carve((size_t)h->splitk_alloc * C * H * 4) : 0;
   L->sc = carve(64);
@@ -303,6 +313,10 @@ void bind_workspace(flce_handle* h, const Layout& L, char* base) {
   h->pa = (int*)(base + L.pa);
   h->ztgt = (float*)(base + L.zt);
   h->dzt = (float*)(base + L.dz);
+  h->ptgt = (float*)(base + L.pt);
+  h->beta = (float*)(base + L.be);
+  h->corr = (float*)(base + L.co);
+  h->shift = (uint8_t*)(base + L.sh);
   h->loss_part = (double*)(base + L.lp);
   h->splitk = h->splitk_alloc > 1 ? (float*)(base + L.sk) : nullptr;
   h->nvalid = (int64_t*)(base + L.sc);
@@ -564,6 +578,8 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       la.inv_temp = soft->inv_temp;
       la.Pq = h->Pq;
       la.pc = h->pc;
+    } else if (h->dz_in_dx) {
+      la.ptgt = h->ptgt;
     }
     FLCE_LAUNCH(K_LOGITS, launch_logits(dt, la, s));
 
@@ -592,6 +608,13 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       fa.alpha_q = h->pmq;
       fa.alpha_mul = soft->inv_temp;
       fa.no_target = true;
+    } else if (h->dz_in_dx) {
+      // dZ is formed inside the dX contraction (row scale, tile shifts,
+      // target correction); the dZ pass below writes only dZ^T
+      fa.beta = h->beta;
+      fa.shift = h->shift;
+      fa.corr = h->corr;
+      fa.ptgt = h->ptgt;
     }
     fa.backward = true;
     fa.loss_part = h->loss_part;
@@ -619,9 +642,24 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       xa.Pq = h->Pq;
       xa.alpha_q = h->pmq;
     }
+    xa.write_rows = soft != nullptr || !h->dz_in_dx;
     FLCE_LAUNCH(K_FIXUP, launch_fixup(dt, xa, s));
 
-    // dX_c = dZ W   (M = Cc, N = H, K = vocabulary)
+    // dX_c = dZ W   (M = Cc, N = H, K = vocabulary); without soft targets
+    // A holds the exponentials and dZ is formed in the contraction
+    DxFuse fz{};
+    fz.shift = h->shift;
+    fz.shift_ld = C;
+    fz.shift_tiles = (int)nt;
+    fz.beta = h->beta;
+    fz.corr = h->corr;
+    fz.y = yc;
+    fz.ignore_index = ignore_index;
+    fz.y_shift = cols.y_shift;
+    fz.V = (int)V;
+    fz.W = W;
+    fz.ldw = H;
+    const DxFuse* fuse = (!soft && h->dz_in_dx) ? &fz : nullptr;
     {
       TileCfg tc;
       int splits;
@@ -645,6 +683,7 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       ga.M = (int)Cc;
       ga.N = (int)H;
       ga.accumulate = false;
+      ga.fuse = fuse;
       char* dXc = (char*)dX + (size_t)t0 * H * es;
       if (splits == 1) {
         ga.out = dXc;
@@ -661,7 +700,7 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
         ga.split_stride = Ck * H;
         FLCE_LAUNCH(K_DX, launch_gemm_store(dt, tc, ga, s));
         FLCE_LAUNCH(K_SPLITK, launch_splitk_reduce(dt, h->splitk, splits, Ck * H, (int)Cc,
-                                                   (int)H, dXc, H, s));
+                                                   (int)H, dXc, H, s, fuse));
       }
     }
     // dW (+)= dZ^T X over the chunks of a group (M = V, N = H, K = gs C + Ck)

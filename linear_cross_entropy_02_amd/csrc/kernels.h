@@ -33,12 +33,37 @@ struct LogitsArgs {
   // ([M x ldp], input dtype) and, per (tile, row), sum_v P_T z / tau out.
   const void* Pq = nullptr;
   float* pc = nullptr;
+  // nullable: per row, the stored exponential at the target's column (the
+  // value the dX contraction reads there), as fp32
+  float* ptgt = nullptr;
 };
+// The stored exponentials of a (row, 128-column tile) are exp2(z log2(e) /
+// tau - k) with k = ceil(m log2(e)), m the tile's max of z / tau: relative to
+// a whole power of two, so that the factor taking them to probabilities is a
+// per-row scale times 2^-s(row, tile) (see FinalizeArgs).
 // Width in columns of one online-logsumexp partial (the wave tile width of
 // the 256 x 256 logits GEMM).
 constexpr int kPartialWidth = 128;
 
 hipError_t launch_logits(Dt dt, const LogitsArgs& a, hipStream_t s);
+
+// dX = dZ W with dZ formed inside the contraction: A is the chunk's stored
+// exponentials P, scaled in registers by 2^-shift (see FinalizeArgs), and
+// the output row t is beta_t acc_t + corr_t W[y_t - y_shift] (the target
+// term only when that row of W is in [0, V)).
+struct DxFuse {
+  const uint8_t* shift;
+  int64_t shift_ld;   // bytes per tile
+  int shift_tiles;
+  const float* beta;
+  const float* corr;
+  const int64_t* y;   // chunk targets
+  int64_t ignore_index;
+  int64_t y_shift;
+  int V;              // rows of W
+  const void* W;      // [V x ldw], input dtype
+  int64_t ldw;
+};
 
 struct GemmOutArgs {
   const void* A; int64_t lda;
@@ -59,6 +84,9 @@ struct GemmOutArgs {
   // B as stored, K rows of N contiguous elements (ldb >= N), rather than
   // N x K: bf16 only, not accumulating, K * ldb * 2 < 2^31 bytes.
   bool b_stored = false;
+  // dX with dZ formed inside the contraction (not accumulating); with
+  // splits > 1 the partial planes are raw and launch_splitk_reduce applies it.
+  const DxFuse* fuse = nullptr;
 };
 hipError_t launch_gemm_store(Dt dt, TileCfg tc, const GemmOutArgs& a, hipStream_t s);
 
@@ -103,6 +131,17 @@ struct FinalizeArgs {
   double* loss_part;     // one slot per block_rows rows; nullable
   int first_chunk;
   int block_rows = 8;    // finalize_rows(nt, C): 8 or 32
+  // Backward with dZ formed inside the dX contraction (all nullable):
+  //   beta  [M]       per-row scale: dZ_tv = beta_t 2^-s_tj P_tv off the target
+  //   shift [nt x ldr] bytes s_tj = K_t - k_tj (255: empty tile), row t of
+  //                   tile j at byte j ldr + (t & ~127) + 8 (t % 16) + (t / 16) % 8
+  //   corr  [M]       dzt_t - beta_t 2^-s P_t,y (the target's correction; 0
+  //                   when the target is ignored or not in these columns)
+  //   ptgt  [M]       in: the stored exponential at the target's column
+  float* beta = nullptr;
+  uint8_t* shift = nullptr;
+  float* corr = nullptr;
+  const float* ptgt = nullptr;
 };
 // Rows per finalize block, hence rows per loss partial: 32 when rows hold
 // at most 256 partial tiles and a chunk of C rows still gives 256 blocks,
@@ -125,11 +164,13 @@ struct FixupArgs {
   bool no_target = false;        // soft targets: no one-hot column
   const void* Pq = nullptr;      // soft targets: teacher exponentials, subtracted
   const float* alpha_q = nullptr;  //   with this scale, [nt x ldr]
+  bool write_rows = true;        // false: only dZ^T is written (P keeps the exponentials)
 };
 hipError_t launch_fixup(Dt dt, const FixupArgs& a, hipStream_t s);
 
 hipError_t launch_splitk_reduce(Dt dt, const float* part, int splits, int64_t stride, int M,
-                                int N, void* out, int64_t ldo, hipStream_t s);
+                                int N, void* out, int64_t ldo, hipStream_t s,
+                                const DxFuse* fuse = nullptr);
 
 hipError_t launch_loss(const double* loss_part, int nparts, const int64_t* n_valid,
                        int reduction_sum, float* loss, hipStream_t s);

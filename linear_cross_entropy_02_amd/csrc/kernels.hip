@@ -70,6 +70,7 @@ struct LogitsEpi {
   int64_t y_shift;  // vocabulary id of column 0 (a vocabulary shard's offset)
   int M, V;
   bool store_p;  // false: partials and target logit only (forward-only calls)
+  float* ptgt;   // nullable: the stored exponential at the target's column
 
   template <int FM, int FN>
   __device__ __forceinline__ void init(f4 (&acc)[FM][FN], const EpiCoord&) const {
@@ -147,25 +148,39 @@ struct LogitsEpi {
         cross += shfl_xor_f(cross, 16);
         cross += shfl_xor_f(cross, 32);
       }
+      // exponentials relative to 2^kq, kq = ceil(tile max log2(e)): a whole
+      // power of two, so that the merge turns them into probabilities with a
+      // per-row scale and an exact power-of-two factor per tile
       const float kl = kLog2e * inv_temp;
-      const float mb = (mx == kNegInf) ? 0.f : mx * kl;
+      const float pmv = mx * inv_temp;
+      const float kq = (mx == kNegInf) ? 0.f : __builtin_ceilf(pmv * kLog2e);
       float sum = 0.f;
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float e = (FULL || lc0 + 16 * j + r < V)
-                              ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][r], kl, -mb))
+                              ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][r], kl, -kq))
                               : 0.f;
           sum += e;
           acc[i][j][r] = e;
         }
       sum += shfl_xor_f(sum, 16);
       sum += shfl_xor_f(sum, 32);
+      if (ptgt && toff[i] >= 0) {
+        // the value stored at the target's column, as the dX contraction reads it
+        const int tk = 4 * (toff[i] >> 4) + (toff[i] & 3);
+        float et = 0.f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) et = (4 * j + r == tk) ? acc[i][j][r] : et;
+        ptgt[row] = Elem<T>::to_f32(Elem<T>::from_f32(et));
+      }
       if (row < M) {
         if (g == 0 && ec.col0 < V) {
           const int64_t o = (int64_t)ptile * ldr + row;
-          pm[o] = mx * inv_temp;
+          pm[o] = pmv;
           ps[o] = sum;
           pa[o] = ai;
           if constexpr (CROSS) pc[o] = cross * inv_temp;
@@ -246,6 +261,49 @@ struct StoreEpi {
   }
 };
 
+// dX epilogue when dZ is formed inside the contraction (the A operand is
+// the stored exponentials scaled by 2^-shift in registers): row t of the
+// output is beta_t acc_t + corr_t W[y_t - y_shift], the second term being
+// the one-hot target's correction (corr is 0 when there is none).  TO is the
+// input dtype, which dX and W share.
+template <typename TO>
+struct DxEpi {
+  TO* out;
+  int64_t ldo;
+  int M, N;
+  DxFuse f;
+
+  template <int FM, int FN>
+  __device__ __forceinline__ void init(f4 (&acc)[FM][FN], const EpiCoord&) const {
+    zero_init(acc);
+  }
+
+  template <int FM, int FN>
+  __device__ __forceinline__ void apply(f4 (&acc)[FM][FN], const EpiCoord& ec) const {
+    const int g = ec.lane >> 4, c = ec.lane & 15;
+    const int lc0 = ec.col0 + 4 * g;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = ec.row0 + 16 * i + c;
+      if (row >= M) continue;
+      const float b = f.beta[row], cr = f.corr[row];
+      const TO* wr = nullptr;
+      if (cr != 0.f) {
+        const int64_t yl = f.y[row] - f.y_shift;
+        if (yl >= 0 && yl < f.V) wr = (const TO*)f.W + yl * f.ldw;
+      }
+      TO* const p = out + (int64_t)row * ldo + lc0;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if (lc0 + 16 * j >= N) continue;
+        f4 v = acc[i][j] * b;
+        if (wr) v += load4(wr + lc0 + 16 * j) * cr;
+        store4(p + 16 * j, v);
+      }
+    }
+  }
+};
+
 // Split-K partial of one block tile, stored compactly: plane
 // (split, slot) of `part` holds the BM x BN block tile row-major, slot being
 // the tile's index within the launch's tile range.  Rows and columns past
@@ -299,7 +357,7 @@ __global__ void __launch_bounds__(256) tile_reduce_kernel(GemmShape g, const flo
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false>
+template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false, bool AS = false>
 static hipError_t run_gemm(const GemmShape& g0, const Epi& epi, hipStream_t s) {
   using G = TileGeom<BM, BN, WAVES>;
   GemmShape g = g0;
@@ -316,17 +374,28 @@ static hipError_t run_gemm(const GemmShape& g0, const Epi& epi, hipStream_t s) {
   if (g.tile_first < 0 || g.tile_first + g.tile_count > g.tiles_m * g.tiles_n)
     return hipErrorInvalidValue;
   const int nblk = g.tile_count * g.splits;
-  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, WAVES, Epi, BT>), dim3(nblk), dim3(G::kThreads),
-                     G::kLdsBytes, s, g, epi);
+  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, WAVES, Epi, BT, AS>), dim3(nblk),
+                     dim3(G::kThreads), G::kLdsBytes, s, g, epi);
   return hipGetLastError();
 }
 
 // The GEMM kernels use more than the default 64 KB of dynamic LDS.
-template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false>
+template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false, bool AS = false>
 static hipError_t set_lds_attr() {
   using G = TileGeom<BM, BN, WAVES>;
-  return hipFuncSetAttribute((const void*)gemm_nt_kernel<T, BM, BN, WAVES, Epi, BT>,
+  return hipFuncSetAttribute((const void*)gemm_nt_kernel<T, BM, BN, WAVES, Epi, BT, AS>,
                              hipFuncAttributeMaxDynamicSharedMemorySize, G::kLdsBytes);
+}
+
+// The dX instantiations with dZ formed inside the contraction, for one B
+// layout: direct output or raw split-K partials, 256- or 128-wide tiles.
+template <typename T, bool BT>
+static hipError_t setup_fused_dx() {
+  hipError_t e;
+  if ((e = set_lds_attr<T, 256, 256, 4, DxEpi<T>, BT, true>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<float, false>, BT, true>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 128, 128, 4, DxEpi<T>, BT, true>()) != hipSuccess) return e;
+  return set_lds_attr<T, 128, 128, 4, StoreEpi<float, false>, BT, true>();
 }
 
 template <typename T>
@@ -341,7 +410,9 @@ static hipError_t setup_t() {
   if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<T, false>>()) != hipSuccess) return e;
   if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<float, false>>()) != hipSuccess) return e;
   if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<float, true>>()) != hipSuccess) return e;
+  if ((e = setup_fused_dx<T, false>()) != hipSuccess) return e;
   if constexpr (std::is_same<T, bf16>::value) {  // dX reading W as stored
+    if ((e = setup_fused_dx<T, true>()) != hipSuccess) return e;
     if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<T, false>, true>()) != hipSuccess) return e;
     if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<float, false>, true>()) != hipSuccess) return e;
     if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<T, false>, true>()) != hipSuccess) return e;
@@ -386,6 +457,7 @@ static hipError_t logits_run(const LogitsArgs& a, const GemmShape& g, hipStream_
   epi.M = a.M;
   epi.V = a.V;
   epi.store_p = a.P != nullptr;
+  epi.ptgt = a.ptgt;
   return run_gemm<T, 256, 256, 4>(g, epi, s);
 }
 
@@ -435,6 +507,48 @@ static hipError_t store_t2(TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
   epi.N = a.N;
   epi.split_stride = a.split_stride;
   epi.accumulate = ACC && a.accumulate;
+  if (a.fuse) {
+    // dZ formed inside the contraction: shifted A fragments; the output
+    // (split-K: the partial planes, summed and finished by splitk_reduce)
+    if constexpr (!ACC) {
+      g.ash = a.fuse->shift;
+      g.ash_ld = a.fuse->shift_ld;
+      g.ash_tiles = a.fuse->shift_tiles;
+      if (g.splits > 1) {
+        if constexpr (std::is_same<TO, float>::value) {
+          if (a.b_stored) {
+            if constexpr (std::is_same<T, bf16>::value) {
+              if (tc != TileCfg::T256)
+                return run_gemm<T, 128, 128, 4, StoreEpi<float, false>, true, true>(g, epi, s);
+              return run_gemm<T, 256, 256, 4, StoreEpi<float, false>, true, true>(g, epi, s);
+            }
+            return hipErrorInvalidValue;
+          }
+          if (tc != TileCfg::T256)
+            return run_gemm<T, 128, 128, 4, StoreEpi<float, false>, false, true>(g, epi, s);
+          return run_gemm<T, 256, 256, 4, StoreEpi<float, false>, false, true>(g, epi, s);
+        }
+        return hipErrorInvalidValue;
+      } else if constexpr (std::is_same<TO, T>::value) {
+        DxEpi<T> de;
+        de.out = (T*)a.out;
+        de.ldo = a.ldo;
+        de.M = a.M;
+        de.N = a.N;
+        de.f = *a.fuse;
+        if (a.b_stored) {
+          if constexpr (std::is_same<T, bf16>::value) {
+            if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4, DxEpi<T>, true, true>(g, de, s);
+            return run_gemm<T, 256, 256, 4, DxEpi<T>, true, true>(g, de, s);
+          }
+          return hipErrorInvalidValue;
+        }
+        if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4, DxEpi<T>, false, true>(g, de, s);
+        return run_gemm<T, 256, 256, 4, DxEpi<T>, false, true>(g, de, s);
+      }
+    }
+    return hipErrorInvalidValue;
+  }
   if (a.b_stored) {
     if constexpr (std::is_same<T, bf16>::value && !ACC) {
       if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4, StoreEpi<TO, ACC>, true>(g, epi, s);
@@ -710,7 +824,7 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   __shared__ float s_f[kFinSlices][kFinRows + 1];
   __shared__ float s_c[kFinSlices][kFinRows + 1];
   __shared__ int s_i[kFinSlices][kFinRows + 1];
-  __shared__ float s_m[kFinRows], s_lse[kFinRows], s_sc[kFinRows];
+  __shared__ float s_m[kFinRows], s_k[kFinRows], s_sc[kFinRows], s_beta[kFinRows];
   __shared__ double s_nll[kFinRows];
   const int rl = threadIdx.x % kFinRows, sl = threadIdx.x / kFinRows;
   // a partial array row of 32 tokens (one 128-byte line) spans 32 / ROWS
@@ -778,14 +892,19 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
     if (live && a.argmax_out) a.argmax_out[row] = am == 0x7fffffff ? am : am + (int)a.y_shift;
   }
   __syncthreads();
-  // pass 2: rescaled sum
+  // The stored exponentials of tile j are relative to 2^k_j, k_j =
+  // ceil(m_j log2 e) (0 for an all -inf tile), exactly as the logits
+  // epilogue computed it; K = ceil(m log2 e) is the largest k_j.
+  auto kq_of = [](float mj) { return mj == kNegInf ? 0.f : __builtin_ceilf(mj * kLog2e); };
+  // pass 2: sum = sum_j s_j 2^(k_j - K) (exact power-of-two rescaling)
   // (soft targets: also sum_j alpha_q_j pc_j = sum_v q_v z_v / tau)
   m = s_m[rl];
+  const float K = kq_of(m);
   float sum = 0.f, cr = 0.f;
 #pragma unroll
   for (int q = 0; q < kFinCache; ++q) {
     const int j = sl + q * kFinSlices;
-    if (cs[q] != 0.f) sum += cs[q] * exp_fast(cm[q] - m);
+    if (cs[q] != 0.f) sum += cs[q] * __builtin_amdgcn_exp2f(kq_of(cm[q]) - K);
     if (a.cross_pc && live && j < a.nt) {
       const int64_t o = (int64_t)j * a.ldr + row;
       cr += a.cross_pc[o] * a.alpha_q[o];
@@ -795,7 +914,7 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
     for (int j = sl + kFinCache * kFinSlices; j < a.nt; j += kFinSlices) {
       const int64_t o = (int64_t)j * a.ldr + row;
       const float sj = a.ps[o];
-      if (sj != 0.f) sum += sj * exp_fast(a.pm[o] - m);
+      if (sj != 0.f) sum += sj * __builtin_amdgcn_exp2f(kq_of(a.pm[o]) - K);
       if (a.cross_pc) cr += a.cross_pc[o] * a.alpha_q[o];
     }
   s_f[sl][rl] = sum;
@@ -812,7 +931,7 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   }
   if (sl == 0) {
     double nll = 0.0;
-    float lse = 0.f, sc = 0.f;
+    float lse = 0.f, beta = 0.f, sc = 0.f;
     if (live) {
       // validity against the whole vocabulary; ownership of the target by
       // these columns (all of them unless this is a vocabulary shard)
@@ -820,40 +939,65 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
       const bool valid = target_valid(yt, a.ignore_index, a.v_total);
       const int64_t yl = yt - a.y_shift;
       const bool owned = valid && !a.no_target && yl >= 0 && yl < a.V;
-      lse = a.lse_in ? a.lse_in[row] : m + log_fast(sum);
+      // lse = ln(2^K sum) = (K + log2 sum) ln 2
+      lse = a.lse_in ? a.lse_in[row] : (K + __builtin_amdgcn_logf(sum)) * kLn2;
       sc = valid ? (a.unit_scale ? 1.f : *a.scale) * a.alpha_mul : 0.f;
+      // probability of column v in tile j: P_v 2^(k_j - K) beta / sc, beta =
+      // sc 2^K e^-lse (= sc / sum when lse is this call's own)
+      if (sc != 0.f)
+        beta = a.lse_in ? sc * __builtin_amdgcn_exp2f(K - a.lse_in[row] * kLog2e) : sc / sum;
       const float zt = owned ? a.ztgt[row] : 0.f;
-      if (a.backward) a.dzt[row] = owned ? sc * (exp_fast(zt - lse) - 1.f) : 0.f;
+      const float dzt = owned ? sc * (exp_fast(zt - lse) - 1.f) : 0.f;
+      if (a.backward) a.dzt[row] = dzt;
+      if (a.beta) a.beta[row] = beta;
+      if (a.corr) {
+        // the target column read by the dX contraction holds P_y 2^-s; its
+        // dZ must be dzt: the output row adds corr times W's target row
+        float c = 0.f;
+        if (owned) {
+          const int jy = (int)(yl / kPartialWidth);
+          const float ky = kq_of(a.pm[(int64_t)jy * a.ldr + row]);
+          c = dzt - beta * __builtin_amdgcn_exp2f(ky - K) * a.ptgt[row];
+        }
+        a.corr[row] = c;
+      }
       if (a.lse_out) a.lse_out[row] = lse;
       if (a.logprob_out) a.logprob_out[row] = valid ? zt - lse : 0.f;
       if (a.m_out) a.m_out[row] = m;
-      if (a.sum_out) a.sum_out[row] = sum;
+      // relative to the max itself: sum_v exp(z_v - m) = sum 2^(K - m log2 e)
+      if (a.sum_out) a.sum_out[row] = sum * __builtin_amdgcn_exp2f(K - m * kLog2e);
       if (a.zt_out) a.zt_out[row] = zt;
       // hard target: lse - z_y; soft targets: lse - sum_v q_v z_v / tau
       nll = valid ? (double)lse - (double)(a.cross_pc ? cr : zt) : 0.0;
     }
-    s_lse[rl] = lse;
+    s_k[rl] = K;
     s_sc[rl] = sc;
+    s_beta[rl] = beta;
     s_nll[rl] = nll;
   }
   __syncthreads();
-  // pass 3: alpha (only when the gradient follows)
+  // pass 3 (only when the gradient follows): alpha_j = beta 2^(k_j - K),
+  // the factor taking tile j's stored exponentials to s valid softmax, and
+  // (for the dX contraction) the shift K - k_j as a byte
   if (live && a.backward) {
-    const float lse = s_lse[rl], sc = s_sc[rl];
+    const float Kr = s_k[rl], beta = s_beta[rl], sc = s_sc[rl];
+    const int64_t perm = (row & ~127) + 8 * (row & 15) + ((row >> 4) & 7);
+    auto put = [&](int j, float mj, float sj) {
+      const int64_t o = (int64_t)j * a.ldr + row;
+      const float kj = kq_of(mj);
+      a.pm[o] = (sj != 0.f) ? beta * __builtin_amdgcn_exp2f(kj - Kr) : 0.f;
+      if (a.shift)
+        a.shift[(int64_t)j * a.ldr + perm] =
+            (uint8_t)((sj != 0.f) ? __builtin_fminf(__builtin_fmaxf(Kr - kj, 0.f), 255.f) : 255.f);
+      if (a.alpha_q) a.alpha_q[o] *= sc;
+    };
 #pragma unroll
     for (int q = 0; q < kFinCache; ++q) {
       const int j = sl + q * kFinSlices;
-      if (j < a.nt) {
-        const int64_t o = (int64_t)j * a.ldr + row;
-        a.pm[o] = (cs[q] != 0.f) ? sc * exp_fast(cm[q] - lse) : 0.f;
-        if (a.alpha_q) a.alpha_q[o] *= sc;
-      }
+      if (j < a.nt) put(j, cm[q], cs[q]);
     }
-    for (int j = sl + kFinCache * kFinSlices; j < a.nt; j += kFinSlices) {
-      const int64_t o = (int64_t)j * a.ldr + row;
-      a.pm[o] = (a.ps[o] != 0.f) ? sc * exp_fast(a.pm[o] - lse) : 0.f;
-      if (a.alpha_q) a.alpha_q[o] *= sc;
-    }
+    for (int j = sl + kFinCache * kFinSlices; j < a.nt; j += kFinSlices)
+      put(j, a.pm[(int64_t)j * a.ldr + row], a.ps[(int64_t)j * a.ldr + row]);
   }
   if (threadIdx.x == 0 && a.loss_part) {
     double total = 0.0;
@@ -918,7 +1062,7 @@ __global__ void __launch_bounds__(256) fixup_kernel(FixupArgs a) {
       T* oe = (T*)&ov;
 #pragma unroll
       for (int k = 0; k < EPV; ++k) oe[k] = Elem<T>::from_f32(d[k]);
-      *(uint4*)src = ov;
+      if (a.write_rows) *(uint4*)src = ov;
 #pragma unroll
       for (int k = 0; k < EPV; ++k) tile[r][cv * EPV + k] = oe[k];
     } else {
@@ -989,7 +1133,7 @@ __global__ void __launch_bounds__(256) fixup_bf16_kernel(FixupArgs a) {
         for (int k = 0; k < 8; ++k) d[k] = (yl == v + k) ? dz : d[k];
       }
       ov = pack8_bf16(d);
-      *(uint4*)src = ov;
+      if (a.write_rows) *(uint4*)src = ov;
     }
     tile[r * 32 + (cv ^ ((r >> 3) & 7))] = ov;
   }
@@ -1038,29 +1182,38 @@ hipError_t launch_fixup(Dt dt, const FixupArgs& a, hipStream_t s) {
 template <typename T>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, int splits,
                                                             int64_t stride, int M, int N,
-                                                            T* __restrict__ out, int64_t ldo) {
+                                                            T* __restrict__ out, int64_t ldo,
+                                                            DxFuse f, bool fused) {
   const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   const int64_t total = (int64_t)M * N;
   if (idx >= total) return;
   const int row = (int)(idx / N), col = (int)(idx % N);  // N % 4 == 0
   f4 s = *(const f4*)(part + idx);
   for (int k = 1; k < splits; ++k) s += *(const f4*)(part + (int64_t)k * stride + idx);
-  T* o = out + (int64_t)row * ldo + col;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = Elem<T>::from_f32(s[e]);
+  if (fused) {
+    // dZ formed inside the contraction: the row scale and the target's term
+    const float cr = f.corr[row];
+    s *= f.beta[row];
+    if (cr != 0.f) {
+      const int64_t yl = f.y[row] - f.y_shift;
+      if (yl >= 0 && yl < f.V) s += load4((const T*)f.W + yl * f.ldw + col) * cr;
+    }
+  }
+  store4(out + (int64_t)row * ldo + col, s);
 }
 
 hipError_t launch_splitk_reduce(Dt dt, const float* part, int splits, int64_t stride, int M, int N,
-                                void* out, int64_t ldo, hipStream_t s) {
+                                void* out, int64_t ldo, hipStream_t s, const DxFuse* fuse) {
   const int64_t total = (int64_t)M * N / 4;
   if (total <= 0) return hipSuccess;
   dim3 grid(cdiv(total, 256));
+  const DxFuse f = fuse ? *fuse : DxFuse{};
   if (dt == Dt::BF16)
     hipLaunchKernelGGL(splitk_reduce_kernel<bf16>, grid, dim3(256), 0, s, part, splits, stride, M,
-                       N, (bf16*)out, ldo);
+                       N, (bf16*)out, ldo, f, fuse != nullptr);
   else
     hipLaunchKernelGGL(splitk_reduce_kernel<float>, grid, dim3(256), 0, s, part, splits, stride, M,
-                       N, (float*)out, ldo);
+                       N, (float*)out, ldo, f, fuse != nullptr);
   return hipGetLastError();
 }
 

@@ -77,7 +77,7 @@ def test_create_reports_unsupported_sizes_without_device(lib, hidden, vocab, chu
 
 
 @pytest.mark.parametrize("hidden,vocab,dtype,flags,status", [
-    (64, 100, flce.FLCE_BF16, 2, flce.FLCE_ERR_INVALID_ARGUMENT),          # unknown flag bit
+    (64, 100, flce.FLCE_BF16, 4, flce.FLCE_ERR_INVALID_ARGUMENT),          # unknown flag bit
     (64, 100, flce.FLCE_BF16, -1, flce.FLCE_ERR_INVALID_ARGUMENT),
     (64, 100, flce.FLCE_F32, flce.FLCE_FLAG_NO_WEIGHT_COPY, flce.FLCE_ERR_UNSUPPORTED),  # fp32
     # W of 2^31 bytes or more: one buffer descriptor no longer spans it below
