@@ -21,13 +21,20 @@ cross-entropy would.
 """
 from __future__ import annotations
 
+import collections
 import threading
+from typing import Optional
 
 import torch
 
 from . import FLCE_OK, FlceError, FusedLinearCrossEntropy, flce_query_error
+from .launch import suggest_launch
 
-_handles: dict = {}
+# Handles (each owning a workspace of up to a few GB) kept for reuse, the
+# least recently used closed beyond this many.
+MAX_CACHED_HANDLES = 4
+
+_handles: "collections.OrderedDict" = collections.OrderedDict()
 _lock = threading.Lock()
 
 
@@ -39,16 +46,25 @@ def _handle(device: torch.device, stream: torch.cuda.Stream, H: int, V: int, dty
     with _lock:
         op = _handles.get(key)
         if op is None:
+            while len(_handles) >= MAX_CACHED_HANDLES:
+                _, old = _handles.popitem(last=False)
+                # the evicted handle's last call may still run on its stream
+                torch.cuda.synchronize(device)
+                old.close()
             with torch.cuda.device(device):
                 op = FusedLinearCrossEntropy(H, V, dtype, chunk_tokens=chunk_tokens,
                                              dw_chunks=dw_chunks, weight_copy=weight_copy)
             _handles[key] = op
+        else:
+            _handles.move_to_end(key)
         return op
 
 
 def clear_handle_cache():
     """Free every cached handle's workspace."""
     with _lock:
+        if _handles:
+            torch.cuda.synchronize()
         for op in _handles.values():
             op.close()
         _handles.clear()
@@ -58,7 +74,7 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
     @staticmethod
     @torch.amp.custom_fwd(device_type="cuda", cast_inputs=torch.bfloat16)
     def forward(ctx, X, W, targets, ignore_index: int = -100, reduction: str = "mean",
-                chunk_tokens: int = 0, dw_chunks: int = 0, weight_copy: bool = True,
+                chunk_tokens: int = 0, dw_chunks: int = 0, weight_copy: Optional[bool] = None,
                 check_targets: bool = False):
         if X.dim() != 2 or W.dim() != 2 or X.shape[1] != W.shape[1]:
             raise ValueError("X must be [T, H] and W [V, H]")
@@ -71,6 +87,11 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
         W = W.contiguous()
         targets = targets.contiguous()
         stream = torch.cuda.current_stream(X.device)
+        # unset launch settings: the ones measured fastest for this shape
+        C, G, wc = suggest_launch(X.shape[0], X.shape[1], W.shape[0], dtype)
+        chunk_tokens = chunk_tokens or C
+        dw_chunks = dw_chunks or G
+        weight_copy = wc if weight_copy is None else weight_copy
         op = _handle(X.device, stream, X.shape[1], W.shape[0], dtype, chunk_tokens, dw_chunks,
                      weight_copy)
         out = op.fwd_bwd(X, W, targets, ignore_index, reduction)
@@ -99,12 +120,14 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
 def linear_cross_entropy(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
                          ignore_index: int = -100, reduction: str = "mean",
                          chunk_tokens: int = 0, dw_chunks: int = 0,
-                         return_lse: bool = False, weight_copy: bool = True,
+                         return_lse: bool = False, weight_copy: Optional[bool] = None,
                          check_targets: bool = False):
     """Cross-entropy of softmax(X W^T) against `targets`, fused: the T x V
     logits are never formed.  Returns the scalar loss (and the per-token
     log-sum-exp when `return_lse`); gradients reach X and W through
-    autograd.  weight_copy=False (bf16) has the dX contraction read W as
+    autograd.  Launch settings left at 0 / None (chunk_tokens, dw_chunks,
+    weight_copy) come from launch.suggest_launch for the shape: the fastest
+    measured.  weight_copy=False (bf16) has the dX contraction read W as
     stored instead of a transposed copy made per call, for less memory.
     check_targets=True raises ValueError for a target outside [0, V) that
     is not ignore_index (one stream synchronisation per call); otherwise

@@ -1,0 +1,37 @@
+"""Launch settings chosen by shape: tokens per chunk C, chunks per dW GEMM G
+and whether the dX contraction reads a transposed copy of W.
+
+The settings are the fastest measured (MI355X, one box, alternating runs)
+for the head shapes the library is tuned on; between them the rule below
+interpolates by hidden size.  They trade workspace for speed: the dZ^T of
+G chunks is kept so that the fp32 dW tiles are read and written once per G
+chunks, and the W^T copy makes the dX contraction read 16-byte fragments.
+  * H >= 2048: C = 2048, G = 4 up to H = 4096 (at 16384 x 4096 x 128256 a
+    step takes 41.4 ms; G = 2: 42.6, G = 1: 45.2, C = 4096, G = 1: 42.8),
+    G = 2 above (8192 x 8192 x 128256: 40.3 ms; G = 1: 42.9); the W^T copy
+    unless it would be as large as a bf16 T x V buffer (H >= T).
+  * H < 2048: C = 8192, G = 1 for batches of 32768 tokens or more
+    (65536 x 512 x 16000), else C = 1024, G = 2 reading W as stored
+    (4096 x 512 x 16000: 0.45 ms; G = 1: 0.48 ms).
+  * fp32: one chunk of up to 4096 tokens, G = 1.
+C never exceeds the batch (rounded up to 256) and G the number of chunks.
+"""
+from __future__ import annotations
+
+
+def suggest_launch(T: int, H: int, V: int, dtype: str = "bf16"):
+    """(chunk_tokens, dw_chunks, weight_copy) for a batch of T tokens."""
+    if dtype == "f32":
+        C, G, wcopy = 4096, 1, True
+    elif H >= 2048:
+        C = 2048
+        G = 4 if H <= 4096 else 2
+        wcopy = H < T
+    elif T >= 32768:
+        C, G, wcopy = 8192, 1, True
+    else:
+        C, G, wcopy = 1024, 2, False
+    tpad = max(256, -(-max(T, 1) // 256) * 256)
+    C = min(C, tpad)
+    G = max(1, min(G, -(-max(T, 1) // C)))
+    return C, G, wcopy
