@@ -45,25 +45,47 @@ def _run(cmd):
         print(out)
 
 
-def build(verbose: bool = False) -> str:
+# Host-side sanitizer build (the ABI tests run against it on the CPU): every
+# -fsanitize applies to the host pass only, the device code is unchanged.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-O1"]
+
+
+def asan_runtime() -> str:
+    """The AddressSanitizer runtime of hipcc's clang (preloaded by a process
+    that loads the sanitizer build, since a shared library does not carry it)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    r = subprocess.run([clang, "--print-file-name=libclang_rt.asan-x86_64.so"],
+                       stdout=subprocess.PIPE, text=True)
+    return r.stdout.strip()
+
+
+def build(verbose: bool = False, sanitize: bool = False, out: str = LIB) -> str:
     cc = hipcc()
-    objdir = os.path.join(PKG, "_build")
+    objdir = os.path.join(PKG, "_build_san" if sanitize else "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []
     for src, lang in (("kernels.hip", "hip"), ("flce_api.cpp", "hip")):
         obj = os.path.join(objdir, src.rsplit(".", 1)[0] + ".o")
         cmd = [cc, "-x", lang, "-c", os.path.join(CSRC, src), "-o", obj] + HIPCC_FLAGS
+        if sanitize:
+            cmd += SANITIZE_FLAGS
         if verbose:
             print(" ".join(cmd))
         _run(cmd)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    if sanitize:
+        cmd += ["-fsanitize=address,undefined", "-shared-libsan"]
     if verbose:
         print(" ".join(cmd))
     _run(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -194,7 +194,12 @@ hipError_t g_setup_err = hipSuccess;
 extern "C" {
 
 const char* flce_status_string(flce_status_t s) {
-  switch (s) {
+  // A C caller may pass any int: read the value through its bytes rather than
+  // as the enumeration type, whose range is only the listed codes.
+  int32_t code;
+  static_assert(sizeof code == sizeof s, "flce_status_t is int-sized");
+  std::memcpy(&code, &s, sizeof code);
+  switch (code) {
     case FLCE_OK: return "FLCE_OK";
     case FLCE_ERR_INVALID_ARGUMENT: return "FLCE_ERR_INVALID_ARGUMENT";
     case FLCE_ERR_UNSUPPORTED: return "FLCE_ERR_UNSUPPORTED";

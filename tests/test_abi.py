@@ -215,3 +215,28 @@ def test_binding_checks_output_buffers():
             op._check_out(dict(good, **{name: bad}), spec, dev)
     with pytest.raises(ValueError, match="on meta"):  # buffers on another device
         op._check_out(good, spec, torch.device("meta"))
+
+
+def test_noalloc_rejects_without_device(lib):
+    # argument and size errors come before any device call
+    big = flce.flce_fwd_bwd_noalloc(4096, 128256, flce.FLCE_BF16, 16, 16, 16, 4, -100,
+                                    flce.FLCE_MEAN, 16, 16, 16, chunk_tokens=2048, stream=0)
+    assert big == flce.FLCE_ERR_UNSUPPORTED
+    assert "static scratch" in flce.last_error()
+    assert flce.flce_fwd_bwd_noalloc(12, 100, flce.FLCE_BF16, 16, 16, 16, 4, -100,
+                                     flce.FLCE_MEAN, 16, 16, 16, stream=0) == \
+        flce.FLCE_ERR_INVALID_ARGUMENT                                    # H % 8 != 0
+    assert flce.flce_fwd_bwd_noalloc(64, 100, flce.FLCE_BF16, 16, None, 16, 4, -100,
+                                     flce.FLCE_MEAN, 16, 16, 16, stream=0) == \
+        flce.FLCE_ERR_INVALID_ARGUMENT                                    # W null
+    assert flce.flce_fwd_bwd_noalloc(64, 100, flce.FLCE_BF16, 16, 16, 16, 4, -100, 3, 16, 16,
+                                     16, stream=0) == flce.FLCE_ERR_INVALID_ARGUMENT
+    assert flce.flce_fwd_bwd_noalloc(64, 100, flce.FLCE_BF16, 24, 16, 16, 4, -100,
+                                     flce.FLCE_MEAN, 16, 16, 16, stream=0) == \
+        flce.FLCE_ERR_INVALID_ARGUMENT                                    # X misaligned
+    assert load_null_cfg(lib) == flce.FLCE_ERR_INVALID_ARGUMENT
+
+
+def load_null_cfg(lib):
+    return lib.flce_fwd_bwd_noalloc(None, 16, 16, 16, 4, -100, flce.FLCE_MEAN, 16, 16, 16, None,
+                                    None, None, None)
