@@ -39,7 +39,7 @@ KERNEL_SOURCES = ("linear_cross_entropy_02_amd/csrc/gemm.h",
 # rocprofv3 runs whose CSV output --summarize-profiles reads (run from the repo root)
 PROFILE_CMDS = {
     "kt": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_kt -o run -- "
-          "python3 bench.py --steps 3 --warmup 1 --cpu-sample 0",
+          "python3 bench.py --steps 3 --warmup 1 --cpu-sample 0 > gpurun_out/prof_kt/bench.json",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o run -- "
              "python3 bench.py --steps 1 --warmup 1 --cpu-sample 0 --no-timing",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o run -- "
@@ -121,10 +121,13 @@ def kernel_source_hash() -> str:
 def short_kernel_name(name: str) -> str:
     import re
     n = name.replace("flce::", "")
-    m = re.match(r"void gemm_nt_kernel<([^,]+), (\d+), (\d+), (\d+), (\w+)<([^>]*)>", n)
+    m = re.match(r"void gemm_nt_kernel<([^,]+), (\d+), (\d+), (\d+), (\w+)<([^>]*)>"
+                 r"(?:, (true|false))?(?:, (true|false))?", n)
     if m:
+        flags = "".join(f",{t}" for t, on in (("Bstored", m.group(7)), ("Ashift", m.group(8)))
+                        if on == "true")
         return (f"gemm<{m.group(1)},{m.group(2)}x{m.group(3)},{m.group(4)}w,"
-                f"{m.group(5)}<{m.group(6).strip()}>>")
+                f"{m.group(5)}<{m.group(6).strip()}>{flags}>")
     return n.split("(")[0].replace("void ", "")
 
 
@@ -142,12 +145,42 @@ def summarize_profiles(d: str):
     lines = ["# Kernel time, fused linear-CE fwd+bwd, llama3-8b head (T=16384, H=4096, V=128256, "
              "bf16, chunk 2048, 4 chunks per dW GEMM)", "",
              "Command (repo root, MI355X):", "", "    " + PROFILE_CMDS["kt"], "",
-             "3 timed + 1 warm-up steps (4 calls of flce_fwd_bwd), per-kernel HIP event timing on.",
+             "1 warm-up, 3 timed and 3 per-kernel-pass steps (7 calls of flce_fwd_bwd); only the "
+             "last 3 carry HIP events around each launch.",
              "", "| kernel | calls | total ms | avg ms | % time |", "|---|---|---|---|---|"]
     for r in stats:
         lines.append(f"| {short_kernel_name(r['Name'])} | {r['Calls']} | "
                      f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['AverageNs']) / 1e6:.4f} | "
                      f"{float(r['Percentage']):.2f} |")
+    # the bench line printed by the same profiled run (its stdout, saved
+    # beside the trace) against the traced average of its roofline kernel
+    try:
+        with open(os.path.join(d, "prof_kt", "bench.json")) as f:
+            line = json.loads(f.read().strip().splitlines()[-1])
+        rf = line["roofline"]
+        tag = {"logits_gemm": "LogitsEpi", "dx_gemm": "StoreEpi<float, false>>",
+               "dw_gemm": "StoreEpi<float, true>>"}[rf["kernel"]]
+        traced = [r for r in stats if tag in short_kernel_name(r["Name"])]
+        avg_all = float(traced[0]["AverageNs"]) * 1e-6
+        # the same launches the bench line timed: those of its per-kernel
+        # pass, the last ones of the trace
+        disp = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                for r in rows("prof_kt", "run_kernel_trace.csv")
+                if tag in short_kernel_name(r["Kernel_Name"])]
+        n_pass = round(line["kernels"][rf["kernel"]]["launches_per_step"] *
+                       min(line["steps"], 3))
+        avg = sum(disp[-n_pass:]) / n_pass * 1e-6
+        frac = rf["flop_per_launch"] / (avg * 1e-3) / 1e12 / rf["peak"]
+        lines += ["", f"Bench line of this run: ms_per_step {line['ms_per_step']}, roofline kernel "
+                      f"{rf['kernel']} at {rf['avg_launch_ms']:.4f} ms per launch (HIP events "
+                      f"around its last {n_pass} launches), frac {rf['frac']}. The trace's "
+                      f"durations of those same {n_pass} launches average {avg:.4f} ms: frac "
+                      f"{frac:.4f} ({100 * (rf['frac'] / frac - 1):+.2f} %). Over all "
+                      f"{len(disp)} launches, warm-up included, the trace averages "
+                      f"{avg_all:.4f} ms."]
+    except (OSError, KeyError, IndexError, ValueError):
+        pass
+    lines += ["", f"Kernel sources hash at measurement: {kernel_source_hash()}"]
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, "kernel_stats_llama3_8b_head.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -184,6 +217,14 @@ def summarize_profiles(d: str):
         wr = write.get(k, 0.0) * 1024 * w_scale
         traffic["kernels"][k] = {"read_bytes": rd, "write_bytes": wr}
         lines.append(f"| {k} | {rd / 1e9:.3f} | {wr / 1e9:.3f} |")
+    calls = {short_kernel_name(r["Name"]): int(r["Calls"]) for r in stats}
+    steps_kt = 3 + 1 + 3  # timed, warm-up and per-kernel steps of the "kt" run
+    per_step = sum((v["read_bytes"] + v["write_bytes"]) * calls.get(k, 0) / steps_kt
+                   for k, v in traffic["kernels"].items() if not k.startswith("__amd"))
+    traffic["per_step_bytes"] = per_step
+    lines += ["", f"Per fwd+bwd step (launches per step from the kernel trace): "
+                  f"{per_step / 1e9:.1f} GB, against {3.42:.2f} GB of algorithmic bytes "
+                  "(X, W, targets, dX, fp32 dW, lse)."]
     lines += ["", f"Kernel sources hash at measurement: {traffic['source_hash']}"]
     with open(os.path.join(PROFILES, "hbm_traffic_llama3_8b_head.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -285,18 +326,18 @@ def measured_traffic(kernel_kind: str, launch):
     return None
 
 
-def per_kernel_rooflines(kernels, T, H, V, dtype, mfma_peak):
+def per_kernel_rooflines(kernels, T, H, V, dtype, mfma_peak, dz_in_dx=False):
     """Achieved rate of each timed kernel of one fwd+bwd step against its own
     bound, from algorithmic work only: 2 T H V flops for each contraction;
     for the bandwidth passes the bytes they must move (the dZ pass reads the
-    exponentials and writes dZ^T, dZ itself being formed inside the dX
-    contraction; a transpose reads and writes its
+    exponentials and writes dZ and dZ^T -- only dZ^T when dZ is formed inside
+    the dX contraction; a transpose reads and writes its
     matrix once; the merge reads the (max, sum, argmax) partials and writes
     alpha, 16 bytes per (token, 128-column tile))."""
     es = 2 if dtype == "bf16" else 4
     nt = -(-V // 128)
     work = {"logits_gemm": ("mfma", 2.0 * T * H * V), "dx_gemm": ("mfma", 2.0 * T * H * V),
-            "dw_gemm": ("mfma", 2.0 * T * H * V), "fixup_dz": ("hbm", 2.0 * T * V * es),
+            "dw_gemm": ("mfma", 2.0 * T * H * V), "fixup_dz": ("hbm", (2.0 if dz_in_dx else 3.0) * T * V * es),
             "transpose_w": ("hbm", 2.0 * V * H * es), "transpose_x": ("hbm", 2.0 * T * H * es),
             "finalize": ("hbm", 16.0 * nt * T)}
     out = {}
@@ -584,7 +625,8 @@ def main():
             roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": 8000.0,
                         "unit": "GB/s", "frac": None, "traffic": None, "source": source}
         if not (fwd_only or n_shards > 1 or Ht > 0):
-            kernel_rooflines = per_kernel_rooflines(kernels, T, H, V, wl.dtype, peak)
+            kernel_rooflines = per_kernel_rooflines(kernels, T, H, V, wl.dtype, peak,
+                                                    args.dz_in_dx)
 
     cpu = None
     if args.cpu_sample > 0 and n_shards == 1 and Ht == 0:
