@@ -63,7 +63,11 @@ def asan_runtime() -> str:
     return r.stdout.strip()
 
 
-def build(verbose: bool = False, sanitize: bool = False, out: str = LIB) -> str:
+def build(verbose: bool = False, sanitize: bool = False, out: str = LIB,
+          defines: tuple = ()) -> str:
+    """Compile csrc/ into `out`.  `defines` ("NAME=VALUE") override the
+    tuning constants the sources leave open to the build (the logits and dW
+    grids' tile-group sizes)."""
     cc = hipcc()
     objdir = os.path.join(PKG, "_build_san" if sanitize else "_build")
     os.makedirs(objdir, exist_ok=True)
@@ -71,6 +75,7 @@ def build(verbose: bool = False, sanitize: bool = False, out: str = LIB) -> str:
     for src, lang in (("kernels.hip", "hip"), ("flce_api.cpp", "hip")):
         obj = os.path.join(objdir, src.rsplit(".", 1)[0] + ".o")
         cmd = [cc, "-x", lang, "-c", os.path.join(CSRC, src), "-o", obj] + HIPCC_FLAGS
+        cmd += [f"-D{d}" for d in defines]
         if sanitize:
             cmd += SANITIZE_FLAGS
         if verbose:
@@ -89,4 +94,6 @@ def build(verbose: bool = False, sanitize: bool = False, out: str = LIB) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    # python -m linear_cross_entropy_02_amd.build [-v] [-DNAME=VALUE ...]
+    print(build(verbose="-v" in sys.argv,
+                defines=tuple(a[2:] for a in sys.argv[1:] if a.startswith("-D"))))

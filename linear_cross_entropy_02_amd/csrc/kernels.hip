@@ -23,6 +23,16 @@
 #include "common.h"
 #include "gemm.h"
 
+// Rows of tiles walked together by the logits and dW grids (see map_tile):
+// 4 for both, measured against 2, 8 and 16 (traffic, clock and time per
+// launch; the build can override them to repeat that measurement).
+#ifndef FLCE_LOGITS_GROUP_M
+#define FLCE_LOGITS_GROUP_M 4
+#endif
+#ifndef FLCE_DW_GROUP_M
+#define FLCE_DW_GROUP_M 4
+#endif
+
 namespace flce {
 
 // ------------------------------------------------------------ epilogues ---
@@ -475,7 +485,7 @@ static hipError_t logits_t(const LogitsArgs& a, hipStream_t s) {
   // Four row tiles per group: the 32 blocks an XCD runs at once form a 4 x 8
   // patch, which keeps both the X chunk and W tiles resident in its L2
   // (walking all 16 row tiles per W tile re-streams X from beyond L2).
-  g.group_m = 4;
+  g.group_m = FLCE_LOGITS_GROUP_M;
   return a.Pq ? logits_run<T, true>(a, g, s) : logits_run<T, false>(a, g, s);
 }
 
@@ -499,7 +509,7 @@ static hipError_t store_t2(TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
     const int ksteps = cdiv(a.K, BK);
     g.k_per_split = cdiv(ksteps, g.splits) * BK;
   }
-  g.group_m = 4;
+  g.group_m = ACC ? FLCE_DW_GROUP_M : 4;
   StoreEpi<TO, ACC> epi;
   epi.out = (TO*)a.out;
   epi.ldo = a.ldo;
