@@ -169,11 +169,23 @@ void plan_gemm(int64_t M, int64_t N, int64_t K, int max_splits, TileCfg* tc, int
   // 128-wide tiles, whose 64 x 64 wave tiles read twice the LDS bytes per
   // MFMA (the dX GEMM of an 8192-token chunk at H = 512, V = 16000, with 62
   // K-steps per split, runs in 0.12 instead of 0.22 ms that way).
+  // The split is the one that finishes soonest in whole rounds of 256
+  // blocks: a tile's time is its K-depth / s, and t x s blocks take
+  // ceil(t s / 256) rounds (96 tiles: 2 ways, 192 blocks, not 3 ways, whose
+  // 288 blocks need two rounds); ties go to fewer splits (less to sum).
   if (t256 >= 64) {
-    const int64_t s = cdiv64(240, t256);
-    if (s <= max_splits && ksteps / s >= 32) {
+    int64_t best = 0;
+    double best_t = 1e30;
+    for (int64_t s = 1; s <= 4 && s <= max_splits && ksteps / s >= 32; ++s) {
+      const double t = (double)cdiv64(t256 * s, 256) / (double)s;
+      if (t < best_t - 1e-9) {
+        best_t = t;
+        best = s;
+      }
+    }
+    if (best >= 1) {  // (unsplit when no split saves a round: still 256-wide)
       *tc = TileCfg::T256;
-      *splits = (int)s;
+      *splits = (int)best;
       return;
     }
   }
