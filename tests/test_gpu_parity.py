@@ -63,6 +63,10 @@ CASES = [
     # three ways in K, unevenly (32 K-steps as 11/11/10 when the first chunk
     # stores dW, 31 as 11/11/9 when the second, ragged one accumulates)
     (workloads.WORKLOADS[4].with_shape(T=4000, H=2560, V=8300, seed=24), 2048),
+    # a 1536-token chunk at H = 4096: 96 dX tiles, split two ways (192 blocks,
+    # one round) rather than three (288 blocks, two rounds); the 64-token
+    # second chunk takes 128-wide tiles split eight ways
+    (workloads.WORKLOADS[4].with_shape(T=1600, H=4096, V=9000, seed=25), 1536),
     # 38 x 16 = 608 dW tiles: the last 96 split two ways
     (workloads.WORKLOADS[4].with_shape(T=4200, H=4096, V=9700, seed=19), 2048),
     # the same split of the dW grid on fp32 operands
