@@ -80,3 +80,44 @@ def test_noalloc_refuses_a_workspace_beyond_the_scratch():
     st = flce.flce_fwd_bwd_noalloc(512, 1000, flce.FLCE_BF16, X[:, :512], None, y, 64, -100,
                                    flce.FLCE_MEAN, out["loss"], out["dX"], out["dW"])
     assert st == flce.FLCE_ERR_INVALID_ARGUMENT
+
+
+def test_noalloc_call_captured_in_a_graph():
+    # what the entry point is for: a capturable call with nothing to allocate.
+    # The first call on the device (eager) looks the scratch up; the graph's
+    # replays, with eager calls on the same scratch between them, must match
+    # a handle's results bit for bit.
+    import torch
+    wl = workloads.WORKLOADS[2].with_shape(T=900, H=256, V=3000, seed=64)
+    ins = [workloads.generate(wl.with_shape(seed=64 + k), keep_f32=False) for k in range(2)]
+    tens = [workloads.to_torch(i, "cuda") for i in ins]
+    op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=256, dw_chunks=2)
+    refs = [op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction) for X, W, y in tens]
+    Xg, Wg, yg = (t.clone() for t in tens[0])
+    out = op.alloc_outputs(wl.T, "cuda")
+    print(f"[gpu-noalloc] graph capture {wl.name}", flush=True)
+    assert noalloc_call(wl, Xg, Wg, yg, out, 256, 2) == flce.FLCE_OK   # eager, first on device
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = noalloc_call(wl, Xg, Wg, yg, out, 256, 2)
+    assert st == flce.FLCE_OK
+    torch.cuda.synchronize()
+    other = op.alloc_outputs(wl.T, "cuda")
+    for r in range(4):
+        k = r % 2
+        for dst, src in zip((Xg, Wg, yg), tens[k]):
+            dst.copy_(src)
+        for t in out.values():
+            t.zero_()
+        g.replay()
+        # eager work on the same scratch between replays, in stream order
+        assert noalloc_call(wl, *tens[1 - k], other, 256, 2) == flce.FLCE_OK
+        torch.cuda.synchronize()
+        for key in KEYS:
+            assert torch.equal(out[key], refs[k][key]), (r, key)
+            assert torch.equal(other[key], refs[1 - k][key]), (r, key)
+    del g
+    op.close()
+    assert torch.cuda.mem_get_info()[0] >= free0 - (64 << 20)   # graph bookkeeping only
