@@ -103,6 +103,10 @@ def parse():
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (3 times), "
                         "to scale HBM byte counters")
+    p.add_argument("--mfma-ceiling", action="store_true",
+                   help="instead of the benchmark: what the bf16 MFMAs sustain with operands in "
+                        "registers (random and zero operands, both instruction shapes, 16 CUs "
+                        "and the whole chip), with the clock sampled during each case")
     p.add_argument("--summarize-profiles", metavar="DIR", default=None,
                    help="turn the rocprofv3 CSV output of the PROFILE_CMDS runs under DIR "
                         "into the summaries in profiles/ (no GPU needed)")
@@ -456,8 +460,68 @@ def calibrate_copy(mib: int):
     print(json.dumps({"calibrate_copy_bytes": n * 4, "repeats": 3}), flush=True)
 
 
+def mfma_ceiling():
+    """Rates of the MFMA probe (libflce_probe.so): for each instruction shape,
+    operand kind and grid, one calibration launch, then launches sized to
+    about 0.25 s each, timed with an event pair on the current stream; the
+    reported rate is the median of 4 such launches after one warm-up, with
+    the clock sampled over them.  One JSON line."""
+    import torch
+
+    from linear_cross_entropy_02_amd import probe
+
+    peak = PEAK_TFLOPS["bf16"]
+    stream = torch.cuda.current_stream()
+    sink = torch.empty(1024 * 256, dtype=torch.float32, device="cuda")
+    results = []
+
+    def timed(shape, blocks, iters, rnd):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        probe.mfma_stream(shape, blocks, iters, rnd, sink, stream)
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b)
+
+    for blocks in (16, 256, 512):
+        for shape in (16, 32):
+            for rnd in (True, False):
+                ms0 = timed(shape, blocks, 2000, rnd)
+                iters = max(2000, int(2000 * 250.0 / max(ms0, 1e-3)))
+                timed(shape, blocks, iters, rnd)
+                sampler = ClockSampler()
+                sampler.start()
+                times = sorted(timed(shape, blocks, iters, rnd) for _ in range(4))
+                clock = sampler.stop()
+                ms = 0.5 * (times[1] + times[2])
+                zero_ok = rnd or bool((sink[:blocks * 256] == 0).all().item())
+                tf = probe.mfma_flops(shape, blocks, iters) / (ms * 1e-3) / 1e12
+                # a CU's share of the peak: 16 CUs can reach 16/256 of it
+                share = peak * min(blocks, 256) / 256.0
+                r = {"instruction": ("v_mfma_f32_16x16x32_bf16" if shape == 16 else
+                                     "v_mfma_f32_32x32x16_bf16"),
+                     "operands": "random" if rnd else "zero", "blocks": blocks,
+                     "waves_per_simd": max(1, blocks // 256), "iters": iters,
+                     "ms_per_launch": round(ms, 3), "tflops": round(tf, 1),
+                     "frac_of_peak": round(tf / peak, 4),
+                     "frac_of_cu_share": round(tf / share, 4),
+                     "gfx_clock_mhz": clock.get("gfx_clock_mhz"),
+                     "socket_power_w": clock.get("socket_power_w"),
+                     "zero_sink_ok": zero_ok}
+                results.append(r)
+                print(f"[mfma-ceiling] {r['instruction']} {r['operands']} blocks={blocks}: "
+                      f"{r['tflops']} TF/s ({100 * r['frac_of_peak']:.1f} % of peak), "
+                      f"clock {r['gfx_clock_mhz']} MHz", file=sys.stderr, flush=True)
+    print(json.dumps({"mfma_ceiling": results, "peak_tflops": peak,
+                      "device": torch.cuda.get_device_name(0)}), flush=True)
+
+
 def main():
     args = parse()
+    if args.mfma_ceiling:
+        mfma_ceiling()
+        return
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles)
         return

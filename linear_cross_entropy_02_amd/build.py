@@ -4,7 +4,8 @@
 
 compiles every source under csrc/ on every call (the CPU-only container
 cross-compiles gfx950 code objects) and writes the shared library next to
-this file.
+this file, together with libflce_probe.so (the MFMA throughput probe, a
+measuring aid that the fused path does not use).
 """
 from __future__ import annotations
 
@@ -17,6 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libflce.so")
+PROBE_LIB = os.path.join(PKG, "libflce_probe.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -93,7 +95,20 @@ def build(verbose: bool = False, sanitize: bool = False, out: str = LIB,
     return out
 
 
+def build_probe(verbose: bool = False, out: str = PROBE_LIB) -> str:
+    """Compile csrc/probe_mfma.hip into its own library `out`."""
+    cc = hipcc()
+    tmp = out + ".tmp"
+    cmd = [cc, "-x", "hip", os.path.join(CSRC, "probe_mfma.hip"), "-shared", "-o", tmp] + HIPCC_FLAGS
+    if verbose:
+        print(" ".join(cmd))
+    _run(cmd)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     # python -m linear_cross_entropy_02_amd.build [-v] [-DNAME=VALUE ...]
     print(build(verbose="-v" in sys.argv,
                 defines=tuple(a[2:] for a in sys.argv[1:] if a.startswith("-D"))))
+    print(build_probe(verbose="-v" in sys.argv))
