@@ -5,8 +5,8 @@
 A step is one flce_fwd_bwd call over one batch: logits GEMM with the
 online-logsumexp epilogue, dZ formation, dX and dW GEMMs, loss -- the whole
 hot path, with inputs resident in HBM.  Prints ONE JSON line with tokens/s
-(value) from K steps timed with nothing but two events around them, the
-GPU clock sampled during those steps, the roofline of the dominant kernel
+(value) from K steps timed with nothing but events between them, the GPU
+clock sampled over a few seconds of the same steps run afterwards, the roofline of the dominant kernel
 (from a separate pass of a few more steps with a HIP event pair around every
 launch on the call's stream) and the float64 CPU oracle timed on a bounded
 token sample of the same workload (cpu_baseline).
@@ -97,6 +97,8 @@ def parse():
                    help="time flce_forward (per-token log-probs and loss, no gradients)")
     p.add_argument("--no-timing", action="store_true",
                    help="skip the per-kernel pass after the timed steps (no roofline)")
+    p.add_argument("--clock-seconds", type=float, default=2.0,
+                   help="length of the clock pass after the timed steps (0: none)")
     p.add_argument("--kernel-steps", type=int, default=5,
                    help="steps of the per-kernel pass (HIP events around every launch), run "
                         "after the timed steps; at most --steps")
@@ -361,7 +363,7 @@ def per_kernel_rooflines(kernels, T, H, V, dtype, mfma_peak, dz_in_dx=False):
 
 class ClockSampler:
     """GFX clock and socket power of device 0 sampled every 20 ms from a side
-    thread (amdsmi GPU metrics) while the timed steps run.  The firmware
+    thread (amdsmi GPU metrics) while steps run.  The firmware
     refreshes that table more slowly than it is read, and its first values
     can predate the load, so the summary is the median (and range) of the
     samples taken in the second half of the window; None without amdsmi."""
@@ -431,7 +433,7 @@ class ClockSampler:
                "gfx_clock_mhz_max": clk[-1], "samples": len(clk),
                "window_s": round(span / 2, 3), "nominal_peak_clock_mhz": 2400,
                "source": "amdsmi gpu metrics current_gfxclks (mean of the XCDs), median of the "
-                         "samples in the second half of the timed steps"}
+                         "samples in the second half of a window of back-to-back steps"}
         if pw:
             out["socket_power_w"] = pw[len(pw) // 2]
         return out
@@ -615,8 +617,6 @@ def main():
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     free_before = torch.cuda.mem_get_info()[0]
-    sampler = ClockSampler()
-    sampler.start()
     start.record(stream)
     marks[0].record(stream)
     for i in range(args.steps):
@@ -624,7 +624,6 @@ def main():
         marks[i + 1].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
-    clock = sampler.stop()
     free_after = torch.cuda.mem_get_info()[0]
     ms = start.elapsed_time(stop) / args.steps
     per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
@@ -633,6 +632,23 @@ def main():
     loss = float(out["loss"].item())
     assert np.isfinite(loss), loss
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # Clock pass, after and apart from the timed region: the same step run
+    # back to back for a few seconds while the clock is sampled (the metrics
+    # table refreshes too slowly to be read over the short timed region).
+    clock = None
+    if args.clock_seconds > 0 and not args.no_timing:
+        sampler = ClockSampler()
+        sampler.start()
+        t_end = time.time() + args.clock_seconds
+        n_clock = 0
+        while time.time() < t_end:
+            for _ in range(4):
+                step()
+            n_clock += 4
+            torch.cuda.synchronize()
+        clock = sampler.stop()
+        clock["steps"] = n_clock
 
     T, H, V = wl.T, wl.H, wl.V
     # fwd+bwd: three contractions of 2 T H V flops; forward only: the logits;
