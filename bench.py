@@ -105,6 +105,10 @@ def parse():
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (3 times), "
                         "to scale HBM byte counters")
+    p.add_argument("--inputs", choices=("random", "pow2", "zero"), default="random",
+                   help="operand data: the workload's random X and W (default); the same with "
+                        "every bf16 mantissa cleared (sign and exponent kept); or all zero. "
+                        "Same work on other bits, to see how the MFMAs' power sets the clock")
     p.add_argument("--mfma-ceiling", action="store_true",
                    help="instead of the benchmark: what the bf16 MFMAs sustain with operands in "
                         "registers (random and zero operands, both instruction shapes, 16 CUs "
@@ -551,6 +555,15 @@ def main():
     t_gen = time.time()
     inp = workloads.generate(wl, keep_f32=args.cpu_sample > 0)
     X, W, y = workloads.to_torch(inp, "cuda")
+    if args.inputs != "random":
+        for t in (X, W):
+            if args.inputs == "zero":
+                t.zero_()
+            elif t.dtype == torch.bfloat16:
+                t.view(torch.int16).bitwise_and_(-128)    # 0xFF80: sign and exponent
+            else:
+                t.view(torch.int32).bitwise_and_(-8388608)  # 0xFF800000
+        args.cpu_sample = 0  # the oracle leg times the random inputs only
     print(f"[bench] inputs for {wl.name} ready in {time.time() - t_gen:.1f}s", file=sys.stderr,
           flush=True)
     n_shards = max(1, args.vocab_shards)
@@ -728,7 +741,7 @@ def main():
                    METRIC_FWD if fwd_only else METRIC), "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
-        "data": "synthetic",
+        "data": "synthetic" if args.inputs == "random" else f"synthetic ({args.inputs} X, W)",
         "config": {"workload": wl.name, "T": T, "H": H, "V": V, "chunk_tokens": op.chunk_tokens,
                    "dw_chunks": op.dw_chunks, "weight_copy": wcopy, "dz_in_dx": args.dz_in_dx,
                    "vocab_shards": n_shards,
