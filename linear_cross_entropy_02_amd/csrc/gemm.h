@@ -164,6 +164,49 @@ template <> __device__ __forceinline__ f4 mma16_after_valu<float>(uint4 a, uint4
 }
 // Orders every accumulator after the preceding asm statements (the MFMA
 // drain): each empty asm claims to modify one accumulator.
+// Order of the FM x FN MFMAs of a substep (fragment row i = A fragment, the
+// instruction's second source; column j = B fragment, its first source),
+// chosen by the epilogue type (Epi::kOrder) for the contraction it serves:
+//   0: row by row, j fastest;
+//   1: row by row with the odd rows backwards, so that consecutive MFMAs
+//      always share an operand (the A fragment within a row, the B fragment
+//      at a row change);
+//   2: column by column with the odd columns backwards (the B fragment
+//      stays within a column).
+// Every accumulator still sees the same K order, so results do not change.
+// The order sets which operand's bits toggle between issues, and the matrix
+// units' power -- and so the clock the chip sustains at its power limit --
+// depends on that: keeping the operand with O(1) values (whose exponents
+// straddle 1.0, where all eight exponent bits flip) fixed measured faster.
+template <int FM, int FN, int ORDER>
+__device__ __forceinline__ constexpr int mma_row(int q) {
+  if constexpr (ORDER == 2) {
+    const int c = q / FM, r = q % FM;
+    return (c & 1) ? FM - 1 - r : r;
+  } else {
+    return q / FN;
+  }
+}
+template <int FM, int FN, int ORDER>
+__device__ __forceinline__ constexpr int mma_col(int q) {
+  if constexpr (ORDER == 2) {
+    return q / FM;
+  } else {
+    const int r = q / FN, c = q % FN;
+    return (ORDER == 1 && (r & 1)) ? FN - 1 - c : c;
+  }
+}
+// n-th fragment read of a substep: r < FM is A fragment r, else B fragment
+// r - FM.  The first MFMAs of the order are served first: one A fragment and
+// every B fragment (orders 0, 1), or one B fragment and every A fragment (2).
+template <int FM, int FN, int ORDER>
+__device__ __forceinline__ constexpr int read_slot(int n) {
+  if constexpr (ORDER == 2)
+    return n == 0 ? FM : n <= FM ? n - 1 : n;
+  else
+    return (n + FM) % (FM + FN);
+}
+
 template <int FM, int FN>
 __device__ __forceinline__ void drain_fence(f4 (&acc)[FM][FN]) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -471,6 +514,11 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
       fb[r - FM] = read_b_tr(bb, wn * G::WN + 16 * (r - FM), s);
   };
 
+  // the shifted-A kernels key their shifts to the first use of each A
+  // fragment in row order (and the fp32 ones mix compiler-visible and asm
+  // MFMAs): they keep order 0
+  constexpr int ORD = AS ? 0 : Epi::kOrder;
+  static_assert(ORD >= 0 && ORD <= 2, "MFMA order");
   constexpr int NR = FM + FN;  // fragment reads per substep
   constexpr int NM = FM * FN;  // MFMAs per substep
   constexpr int NDMA = A_INS + B_INS;
@@ -527,7 +575,7 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
       for (int i = 0; i < FM; ++i) psh[i] = shift_word<T>(shw[i >> 2], i & 3);
     }
 #pragma unroll
-    for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r, fa0, fb0);
+    for (int n = 0; n < NR; ++n) read_one(0, 0, 0, ORD == 2 ? read_slot<FM, FN, ORD>(n) : n, fa0, fb0);
     // stage kt sits in A buffer kt % 3 and B buffer kt % 2
     int a_cur = 0, a_nxt = 1, a_dma = 2;
     for (int kt = 0; kt < nk; ++kt) {
@@ -542,10 +590,11 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
       }
 #pragma unroll
       for (int q = 0; q < NM; ++q) {
+        const int i = mma_row<FM, FN, ORD>(q), j = mma_col<FM, FN, ORD>(q);
         if (AS && q % FN == 0)
-          acc[q / FN][q % FN] = mma16_after_valu<T>(fb0[q % FN], fa0[q / FN], acc[q / FN][q % FN]);
+          acc[i][j] = mma16_after_valu<T>(fb0[j], fa0[i], acc[i][j]);
         else
-          acc[q / FN][q % FN] = mma16<T>(fb0[q % FN], fa0[q / FN], acc[q / FN][q % FN]);
+          acc[i][j] = mma16<T>(fb0[j], fa0[i], acc[i][j]);
         if constexpr (AS)  // the next fragment, kShiftLead MFMAs before its first use
           if (q % FN == FN - kShiftLead && q / FN + 1 < FM)
             shift_frag<T>(fa0[q / FN + 1], psh[q / FN + 1]);
@@ -554,7 +603,7 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
           if (k % 3 == 2 && k / 3 < A_INS)
             issue_a(a_dma, k2, k / 3);
           else
-            read_one(a_cur, b_cur, 1, (k - min((k + 1) / 3, A_INS) + FM) % NR, fa1, fb1);
+            read_one(a_cur, b_cur, 1, read_slot<FM, FN, ORD>(k - min((k + 1) / 3, A_INS)), fa1, fb1);
         }
       }
       __builtin_amdgcn_s_waitcnt(kWaitMid);  // stage kt + 1 landed, own reads done
@@ -569,10 +618,11 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
       }
 #pragma unroll
       for (int q = 0; q < NM; ++q) {
+        const int i = mma_row<FM, FN, ORD>(q), j = mma_col<FM, FN, ORD>(q);
         if (AS && q % FN == 0)
-          acc[q / FN][q % FN] = mma16_after_valu<T>(fb1[q % FN], fa1[q / FN], acc[q / FN][q % FN]);
+          acc[i][j] = mma16_after_valu<T>(fb1[j], fa1[i], acc[i][j]);
         else
-          acc[q / FN][q % FN] = mma16<T>(fb1[q % FN], fa1[q / FN], acc[q / FN][q % FN]);
+          acc[i][j] = mma16<T>(fb1[j], fa1[i], acc[i][j]);
         if constexpr (AS)
           if (q % FN == FN - kShiftLead && q / FN + 1 < FM)
             shift_frag<T>(fa1[q / FN + 1], psh[q / FN + 1]);
@@ -581,7 +631,7 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
           if (k % 3 == 2 && k / 3 < B_INS)
             issue_b(b_cur, k2, k / 3);
           else
-            read_one(a_nxt, b_nxt, 0, (k - min((k + 1) / 3, B_INS) + FM) % NR, fa0, fb0);
+            read_one(a_nxt, b_nxt, 0, read_slot<FM, FN, ORD>(k - min((k + 1) / 3, B_INS)), fa0, fb0);
         }
       }
       const int t = a_cur;

@@ -65,6 +65,10 @@ __device__ __forceinline__ f4 load4(const bf16* p) {
 // exp(z_T / tau - m_T) of the same columns.
 template <typename T, bool CROSS = false>
 struct LogitsEpi {
+  // MFMA issue order (gemm.h): X is the A operand here and W the B operand;
+  // X's O(1) values toggle more exponent bits than W's small ones, so the
+  // A fragment stays put within a fragment row
+  static constexpr int kOrder = 1;
   T* P;
   int64_t ldp;
   float inv_temp;
@@ -223,6 +227,10 @@ struct LogitsEpi {
 template <typename TO, bool ACC>
 struct StoreEpi {
   static_assert(!ACC || std::is_same<TO, float>::value, "accumulation is fp32 only");
+  // MFMA issue order (gemm.h).  ACC: dW = dZ^T X, whose B operand is X: the
+  // B fragment stays put within a fragment column.  Otherwise dX = dZ W (or
+  // its split-K partials): the A fragment (dZ) stays put within a row.
+  static constexpr int kOrder = ACC ? 2 : 1;
   TO* out;
   int64_t ldo;
   int M, N;
@@ -278,6 +286,7 @@ struct StoreEpi {
 // input dtype, which dX and W share.
 template <typename TO>
 struct DxEpi {
+  static constexpr int kOrder = 0;  // shifted-A kernels keep the plain order
   TO* out;
   int64_t ldo;
   int M, N;
@@ -320,6 +329,7 @@ struct DxEpi {
 // the matrix edge hold zeros (their operand rows read as zero).
 template <int BM, int BN>
 struct TilePartialEpi {
+  static constexpr int kOrder = 2;  // dW's tail tiles: as StoreEpi<float, true>
   float* part;
   int tile_count;
 
