@@ -39,7 +39,7 @@ KERNEL_SOURCES = ("linear_cross_entropy_02_amd/csrc/gemm.h",
 # rocprofv3 runs whose CSV output --summarize-profiles reads (run from the repo root)
 PROFILE_CMDS = {
     "kt": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_kt -o run -- "
-          "python3 bench.py --steps 3 --warmup 1 --cpu-sample 0 > gpurun_out/prof_kt/bench.json",
+          "python3 bench.py --steps 3 --warmup 1 --cpu-sample 0 --clock-seconds 0 > gpurun_out/prof_kt/bench.json",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o run -- "
              "python3 bench.py --steps 1 --warmup 1 --cpu-sample 0 --no-timing",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o run -- "
