@@ -327,12 +327,14 @@ def measured_traffic(kernel_kind: str, launch):
         return None
     if t.get("source_hash") != kernel_source_hash() or t.get("launch") != list(launch):
         return None
-    # logits: LogitsEpi; dX: stores the input dtype; dW: the accumulating fp32 store
-    tag = {"logits_gemm": "LogitsEpi", "dx_gemm": "StoreEpi<bf16, false>",
-           "dw_gemm": "StoreEpi<float, true>"}.get(kernel_kind)
-    for k, v in t["kernels"].items():
-        if tag and tag in k:
-            return round(v["read_bytes"] + v["write_bytes"])
+    # logits: LogitsEpi; dX: fp32 split-K partials, else a direct store of the
+    # input dtype; dW: the accumulating fp32 store
+    tags = {"logits_gemm": ("LogitsEpi",), "dx_gemm": ("StoreEpi<float, false>", "StoreEpi<bf16, false>"),
+            "dw_gemm": ("StoreEpi<float, true>",)}.get(kernel_kind, ())
+    for tag in tags:
+        for k, v in t["kernels"].items():
+            if tag in k:
+                return round(v["read_bytes"] + v["write_bytes"])
     return None
 
 
