@@ -3,6 +3,8 @@
 Sizes here let the full oracle finish in seconds while spanning several
 GEMM tiles, several token chunks and ragged tails in every dimension.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -341,3 +343,64 @@ def test_non_finite_inputs_poison_like_the_oracle():
         if fin.any():
             assert np.abs(lse[fin] - ref["lse"][fin]).max() <= 1e-3, name
         assert np.isnan(ref["loss"]), name
+
+
+# Degenerate heads: one token; every token ignored (the mean over zero
+# tokens is defined as 0, and so are its gradients); one valid token among
+# ignored ones; a sum over a batch with a single valid token
+DEGENERATE_CASES = [
+    dataclasses.replace(workloads.WORKLOADS[2].with_shape(T=1, H=64, V=1000, seed=51),
+                        ignore_frac=0.0),
+    dataclasses.replace(workloads.WORKLOADS[2].with_shape(T=300, H=64, V=700, seed=52),
+                        ignore_frac=1.0),
+    dataclasses.replace(workloads.WORKLOADS[2].with_shape(T=300, H=64, V=700, seed=53),
+                        ignore_frac=1.0, reduction="sum"),
+    dataclasses.replace(workloads.WORKLOADS[1].with_shape(T=1, H=16, V=40, seed=54),
+                        ignore_frac=0.0),
+]
+
+
+@pytest.mark.parametrize("wl", DEGENERATE_CASES,
+                         ids=[f"{c.name}-T{c.T}-ign{c.ignore_frac}-{c.reduction}"
+                              for c in DEGENERATE_CASES])
+def test_degenerate_heads(wl):
+    inp, out = run(wl, 256)
+    ref = oracle(inp, wl)
+    check_full(out, ref, inp, wl)
+    if wl.ignore_frac == 1.0:
+        assert ref["n_valid"] == 0
+        assert float(out["loss"].item()) == 0.0
+        assert not to_np(out["dX"]).any() and not to_np(out["dW"]).any()
+
+
+def test_single_valid_token_among_ignored():
+    wl = dataclasses.replace(workloads.WORKLOADS[2].with_shape(T=500, H=128, V=3000, seed=55),
+                             ignore_frac=0.0)
+    inp = workloads.generate(wl)
+    inp.y[:] = wl.ignore_index
+    inp.y[317] = 1234
+    inp, out = run(wl, 256, inp=inp)
+    ref = oracle(inp, wl)
+    assert ref["n_valid"] == 1
+    check_full(out, ref, inp, wl)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_one_word_vocabulary(dtype):
+    # V = 1: the softmax is 1, so loss and gradients vanish up to the rounding
+    # of lse - z; lse equals the single logit and the argmax is 0
+    base = workloads.WORKLOADS[2] if dtype == "bf16" else workloads.WORKLOADS[1]
+    wl = dataclasses.replace(base.with_shape(T=700, H=64, V=1, seed=56), ignore_frac=0.1)
+    inp, out = run(wl, 256)
+    ref = oracle(inp, wl)
+    z = inp.X.astype(np.float64) @ inp.W.astype(np.float64).T
+    lse = to_np(out["lse"])
+    assert np.abs(lse - z[:, 0]).max() <= 1e-5 * max(1.0, np.abs(z).max())
+    assert np.all(to_np(out["argmax"]) == 0)
+    assert int(out["n_valid"].item()) == ref["n_valid"]
+    assert abs(float(out["loss"].item())) <= 1e-6
+    # |dX_t| = s |p - 1| |W_0| with |p - 1| at the rounding of exp(z - lse)
+    s = 1.0 / ref["n_valid"]
+    wn = float(np.linalg.norm(inp.W.astype(np.float64)))
+    assert np.linalg.norm(to_np(out["dX"]), axis=1).max() <= 1e-5 * s * wn
+    assert np.linalg.norm(to_np(out["dW"])) <= 1e-5 * np.linalg.norm(inp.X.astype(np.float64))
