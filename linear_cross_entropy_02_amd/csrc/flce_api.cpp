@@ -47,6 +47,12 @@ const char* kKindNames[K_NUM] = {"count_valid",   "transpose_w", "transpose_x", 
 
 constexpr int64_t kDefaultChunk = 4096;
 constexpr int kMaxDwChunks = 8;
+// With dZ formed inside the dX contraction, the tile references of the
+// stored exponentials are multiples of 2^32: the tiles of a row then mostly
+// share one (its logits would have to straddle a multiple of 32 log2(e)
+// nats), and the dZ pass rewrites only the others.  Values more than ~65
+// nats below their tile's max flush to zero, where their softmax is < e^-65.
+constexpr float kRowRefQuantum = 32.f;
 
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -597,6 +603,7 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       la.pc = h->pc;
     } else if (h->dz_in_dx) {
       la.ptgt = h->ptgt;
+      la.kq_quantum = kRowRefQuantum;
     }
     FLCE_LAUNCH(K_LOGITS, launch_logits(dt, la, s));
 
@@ -626,12 +633,16 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       fa.alpha_mul = soft->inv_temp;
       fa.no_target = true;
     } else if (h->dz_in_dx) {
-      // dZ is formed inside the dX contraction (row scale, tile shifts,
-      // target correction); the dZ pass below writes only dZ^T
+      // dZ is formed inside the dX contraction (row scale, target
+      // correction) from the stored exponentials, once the dZ pass below has
+      // brought each row's to one reference; that pass writes only dZ^T
       fa.beta = h->beta;
       fa.shift = h->shift;
       fa.corr = h->corr;
       fa.ptgt = h->ptgt;
+      fa.kq_quantum = kRowRefQuantum;
+      fa.rescaled_rows = true;
+      fa.round_bf16 = dt == Dt::BF16;
     }
     fa.backward = true;
     fa.loss_part = h->loss_part;
@@ -660,12 +671,13 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       xa.alpha_q = h->pmq;
     }
     xa.write_rows = soft != nullptr || !h->dz_in_dx;
+    if (!soft && h->dz_in_dx) xa.rescale_shift = h->shift;
     FLCE_LAUNCH(K_FIXUP, launch_fixup(dt, xa, s));
 
     // dX_c = dZ W   (M = Cc, N = H, K = vocabulary); without soft targets
     // A holds the exponentials and dZ is formed in the contraction
     DxFuse fz{};
-    fz.shift = h->shift;
+    fz.shift = nullptr;  // the rows of P share one reference: no shifts
     fz.shift_ld = C;
     fz.shift_tiles = (int)nt;
     fz.beta = h->beta;

@@ -85,6 +85,7 @@ struct LogitsEpi {
   int M, V;
   bool store_p;  // false: partials and target logit only (forward-only calls)
   float* ptgt;   // nullable: the stored exponential at the target's column
+  float kq_quantum;  // the tile reference is a multiple of this power of two
 
   template <int FM, int FN>
   __device__ __forceinline__ void init(f4 (&acc)[FM][FN], const EpiCoord&) const {
@@ -162,12 +163,14 @@ struct LogitsEpi {
         cross += shfl_xor_f(cross, 16);
         cross += shfl_xor_f(cross, 32);
       }
-      // exponentials relative to 2^kq, kq = ceil(tile max log2(e)): a whole
-      // power of two, so that the merge turns them into probabilities with a
-      // per-row scale and an exact power-of-two factor per tile
+      // exponentials relative to 2^kq, kq = q ceil(tile max log2(e) / q): a
+      // whole power of two, so that the merge turns them into probabilities
+      // with a per-row scale and an exact power-of-two factor per tile (q a
+      // power of two: the division is exact)
       const float kl = kLog2e * inv_temp;
       const float pmv = mx * inv_temp;
-      const float kq = (mx == kNegInf) ? 0.f : __builtin_ceilf(pmv * kLog2e);
+      const float kq =
+          (mx == kNegInf) ? 0.f : __builtin_ceilf(pmv * kLog2e / kq_quantum) * kq_quantum;
       float sum = 0.f;
 #pragma unroll
       for (int j = 0; j < FN; ++j)
@@ -286,7 +289,9 @@ struct StoreEpi {
 // input dtype, which dX and W share.
 template <typename TO>
 struct DxEpi {
-  static constexpr int kOrder = 0;  // shifted-A kernels keep the plain order
+  // MFMA issue order (gemm.h; the shifted-A kernels keep order 0): as the
+  // other dX kernels, the A fragment (the exponentials) stays put in a row
+  static constexpr int kOrder = 1;
   TO* out;
   int64_t ldo;
   int M, N;
@@ -408,14 +413,18 @@ static hipError_t set_lds_attr() {
 }
 
 // The dX instantiations with dZ formed inside the contraction, for one B
-// layout: direct output or raw split-K partials, 256- or 128-wide tiles.
+// layout: direct output or raw split-K partials, 256- or 128-wide tiles,
+// A fragments shifted in registers or read as they are (the raw partials of
+// the latter are the plain dX kernels, set up with them).
 template <typename T, bool BT>
 static hipError_t setup_fused_dx() {
   hipError_t e;
   if ((e = set_lds_attr<T, 256, 256, 4, DxEpi<T>, BT, true>()) != hipSuccess) return e;
   if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<float, false>, BT, true>()) != hipSuccess) return e;
   if ((e = set_lds_attr<T, 128, 128, 4, DxEpi<T>, BT, true>()) != hipSuccess) return e;
-  return set_lds_attr<T, 128, 128, 4, StoreEpi<float, false>, BT, true>();
+  if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<float, false>, BT, true>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<T, 256, 256, 4, DxEpi<T>, BT, false>()) != hipSuccess) return e;
+  return set_lds_attr<T, 128, 128, 4, DxEpi<T>, BT, false>();
 }
 
 template <typename T>
@@ -464,6 +473,7 @@ static hipError_t logits_run(const LogitsArgs& a, const GemmShape& g, hipStream_
   epi.P = (T*)a.P;
   epi.ldp = a.ldp;
   epi.inv_temp = a.inv_temp;
+  epi.kq_quantum = a.kq_quantum;
   epi.Pq = (const T*)a.Pq;
   epi.pc = a.pc;
   epi.pm = a.pm;
@@ -503,6 +513,49 @@ hipError_t launch_logits(Dt dt, const LogitsArgs& a, hipStream_t s) {
   return dt == Dt::BF16 ? logits_t<bf16>(a, s) : logits_t<float>(a, s);
 }
 
+// The dX contraction with dZ formed inside it (GemmOutArgs::fuse): AS =
+// true scales the A fragments by their tile's 2^-s in registers; AS = false
+// reads A as it is (its rows already share one reference).  With splits the
+// raw partial planes go out and splitk_reduce finishes them; else DxEpi
+// finishes each row (row scale, target correction).
+template <typename T, typename TO, bool AS>
+static hipError_t fused_dx(TileCfg tc, const GemmOutArgs& a, const GemmShape& g,
+                           const StoreEpi<TO, false>& epi, hipStream_t s) {
+  if (g.splits > 1) {
+    if constexpr (std::is_same<TO, float>::value) {
+      if (a.b_stored) {
+        if constexpr (std::is_same<T, bf16>::value) {
+          if (tc != TileCfg::T256)
+            return run_gemm<T, 128, 128, 4, StoreEpi<float, false>, true, AS>(g, epi, s);
+          return run_gemm<T, 256, 256, 4, StoreEpi<float, false>, true, AS>(g, epi, s);
+        }
+        return hipErrorInvalidValue;
+      }
+      if (tc != TileCfg::T256)
+        return run_gemm<T, 128, 128, 4, StoreEpi<float, false>, false, AS>(g, epi, s);
+      return run_gemm<T, 256, 256, 4, StoreEpi<float, false>, false, AS>(g, epi, s);
+    }
+    return hipErrorInvalidValue;
+  } else if constexpr (std::is_same<TO, T>::value) {
+    DxEpi<T> de;
+    de.out = (T*)a.out;
+    de.ldo = a.ldo;
+    de.M = a.M;
+    de.N = a.N;
+    de.f = *a.fuse;
+    if (a.b_stored) {
+      if constexpr (std::is_same<T, bf16>::value) {
+        if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4, DxEpi<T>, true, AS>(g, de, s);
+        return run_gemm<T, 256, 256, 4, DxEpi<T>, true, AS>(g, de, s);
+      }
+      return hipErrorInvalidValue;
+    }
+    if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4, DxEpi<T>, false, AS>(g, de, s);
+    return run_gemm<T, 256, 256, 4, DxEpi<T>, false, AS>(g, de, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename T, typename TO, bool ACC>
 static hipError_t store_t2(TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
   GemmShape g{};
@@ -528,44 +581,14 @@ static hipError_t store_t2(TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
   epi.split_stride = a.split_stride;
   epi.accumulate = ACC && a.accumulate;
   if (a.fuse) {
-    // dZ formed inside the contraction: shifted A fragments; the output
-    // (split-K: the partial planes, summed and finished by splitk_reduce)
+    // dZ formed inside the contraction; split-K: the partial planes, summed
+    // and finished by splitk_reduce
     if constexpr (!ACC) {
       g.ash = a.fuse->shift;
       g.ash_ld = a.fuse->shift_ld;
       g.ash_tiles = a.fuse->shift_tiles;
-      if (g.splits > 1) {
-        if constexpr (std::is_same<TO, float>::value) {
-          if (a.b_stored) {
-            if constexpr (std::is_same<T, bf16>::value) {
-              if (tc != TileCfg::T256)
-                return run_gemm<T, 128, 128, 4, StoreEpi<float, false>, true, true>(g, epi, s);
-              return run_gemm<T, 256, 256, 4, StoreEpi<float, false>, true, true>(g, epi, s);
-            }
-            return hipErrorInvalidValue;
-          }
-          if (tc != TileCfg::T256)
-            return run_gemm<T, 128, 128, 4, StoreEpi<float, false>, false, true>(g, epi, s);
-          return run_gemm<T, 256, 256, 4, StoreEpi<float, false>, false, true>(g, epi, s);
-        }
-        return hipErrorInvalidValue;
-      } else if constexpr (std::is_same<TO, T>::value) {
-        DxEpi<T> de;
-        de.out = (T*)a.out;
-        de.ldo = a.ldo;
-        de.M = a.M;
-        de.N = a.N;
-        de.f = *a.fuse;
-        if (a.b_stored) {
-          if constexpr (std::is_same<T, bf16>::value) {
-            if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4, DxEpi<T>, true, true>(g, de, s);
-            return run_gemm<T, 256, 256, 4, DxEpi<T>, true, true>(g, de, s);
-          }
-          return hipErrorInvalidValue;
-        }
-        if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4, DxEpi<T>, false, true>(g, de, s);
-        return run_gemm<T, 256, 256, 4, DxEpi<T>, false, true>(g, de, s);
-      }
+      if (a.fuse->shift) return fused_dx<T, TO, true>(tc, a, g, epi, s);
+      return fused_dx<T, TO, false>(tc, a, g, epi, s);
     }
     return hipErrorInvalidValue;
   }
@@ -838,6 +861,12 @@ hipError_t launch_transpose(Dt dt, const void* src, int rows, int cols, int64_t 
 // 8 x 128 for long rows (a 128256-word vocabulary has 1002 partial tiles),
 // 32 x 32 for rows of at most 256 tiles, which otherwise leave most slices
 // idle and spend the block's time in three 128-slice tree reductions.
+// Byte of row `row` within a tile's row of shift bytes: the 16 x 8 order in
+// which a 128-row wave tile of the shifted-A contraction loads them.
+__device__ __forceinline__ int64_t shift_slot(int row) {
+  return (row & ~127) + 8 * (row & 15) + ((row >> 4) & 7);
+}
+
 template <int ROWS>
 __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   constexpr int kFinRows = ROWS, kFinSlices = 1024 / ROWS, kFinCache = 8;
@@ -913,9 +942,12 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   }
   __syncthreads();
   // The stored exponentials of tile j are relative to 2^k_j, k_j =
-  // ceil(m_j log2 e) (0 for an all -inf tile), exactly as the logits
-  // epilogue computed it; K = ceil(m log2 e) is the largest k_j.
-  auto kq_of = [](float mj) { return mj == kNegInf ? 0.f : __builtin_ceilf(mj * kLog2e); };
+  // q ceil(m_j log2 e / q) (0 for an all -inf tile), exactly as the logits
+  // epilogue computed it; K = q ceil(m log2 e / q) is the largest k_j.
+  const float kqq = a.kq_quantum;
+  auto kq_of = [kqq](float mj) {
+    return mj == kNegInf ? 0.f : __builtin_ceilf(mj * kLog2e / kqq) * kqq;
+  };
   // pass 2: sum = sum_j s_j 2^(k_j - K) (exact power-of-two rescaling)
   // (soft targets: also sum_j alpha_q_j pc_j = sum_v q_v z_v / tau)
   m = s_m[rl];
@@ -977,7 +1009,15 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
         if (owned) {
           const int jy = (int)(yl / kPartialWidth);
           const float ky = kq_of(a.pm[(int64_t)jy * a.ldr + row]);
-          c = dzt - beta * __builtin_amdgcn_exp2f(ky - K) * a.ptgt[row];
+          if (a.rescaled_rows) {
+            // what the dZ pass leaves at the target's column: the stored
+            // value times 2^(k_y - K), rounded to the input dtype
+            float pv = __builtin_ldexpf(a.ptgt[row], (int)(ky - K));
+            if (a.round_bf16) pv = Elem<bf16>::to_f32(Elem<bf16>::from_f32(pv));
+            c = dzt - beta * pv;
+          } else {
+            c = dzt - beta * __builtin_amdgcn_exp2f(ky - K) * a.ptgt[row];
+          }
         }
         a.corr[row] = c;
       }
@@ -1001,7 +1041,7 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   // (for the dX contraction) the shift K - k_j as a byte
   if (live && a.backward) {
     const float Kr = s_k[rl], beta = s_beta[rl], sc = s_sc[rl];
-    const int64_t perm = (row & ~127) + 8 * (row & 15) + ((row >> 4) & 7);
+    const int64_t perm = shift_slot(row);
     auto put = [&](int j, float mj, float sj) {
       const int64_t o = (int64_t)j * a.ldr + row;
       const float kj = kq_of(mj);
@@ -1051,6 +1091,9 @@ __global__ void __launch_bounds__(256) fixup_kernel(FixupArgs a) {
   const int tid = threadIdx.x;
   T* P = (T*)a.P;
   T* Pt = (T*)a.Pt;
+  // rescaling: stored vectors and shift bytes kept for stores after the loop
+  uint4 keep[PER];
+  int kshift[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
     const int q = tid + 256 * p;
@@ -1059,10 +1102,16 @@ __global__ void __launch_bounds__(256) fixup_kernel(FixupArgs a) {
     float d[EPV];
 #pragma unroll
     for (int k = 0; k < EPV; ++k) d[k] = 0.f;
+    keep[p] = make_uint4(0u, 0u, 0u, 0u);
+    kshift[p] = 0;
     if (t < a.M) {
       T* src = P + (int64_t)t * a.ldp + v;
       uint4 pv = *(const uint4*)src;
       const T* pe = (const T*)&pv;
+      if (a.rescale_shift && v < a.V) {
+        keep[p] = pv;
+        kshift[p] = a.rescale_shift[(int64_t)(v / kPartialWidth) * a.ldr + shift_slot(t)];
+      }
       const float al = (v < a.V) ? a.alpha[(int64_t)(v / kPartialWidth) * a.ldr + t] : 0.f;
       const int64_t yt = a.y[t];
       const int64_t yl = yt - a.y_shift;  // target's column among these V
@@ -1089,6 +1138,22 @@ __global__ void __launch_bounds__(256) fixup_kernel(FixupArgs a) {
 #pragma unroll
       for (int k = 0; k < EPV; ++k) tile[r][cv * EPV + k] = Elem<T>::from_f32(0.f);
     }
+  }
+  if (a.rescale_shift) {
+    // segments whose tile reference lies below the row's: store P 2^-s
+#pragma unroll
+    for (int p = 0; p < PER; ++p)
+      if (kshift[p] != 0) {
+        const int q = tid + 256 * p;
+        const int r = q / VPR, cv = q % VPR;
+        uint4 rv;
+        const T* pe = (const T*)&keep[p];
+        T* re = (T*)&rv;
+#pragma unroll
+        for (int k = 0; k < EPV; ++k)
+          re[k] = Elem<T>::from_f32(__builtin_ldexpf(Elem<T>::to_f32(pe[k]), -kshift[p]));
+        *(uint4*)(P + (int64_t)(t0 + r) * a.ldp + v0 + cv * EPV) = rv;
+      }
   }
   __syncthreads();
 #pragma unroll
@@ -1120,42 +1185,71 @@ __global__ void __launch_bounds__(256) fixup_bf16_kernel(FixupArgs a) {
   const int tid = threadIdx.x;
   uint16_t* const P = (uint16_t*)a.P;
   uint16_t* const Pt = (uint16_t*)a.Pt;
-  // phase 1: row r = tid / 32 + 8 p, column octet cv = tid % 32
+  // phase 1: row r = tid / 32 + 8 p, column octet cv = tid % 32.  The eight
+  // rows' loads go out first (rows past M read row 0 and columns past V tile
+  // 0's partials: in bounds, their values unused), then the rows are formed,
+  // and the row stores come last, so that no store stands between loads the
+  // compiler may not move across it.
   const int cv = tid & 31;
   const int v = v0 + cv * 8;
   const bool vlive = v < a.V;
-  const int64_t aoff = (int64_t)(v / kPartialWidth) * a.ldr;
+  const int64_t aoff = vlive ? (int64_t)(v / kPartialWidth) * a.ldr : 0;
+  uint4 pv[8];
+  float al[8];
+  int64_t yt[8];
+  int sb[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int t = t0 + (tid >> 5) + 8 * p;
+    const int tc = t < a.M ? t : 0;
+    pv[p] = *(const uint4*)(P + (int64_t)tc * a.ldp + v);
+    al[p] = a.alpha[aoff + tc];
+    yt[p] = a.y[tc];
+    sb[p] = a.rescale_shift ? a.rescale_shift[aoff + shift_slot(tc)] : 0;
+  }
+  uint4 ov[8];
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int r = (tid >> 5) + 8 * p;
     const int t = t0 + r;
-    uint4 ov = make_uint4(0u, 0u, 0u, 0u);
-    if (t < a.M) {
-      uint16_t* const src = P + (int64_t)t * a.ldp + v;
-      const uint4 pv = *(const uint4*)src;
-      float d[8];
-      unpack8_bf16(pv, d);
-      const float al = vlive ? a.alpha[aoff + t] : 0.f;
+    const bool live = t < a.M;
+    float d[8];
+    unpack8_bf16(pv[p], d);
+    const float alp = (live && vlive) ? al[p] : 0.f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) d[k] = (v + k < a.V) ? al * d[k] : 0.f;
-      if (a.Pq) {  // soft targets: minus the teacher's probability, same scale
-        float q[8];
-        unpack8_bf16(*(const uint4*)((const uint16_t*)a.Pq + (int64_t)t * a.ldp + v), q);
-        const float aq = vlive ? a.alpha_q[aoff + t] : 0.f;
+    for (int k = 0; k < 8; ++k) d[k] = (v + k < a.V) ? alp * d[k] : 0.f;
+    if (a.Pq) {  // soft targets: minus the teacher's probability, same scale
+      const int tc = live ? t : 0;
+      float q[8];
+      unpack8_bf16(*(const uint4*)((const uint16_t*)a.Pq + (int64_t)tc * a.ldp + v), q);
+      const float aq = (live && vlive) ? a.alpha_q[aoff + tc] : 0.f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) d[k] = (v + k < a.V) ? __builtin_fmaf(-aq, q[k], d[k]) : 0.f;
-      }
-      const int64_t yt = a.y[t];
-      const int64_t yl = yt - a.y_shift;
-      if (!a.no_target && yt != a.ignore_index && yl >= v && yl < v + 8 && yl < a.V) {
-        const float dz = a.dzt[t];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) d[k] = (yl == v + k) ? dz : d[k];
-      }
-      ov = pack8_bf16(d);
-      if (a.write_rows) *(uint4*)src = ov;
+      for (int k = 0; k < 8; ++k) d[k] = (v + k < a.V) ? __builtin_fmaf(-aq, q[k], d[k]) : 0.f;
     }
-    tile[r * 32 + (cv ^ ((r >> 3) & 7))] = ov;
+    const int64_t yl = yt[p] - a.y_shift;
+    if (live && !a.no_target && yt[p] != a.ignore_index && yl >= v && yl < v + 8 && yl < a.V) {
+      const float dz = a.dzt[t];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) d[k] = (yl == v + k) ? dz : d[k];
+    }
+    ov[p] = pack8_bf16(d);
+    tile[r * 32 + (cv ^ ((r >> 3) & 7))] = ov[p];
+  }
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int t = t0 + (tid >> 5) + 8 * p;
+    if (t >= a.M) continue;
+    uint16_t* const dst = P + (int64_t)t * a.ldp + v;
+    if (a.write_rows) {
+      *(uint4*)dst = ov[p];
+    } else if (sb[p] != 0 && vlive) {
+      // this tile's reference lies below the row's: store P 2^-s instead
+      float e[8];
+      unpack8_bf16(pv[p], e);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) e[k] = __builtin_ldexpf(e[k], -sb[p]);
+      *(uint4*)dst = pack8_bf16(e);
+    }
   }
   __syncthreads();
   // phase 2: token group tg = tid % 8, column octet vo = tid / 8
