@@ -81,9 +81,9 @@ def parse():
                    help="dX through a transposed copy of W made per call (on) or reading W "
                         "as stored (off; bf16, no copy in the workspace); auto = the "
                         "workload's launch configuration")
-    p.add_argument("--dz-in-dx", action="store_true",
-                   help="form dZ inside the dX contraction (FLCE_FLAG_DZ_IN_DX) instead of in the "
-                        "pass that also writes dZ^T")
+    p.add_argument("--dz-in-place", action="store_true",
+                   help="write dZ over the exponentials for the dX contraction "
+                        "(FLCE_FLAG_DZ_IN_PLACE) instead of forming it inside that contraction")
     p.add_argument("--cpu-sample", type=int, default=3072,
                    help="tokens of the workload the CPU oracle is timed on (0 = skip)")
     p.add_argument("--vocab-shards", type=int, default=1, metavar="N",
@@ -132,10 +132,9 @@ def short_kernel_name(name: str) -> str:
     import re
     n = name.replace("flce::", "")
     m = re.match(r"void gemm_nt_kernel<([^,]+), (\d+), (\d+), (\d+), (\w+)<([^>]*)>"
-                 r"(?:, (true|false))?(?:, (true|false))?", n)
+                 r"(?:, (true|false))?", n)
     if m:
-        flags = "".join(f",{t}" for t, on in (("Bstored", m.group(7)), ("Ashift", m.group(8)))
-                        if on == "true")
+        flags = ",Bstored" if m.group(7) == "true" else ""
         return (f"gemm<{m.group(1)},{m.group(2)}x{m.group(3)},{m.group(4)}w,"
                 f"{m.group(5)}<{m.group(6).strip()}>{flags}>")
     return n.split("(")[0].replace("void ", "")
@@ -338,18 +337,19 @@ def measured_traffic(kernel_kind: str, launch):
     return None
 
 
-def per_kernel_rooflines(kernels, T, H, V, dtype, mfma_peak, dz_in_dx=False):
+def per_kernel_rooflines(kernels, T, H, V, dtype, mfma_peak, dz_in_place=False):
     """Achieved rate of each timed kernel of one fwd+bwd step against its own
     bound, from algorithmic work only: 2 T H V flops for each contraction;
     for the bandwidth passes the bytes they must move (the dZ pass reads the
-    exponentials and writes dZ and dZ^T -- only dZ^T when dZ is formed inside
-    the dX contraction; a transpose reads and writes its
-    matrix once; the merge reads the (max, sum, argmax) partials and writes
-    alpha, 16 bytes per (token, 128-column tile))."""
+    exponentials and writes dZ^T -- and dZ over the exponentials too with
+    dz_in_place; its rewrite of the few tiles whose reference lies below
+    their row's is not counted; a transpose reads and writes its matrix once;
+    the merge reads the (max, sum, argmax) partials and writes alpha, 16
+    bytes per (token, 128-column tile))."""
     es = 2 if dtype == "bf16" else 4
     nt = -(-V // 128)
     work = {"logits_gemm": ("mfma", 2.0 * T * H * V), "dx_gemm": ("mfma", 2.0 * T * H * V),
-            "dw_gemm": ("mfma", 2.0 * T * H * V), "fixup_dz": ("hbm", (2.0 if dz_in_dx else 3.0) * T * V * es),
+            "dw_gemm": ("mfma", 2.0 * T * H * V), "fixup_dz": ("hbm", (3.0 if dz_in_place else 2.0) * T * V * es),
             "transpose_w": ("hbm", 2.0 * V * H * es), "transpose_x": ("hbm", 2.0 * T * H * es),
             "finalize": ("hbm", 16.0 * nt * T)}
     out = {}
@@ -606,7 +606,7 @@ def main():
     else:
         op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=args.chunk,
                                           dw_chunks=args.dw_chunks, weight_copy=wcopy,
-                                          dz_in_dx=args.dz_in_dx)
+                                          dz_in_place=args.dz_in_place)
     if n_shards > 1 or Ht > 0:
         pass  # step() is set above
     elif fwd_only:
@@ -721,7 +721,7 @@ def main():
                         "unit": "GB/s", "frac": None, "traffic": None, "source": source}
         if not (fwd_only or n_shards > 1 or Ht > 0):
             kernel_rooflines = per_kernel_rooflines(kernels, T, H, V, wl.dtype, peak,
-                                                    args.dz_in_dx)
+                                                    args.dz_in_place)
 
     cpu = None
     if args.cpu_sample > 0 and n_shards == 1 and Ht == 0:
@@ -745,7 +745,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic" if args.inputs == "random" else f"synthetic ({args.inputs} X, W)",
         "config": {"workload": wl.name, "T": T, "H": H, "V": V, "chunk_tokens": op.chunk_tokens,
-                   "dw_chunks": op.dw_chunks, "weight_copy": wcopy, "dz_in_dx": args.dz_in_dx,
+                   "dw_chunks": op.dw_chunks, "weight_copy": wcopy, "dz_in_place": args.dz_in_place,
                    "vocab_shards": n_shards,
                    "V_total": wl.V,
                    "teacher_hidden": Ht,

@@ -72,7 +72,7 @@ typedef struct {
                            to a multiple of 256.  The workspace is
                            O((1+G)*C*V + V*H) and does not depend on the number
                            of tokens T.                                         */
-  int32_t flags;        /* 0, or FLCE_FLAG_NO_WEIGHT_COPY and/or FLCE_FLAG_DZ_IN_DX */
+  int32_t flags;        /* 0, or FLCE_FLAG_NO_WEIGHT_COPY and/or FLCE_FLAG_DZ_IN_PLACE */
 } flce_config_t;
 
 /* The dX GEMM reads W in its stored [V x H] layout instead of a transposed
@@ -82,19 +82,20 @@ typedef struct {
  * V*H*2 must stay below 2^31 bytes; FLCE_ERR_UNSUPPORTED otherwise. */
 #define FLCE_FLAG_NO_WEIGHT_COPY 1
 
-/* dZ is formed inside the dX contraction instead of by the pass that also
- * writes dZ^T for the dW contraction ("gradient of softmax + CE loss" in
- * "Alisa's book of LLMs": dZ = p - onehot, never written for dX).  The
- * logits epilogue stores each (row, 128-column tile) of exponentials
- * relative to a whole power of two; the dX GEMM scales its A fragments by the
- * tile's power of two in registers (an exact integer shift of the exponent
- * field) and finishes each output row with a per-row scale and the target's
- * correction times that row of W.  The dZ pass then writes only dZ^T (2/3
- * of its traffic), for a dX GEMM whose K loop carries one VALU instruction
- * per two A elements per wave.  Same results to the tolerances; only the
- * hard-target fused call and the vocabulary-shard backward use it (the
- * soft-target call ignores it). */
-#define FLCE_FLAG_DZ_IN_DX 2
+/* How dZ reaches the dX contraction ("gradient of softmax + CE loss" in
+ * "Alisa's book of LLMs": dZ = p - onehot).  By default dZ is formed inside
+ * it and never written for it: the logits epilogue stores each (row,
+ * 128-column tile) of exponentials relative to a power of two 2^(32 j); the
+ * pass that writes dZ^T for the dW contraction also rewrites, in place, the
+ * tiles whose power lies below their row's (so a row's exponentials share
+ * one), and the dX GEMM reads the exponentials and finishes each output row
+ * with the row's scale and the target's correction times that row of W.
+ * With this flag the pass instead writes dZ itself over the exponentials
+ * (one more T*V write; measured ~2 % slower per call at 16384 x 4096 x
+ * 128256) and the dX GEMM reads it.  Same results to the tolerances.  The
+ * soft-target call always writes dZ (its rows hold two sets of
+ * exponentials). */
+#define FLCE_FLAG_DZ_IN_PLACE 2
 
 typedef struct flce_handle* flce_handle_t;
 

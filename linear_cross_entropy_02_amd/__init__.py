@@ -47,7 +47,7 @@ class flce_config_t(ctypes.Structure):
 
 
 FLCE_FLAG_NO_WEIGHT_COPY = 1
-FLCE_FLAG_DZ_IN_DX = 2
+FLCE_FLAG_DZ_IN_PLACE = 2
 
 
 class FlceError(RuntimeError):
@@ -283,7 +283,7 @@ class FusedLinearCrossEntropy:
     """
 
     def __init__(self, hidden: int, vocab: int, dtype="bf16", chunk_tokens: int = 0,
-                 dw_chunks: int = 0, weight_copy: bool = True, dz_in_dx: bool = False):
+                 dw_chunks: int = 0, weight_copy: bool = True, dz_in_place: bool = False):
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("FusedLinearCrossEntropy needs a HIP device")
@@ -291,7 +291,7 @@ class FusedLinearCrossEntropy:
         self.dtype = FLCE_BF16 if dtype == "bf16" else FLCE_F32
         self.hidden, self.vocab = hidden, vocab
         flags = (0 if weight_copy else FLCE_FLAG_NO_WEIGHT_COPY) | \
-            (FLCE_FLAG_DZ_IN_DX if dz_in_dx else 0)
+            (FLCE_FLAG_DZ_IN_PLACE if dz_in_place else 0)
         st, h = flce_create(hidden, vocab, self.dtype, chunk_tokens, dw_chunks, flags)
         if st != FLCE_OK:
             raise FlceError(st, "flce_create")

@@ -47,12 +47,6 @@ const char* kKindNames[K_NUM] = {"count_valid",   "transpose_w", "transpose_x", 
 
 constexpr int64_t kDefaultChunk = 4096;
 constexpr int kMaxDwChunks = 8;
-// With dZ formed inside the dX contraction, the tile references of the
-// stored exponentials are multiples of 2^32: the tiles of a row then mostly
-// share one (its logits would have to straddle a multiple of 32 log2(e)
-// nats), and the dZ pass rewrites only the others.  Values more than ~65
-// nats below their tile's max flush to zero, where their softmax is < e^-65.
-constexpr float kRowRefQuantum = 32.f;
 
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -73,7 +67,7 @@ struct flce_handle {
   int64_t Ht = 0;          // teacher hidden size (soft-target handles only)
   int splitk_alloc = 1;  // split-K planes the workspace holds for a full chunk
   bool w_copy = true;      // dX reads W^T (a copy made per call) or W as stored
-  bool dz_in_dx = false;   // dZ formed inside the dX contraction (FLCE_FLAG_DZ_IN_DX)
+  bool dz_in_dx = true;    // dZ formed inside the dX contraction (not FLCE_FLAG_DZ_IN_PLACE)
   size_t ws_bytes = 0;
   char* ws = nullptr;
   void* Wt = nullptr;      // W^T           [H x Vpad]
@@ -267,7 +261,7 @@ flce_status_t configure(const flce_config_t* cfg, int64_t Ht, flce_handle* h, La
   C = round_up(C, 256);
   const int64_t G = cfg->dw_chunks ? cfg->dw_chunks : 1;
   if (C * G > (1 << 20)) return FLCE_ERR_UNSUPPORTED;
-  if (cfg->flags & ~(FLCE_FLAG_NO_WEIGHT_COPY | FLCE_FLAG_DZ_IN_DX)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (cfg->flags & ~(FLCE_FLAG_NO_WEIGHT_COPY | FLCE_FLAG_DZ_IN_PLACE)) return FLCE_ERR_INVALID_ARGUMENT;
   const bool no_wcopy = (cfg->flags & FLCE_FLAG_NO_WEIGHT_COPY) != 0;
   // W as stored: bf16 transposing LDS reads; one buffer descriptor spans W,
   // whose size must stay below the out-of-range offset (2^31) that reads 0
@@ -280,7 +274,7 @@ flce_status_t configure(const flce_config_t* cfg, int64_t Ht, flce_handle* h, La
   h->G = (int)G;
   h->Ht = Ht;
   h->w_copy = !no_wcopy;
-  h->dz_in_dx = (cfg->flags & FLCE_FLAG_DZ_IN_DX) != 0;
+  h->dz_in_dx = (cfg->flags & FLCE_FLAG_DZ_IN_PLACE) == 0;
   h->Vpad = round_up(V, 256);
   h->nt = cdiv64(V, kPartialWidth);
   {
@@ -603,7 +597,6 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       la.pc = h->pc;
     } else if (h->dz_in_dx) {
       la.ptgt = h->ptgt;
-      la.kq_quantum = kRowRefQuantum;
     }
     FLCE_LAUNCH(K_LOGITS, launch_logits(dt, la, s));
 
@@ -640,8 +633,6 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       fa.shift = h->shift;
       fa.corr = h->corr;
       fa.ptgt = h->ptgt;
-      fa.kq_quantum = kRowRefQuantum;
-      fa.rescaled_rows = true;
       fa.round_bf16 = dt == Dt::BF16;
     }
     fa.backward = true;
@@ -677,9 +668,6 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
     // dX_c = dZ W   (M = Cc, N = H, K = vocabulary); without soft targets
     // A holds the exponentials and dZ is formed in the contraction
     DxFuse fz{};
-    fz.shift = nullptr;  // the rows of P share one reference: no shifts
-    fz.shift_ld = C;
-    fz.shift_tiles = (int)nt;
     fz.beta = h->beta;
     fz.corr = h->corr;
     fz.y = yc;

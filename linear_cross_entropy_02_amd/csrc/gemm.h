@@ -55,14 +55,6 @@
 // runs 8-12 % slower than with a transposed copy of B; it saves the copy's
 // memory.
 //
-// AS: the A operand holds softmax numerators stored relative to a per
-// (row, 128-column K tile) power of two, and each A fragment is scaled by
-// 2^-s(row, tile) in registers between its LDS read and its MFMAs: the
-// saturating 16-bit (bf16) or 32-bit (fp32) integer subtraction of s from the
-// exponent field, exact for these non-negative values (a result that would
-// leave the normal range becomes 0).  s comes as one byte per (tile, row) in
-// the layout byte (t & ~127) + 8 (t % 16) + (t / 16) % 8 of each tile's row,
-// so a lane reads its FM rows' bytes in one 8- or 4-byte load per tile.
 #pragma once
 
 #include "common.h"
@@ -81,10 +73,6 @@ struct GemmShape {
   // Logical tiles this launch covers: [tile_first, tile_first + tile_count)
   // of the grid's walk order (set by the launcher; all tiles by default).
   int tile_first, tile_count;
-  // AS only: the per-(tile, row) exponent shifts of A, ash_ld bytes per tile
-  const uint8_t* ash;
-  int64_t ash_ld;
-  int ash_tiles;     // tiles the shift array holds
 };
 
 struct TileCoord {
@@ -144,24 +132,6 @@ template <> __device__ __forceinline__ f4 mma16<float>(uint4 a, uint4 b, f4 c) {
   return c;
 }
 
-// The same MFMA after two wait states: the first MFMA that reads an A
-// fragment rewritten by VALU code (the AS shifts, or register copies the
-// compiler places before the asm) must not issue sooner, and the hazard
-// recognizer does not look inside asm.
-template <typename T> __device__ __forceinline__ f4 mma16_after_valu(uint4 a, uint4 b, f4 c);
-template <> __device__ __forceinline__ f4 mma16_after_valu<bf16>(uint4 a, uint4 b, f4 c) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  typedef int i4v __attribute__((ext_vector_type(4)));
-  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
-               : "+a"(c)
-               : "v"(__builtin_bit_cast(i4v, a)), "v"(__builtin_bit_cast(i4v, b)));
-#endif
-  return c;
-}
-template <> __device__ __forceinline__ f4 mma16_after_valu<float>(uint4 a, uint4 b, f4 c) {
-  // compiler-visible MFMAs: the hazard recognizer orders them after the shifts
-  return mma16<float>(a, b, c);
-}
 // Orders every accumulator after the preceding asm statements (the MFMA
 // drain): each empty asm claims to modify one accumulator.
 // Order of the FM x FN MFMAs of a substep (fragment row i = A fragment, the
@@ -316,77 +286,19 @@ __device__ __forceinline__ void load16_acc(f4& dst, i4v rsrc, uint32_t voff) {
 #endif
 }
 
-// One 4- or 8-byte load per lane from a buffer resource into VGPRs, issued
-// as asm like dma16 so the compiler's wait-count model never sees it: the
-// caller issues it before DMAs that a later explicit vmcnt wait covers, and
-// reads the result only after that wait, through fence_v().
-template <int N>
-__device__ __forceinline__ void load_shift(uint32_t (&dst)[N], i4v rsrc, uint32_t voff,
-                                           uint32_t soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const i4v r = {__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
-                 __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
-  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
-  if constexpr (N == 2)
-    asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen"
-                 : "=v"(*(uint2*)dst) : "v"(voff), "s"(r), "s"(so) : "memory");
-  else
-    asm volatile("buffer_load_dword %0, %1, %2, %3 offen"
-                 : "=v"(dst[0]) : "v"(voff), "s"(r), "s"(so) : "memory");
-#endif
-}
-// Orders later reads of the registers after the preceding asm statements
-// (the explicit wait that lands an asm load).
-template <int N>
-__device__ __forceinline__ void fence_v(uint32_t (&v)[N]) {
-#if defined(__HIP_DEVICE_COMPILE__)
-#pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
-#endif
-}
-// Shift bytes (little-endian in w) -> the subtrahend of one fragment: s at
-// the exponent field of each bf16 half, or of the fp32 value.
-template <typename T>
-__device__ __forceinline__ uint32_t shift_word(uint32_t w, int byte) {
-  const uint32_t b = __builtin_amdgcn_ubfe(w, 8 * byte, 8);
-  if constexpr (sizeof(T) == 2)
-    return b * 0x00800080u;
-  else
-    return b << 23;
-}
-// x -> x 2^-s for the four registers of one A fragment (non-negative bf16
-// pairs or fp32 values), with saturation at 0.  Asm, so it stays where it is
-// placed among the asm MFMAs; the first MFMA reading the fragment is
-// mma16_after_valu (the hazard recognizer does not look inside asm).
-template <typename T>
-__device__ __forceinline__ void shift_frag(uint4& f, uint32_t sh) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  if constexpr (sizeof(T) == 2)
-    asm volatile(
-        "v_pk_sub_u16 %0, %0, %4 clamp\n\tv_pk_sub_u16 %1, %1, %4 clamp\n\t"
-        "v_pk_sub_u16 %2, %2, %4 clamp\n\tv_pk_sub_u16 %3, %3, %4 clamp"
-        : "+v"(f.x), "+v"(f.y), "+v"(f.z), "+v"(f.w) : "v"(sh));
-  else
-    asm volatile(
-        "v_sub_u32_e64 %0, %0, %4 clamp\n\tv_sub_u32_e64 %1, %1, %4 clamp\n\t"
-        "v_sub_u32_e64 %2, %2, %4 clamp\n\tv_sub_u32_e64 %3, %3, %4 clamp"
-        : "+v"(f.x), "+v"(f.y), "+v"(f.z), "+v"(f.w) : "v"(sh));
-#endif
-}
-
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// K-loop schedule, one 128-byte K-stage per iteration, two LDS stages:
+// K-loop schedule (the pipeline described at the top), per 128-byte stage:
 //   [A] substep-0 MFMAs on fragments already in registers, with the
-//       substep-1 fragment reads of the same stage threaded through them;
-//   barrier: this wave's reads of the stage are done and the next stage's
-//       DMA has landed (vmcnt), in every wave;
-//   [B] substep-1 MFMAs, with the DMA of the stage after next (into the
-//       buffer just released) and the next stage's substep-0 fragment reads
-//       threaded through them.
+//       substep-1 fragment reads of the same stage and the A DMAs of the
+//       stage after next threaded through them;
+//   wait + barrier: this wave's reads of the stage are done and the next
+//       stage has landed, in every wave;
+//   [B] substep-1 MFMAs, with the next stage's substep-0 fragment reads and
+//       the B DMAs of the stage after next threaded through them.
 // The wave never waits on LDS after the barrier: the fragments its MFMAs
 // need were read before it.
-template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false, bool AS = false>
+template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false>
 __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi epi) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the launch stub
   using G = TileGeom<BM, BN, WAVES>;
@@ -397,7 +309,6 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
   constexpr int B_INS = BN / (8 * WAVES);
   constexpr int FM = G::FM, FN = G::FN;
   static_assert(!BT || (sizeof(T) == 2 && WAVES == 4), "stored-layout B: bf16, 4 waves");
-  static_assert(!AS || (WAVES == 4 && (FM == 8 || FM == 4)), "shifted A: 4 waves, 64/128-row waves");
   constexpr int UPR = BN / 8;  // BT: 16-byte units per k-row of a B stage
   extern __shared__ uint4 lds[];  // G::kLdsBytes, sized at launch
 
@@ -514,10 +425,7 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
       fb[r - FM] = read_b_tr(bb, wn * G::WN + 16 * (r - FM), s);
   };
 
-  // the shifted-A kernels key their shifts to the first use of each A
-  // fragment in row order (and the fp32 ones mix compiler-visible and asm
-  // MFMAs): they keep order 0
-  constexpr int ORD = AS ? 0 : Epi::kOrder;
+  constexpr int ORD = Epi::kOrder;
   static_assert(ORD >= 0 && ORD <= 2, "MFMA order");
   constexpr int NR = FM + FN;  // fragment reads per substep
   constexpr int NM = FM * FN;  // MFMAs per substep
@@ -533,32 +441,8 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
   // s_waitcnt vmcnt(A_INS) lgkmcnt(0): all but the A DMAs of this phase A
   constexpr int kWaitMid = (A_INS & 0xF) | ((A_INS >> 4) << 14) | 0x0070;
 
-  // AS: the lane's FM rows of the wave tile sit at bytes sh_off .. + FM - 1
-  // of a tile's row of shifts; tile of K offset k: k / 128 (clamped)
-  constexpr int SHW = AS ? FM / 4 : 1;  // 32-bit words of shift bytes per lane
-#ifndef FLCE_SHIFT_LEAD
-#define FLCE_SHIFT_LEAD 2
-#endif
-  // MFMAs between a fragment's shift and its first MFMA: late enough that the
-  // fragment's LDS read has landed without a wait, early enough to cover the
-  // shift's latency
-  constexpr int kShiftLead = FN < FLCE_SHIFT_LEAD ? FN : FLCE_SHIFT_LEAD;
-  i4v rS = {0, 0, 0, 0};
-  uint32_t sh_off = 0;
-  uint32_t shw[SHW], psh[FM], psh_n[FM];
-  auto shift_tile = [&](int k0) -> uint32_t {
-    const int j = min(k0, k_end - 1) >> 7;
-    return (uint32_t)((int64_t)min(j, g.ash_tiles - 1) * g.ash_ld);
-  };
-  if constexpr (AS) {
-    const int r0 = m0 + wm * G::WM;
-    sh_off = (uint32_t)((r0 & ~127) + 8 * (lane & 15) + (r0 & 64 ? 4 : 0));
-    rS = make_rsrc(g.ash, (uint32_t)((int64_t)g.ash_tiles * g.ash_ld));
-  }
-
   uint4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
   if (nk > 0) {
-    if constexpr (AS) load_shift(shw, rS, sh_off, shift_tile(k_begin));  // lands with stage 0
 #pragma unroll
     for (int j = 0; j < A_INS; ++j) issue_a(0, k_begin, j);
 #pragma unroll
@@ -569,11 +453,6 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
     for (int j = 0; j < B_INS; ++j) issue_b(1, k_begin + BK, j);
     __builtin_amdgcn_s_waitcnt(kWaitStage0);  // initial accumulators and stage 0 landed
     __builtin_amdgcn_s_barrier();
-    if constexpr (AS) {
-      fence_v(shw);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) psh[i] = shift_word<T>(shw[i >> 2], i & 3);
-    }
 #pragma unroll
     for (int n = 0; n < NR; ++n) read_one(0, 0, 0, ORD == 2 ? read_slot<FM, FN, ORD>(n) : n, fa0, fb0);
     // stage kt sits in A buffer kt % 3 and B buffer kt % 2
@@ -583,21 +462,10 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
       const int k2 = k_begin + (kt + 2) * BK;  // past the end: zero fill, unused
       // [A]: substep-0 MFMAs; substep-1 reads of stage kt; A half of stage
       // kt + 2 into the A buffer stage kt - 1 used (read before the last barrier)
-      if constexpr (AS) {
-        // the shifts of stage kt + 1's tile, landed by this stage's mid wait
-        load_shift(shw, rS, sh_off, shift_tile(k_begin + (kt + 1) * BK));
-        shift_frag<T>(fa0[0], psh[0]);
-      }
 #pragma unroll
       for (int q = 0; q < NM; ++q) {
         const int i = mma_row<FM, FN, ORD>(q), j = mma_col<FM, FN, ORD>(q);
-        if (AS && q % FN == 0)
-          acc[i][j] = mma16_after_valu<T>(fb0[j], fa0[i], acc[i][j]);
-        else
-          acc[i][j] = mma16<T>(fb0[j], fa0[i], acc[i][j]);
-        if constexpr (AS)  // the next fragment, kShiftLead MFMAs before its first use
-          if (q % FN == FN - kShiftLead && q / FN + 1 < FM)
-            shift_frag<T>(fa0[q / FN + 1], psh[q / FN + 1]);
+        acc[i][j] = mma16<T>(fb0[j], fa0[i], acc[i][j]);
         if (q % SPA == SPA - 1 && q / SPA < NSA) {
           const int k = q / SPA;  // one DMA after every second read
           if (k % 3 == 2 && k / 3 < A_INS)
@@ -610,22 +478,10 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
       __builtin_amdgcn_s_barrier();
       // [B]: substep-1 MFMAs; substep-0 reads of stage kt + 1; B half of
       // stage kt + 2 into the B buffer of stage kt (fully read before the barrier)
-      if constexpr (AS) {
-        shift_frag<T>(fa1[0], psh[0]);
-        fence_v(shw);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) psh_n[i] = shift_word<T>(shw[i >> 2], i & 3);
-      }
 #pragma unroll
       for (int q = 0; q < NM; ++q) {
         const int i = mma_row<FM, FN, ORD>(q), j = mma_col<FM, FN, ORD>(q);
-        if (AS && q % FN == 0)
-          acc[i][j] = mma16_after_valu<T>(fb1[j], fa1[i], acc[i][j]);
-        else
-          acc[i][j] = mma16<T>(fb1[j], fa1[i], acc[i][j]);
-        if constexpr (AS)
-          if (q % FN == FN - kShiftLead && q / FN + 1 < FM)
-            shift_frag<T>(fa1[q / FN + 1], psh[q / FN + 1]);
+        acc[i][j] = mma16<T>(fb1[j], fa1[i], acc[i][j]);
         if (q % SPB == SPB - 1 && q / SPB < NSB) {
           const int k = q / SPB;
           if (k % 3 == 2 && k / 3 < B_INS)
@@ -638,10 +494,6 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
       a_cur = a_nxt;
       a_nxt = a_dma;
       a_dma = t;
-      if constexpr (AS) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) psh[i] = psh_n[i];
-      }
       // Drain the MFMA pipe before leaving the loop: the register allocator
       // may copy accumulators on the exit edge, and the hazard recognizer
       // does not see the asm MFMAs whose results those copies read.

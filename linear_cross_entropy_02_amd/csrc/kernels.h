@@ -36,15 +36,11 @@ struct LogitsArgs {
   // nullable: per row, the stored exponential at the target's column, as
   // fp32
   float* ptgt = nullptr;
-  // the tile reference k is a multiple of this many powers of two (1, or 32
-  // so that the tiles of a row mostly share one reference)
-  float kq_quantum = 1.f;
 };
 // The stored exponentials of a (row, 128-column tile) are exp2(z log2(e) /
-// tau - k) with k = q ceil(m log2(e) / q), m the tile's max of z / tau and q
-// the quantum: relative to a whole power of two, so that the factor taking
-// them to probabilities is a per-row scale times 2^-s(row, tile) (see
-// FinalizeArgs).
+// tau - k) with k = 32 ceil(m log2(e) / 32), m the tile's max of z / tau:
+// relative to a whole power of two, so that the factor taking them to
+// probabilities is a per-row scale times 2^-s(row, tile) (see FinalizeArgs).
 // Width in columns of one online-logsumexp partial (the wave tile width of
 // the 256 x 256 logits GEMM).
 constexpr int kPartialWidth = 128;
@@ -56,11 +52,6 @@ hipError_t launch_logits(Dt dt, const LogitsArgs& a, hipStream_t s);
 // the output row t is beta_t acc_t + corr_t W[y_t - y_shift] (the target
 // term only when that row of W is in [0, V)).
 struct DxFuse {
-  // shift: A fragments are scaled by 2^-s per (row, 128-column tile) in
-  // registers; nullptr: the rows of A already share one reference
-  const uint8_t* shift;
-  int64_t shift_ld;   // bytes per tile
-  int shift_tiles;
   const float* beta;
   const float* corr;
   const int64_t* y;   // chunk targets
@@ -138,24 +129,20 @@ struct FinalizeArgs {
   int first_chunk;
   int block_rows = 8;    // finalize_rows(nt, C): 8 or 32
   // Backward with dZ formed inside the dX contraction (all nullable):
-  //   beta  [M]       per-row scale: dZ_tv = beta_t 2^-s_tj P_tv off the target
-  //   shift [nt x ldr] bytes s_tj = K_t - k_tj (255: empty tile, or 255 and
-  //                   more), row t of tile j at byte
-  //                   j ldr + (t & ~127) + 8 (t % 16) + (t / 16) % 8
-  //   corr  [M]       dzt_t - beta_t x (the value the contraction reads at
-  //                   the target's column): the target's correction; 0 when
-  //                   the target is ignored or not in these columns
-  //   ptgt  [M]       in: the stored exponential at the target's column
-  // That value is 2^-s P_t,y when the contraction shifts its operand in
-  // registers; with rescaled_rows, the dZ pass rewrites P_t,y as
-  // round(2^-s P_t,y) in the input dtype (round_bf16) and corr uses that.
+  //   beta  [M]        per-row scale: dZ_tv = beta_t 2^-s_tj P_tv off the target
+  //   shift [nt x ldr] bytes s_tj = K_t - k_tj, tile-major like the partials
+  //                    (0 for an empty tile, 255 for 255 and more): the dZ
+  //                    pass rewrites P_tv as round(2^-s P_tv) where s != 0,
+  //                    so that row t's exponentials share the reference 2^K_t
+  //   corr  [M]        dzt_t - beta_t round(2^-s P_t,y): the target's
+  //                    correction (0 when the target is ignored or not in
+  //                    these columns), round() to the input dtype
+  //   ptgt  [M]        in: the stored exponential at the target's column
   float* beta = nullptr;
   uint8_t* shift = nullptr;
   float* corr = nullptr;
   const float* ptgt = nullptr;
-  float kq_quantum = 1.f;     // as LogitsArgs::kq_quantum
-  bool rescaled_rows = false;
-  bool round_bf16 = false;
+  bool round_bf16 = false;    // the input dtype is bf16
 };
 // Rows per finalize block, hence rows per loss partial: 32 when rows hold
 // at most 256 partial tiles and a chunk of C rows still gives 256 blocks,
@@ -176,10 +163,9 @@ struct FixupArgs {
   const int64_t* y; int64_t ignore_index;
   int64_t y_shift;               // vocabulary id of column 0 (shard offset)
   bool no_target = false;        // soft targets: no one-hot column
-  // nullable (finalize's shift bytes): rewrite, in place, the row segments
-  // whose tile reference lies below the row's as P 2^-s in the input dtype,
-  // so that a row's stored exponentials share one reference (rows with a
-  // zero alpha are left alone)
+  // nullable (finalize's shift bytes, [nt x ldr]): rewrite, in place, the
+  // row segments whose tile reference lies below the row's as P 2^-s in the
+  // input dtype, so that each row's stored exponentials share one reference
   const uint8_t* rescale_shift = nullptr;
   const void* Pq = nullptr;      // soft targets: teacher exponentials, subtracted
   const float* alpha_q = nullptr;  //   with this scale, [nt x ldr]

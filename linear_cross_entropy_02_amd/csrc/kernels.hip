@@ -35,6 +35,19 @@
 
 namespace flce {
 
+// Power-of-two references of the stored exponentials: a tile whose max (of
+// z / tau) is m stores exp2(z log2(e) - k) with k = q ceil(m log2(e) / q),
+// q = kRefQuantum.  Any whole power of two at or above the max would do; a
+// coarse one makes the tiles of a row mostly share it (their maxima would
+// have to straddle a multiple of 32 log2(e) ~ 22 nats), so that the dZ pass
+// can leave those rows' exponentials as they are for the dX contraction and
+// rewrite only the lower tiles of the others.  Values more than ~65 nats
+// below their tile's max flush to zero; their softmax is < e^-65 of it.
+constexpr float kRefQuantum = 32.f;
+__device__ __forceinline__ float ref_power(float m) {
+  return __builtin_ceilf(m * kLog2e / kRefQuantum) * kRefQuantum;
+}
+
 // ------------------------------------------------------------ epilogues ---
 
 // Stores four consecutive values of one row in the output type.
@@ -85,7 +98,6 @@ struct LogitsEpi {
   int M, V;
   bool store_p;  // false: partials and target logit only (forward-only calls)
   float* ptgt;   // nullable: the stored exponential at the target's column
-  float kq_quantum;  // the tile reference is a multiple of this power of two
 
   template <int FM, int FN>
   __device__ __forceinline__ void init(f4 (&acc)[FM][FN], const EpiCoord&) const {
@@ -163,14 +175,13 @@ struct LogitsEpi {
         cross += shfl_xor_f(cross, 16);
         cross += shfl_xor_f(cross, 32);
       }
-      // exponentials relative to 2^kq, kq = q ceil(tile max log2(e) / q): a
-      // whole power of two, so that the merge turns them into probabilities
-      // with a per-row scale and an exact power-of-two factor per tile (q a
-      // power of two: the division is exact)
+      // exponentials relative to 2^kq, kq = q ceil(tile max log2(e) / q)
+      // with q = kRefQuantum: a whole power of two, so that the merge turns
+      // them into probabilities with a per-row scale and an exact
+      // power-of-two factor per tile (q is a power of two: / q is exact)
       const float kl = kLog2e * inv_temp;
       const float pmv = mx * inv_temp;
-      const float kq =
-          (mx == kNegInf) ? 0.f : __builtin_ceilf(pmv * kLog2e / kq_quantum) * kq_quantum;
+      const float kq = (mx == kNegInf) ? 0.f : ref_power(pmv);
       float sum = 0.f;
 #pragma unroll
       for (int j = 0; j < FN; ++j)
@@ -289,8 +300,8 @@ struct StoreEpi {
 // input dtype, which dX and W share.
 template <typename TO>
 struct DxEpi {
-  // MFMA issue order (gemm.h; the shifted-A kernels keep order 0): as the
-  // other dX kernels, the A fragment (the exponentials) stays put in a row
+  // MFMA issue order (gemm.h): as the other dX kernels, the A fragment (the
+  // exponentials) stays put within a fragment row
   static constexpr int kOrder = 1;
   TO* out;
   int64_t ldo;
@@ -382,7 +393,7 @@ __global__ void __launch_bounds__(256) tile_reduce_kernel(GemmShape g, const flo
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false, bool AS = false>
+template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false>
 static hipError_t run_gemm(const GemmShape& g0, const Epi& epi, hipStream_t s) {
   using G = TileGeom<BM, BN, WAVES>;
   GemmShape g = g0;
@@ -399,32 +410,27 @@ static hipError_t run_gemm(const GemmShape& g0, const Epi& epi, hipStream_t s) {
   if (g.tile_first < 0 || g.tile_first + g.tile_count > g.tiles_m * g.tiles_n)
     return hipErrorInvalidValue;
   const int nblk = g.tile_count * g.splits;
-  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, WAVES, Epi, BT, AS>), dim3(nblk),
+  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, WAVES, Epi, BT>), dim3(nblk),
                      dim3(G::kThreads), G::kLdsBytes, s, g, epi);
   return hipGetLastError();
 }
 
 // The GEMM kernels use more than the default 64 KB of dynamic LDS.
-template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false, bool AS = false>
+template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false>
 static hipError_t set_lds_attr() {
   using G = TileGeom<BM, BN, WAVES>;
-  return hipFuncSetAttribute((const void*)gemm_nt_kernel<T, BM, BN, WAVES, Epi, BT, AS>,
+  return hipFuncSetAttribute((const void*)gemm_nt_kernel<T, BM, BN, WAVES, Epi, BT>,
                              hipFuncAttributeMaxDynamicSharedMemorySize, G::kLdsBytes);
 }
 
-// The dX instantiations with dZ formed inside the contraction, for one B
-// layout: direct output or raw split-K partials, 256- or 128-wide tiles,
-// A fragments shifted in registers or read as they are (the raw partials of
-// the latter are the plain dX kernels, set up with them).
+// The dX instantiations that finish dZ W rows themselves (DxEpi: row scale
+// and target correction), for one B layout, 256- or 128-wide tiles (their
+// split-K partials are the plain fp32-partial kernels).
 template <typename T, bool BT>
 static hipError_t setup_fused_dx() {
   hipError_t e;
-  if ((e = set_lds_attr<T, 256, 256, 4, DxEpi<T>, BT, true>()) != hipSuccess) return e;
-  if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<float, false>, BT, true>()) != hipSuccess) return e;
-  if ((e = set_lds_attr<T, 128, 128, 4, DxEpi<T>, BT, true>()) != hipSuccess) return e;
-  if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<float, false>, BT, true>()) != hipSuccess) return e;
-  if ((e = set_lds_attr<T, 256, 256, 4, DxEpi<T>, BT, false>()) != hipSuccess) return e;
-  return set_lds_attr<T, 128, 128, 4, DxEpi<T>, BT, false>();
+  if ((e = set_lds_attr<T, 256, 256, 4, DxEpi<T>, BT>()) != hipSuccess) return e;
+  return set_lds_attr<T, 128, 128, 4, DxEpi<T>, BT>();
 }
 
 template <typename T>
@@ -473,7 +479,6 @@ static hipError_t logits_run(const LogitsArgs& a, const GemmShape& g, hipStream_
   epi.P = (T*)a.P;
   epi.ldp = a.ldp;
   epi.inv_temp = a.inv_temp;
-  epi.kq_quantum = a.kq_quantum;
   epi.Pq = (const T*)a.Pq;
   epi.pc = a.pc;
   epi.pm = a.pm;
@@ -513,12 +518,11 @@ hipError_t launch_logits(Dt dt, const LogitsArgs& a, hipStream_t s) {
   return dt == Dt::BF16 ? logits_t<bf16>(a, s) : logits_t<float>(a, s);
 }
 
-// The dX contraction with dZ formed inside it (GemmOutArgs::fuse): AS =
-// true scales the A fragments by their tile's 2^-s in registers; AS = false
-// reads A as it is (its rows already share one reference).  With splits the
+// The dX contraction with dZ formed inside it (GemmOutArgs::fuse): A holds
+// the exponentials, each row relative to one power of two.  With splits the
 // raw partial planes go out and splitk_reduce finishes them; else DxEpi
 // finishes each row (row scale, target correction).
-template <typename T, typename TO, bool AS>
+template <typename T, typename TO>
 static hipError_t fused_dx(TileCfg tc, const GemmOutArgs& a, const GemmShape& g,
                            const StoreEpi<TO, false>& epi, hipStream_t s) {
   if (g.splits > 1) {
@@ -526,14 +530,13 @@ static hipError_t fused_dx(TileCfg tc, const GemmOutArgs& a, const GemmShape& g,
       if (a.b_stored) {
         if constexpr (std::is_same<T, bf16>::value) {
           if (tc != TileCfg::T256)
-            return run_gemm<T, 128, 128, 4, StoreEpi<float, false>, true, AS>(g, epi, s);
-          return run_gemm<T, 256, 256, 4, StoreEpi<float, false>, true, AS>(g, epi, s);
+            return run_gemm<T, 128, 128, 4, StoreEpi<float, false>, true>(g, epi, s);
+          return run_gemm<T, 256, 256, 4, StoreEpi<float, false>, true>(g, epi, s);
         }
         return hipErrorInvalidValue;
       }
-      if (tc != TileCfg::T256)
-        return run_gemm<T, 128, 128, 4, StoreEpi<float, false>, false, AS>(g, epi, s);
-      return run_gemm<T, 256, 256, 4, StoreEpi<float, false>, false, AS>(g, epi, s);
+      if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4, StoreEpi<float, false>>(g, epi, s);
+      return run_gemm<T, 256, 256, 4, StoreEpi<float, false>>(g, epi, s);
     }
     return hipErrorInvalidValue;
   } else if constexpr (std::is_same<TO, T>::value) {
@@ -545,13 +548,13 @@ static hipError_t fused_dx(TileCfg tc, const GemmOutArgs& a, const GemmShape& g,
     de.f = *a.fuse;
     if (a.b_stored) {
       if constexpr (std::is_same<T, bf16>::value) {
-        if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4, DxEpi<T>, true, AS>(g, de, s);
-        return run_gemm<T, 256, 256, 4, DxEpi<T>, true, AS>(g, de, s);
+        if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4, DxEpi<T>, true>(g, de, s);
+        return run_gemm<T, 256, 256, 4, DxEpi<T>, true>(g, de, s);
       }
       return hipErrorInvalidValue;
     }
-    if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4, DxEpi<T>, false, AS>(g, de, s);
-    return run_gemm<T, 256, 256, 4, DxEpi<T>, false, AS>(g, de, s);
+    if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4, DxEpi<T>>(g, de, s);
+    return run_gemm<T, 256, 256, 4, DxEpi<T>>(g, de, s);
   }
   return hipErrorInvalidValue;
 }
@@ -583,13 +586,7 @@ static hipError_t store_t2(TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
   if (a.fuse) {
     // dZ formed inside the contraction; split-K: the partial planes, summed
     // and finished by splitk_reduce
-    if constexpr (!ACC) {
-      g.ash = a.fuse->shift;
-      g.ash_ld = a.fuse->shift_ld;
-      g.ash_tiles = a.fuse->shift_tiles;
-      if (a.fuse->shift) return fused_dx<T, TO, true>(tc, a, g, epi, s);
-      return fused_dx<T, TO, false>(tc, a, g, epi, s);
-    }
+    if constexpr (!ACC) return fused_dx<T, TO>(tc, a, g, epi, s);
     return hipErrorInvalidValue;
   }
   if (a.b_stored) {
@@ -861,12 +858,6 @@ hipError_t launch_transpose(Dt dt, const void* src, int rows, int cols, int64_t 
 // 8 x 128 for long rows (a 128256-word vocabulary has 1002 partial tiles),
 // 32 x 32 for rows of at most 256 tiles, which otherwise leave most slices
 // idle and spend the block's time in three 128-slice tree reductions.
-// Byte of row `row` within a tile's row of shift bytes: the 16 x 8 order in
-// which a 128-row wave tile of the shifted-A contraction loads them.
-__device__ __forceinline__ int64_t shift_slot(int row) {
-  return (row & ~127) + 8 * (row & 15) + ((row >> 4) & 7);
-}
-
 template <int ROWS>
 __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   constexpr int kFinRows = ROWS, kFinSlices = 1024 / ROWS, kFinCache = 8;
@@ -942,12 +933,9 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   }
   __syncthreads();
   // The stored exponentials of tile j are relative to 2^k_j, k_j =
-  // q ceil(m_j log2 e / q) (0 for an all -inf tile), exactly as the logits
-  // epilogue computed it; K = q ceil(m log2 e / q) is the largest k_j.
-  const float kqq = a.kq_quantum;
-  auto kq_of = [kqq](float mj) {
-    return mj == kNegInf ? 0.f : __builtin_ceilf(mj * kLog2e / kqq) * kqq;
-  };
+  // ref_power(m_j) (0 for an all -inf tile), exactly as the logits epilogue
+  // computed it; K = ref_power(m) is the largest k_j.
+  auto kq_of = [](float mj) { return mj == kNegInf ? 0.f : ref_power(mj); };
   // pass 2: sum = sum_j s_j 2^(k_j - K) (exact power-of-two rescaling)
   // (soft targets: also sum_j alpha_q_j pc_j = sum_v q_v z_v / tau)
   m = s_m[rl];
@@ -1009,15 +997,11 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
         if (owned) {
           const int jy = (int)(yl / kPartialWidth);
           const float ky = kq_of(a.pm[(int64_t)jy * a.ldr + row]);
-          if (a.rescaled_rows) {
-            // what the dZ pass leaves at the target's column: the stored
-            // value times 2^(k_y - K), rounded to the input dtype
-            float pv = __builtin_ldexpf(a.ptgt[row], (int)(ky - K));
-            if (a.round_bf16) pv = Elem<bf16>::to_f32(Elem<bf16>::from_f32(pv));
-            c = dzt - beta * pv;
-          } else {
-            c = dzt - beta * __builtin_amdgcn_exp2f(ky - K) * a.ptgt[row];
-          }
+          // what the dZ pass leaves at the target's column: the stored
+          // value times 2^(k_y - K), rounded to the input dtype
+          float pv = __builtin_ldexpf(a.ptgt[row], (int)(ky - K));
+          if (a.round_bf16) pv = Elem<bf16>::to_f32(Elem<bf16>::from_f32(pv));
+          c = dzt - beta * pv;
         }
         a.corr[row] = c;
       }
@@ -1041,14 +1025,13 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   // (for the dX contraction) the shift K - k_j as a byte
   if (live && a.backward) {
     const float Kr = s_k[rl], beta = s_beta[rl], sc = s_sc[rl];
-    const int64_t perm = shift_slot(row);
     auto put = [&](int j, float mj, float sj) {
       const int64_t o = (int64_t)j * a.ldr + row;
       const float kj = kq_of(mj);
       a.pm[o] = (sj != 0.f) ? beta * __builtin_amdgcn_exp2f(kj - Kr) : 0.f;
       if (a.shift)
-        a.shift[(int64_t)j * a.ldr + perm] =
-            (uint8_t)((sj != 0.f) ? __builtin_fminf(__builtin_fmaxf(Kr - kj, 0.f), 255.f) : 255.f);
+        a.shift[o] =
+            (uint8_t)((sj != 0.f) ? __builtin_fminf(__builtin_fmaxf(Kr - kj, 0.f), 255.f) : 0.f);
       if (a.alpha_q) a.alpha_q[o] *= sc;
     };
 #pragma unroll
@@ -1110,7 +1093,7 @@ __global__ void __launch_bounds__(256) fixup_kernel(FixupArgs a) {
       const T* pe = (const T*)&pv;
       if (a.rescale_shift && v < a.V) {
         keep[p] = pv;
-        kshift[p] = a.rescale_shift[(int64_t)(v / kPartialWidth) * a.ldr + shift_slot(t)];
+        kshift[p] = a.rescale_shift[(int64_t)(v / kPartialWidth) * a.ldr + t];
       }
       const float al = (v < a.V) ? a.alpha[(int64_t)(v / kPartialWidth) * a.ldr + t] : 0.f;
       const int64_t yt = a.y[t];
@@ -1205,7 +1188,7 @@ __global__ void __launch_bounds__(256) fixup_bf16_kernel(FixupArgs a) {
     pv[p] = *(const uint4*)(P + (int64_t)tc * a.ldp + v);
     al[p] = a.alpha[aoff + tc];
     yt[p] = a.y[tc];
-    sb[p] = a.rescale_shift ? a.rescale_shift[aoff + shift_slot(tc)] : 0;
+    sb[p] = a.rescale_shift ? a.rescale_shift[aoff + tc] : 0;
   }
   uint4 ov[8];
 #pragma unroll

@@ -1,16 +1,21 @@
-"""GPU parity of the dZ-in-dX mode (FLCE_FLAG_DZ_IN_DX) against the oracle.
+"""GPU parity of the two ways dZ reaches the dX contraction, against the
+oracle.
 
-In this mode the dX contraction reads the stored exponentials and forms
-dZ itself: the tile references are multiples of 2^32, the dZ pass rewrites
-the row segments whose reference lies below their row's (so that each row's
-exponentials share one), and each output row is finished with a per-row
-scale plus the target's correction times that row of W.  The cases cover every
-instantiation that path has: 256-wide tiles split in K (partials finished by
-the split-K sum) and written directly, 128-wide tiles split and direct, fp32,
-W read as stored, several chunks with dW groups, the outlier-row head with
-its wide logit range, ignored runs, targets at both vocabulary ends, an
-ignore index that is a real id, and a vocabulary shard's backward (the
-given-lse path).
+Default: the dX contraction reads the stored exponentials and forms dZ
+itself.  Their tile references are powers 2^(32 j); the dZ pass rewrites in
+place the row segments whose reference lies below their row's (so that each
+row's exponentials share one) and writes dZ^T; each output row of dX is
+finished with the row's scale plus the target's correction times that row of
+W.  FLCE_FLAG_DZ_IN_PLACE: the dZ pass writes dZ over the exponentials and
+the dX contraction reads it.
+
+The rest of the GPU suite runs the default; the cases here run the in-place
+mode over every instantiation both paths have (256-wide tiles split in K and
+written directly, 128-wide tiles split and direct, fp32, W read as stored,
+several chunks with dW groups, the outlier-row head with its wide logit
+range, ignored runs, targets at both vocabulary ends, an ignore index that is
+a real id, a vocabulary shard's backward), compare the two modes, and give
+the default rows whose tiles straddle a reference.
 """
 import dataclasses
 
@@ -25,16 +30,16 @@ from oracle import flce_reference
 pytestmark = pytest.mark.gpu
 
 
-def run(wl, chunk, dw_chunks=0, weight_copy=True, dz_in_dx=True, inp=None):
+def run(wl, chunk, dw_chunks=0, weight_copy=True, dz_in_place=True, inp=None):
     import torch
     if inp is None:
         inp = workloads.generate(wl)
     X, W, y = workloads.to_torch(inp, "cuda")
     op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=chunk,
                                       dw_chunks=dw_chunks, weight_copy=weight_copy,
-                                      dz_in_dx=dz_in_dx)
-    print(f"[gpu-dz-in-dx] {wl.name} T={wl.T} H={wl.H} V={wl.V} {wl.dtype} chunk={op.chunk_tokens} "
-          f"G={op.dw_chunks} wcopy={weight_copy} dz_in_dx={dz_in_dx}", flush=True)
+                                      dz_in_place=dz_in_place)
+    print(f"[gpu-dz-modes] {wl.name} T={wl.T} H={wl.H} V={wl.V} {wl.dtype} chunk={op.chunk_tokens} "
+          f"G={op.dw_chunks} wcopy={weight_copy} dz_in_place={dz_in_place}", flush=True)
     out = op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction)
     torch.cuda.synchronize()
     op.close()
@@ -60,31 +65,28 @@ CASES = [
 @pytest.mark.parametrize("wl,chunk,g,wcopy", CASES,
                          ids=[f"{c[0].name}-C{c[1]}-G{c[2]}" + ("" if c[3] else "-no-wcopy")
                               for c in CASES])
-def test_dz_in_dx_vs_oracle(wl, chunk, g, wcopy):
+def test_dz_in_place_vs_oracle(wl, chunk, g, wcopy):
     inp, out = run(wl, chunk, g, wcopy)
     ref = flce_reference(inp.X, inp.W, inp.y, wl.ignore_index, wl.reduction)
     check_full(out, ref, inp, wl)
 
 
-def test_dz_in_dx_agrees_with_the_dz_pass():
-    # both modes compute the same gradients up to bf16 rounding of dZ; argmax
-    # and counts are identical, while lse and the loss differ by rounding only
-    # (the tile references are coarser here, so lse = (K + log2 sum) ln 2 is
-    # summed from other parts)
+def test_the_two_modes_agree():
+    # the same gradients up to bf16 rounding of dZ (formed in registers
+    # against written out); lse, argmax, counts and the loss come from the
+    # same kernels and are identical
     wl = workloads.WORKLOADS[4].with_shape(T=1500, H=512, V=20000, seed=80)
     inp = workloads.generate(wl)
     _, a = run(wl, 512, inp=inp)
-    _, b = run(wl, 512, inp=inp, dz_in_dx=False)
-    for k in ("argmax", "n_valid"):
+    _, b = run(wl, 512, inp=inp, dz_in_place=False)
+    for k in ("loss", "lse", "argmax", "n_valid"):
         assert np.array_equal(to_np(a[k]), to_np(b[k])), k
-    assert np.abs(to_np(a["lse"]) - to_np(b["lse"])).max() <= 2e-5
-    assert abs(float(a["loss"].item()) - float(b["loss"].item())) <= 1e-5 * abs(float(b["loss"].item()))
     assert rel_frob(to_np(a["dX"]), to_np(b["dX"])) < 1e-2
     assert rel_frob(to_np(a["dW"]), to_np(b["dW"])) < 1e-2
 
 
 @pytest.mark.parametrize("reduction", ["mean", "sum"])
-def test_dz_in_dx_targets_at_vocab_ends_and_real_ignore_id(reduction):
+def test_dz_in_place_targets_at_vocab_ends_and_real_ignore_id(reduction):
     wl = dataclasses.replace(workloads.WORKLOADS[2].with_shape(T=600, H=128, V=3000, seed=81),
                              ignore_index=7, ignore_frac=0.0, reduction=reduction)
     inp = workloads.generate(wl)
@@ -95,7 +97,8 @@ def test_dz_in_dx_targets_at_vocab_ends_and_real_ignore_id(reduction):
     check_full(out, flce_reference(inp.X, inp.W, inp.y, wl.ignore_index, wl.reduction), inp, wl)
 
 
-def test_dz_in_dx_vocab_shard_backward():
+@pytest.mark.parametrize("dz_in_place", [True, False])
+def test_vocab_shard_backward(dz_in_place):
     # a shard's backward from a given lse: the row scale comes from that lse
     import torch
     wl = workloads.WORKLOADS[4].with_shape(T=600, H=512, V=20000, seed=82)
@@ -107,7 +110,8 @@ def test_dz_in_dx_vocab_shard_backward():
     dW = np.zeros((wl.V, wl.H))
     bounds = [0, 7000, 13001, wl.V]
     for v0, v1 in zip(bounds[:-1], bounds[1:]):
-        op = flce.FusedLinearCrossEntropy(wl.H, v1 - v0, wl.dtype, chunk_tokens=256, dz_in_dx=True)
+        op = flce.FusedLinearCrossEntropy(wl.H, v1 - v0, wl.dtype, chunk_tokens=256,
+                                          dz_in_place=dz_in_place)
         Ws = W[v0:v1].contiguous()
         dXp, dWs = op.shard_backward(X, Ws, y, lse, v0, wl.V, wl.ignore_index, wl.reduction)
         torch.cuda.synchronize()
@@ -163,5 +167,5 @@ def test_rows_whose_tiles_straddle_a_reference(dtype):
     tile_mass = p.reshape(wl.T, -1, 128).sum(axis=2)
     low = np.where(kq < kq.max(axis=1, keepdims=True), tile_mass, 0).sum(axis=1)
     assert np.median(low[mixed] / tile_mass[mixed].sum(axis=1)) > 0.1
-    _, out = run(wl, 256, inp=inp)
+    _, out = run(wl, 256, inp=inp, dz_in_place=False)
     check_full(out, flce_reference(inp.X, inp.W, inp.y, wl.ignore_index, wl.reduction), inp, wl)

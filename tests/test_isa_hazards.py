@@ -4,8 +4,7 @@
 The MFMAs are inline asm, which the compiler's hazard recognizer does not
 look inside, so the distances the hardware needs are kept by the code:
   * two wait states between a VALU write of a VGPR and an MFMA reading it
-    as a source (the exponent shifts of the dZ-in-dX mode, and any register
-    copy the compiler places before an asm MFMA);
+    as a source (any register copy the compiler places before an asm MFMA);
   * a drain between the last MFMA of a K loop and the first non-MFMA read of
     its accumulators (s_nop 7 three times in the last iteration and four
     times after the loop; the check asks for 18, what a 16-pass MFMA result
