@@ -68,21 +68,22 @@ struct flce_handle {
   int splitk_alloc = 1;  // split-K planes the workspace holds for a full chunk
   bool w_copy = true;      // dX reads W^T (a copy made per call) or W as stored
   bool dz_in_dx = true;    // dZ formed inside the dX contraction (not FLCE_FLAG_DZ_IN_PLACE)
+  // ... and the dW contraction reads the exponentials as stored, G chunks of
+  // them side by side (bf16, hard targets, G C Vpad 2 < 2^31 bytes): no dZ^T
+  bool dw_reads_p = false;
   size_t ws_bytes = 0;
   char* ws = nullptr;
   void* Wt = nullptr;      // W^T           [H x Vpad]
-  void* P = nullptr;       // exp / dZ      [C x Vpad]
-  void* Pt = nullptr;      // dZ^T of G chunks [Vpad x G*C]
+  void* P = nullptr;       // exp / dZ      [C x Vpad], or [G*C x Vpad] (dw_reads_p)
+  void* Pt = nullptr;      // dZ^T of G chunks [Vpad x G*C] (not with dw_reads_p)
   void* Xt = nullptr;      // X^T of G chunks  [H x G*C]
   float* pm = nullptr;     // tile max / alpha [nt x C], tile-major
   float* ps = nullptr;     // tile sum      [nt x C]
   int* pa = nullptr;       // tile argmax   [nt x C]
   float* ztgt = nullptr;   // [C]
   float* dzt = nullptr;    // [C]
-  float* ptgt = nullptr;   // [C] stored exponential at the target's column
-  float* beta = nullptr;   // [C] row scale of dZ inside the dX contraction
+  float* beta = nullptr;   // [C], or [G*C]: row scale of dZ inside the contractions
   float* corr = nullptr;   // [C] target correction of the dX rows
-  uint8_t* shift = nullptr;  // [nt x C] per-(tile, row) exponent shifts
   double* loss_part = nullptr;  // [C / kFinalizeRows]
   float* splitk = nullptr;      // [splitk_alloc x C x H]
   void* Pq = nullptr;           // teacher exp(z_T / tau - m_tile) [C x Vpad]
@@ -238,7 +239,7 @@ namespace {
 // Byte offsets of the workspace buffers of one handle, from (H, V, C, G,
 // dtype, weight copy, teacher) only.
 struct Layout {
-  size_t Wt, P, Pt, Xt, pm, ps, pa, zt, dz, pt, be, co, sh, lp, sk, sc, cp, Pq, pmq, psq, paq, pc;
+  size_t Wt, P, Pt, Xt, pm, ps, pa, zt, dz, be, co, lp, sk, sc, cp, Pq, pmq, psq, paq, pc;
   size_t total;
 };
 
@@ -276,6 +277,9 @@ flce_status_t configure(const flce_config_t* cfg, int64_t Ht, flce_handle* h, La
   h->w_copy = !no_wcopy;
   h->dz_in_dx = (cfg->flags & FLCE_FLAG_DZ_IN_PLACE) == 0;
   h->Vpad = round_up(V, 256);
+  // the dW GEMM's one buffer descriptor spans the G chunks' exponentials
+  h->dw_reads_p = h->dz_in_dx && dt == Dt::BF16 && Ht == 0 &&
+                  G * C * h->Vpad * 2 < ((int64_t)1 << 31);
   h->nt = cdiv64(V, kPartialWidth);
   {
     TileCfg tc;
@@ -291,18 +295,16 @@ flce_status_t configure(const flce_config_t* cfg, int64_t Ht, flce_handle* h, La
     return o;
   };
   L->Wt = h->w_copy ? carve((size_t)H * h->Vpad * es) : 0;
-  L->P = carve((size_t)C * h->Vpad * es);
-  L->Pt = carve((size_t)h->Vpad * h->G * C * es);
+  L->P = carve((size_t)(h->dw_reads_p ? h->G * C : C) * h->Vpad * es);
+  L->Pt = h->dw_reads_p ? 0 : carve((size_t)h->Vpad * h->G * C * es);
   L->Xt = carve((size_t)H * h->G * C * es);
   L->pm = carve((size_t)C * h->nt * 4);
   L->ps = carve((size_t)C * h->nt * 4);
   L->pa = carve((size_t)C * h->nt * 4);
   L->zt = carve((size_t)C * 4);
   L->dz = carve((size_t)C * 4);
-  L->pt = carve((size_t)C * 4);
-  L->be = carve((size_t)C * 4);
+  L->be = carve((size_t)(h->dw_reads_p ? h->G * C : C) * 4);
   L->co = carve((size_t)C * 4);
-  L->sh = carve((size_t)C * h->nt);
   L->lp = carve((size_t)cdiv64(C, kFinalizeRows) * 8);
   L->sk = h->splitk_alloc > 1 ? carve((size_t)h->splitk_alloc * C * H * 4) : 0;
   L->sc = carve(64);
@@ -323,17 +325,15 @@ void bind_workspace(flce_handle* h, const Layout& L, char* base) {
   h->ws = base;
   h->Wt = h->w_copy ? base + L.Wt : nullptr;
   h->P = base + L.P;
-  h->Pt = base + L.Pt;
+  h->Pt = h->dw_reads_p ? nullptr : base + L.Pt;
   h->Xt = base + L.Xt;
   h->pm = (float*)(base + L.pm);
   h->ps = (float*)(base + L.ps);
   h->pa = (int*)(base + L.pa);
   h->ztgt = (float*)(base + L.zt);
   h->dzt = (float*)(base + L.dz);
-  h->ptgt = (float*)(base + L.pt);
   h->beta = (float*)(base + L.be);
   h->corr = (float*)(base + L.co);
-  h->shift = (uint8_t*)(base + L.sh);
   h->loss_part = (double*)(base + L.lp);
   h->splitk = h->splitk_alloc > 1 ? (float*)(base + L.sk) : nullptr;
   h->nvalid = (int64_t*)(base + L.sc);
@@ -521,11 +521,19 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
     // the batch's last is full, so the slots of a group are contiguous in K
     const int64_t gs = c % G;
     const bool last = t0 + Cc >= T;
+    // dZ formed inside the contractions (hard targets); dW reading the
+    // exponentials, each chunk's in its own slot of the G-chunk buffer
+    const bool fused = !soft && h->dz_in_dx;
+    const bool dw_p = fused && h->dw_reads_p;
+    char* const Pc = (char*)h->P + (dw_p ? (size_t)gs * C * Vpad * es : 0);
+    float* const beta_c = h->beta + (dw_p ? gs * C : 0);
 
     // X^T of the whole group at its first chunk (X is an input, all of it
     // available): one transpose per dW GEMM; the previous group's dW GEMM,
-    // earlier in the stream, has finished reading the buffer
-    if (gs == 0) {
+    // earlier in the stream, has finished reading the buffer.  When dW reads
+    // the exponentials, X^T carries the rows' beta and is made at the
+    // group's last chunk instead, once all of them are known.
+    if (gs == 0 && !dw_p) {
       const int64_t Cg = (T - t0 < GC) ? (T - t0) : GC;
       FLCE_LAUNCH(K_TRANSPOSE_X, launch_transpose(dt, Xc, (int)Cg, (int)H, H, h->Xt, GC,
                                                   (int)round_up(Cg, 64), s));
@@ -581,7 +589,7 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
     la.M = (int)Cc;
     la.V = (int)V;
     la.H = (int)H;
-    la.P = h->P;
+    la.P = Pc;
     la.ldp = Vpad;
     la.pm = h->pm;
     la.ps = h->ps;
@@ -595,8 +603,6 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       la.inv_temp = soft->inv_temp;
       la.Pq = h->Pq;
       la.pc = h->pc;
-    } else if (h->dz_in_dx) {
-      la.ptgt = h->ptgt;
     }
     FLCE_LAUNCH(K_LOGITS, launch_logits(dt, la, s));
 
@@ -625,23 +631,26 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       fa.alpha_q = h->pmq;
       fa.alpha_mul = soft->inv_temp;
       fa.no_target = true;
-    } else if (h->dz_in_dx) {
-      // dZ is formed inside the dX contraction (row scale, target
-      // correction) from the stored exponentials, once the dZ pass below has
-      // brought each row's to one reference; that pass writes only dZ^T
-      fa.beta = h->beta;
-      fa.shift = h->shift;
+    } else if (fused) {
+      // dZ is formed inside the contractions from the stored exponentials,
+      // which the merge brings to one reference per row (and whose target
+      // column it sets); the row scale and target correction come out
+      fa.P = Pc;
+      fa.ldp = Vpad;
+      fa.p_es = (int)es;
+      fa.beta = beta_c;
       fa.corr = h->corr;
-      fa.ptgt = h->ptgt;
-      fa.round_bf16 = dt == Dt::BF16;
     }
     fa.backward = true;
     fa.loss_part = h->loss_part;
     fa.first_chunk = c == 0;
     FLCE_LAUNCH(K_FINALIZE, launch_finalize(fa, s));
 
+    // The dZ pass: dZ^T for the dW contraction (with dZ over the
+    // exponentials too unless dZ is formed inside dX); none when dW reads
+    // the exponentials themselves
     FixupArgs xa{};
-    xa.P = h->P;
+    xa.P = Pc;
     xa.ldp = Vpad;
     xa.Pt = (char*)h->Pt + (size_t)gs * C * es;
     xa.ldpt = GC;
@@ -661,14 +670,13 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       xa.Pq = h->Pq;
       xa.alpha_q = h->pmq;
     }
-    xa.write_rows = soft != nullptr || !h->dz_in_dx;
-    if (!soft && h->dz_in_dx) xa.rescale_shift = h->shift;
-    FLCE_LAUNCH(K_FIXUP, launch_fixup(dt, xa, s));
+    xa.write_rows = !fused;
+    if (!dw_p) FLCE_LAUNCH(K_FIXUP, launch_fixup(dt, xa, s));
 
     // dX_c = dZ W   (M = Cc, N = H, K = vocabulary); without soft targets
     // A holds the exponentials and dZ is formed in the contraction
     DxFuse fz{};
-    fz.beta = h->beta;
+    fz.beta = beta_c;
     fz.corr = h->corr;
     fz.y = yc;
     fz.ignore_index = ignore_index;
@@ -676,7 +684,7 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
     fz.V = (int)V;
     fz.W = W;
     fz.ldw = H;
-    const DxFuse* fuse = (!soft && h->dz_in_dx) ? &fz : nullptr;
+    const DxFuse* fuse = fused ? &fz : nullptr;
     {
       TileCfg tc;
       int splits;
@@ -684,7 +692,7 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       if (max_splits > 8) max_splits = 8;
       plan_gemm(Cc, H, KV, max_splits, &tc, &splits);
       GemmOutArgs ga{};
-      ga.A = h->P;
+      ga.A = Pc;
       ga.lda = Vpad;
       if (h->w_copy) {
         ga.B = h->Wt;
@@ -728,13 +736,28 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       int splits;
       plan_gemm(V, H, Kg, 1, &tc, &splits);
       GemmOutArgs ga{};
-      ga.A = h->Pt;
-      ga.lda = GC;
+      if (dw_p) {
+        // dW = sum_t P_t^T (beta_t X_t): A is the group's exponentials as
+        // stored (token rows, K = its tokens exactly: rows past them read as
+        // zero), B the rows' X^T scaled by beta; the target columns hold
+        // dZ / beta (set by the merge)
+        const int64_t g0 = t0 - gs * C;  // the group's first token
+        const int64_t Cg = gs * C + Cc;
+        FLCE_LAUNCH(K_TRANSPOSE_X,
+                    launch_transpose(dt, (const char*)X + (size_t)g0 * H * es, (int)Cg, (int)H, H,
+                                     h->Xt, GC, (int)round_up(Cg, 64), s, h->beta));
+        ga.A = h->P;
+        ga.lda = Vpad;
+        ga.a_stored = true;
+      } else {
+        ga.A = h->Pt;
+        ga.lda = GC;
+      }
       ga.B = h->Xt;
       ga.ldb = GC;
       ga.M = (int)V;
       ga.N = (int)H;
-      ga.K = (int)Kg;
+      ga.K = (int)(dw_p ? gs * C + Cc : Kg);
       ga.out = dW;
       ga.ldo = H;
       ga.out_f32 = true;

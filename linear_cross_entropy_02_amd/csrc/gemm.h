@@ -55,6 +55,11 @@
 // runs 8-12 % slower than with a transposed copy of B; it saves the copy's
 // memory.
 //
+// AT (bf16 only): the same for A, given as K rows of M contiguous elements
+// (dW = dZ^T X reading the exponentials as the logits epilogue stored them:
+// token rows of vocabulary columns), with A stages of 64 k-rows of BM
+// elements and the same transposing fragment reads.
+//
 #pragma once
 
 #include "common.h"
@@ -298,7 +303,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 //       the B DMAs of the stage after next threaded through them.
 // The wave never waits on LDS after the barrier: the fragments its MFMAs
 // need were read before it.
-template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false>
+template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false, bool AT = false>
 __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi epi) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the launch stub
   using G = TileGeom<BM, BN, WAVES>;
@@ -309,7 +314,9 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
   constexpr int B_INS = BN / (8 * WAVES);
   constexpr int FM = G::FM, FN = G::FN;
   static_assert(!BT || (sizeof(T) == 2 && WAVES == 4), "stored-layout B: bf16, 4 waves");
-  constexpr int UPR = BN / 8;  // BT: 16-byte units per k-row of a B stage
+  static_assert(!AT || (sizeof(T) == 2 && WAVES == 4), "stored-layout A: bf16, 4 waves");
+  constexpr int UPR = BN / 8;   // BT: 16-byte units per k-row of a B stage
+  constexpr int UPRA = BM / 8;  // AT: the same for an A stage
   extern __shared__ uint4 lds[];  // G::kLdsBytes, sized at launch
 
   const TileCoord tc = map_tile(g);
@@ -327,8 +334,10 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
   const int nk = (k_end - k_begin + BK - 1) / BK;
 
   const int a_rows = min(BM, g.M - m0), b_rows = min(BN, g.N - n0);
-  const i4v rA =
-      make_rsrc((const T*)g.A + (int64_t)m0 * g.lda, (uint32_t)((int64_t)a_rows * g.lda * ES));
+  // AT: from A's column m0 over all K rows (the host keeps K lda ES < 2^31)
+  const i4v rA = AT ? make_rsrc((const T*)g.A + m0, (uint32_t)((int64_t)g.K * g.lda * ES))
+                    : make_rsrc((const T*)g.A + (int64_t)m0 * g.lda,
+                                (uint32_t)((int64_t)a_rows * g.lda * ES));
   // BT: from B's column n0 over all K rows (the host keeps K ldb ES < 2^31,
   // below the out-of-range offset)
   const i4v rB = BT ? make_rsrc((const T*)g.B + n0, (uint32_t)((int64_t)g.K * g.ldb * ES))
@@ -342,10 +351,24 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
   // same in all of its loads.
   uint32_t a_off[A_INS], b_off[B_INS];
   const int kv_lane = (lane & 7) ^ ((lane >> 3) & 7);
+  // AT: as BT below, for the A stages (a_krow, a_min: the unit's k-row and
+  // whether its columns lie inside M)
+  int a_krow[A_INS];
+  bool a_min[A_INS];
 #pragma unroll
   for (int j = 0; j < A_INS; ++j) {
-    const int row = wave * (BM / WAVES) + 8 * j + (lane >> 3);
-    a_off[j] = (uint32_t)(((int64_t)row * g.lda + kv_lane * EPV) * ES);
+    if constexpr (!AT) {
+      const int row = wave * (BM / WAVES) + 8 * j + (lane >> 3);
+      a_off[j] = (uint32_t)(((int64_t)row * g.lda + kv_lane * EPV) * ES);
+      a_krow[j] = 0;
+      a_min[j] = true;
+    } else {
+      const int p = wave * (16 * UPRA) + 64 * j + lane;
+      const int r = p / UPRA, u = (p % UPRA) ^ tr_swz(p / UPRA);
+      a_off[j] = (uint32_t)(((int64_t)r * g.lda + 8 * u) * ES);
+      a_krow[j] = r;
+      a_min[j] = m0 + 8 * u < g.M;
+    }
   }
   // BT: slot p of a B stage holds k-row p / UPR, unit (p % UPR) ^ tr_swz(row);
   // b_krow is that k-row, b_nin whether the unit's columns lie inside N.
@@ -387,8 +410,15 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
   // buffer `bb` (0..1).  Past the end of K every offset is out of range and
   // the buffer fills with zeros.
   auto issue_a = [&](int ab, int k0, int j) {
-    const bool kin = kv_lane * EPV < k_end - k0;
-    dma16(rA, lds_a + (uint32_t)ab * G::kABufBytes + 1024 * j, kin ? a_off[j] : kOobOffset, k0 * ES);
+    if constexpr (!AT) {
+      const bool kin = kv_lane * EPV < k_end - k0;
+      dma16(rA, lds_a + (uint32_t)ab * G::kABufBytes + 1024 * j, kin ? a_off[j] : kOobOffset,
+            k0 * ES);
+    } else {
+      const bool in = a_min[j] && a_krow[j] < k_end - k0;
+      dma16(rA, lds_a + (uint32_t)ab * G::kABufBytes + 1024 * j, in ? a_off[j] : kOobOffset,
+            (uint32_t)((int64_t)k0 * g.lda * ES));
+    }
   };
   auto issue_b = [&](int bb, int k0, int j) {
     if constexpr (!BT) {
@@ -412,13 +442,26 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
         lds_read_tr16(buf + (k0r + 4) * (BN * 2) + ((u ^ tr_swz(k0r + 4)) << 4) + (tr_q & 1) * 8);
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
   };
+  // AT fragment: rows m16 .. m16 + 15 of the stage in A buffer ab, substep s
+  auto read_a_tr = [&](int ab, int m16, int s) -> uint4 {
+    const uint32_t buf = lds_base + (uint32_t)ab * G::kABufBytes;
+    const int u = (m16 >> 3) + (tr_q >> 1);
+    const int k0r = 32 * s + 8 * tr_g + tr_i;
+    const uint2 lo = lds_read_tr16(buf + k0r * (BM * 2) + ((u ^ tr_swz(k0r)) << 4) + (tr_q & 1) * 8);
+    const uint2 hi =
+        lds_read_tr16(buf + (k0r + 4) * (BM * 2) + ((u ^ tr_swz(k0r + 4)) << 4) + (tr_q & 1) * 8);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  };
   // Fragment read r of substep s from A buffer ab / B buffer bb: r < FM
   // reads A fragment r, else B fragment r - FM.
   auto read_one = [&](int ab, int bb, int s, int r, uint4 (&fa)[FM], uint4 (&fb)[FN]) {
     const int kv = 4 * s + (lane >> 4);
-    if (r < FM)
-      fa[r] = lds[ab * (G::kABufBytes / 16) + swz(wm * G::WM + 16 * r + (lane & 15), kv)];
-    else if constexpr (!BT)
+    if (r < FM) {
+      if constexpr (!AT)
+        fa[r] = lds[ab * (G::kABufBytes / 16) + swz(wm * G::WM + 16 * r + (lane & 15), kv)];
+      else
+        fa[r] = read_a_tr(ab, wm * G::WM + 16 * r, s);
+    } else if constexpr (!BT)
       fb[r - FM] = lds[(3 * G::kABufBytes + bb * G::kBBufBytes) / 16 +
                        swz(wn * G::WN + 16 * (r - FM) + (lane & 15), kv)];
     else

@@ -33,9 +33,6 @@ struct LogitsArgs {
   // ([M x ldp], input dtype) and, per (tile, row), sum_v P_T z / tau out.
   const void* Pq = nullptr;
   float* pc = nullptr;
-  // nullable: per row, the stored exponential at the target's column, as
-  // fp32
-  float* ptgt = nullptr;
 };
 // The stored exponentials of a (row, 128-column tile) are exp2(z log2(e) /
 // tau - k) with k = 32 ceil(m log2(e) / 32), m the tile's max of z / tau:
@@ -81,6 +78,10 @@ struct GemmOutArgs {
   // B as stored, K rows of N contiguous elements (ldb >= N), rather than
   // N x K: bf16 only, not accumulating, K * ldb * 2 < 2^31 bytes.
   bool b_stored = false;
+  // A as stored, K rows of M contiguous elements (lda >= M), rather than
+  // M x K: bf16 only, the accumulating fp32 store (dW), K * lda * 2 < 2^31
+  // bytes; K need not be a multiple of 8 (rows past K read as zero).
+  bool a_stored = false;
   // dX with dZ formed inside the contraction (not accumulating); with
   // splits > 1 the partial planes are raw and launch_splitk_reduce applies it.
   const DxFuse* fuse = nullptr;
@@ -95,8 +96,11 @@ hipError_t launch_count(const int64_t* y, int64_t T, int64_t ignore_index, int64
                         int64_t* n_valid_out, long long* part, hipStream_t s);
 
 // dst[c][r] = src[r][c] for r < rows, 0 for rows <= r < rows_out; c < cols.
+// row_scale (nullable, [rows]): each source row is multiplied by its entry
+// on the way, rounded to the dtype.
 hipError_t launch_transpose(Dt dt, const void* src, int rows, int cols, int64_t ld_src,
-                            void* dst, int64_t ld_dst, int rows_out, hipStream_t s);
+                            void* dst, int64_t ld_dst, int rows_out, hipStream_t s,
+                            const float* row_scale = nullptr);
 
 struct FinalizeArgs {
   int M, nt, V;
@@ -128,21 +132,20 @@ struct FinalizeArgs {
   double* loss_part;     // one slot per block_rows rows; nullable
   int first_chunk;
   int block_rows = 8;    // finalize_rows(nt, C): 8 or 32
-  // Backward with dZ formed inside the dX contraction (all nullable):
-  //   beta  [M]        per-row scale: dZ_tv = beta_t 2^-s_tj P_tv off the target
-  //   shift [nt x ldr] bytes s_tj = K_t - k_tj, tile-major like the partials
-  //                    (0 for an empty tile, 255 for 255 and more): the dZ
-  //                    pass rewrites P_tv as round(2^-s P_tv) where s != 0,
-  //                    so that row t's exponentials share the reference 2^K_t
-  //   corr  [M]        dzt_t - beta_t round(2^-s P_t,y): the target's
-  //                    correction (0 when the target is ignored or not in
-  //                    these columns), round() to the input dtype
-  //   ptgt  [M]        in: the stored exponential at the target's column
+  // Backward with dZ formed inside the dX contraction (P non-null): the
+  // merge brings each row's stored exponentials to one reference 2^K_t,
+  // rewriting in place the tiles whose reference lies below it, writes the
+  // target's column as round(dzt / beta) in the input dtype, and
+  //   beta  [M]  per-row scale: dZ_tv = beta_t P_tv (target included)
+  //   corr  [M]  dzt_t - beta_t round(dzt_t / beta_t): what the dX
+  //              contraction adds times W's target row (0 when the target is
+  //              ignored or not in these columns)
+  // while pm becomes beta for every tile (the factor a dZ pass applies).
+  void* P = nullptr;  // [M x ldp], p_es bytes per element
+  int64_t ldp = 0;
+  int p_es = 2;
   float* beta = nullptr;
-  uint8_t* shift = nullptr;
   float* corr = nullptr;
-  const float* ptgt = nullptr;
-  bool round_bf16 = false;    // the input dtype is bf16
 };
 // Rows per finalize block, hence rows per loss partial: 32 when rows hold
 // at most 256 partial tiles and a chunk of C rows still gives 256 blocks,
@@ -163,10 +166,7 @@ struct FixupArgs {
   const int64_t* y; int64_t ignore_index;
   int64_t y_shift;               // vocabulary id of column 0 (shard offset)
   bool no_target = false;        // soft targets: no one-hot column
-  // nullable (finalize's shift bytes, [nt x ldr]): rewrite, in place, the
-  // row segments whose tile reference lies below the row's as P 2^-s in the
-  // input dtype, so that each row's stored exponentials share one reference
-  const uint8_t* rescale_shift = nullptr;
+
   const void* Pq = nullptr;      // soft targets: teacher exponentials, subtracted
   const float* alpha_q = nullptr;  //   with this scale, [nt x ldr]
   bool write_rows = true;        // false: only dZ^T is written (P keeps the exponentials)

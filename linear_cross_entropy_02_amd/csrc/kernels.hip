@@ -97,7 +97,6 @@ struct LogitsEpi {
   int64_t y_shift;  // vocabulary id of column 0 (a vocabulary shard's offset)
   int M, V;
   bool store_p;  // false: partials and target logit only (forward-only calls)
-  float* ptgt;   // nullable: the stored exponential at the target's column
 
   template <int FM, int FN>
   __device__ __forceinline__ void init(f4 (&acc)[FM][FN], const EpiCoord&) const {
@@ -195,16 +194,6 @@ struct LogitsEpi {
         }
       sum += shfl_xor_f(sum, 16);
       sum += shfl_xor_f(sum, 32);
-      if (ptgt && toff[i] >= 0) {
-        // the value stored at the target's column, as the dX contraction reads it
-        const int tk = 4 * (toff[i] >> 4) + (toff[i] & 3);
-        float et = 0.f;
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) et = (4 * j + r == tk) ? acc[i][j][r] : et;
-        ptgt[row] = Elem<T>::to_f32(Elem<T>::from_f32(et));
-      }
       if (row < M) {
         if (g == 0 && ec.col0 < V) {
           const int64_t o = (int64_t)ptile * ldr + row;
@@ -393,7 +382,7 @@ __global__ void __launch_bounds__(256) tile_reduce_kernel(GemmShape g, const flo
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false>
+template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false, bool AT = false>
 static hipError_t run_gemm(const GemmShape& g0, const Epi& epi, hipStream_t s) {
   using G = TileGeom<BM, BN, WAVES>;
   GemmShape g = g0;
@@ -410,16 +399,16 @@ static hipError_t run_gemm(const GemmShape& g0, const Epi& epi, hipStream_t s) {
   if (g.tile_first < 0 || g.tile_first + g.tile_count > g.tiles_m * g.tiles_n)
     return hipErrorInvalidValue;
   const int nblk = g.tile_count * g.splits;
-  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, WAVES, Epi, BT>), dim3(nblk),
+  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, WAVES, Epi, BT, AT>), dim3(nblk),
                      dim3(G::kThreads), G::kLdsBytes, s, g, epi);
   return hipGetLastError();
 }
 
 // The GEMM kernels use more than the default 64 KB of dynamic LDS.
-template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false>
+template <typename T, int BM, int BN, int WAVES, class Epi, bool BT = false, bool AT = false>
 static hipError_t set_lds_attr() {
   using G = TileGeom<BM, BN, WAVES>;
-  return hipFuncSetAttribute((const void*)gemm_nt_kernel<T, BM, BN, WAVES, Epi, BT>,
+  return hipFuncSetAttribute((const void*)gemm_nt_kernel<T, BM, BN, WAVES, Epi, BT, AT>,
                              hipFuncAttributeMaxDynamicSharedMemorySize, G::kLdsBytes);
 }
 
@@ -446,7 +435,15 @@ static hipError_t setup_t() {
   if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<float, false>>()) != hipSuccess) return e;
   if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<float, true>>()) != hipSuccess) return e;
   if ((e = setup_fused_dx<T, false>()) != hipSuccess) return e;
-  if constexpr (std::is_same<T, bf16>::value) {  // dX reading W as stored
+  if constexpr (std::is_same<T, bf16>::value) {
+    // dW reading the exponentials as stored
+    if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<float, true>, false, true>()) != hipSuccess)
+      return e;
+    if ((e = set_lds_attr<T, 128, 128, 4, StoreEpi<float, true>, false, true>()) != hipSuccess)
+      return e;
+    if ((e = set_lds_attr<T, 256, 256, 4, TilePartialEpi<256, 256>, false, true>()) != hipSuccess)
+      return e;
+    // dX reading W as stored
     if ((e = setup_fused_dx<T, true>()) != hipSuccess) return e;
     if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<T, false>, true>()) != hipSuccess) return e;
     if ((e = set_lds_attr<T, 256, 256, 4, StoreEpi<float, false>, true>()) != hipSuccess) return e;
@@ -492,7 +489,6 @@ static hipError_t logits_run(const LogitsArgs& a, const GemmShape& g, hipStream_
   epi.M = a.M;
   epi.V = a.V;
   epi.store_p = a.P != nullptr;
-  epi.ptgt = a.ptgt;
   return run_gemm<T, 256, 256, 4>(g, epi, s);
 }
 
@@ -559,6 +555,57 @@ static hipError_t fused_dx(TileCfg tc, const GemmOutArgs& a, const GemmShape& g,
   return hipErrorInvalidValue;
 }
 
+// The plain grid of a store (not fused, B in the K-contiguous layout), A
+// K-contiguous or (AT, dW reading the exponentials as stored) as stored.
+template <typename T, typename TO, bool ACC, bool AT>
+static hipError_t grid_store(TileCfg tc, const GemmOutArgs& a, const GemmShape& g,
+                             const StoreEpi<TO, ACC>& epi, hipStream_t s) {
+  if constexpr (ACC) {
+    // The grid's last partial round (rem tiles, under half the CUs busy for
+    // a whole tile) is split 2-4 ways in K instead: the full rounds run as
+    // usual, the rem tiles' K-slices write fp32 partial tiles, and a pass
+    // sums them (with the old output) in a fixed order.  A 256-wide grid of
+    // under half a round splits whole that way rather than fall back to
+    // 128-wide tiles.
+    constexpr int BK = 8 * Elem<T>::kVec;
+    const int tiles = cdiv(a.M, 256) * cdiv(a.N, 256);
+    const int nfull = tiles / g_num_cus * g_num_cus, rem = tiles - nfull;
+    const int sp = rem > 0 ? min(4, g_num_cus / rem) : 0;
+    if (a.tail_part && g.splits == 1 && (nfull >= g_num_cus || (nfull == 0 && tc != TileCfg::T256)) &&
+        rem > 0 && 2 * rem <= g_num_cus && cdiv(a.K, BK) >= 8 * sp &&
+        (size_t)sp * rem * 256 * 256 * sizeof(float) <= a.tail_part_bytes) {
+      if (nfull > 0) {
+        GemmShape gm = g;
+        gm.tile_first = 0;
+        gm.tile_count = nfull;
+        hipError_t e = run_gemm<T, 256, 256, 4, StoreEpi<TO, ACC>, false, AT>(gm, epi, s);
+        if (e != hipSuccess) return e;
+      }
+      hipError_t e;
+      GemmShape gt = g;
+      gt.tile_first = nfull;
+      gt.tile_count = rem;
+      gt.splits = sp;
+      gt.k_per_split = cdiv(cdiv(a.K, BK), sp) * BK;
+      TilePartialEpi<256, 256> pe;
+      pe.part = a.tail_part;
+      pe.tile_count = rem;
+      if ((e = run_gemm<T, 256, 256, 4, TilePartialEpi<256, 256>, false, AT>(gt, pe, s)) != hipSuccess)
+        return e;
+      // the walk the GEMM used (run_gemm's own view of the grid)
+      gt.tiles_m = cdiv(a.M, 256);
+      gt.tiles_n = cdiv(a.N, 256);
+      gt.group_m = min(max(gt.group_m, 1), gt.tiles_m);
+      hipLaunchKernelGGL((tile_reduce_kernel<256, 256>), dim3(rem * (256 * 256 / 1024)),
+                         dim3(256), 0, s, gt, (const float*)a.tail_part, sp, (float*)a.out,
+                         a.ldo, (bool)(ACC && a.accumulate));
+      return hipGetLastError();
+    }
+  }
+  if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4, StoreEpi<TO, ACC>, false, AT>(g, epi, s);
+  return run_gemm<T, 256, 256, 4, StoreEpi<TO, ACC>, false, AT>(g, epi, s);
+}
+
 template <typename T, typename TO, bool ACC>
 static hipError_t store_t2(TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
   GemmShape g{};
@@ -596,49 +643,11 @@ static hipError_t store_t2(TileCfg tc, const GemmOutArgs& a, hipStream_t s) {
     }
     return hipErrorInvalidValue;
   }
-  if constexpr (ACC) {
-    // The grid's last partial round (rem tiles, under half the CUs busy for
-    // a whole tile) is split 2-4 ways in K instead: the full rounds run as
-    // usual, the rem tiles' K-slices write fp32 partial tiles, and a pass
-    // sums them (with the old output) in a fixed order.  A 256-wide grid of
-    // under half a round splits whole that way rather than fall back to
-    // 128-wide tiles.
-    constexpr int BK = 8 * Elem<T>::kVec;
-    const int tiles = cdiv(a.M, 256) * cdiv(a.N, 256);
-    const int nfull = tiles / g_num_cus * g_num_cus, rem = tiles - nfull;
-    const int sp = rem > 0 ? min(4, g_num_cus / rem) : 0;
-    if (a.tail_part && g.splits == 1 && (nfull >= g_num_cus || (nfull == 0 && tc != TileCfg::T256)) &&
-        rem > 0 && 2 * rem <= g_num_cus && cdiv(a.K, BK) >= 8 * sp &&
-        (size_t)sp * rem * 256 * 256 * sizeof(float) <= a.tail_part_bytes) {
-      if (nfull > 0) {
-        GemmShape gm = g;
-        gm.tile_first = 0;
-        gm.tile_count = nfull;
-        hipError_t e = run_gemm<T, 256, 256, 4>(gm, epi, s);
-        if (e != hipSuccess) return e;
-      }
-      hipError_t e;
-      GemmShape gt = g;
-      gt.tile_first = nfull;
-      gt.tile_count = rem;
-      gt.splits = sp;
-      gt.k_per_split = cdiv(cdiv(a.K, BK), sp) * BK;
-      TilePartialEpi<256, 256> pe;
-      pe.part = a.tail_part;
-      pe.tile_count = rem;
-      if ((e = run_gemm<T, 256, 256, 4>(gt, pe, s)) != hipSuccess) return e;
-      // the walk the GEMM used (run_gemm's own view of the grid)
-      gt.tiles_m = cdiv(a.M, 256);
-      gt.tiles_n = cdiv(a.N, 256);
-      gt.group_m = min(max(gt.group_m, 1), gt.tiles_m);
-      hipLaunchKernelGGL((tile_reduce_kernel<256, 256>), dim3(rem * (256 * 256 / 1024)),
-                         dim3(256), 0, s, gt, (const float*)a.tail_part, sp, (float*)a.out,
-                         a.ldo, (bool)(ACC && a.accumulate));
-      return hipGetLastError();
-    }
+  if (a.a_stored) {
+    if constexpr (std::is_same<T, bf16>::value && ACC) return grid_store<T, TO, ACC, true>(tc, a, g, epi, s);
+    return hipErrorInvalidValue;
   }
-  if (tc != TileCfg::T256) return run_gemm<T, 128, 128, 4>(g, epi, s);
-  return run_gemm<T, 256, 256, 4>(g, epi, s);
+  return grid_store<T, TO, ACC, false>(tc, a, g, epi, s);
 }
 
 template <typename T>
@@ -741,7 +750,8 @@ hipError_t launch_count(const int64_t* y, int64_t T, int64_t ignore_index, int64
 template <typename T>
 __global__ void __launch_bounds__(256) transpose_kernel(const T* __restrict__ src, int rows, int cols,
                                                         int64_t ld_src, T* __restrict__ dst,
-                                                        int64_t ld_dst, int rows_out) {
+                                                        int64_t ld_dst, int rows_out,
+                                                        const float* __restrict__ row_scale) {
   constexpr int EPV = Elem<T>::kVec;
   constexpr int VPR = 64 / EPV;              // vectors per 64-element row
   constexpr int PER = 64 * VPR / 256;        // vectors per thread
@@ -756,8 +766,10 @@ __global__ void __launch_bounds__(256) transpose_kernel(const T* __restrict__ sr
     uint4 val = {0u, 0u, 0u, 0u};
     if (gr < rows && gc < cols) val = *(const uint4*)(src + (int64_t)gr * ld_src + gc);
     const T* e = (const T*)&val;
+    const float sc = (row_scale && gr < rows) ? row_scale[gr] : 1.f;
 #pragma unroll
-    for (int k = 0; k < EPV; ++k) tile[r][cv * EPV + k] = e[k];
+    for (int k = 0; k < EPV; ++k)
+      tile[r][cv * EPV + k] = row_scale ? Elem<T>::from_f32(sc * Elem<T>::to_f32(e[k])) : e[k];
   }
   __syncthreads();
 #pragma unroll
@@ -781,7 +793,8 @@ __global__ void __launch_bounds__(256) transpose_kernel(const T* __restrict__ sr
 __global__ void __launch_bounds__(256) transpose_bf16_kernel(const uint16_t* __restrict__ src,
                                                              int rows, int cols, int64_t ld_src,
                                                              uint16_t* __restrict__ dst,
-                                                             int64_t ld_dst, int rows_out) {
+                                                             int64_t ld_dst, int rows_out,
+                                                             const float* __restrict__ row_scale) {
   __shared__ uint4 tile[64 * 32];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 256;
   const int tid = threadIdx.x;
@@ -793,6 +806,14 @@ __global__ void __launch_bounds__(256) transpose_bf16_kernel(const uint16_t* __r
     const int gr = r0 + r;
     uint4 val = make_uint4(0u, 0u, 0u, 0u);
     if (gr < rows && gc < cols) val = *(const uint4*)(src + (int64_t)gr * ld_src + gc);
+    if (row_scale && gr < rows) {  // row gr times its scale, rounded to bf16
+      float e[8];
+      unpack8_bf16(val, e);
+      const float sc = row_scale[gr];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) e[k] *= sc;
+      val = pack8_bf16(e);
+    }
     tile[r * 32 + (cv ^ ((r >> 3) & 7))] = val;
   }
   __syncthreads();
@@ -823,21 +844,21 @@ __global__ void __launch_bounds__(256) transpose_bf16_kernel(const uint16_t* __r
 }
 
 hipError_t launch_transpose(Dt dt, const void* src, int rows, int cols, int64_t ld_src, void* dst,
-                            int64_t ld_dst, int rows_out, hipStream_t s) {
+                            int64_t ld_dst, int rows_out, hipStream_t s, const float* row_scale) {
   if (rows_out <= 0 || cols <= 0) return hipSuccess;
   if (dt == Dt::BF16 && cols % 8 == 0 && rows_out % 8 == 0 && ld_src % 8 == 0 && ld_dst % 8 == 0) {
     dim3 grid(cdiv(rows_out, 64), cdiv(cols, 256));
     hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, (const uint16_t*)src, rows,
-                       cols, ld_src, (uint16_t*)dst, ld_dst, rows_out);
+                       cols, ld_src, (uint16_t*)dst, ld_dst, rows_out, row_scale);
     return hipGetLastError();
   }
   dim3 grid(cdiv(rows_out, 64), cdiv(cols, 64));
   if (dt == Dt::BF16)
     hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)src, rows, cols,
-                       ld_src, (bf16*)dst, ld_dst, rows_out);
+                       ld_src, (bf16*)dst, ld_dst, rows_out, row_scale);
   else
     hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s, (const float*)src, rows,
-                       cols, ld_src, (float*)dst, ld_dst, rows_out);
+                       cols, ld_src, (float*)dst, ld_dst, rows_out, row_scale);
   return hipGetLastError();
 }
 
@@ -865,6 +886,8 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   __shared__ float s_c[kFinSlices][kFinRows + 1];
   __shared__ int s_i[kFinSlices][kFinRows + 1];
   __shared__ float s_m[kFinRows], s_k[kFinRows], s_sc[kFinRows], s_beta[kFinRows];
+  __shared__ float s_dzt[kFinRows];
+  __shared__ int s_yl[kFinRows];
   __shared__ double s_nll[kFinRows];
   const int rl = threadIdx.x % kFinRows, sl = threadIdx.x / kFinRows;
   // a partial array row of 32 tokens (one 128-byte line) spans 32 / ROWS
@@ -990,21 +1013,8 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
       const float dzt = owned ? sc * (exp_fast(zt - lse) - 1.f) : 0.f;
       if (a.backward) a.dzt[row] = dzt;
       if (a.beta) a.beta[row] = beta;
-      if (a.corr) {
-        // the target column read by the dX contraction holds P_y 2^-s; its
-        // dZ must be dzt: the output row adds corr times W's target row
-        float c = 0.f;
-        if (owned) {
-          const int jy = (int)(yl / kPartialWidth);
-          const float ky = kq_of(a.pm[(int64_t)jy * a.ldr + row]);
-          // what the dZ pass leaves at the target's column: the stored
-          // value times 2^(k_y - K), rounded to the input dtype
-          float pv = __builtin_ldexpf(a.ptgt[row], (int)(ky - K));
-          if (a.round_bf16) pv = Elem<bf16>::to_f32(Elem<bf16>::from_f32(pv));
-          c = dzt - beta * pv;
-        }
-        a.corr[row] = c;
-      }
+      s_dzt[rl] = dzt;
+      s_yl[rl] = owned ? (int)yl : -1;
       if (a.lse_out) a.lse_out[row] = lse;
       if (a.logprob_out) a.logprob_out[row] = valid ? zt - lse : 0.f;
       if (a.m_out) a.m_out[row] = m;
@@ -1021,17 +1031,42 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   }
   __syncthreads();
   // pass 3 (only when the gradient follows): alpha_j = beta 2^(k_j - K),
-  // the factor taking tile j's stored exponentials to s valid softmax, and
-  // (for the dX contraction) the shift K - k_j as a byte
+  // the factor taking tile j's stored exponentials to s valid softmax.
+  // With P (dZ formed inside the dX contraction) the row's exponentials are
+  // brought to 2^K instead: a tile with k_j < K is rewritten in place as
+  // P 2^(k_j - K) (exact unless it flushes to zero; rare, since the
+  // references are multiples of 2^32), and alpha_j = beta for every tile.
   if (live && a.backward) {
     const float Kr = s_k[rl], beta = s_beta[rl], sc = s_sc[rl];
+    auto rescale = [&](int j, int sh) {
+      char* const seg = (char*)a.P + ((int64_t)row * a.ldp + (int64_t)j * kPartialWidth) * a.p_es;
+      for (int q = 0; q < kPartialWidth * a.p_es / 16; ++q) {
+        uint4 v = ((const uint4*)seg)[q];
+        if (a.p_es == 2) {
+          float e[8];
+          unpack8_bf16(v, e);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) e[k] = __builtin_ldexpf(e[k], -sh);
+          v = pack8_bf16(e);
+        } else {
+          v.x = __builtin_bit_cast(uint32_t, __builtin_ldexpf(__builtin_bit_cast(float, v.x), -sh));
+          v.y = __builtin_bit_cast(uint32_t, __builtin_ldexpf(__builtin_bit_cast(float, v.y), -sh));
+          v.z = __builtin_bit_cast(uint32_t, __builtin_ldexpf(__builtin_bit_cast(float, v.z), -sh));
+          v.w = __builtin_bit_cast(uint32_t, __builtin_ldexpf(__builtin_bit_cast(float, v.w), -sh));
+        }
+        ((uint4*)seg)[q] = v;
+      }
+    };
     auto put = [&](int j, float mj, float sj) {
       const int64_t o = (int64_t)j * a.ldr + row;
       const float kj = kq_of(mj);
-      a.pm[o] = (sj != 0.f) ? beta * __builtin_amdgcn_exp2f(kj - Kr) : 0.f;
-      if (a.shift)
-        a.shift[o] =
-            (uint8_t)((sj != 0.f) ? __builtin_fminf(__builtin_fmaxf(Kr - kj, 0.f), 255.f) : 0.f);
+      if (a.P) {
+        a.pm[o] = (sj != 0.f) ? beta : 0.f;
+        if (sj != 0.f && kj < Kr && beta != 0.f)
+          rescale(j, (int)__builtin_fminf(Kr - kj, 1024.f));
+      } else {
+        a.pm[o] = (sj != 0.f) ? beta * __builtin_amdgcn_exp2f(kj - Kr) : 0.f;
+      }
       if (a.alpha_q) a.alpha_q[o] *= sc;
     };
 #pragma unroll
@@ -1041,6 +1076,36 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
     }
     for (int j = sl + kFinCache * kFinSlices; j < a.nt; j += kFinSlices)
       put(j, a.pm[(int64_t)j * a.ldr + row], a.ps[(int64_t)j * a.ldr + row]);
+  }
+  if (a.P && a.backward) {
+    // The target's column, after its tile's rewrite above: it holds
+    // round(dzt / beta), so that beta times it is the target's dZ for the
+    // dW contraction; corr = dzt - beta round(dzt / beta) is what the dX
+    // contraction adds to it (times W's target row).  A row whose beta is 0
+    // with a target (a non-finite sum) keeps corr = dzt, NaN or not.
+    __syncthreads();
+    if (live && sl == 0) {
+      const int yl = s_yl[rl];
+      const float beta = s_beta[rl], dzt = s_dzt[rl];
+      float c = 0.f;
+      if (yl >= 0) {
+        if (beta != 0.f) {
+          float q = dzt / beta;
+          char* const at = (char*)a.P + ((int64_t)row * a.ldp + yl) * a.p_es;
+          if (a.p_es == 2) {
+            const bf16 qb = Elem<bf16>::from_f32(q);
+            *(bf16*)at = qb;
+            q = Elem<bf16>::to_f32(qb);
+          } else {
+            *(float*)at = q;
+          }
+          c = dzt - beta * q;
+        } else {
+          c = dzt;
+        }
+      }
+      a.corr[row] = c;
+    }
   }
   if (threadIdx.x == 0 && a.loss_part) {
     double total = 0.0;
@@ -1074,9 +1139,6 @@ __global__ void __launch_bounds__(256) fixup_kernel(FixupArgs a) {
   const int tid = threadIdx.x;
   T* P = (T*)a.P;
   T* Pt = (T*)a.Pt;
-  // rescaling: stored vectors and shift bytes kept for stores after the loop
-  uint4 keep[PER];
-  int kshift[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
     const int q = tid + 256 * p;
@@ -1085,16 +1147,10 @@ __global__ void __launch_bounds__(256) fixup_kernel(FixupArgs a) {
     float d[EPV];
 #pragma unroll
     for (int k = 0; k < EPV; ++k) d[k] = 0.f;
-    keep[p] = make_uint4(0u, 0u, 0u, 0u);
-    kshift[p] = 0;
     if (t < a.M) {
       T* src = P + (int64_t)t * a.ldp + v;
       uint4 pv = *(const uint4*)src;
       const T* pe = (const T*)&pv;
-      if (a.rescale_shift && v < a.V) {
-        keep[p] = pv;
-        kshift[p] = a.rescale_shift[(int64_t)(v / kPartialWidth) * a.ldr + t];
-      }
       const float al = (v < a.V) ? a.alpha[(int64_t)(v / kPartialWidth) * a.ldr + t] : 0.f;
       const int64_t yt = a.y[t];
       const int64_t yl = yt - a.y_shift;  // target's column among these V
@@ -1121,22 +1177,6 @@ __global__ void __launch_bounds__(256) fixup_kernel(FixupArgs a) {
 #pragma unroll
       for (int k = 0; k < EPV; ++k) tile[r][cv * EPV + k] = Elem<T>::from_f32(0.f);
     }
-  }
-  if (a.rescale_shift) {
-    // segments whose tile reference lies below the row's: store P 2^-s
-#pragma unroll
-    for (int p = 0; p < PER; ++p)
-      if (kshift[p] != 0) {
-        const int q = tid + 256 * p;
-        const int r = q / VPR, cv = q % VPR;
-        uint4 rv;
-        const T* pe = (const T*)&keep[p];
-        T* re = (T*)&rv;
-#pragma unroll
-        for (int k = 0; k < EPV; ++k)
-          re[k] = Elem<T>::from_f32(__builtin_ldexpf(Elem<T>::to_f32(pe[k]), -kshift[p]));
-        *(uint4*)(P + (int64_t)(t0 + r) * a.ldp + v0 + cv * EPV) = rv;
-      }
   }
   __syncthreads();
 #pragma unroll
@@ -1180,7 +1220,6 @@ __global__ void __launch_bounds__(256) fixup_bf16_kernel(FixupArgs a) {
   uint4 pv[8];
   float al[8];
   int64_t yt[8];
-  int sb[8];
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int t = t0 + (tid >> 5) + 8 * p;
@@ -1188,7 +1227,6 @@ __global__ void __launch_bounds__(256) fixup_bf16_kernel(FixupArgs a) {
     pv[p] = *(const uint4*)(P + (int64_t)tc * a.ldp + v);
     al[p] = a.alpha[aoff + tc];
     yt[p] = a.y[tc];
-    sb[p] = a.rescale_shift ? a.rescale_shift[aoff + tc] : 0;
   }
   uint4 ov[8];
 #pragma unroll
@@ -1218,20 +1256,11 @@ __global__ void __launch_bounds__(256) fixup_bf16_kernel(FixupArgs a) {
     ov[p] = pack8_bf16(d);
     tile[r * 32 + (cv ^ ((r >> 3) & 7))] = ov[p];
   }
+  if (a.write_rows) {
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int t = t0 + (tid >> 5) + 8 * p;
-    if (t >= a.M) continue;
-    uint16_t* const dst = P + (int64_t)t * a.ldp + v;
-    if (a.write_rows) {
-      *(uint4*)dst = ov[p];
-    } else if (sb[p] != 0 && vlive) {
-      // this tile's reference lies below the row's: store P 2^-s instead
-      float e[8];
-      unpack8_bf16(pv[p], e);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) e[k] = __builtin_ldexpf(e[k], -sb[p]);
-      *(uint4*)dst = pack8_bf16(e);
+    for (int p = 0; p < 8; ++p) {
+      const int t = t0 + (tid >> 5) + 8 * p;
+      if (t < a.M) *(uint4*)(P + (int64_t)t * a.ldp + v) = ov[p];
     }
   }
   __syncthreads();
