@@ -81,9 +81,10 @@ def parse():
                    help="dX through a transposed copy of W made per call (on) or reading W "
                         "as stored (off; bf16, no copy in the workspace); auto = the "
                         "workload's launch configuration")
-    p.add_argument("--dz-in-place", action="store_true",
+    p.add_argument("--dz-in-place", choices=("auto", "on", "off"), default="auto",
                    help="write dZ over the exponentials for the dX contraction "
-                        "(FLCE_FLAG_DZ_IN_PLACE) instead of forming it inside that contraction")
+                        "(FLCE_FLAG_DZ_IN_PLACE, on) or form it inside that contraction (off); "
+                        "auto = the workload's launch configuration")
     p.add_argument("--cpu-sample", type=int, default=3072,
                    help="tokens of the workload the CPU oracle is timed on (0 = skip)")
     p.add_argument("--vocab-shards", type=int, default=1, metavar="N",
@@ -554,6 +555,8 @@ def main():
     args.dw_chunks = args.dw_chunks or dwc
     wcopy = (workloads.weight_copy(args.workload, mode) if args.weight_copy == "auto"
              else args.weight_copy == "on")
+    args.dz_in_place = (workloads.dz_in_place(args.workload, mode) if args.dz_in_place == "auto"
+                        else args.dz_in_place == "on")
     t_gen = time.time()
     inp = workloads.generate(wl, keep_f32=args.cpu_sample > 0)
     X, W, y = workloads.to_torch(inp, "cuda")

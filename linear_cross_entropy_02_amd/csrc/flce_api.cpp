@@ -39,14 +39,21 @@ enum Kind {
   K_DW,
   K_LOSS,
   K_ZERO,
+  K_ROWREF,
   K_NUM
 };
 const char* kKindNames[K_NUM] = {"count_valid",   "transpose_w", "transpose_x", "logits_gemm",
                                  "finalize",      "fixup_dz",    "dx_gemm",     "splitk_reduce",
-                                 "dw_gemm",       "loss",        "zero_fill"};
+                                 "dw_gemm",       "loss",        "zero_fill",   "row_reference"};
 
 constexpr int64_t kDefaultChunk = 4096;
 constexpr int kMaxDwChunks = 8;
+// The dW GEMM reads the exponentials as stored (no dZ pass, no dZ^T) up to
+// this hidden size: its transposing LDS reads cost ~7 % of that GEMM, whose
+// time grows with H while the pass it replaces does not.
+#ifndef FLCE_DW_READS_P_MAX_H
+#define FLCE_DW_READS_P_MAX_H 4096
+#endif
 
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -84,6 +91,9 @@ struct flce_handle {
   float* dzt = nullptr;    // [C]
   float* beta = nullptr;   // [C], or [G*C]: row scale of dZ inside the contractions
   float* corr = nullptr;   // [C] target correction of the dX rows
+  uint8_t* shift = nullptr;  // [nt x C] tile reference below the row's, as a shift
+  int* tcol = nullptr;     // [C] target column to set in P (-1: none)
+  float* tval = nullptr;   // [C] its value
   double* loss_part = nullptr;  // [C / kFinalizeRows]
   float* splitk = nullptr;      // [splitk_alloc x C x H]
   void* Pq = nullptr;           // teacher exp(z_T / tau - m_tile) [C x Vpad]
@@ -239,7 +249,7 @@ namespace {
 // Byte offsets of the workspace buffers of one handle, from (H, V, C, G,
 // dtype, weight copy, teacher) only.
 struct Layout {
-  size_t Wt, P, Pt, Xt, pm, ps, pa, zt, dz, be, co, lp, sk, sc, cp, Pq, pmq, psq, paq, pc;
+  size_t Wt, P, Pt, Xt, pm, ps, pa, zt, dz, be, co, sh, tc, tv, lp, sk, sc, cp, Pq, pmq, psq, paq, pc;
   size_t total;
 };
 
@@ -278,7 +288,7 @@ flce_status_t configure(const flce_config_t* cfg, int64_t Ht, flce_handle* h, La
   h->dz_in_dx = (cfg->flags & FLCE_FLAG_DZ_IN_PLACE) == 0;
   h->Vpad = round_up(V, 256);
   // the dW GEMM's one buffer descriptor spans the G chunks' exponentials
-  h->dw_reads_p = h->dz_in_dx && dt == Dt::BF16 && Ht == 0 &&
+  h->dw_reads_p = h->dz_in_dx && dt == Dt::BF16 && Ht == 0 && H <= FLCE_DW_READS_P_MAX_H &&
                   G * C * h->Vpad * 2 < ((int64_t)1 << 31);
   h->nt = cdiv64(V, kPartialWidth);
   {
@@ -305,6 +315,9 @@ flce_status_t configure(const flce_config_t* cfg, int64_t Ht, flce_handle* h, La
   L->dz = carve((size_t)C * 4);
   L->be = carve((size_t)(h->dw_reads_p ? h->G * C : C) * 4);
   L->co = carve((size_t)C * 4);
+  L->sh = carve((size_t)C * round_up(h->nt, 16));
+  L->tc = carve((size_t)C * 4);
+  L->tv = carve((size_t)C * 4);
   L->lp = carve((size_t)cdiv64(C, kFinalizeRows) * 8);
   L->sk = h->splitk_alloc > 1 ? carve((size_t)h->splitk_alloc * C * H * 4) : 0;
   L->sc = carve(64);
@@ -334,6 +347,9 @@ void bind_workspace(flce_handle* h, const Layout& L, char* base) {
   h->dzt = (float*)(base + L.dz);
   h->beta = (float*)(base + L.be);
   h->corr = (float*)(base + L.co);
+  h->shift = (uint8_t*)(base + L.sh);
+  h->tcol = (int*)(base + L.tc);
+  h->tval = (float*)(base + L.tv);
   h->loss_part = (double*)(base + L.lp);
   h->splitk = h->splitk_alloc > 1 ? (float*)(base + L.sk) : nullptr;
   h->nvalid = (int64_t*)(base + L.sc);
@@ -633,18 +649,34 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       fa.no_target = true;
     } else if (fused) {
       // dZ is formed inside the contractions from the stored exponentials,
-      // which the merge brings to one reference per row (and whose target
-      // column it sets); the row scale and target correction come out
-      fa.P = Pc;
-      fa.ldp = Vpad;
-      fa.p_es = (int)es;
+      // which the row-reference pass below brings to one reference per row
+      // (setting the target's column); the row scale, target correction and
+      // what that pass needs come out
+      fa.shift = h->shift;
+      fa.ld_shift = round_up(nt, 16);
       fa.beta = beta_c;
       fa.corr = h->corr;
+      fa.tcol = h->tcol;
+      fa.tval = h->tval;
+      fa.round_bf16 = dt == Dt::BF16;
     }
     fa.backward = true;
     fa.loss_part = h->loss_part;
     fa.first_chunk = c == 0;
     FLCE_LAUNCH(K_FINALIZE, launch_finalize(fa, s));
+    if (fused) {
+      RowRefArgs ra{};
+      ra.P = Pc;
+      ra.ldp = Vpad;
+      ra.M = (int)Cc;
+      ra.V = (int)V;
+      ra.nt = (int)nt;
+      ra.shift = h->shift;
+      ra.ld_shift = round_up(nt, 16);
+      ra.tcol = h->tcol;
+      ra.tval = h->tval;
+      FLCE_LAUNCH(K_ROWREF, launch_rowref(dt, ra, s));
+    }
 
     // The dZ pass: dZ^T for the dW contraction (with dZ over the
     // exponentials too unless dZ is formed inside dX); none when dW reads

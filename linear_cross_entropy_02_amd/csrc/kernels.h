@@ -132,21 +132,37 @@ struct FinalizeArgs {
   double* loss_part;     // one slot per block_rows rows; nullable
   int first_chunk;
   int block_rows = 8;    // finalize_rows(nt, C): 8 or 32
-  // Backward with dZ formed inside the dX contraction (P non-null): the
-  // merge brings each row's stored exponentials to one reference 2^K_t,
-  // rewriting in place the tiles whose reference lies below it, writes the
-  // target's column as round(dzt / beta) in the input dtype, and
-  //   beta  [M]  per-row scale: dZ_tv = beta_t P_tv (target included)
-  //   corr  [M]  dzt_t - beta_t round(dzt_t / beta_t): what the dX
-  //              contraction adds times W's target row (0 when the target is
-  //              ignored or not in these columns)
-  // while pm becomes beta for every tile (the factor a dZ pass applies).
-  void* P = nullptr;  // [M x ldp], p_es bytes per element
-  int64_t ldp = 0;
-  int p_es = 2;
+  // Backward with dZ formed inside the contractions (shift non-null): the
+  // row-reference pass (RowRefArgs) then brings each row's stored
+  // exponentials to one reference 2^K_t and sets the target's column, so that
+  // dZ_tv = beta_t P_tv throughout; pm becomes beta for every tile (the
+  // factor a dZ pass applies).  Per row or (tile, row):
+  //   shift [M x ld_shift] K_t - k_tj as a byte (255: 255 or more, the
+  //                    tile flushes to zero; 0: as it is), row-major
+  //   beta  [M]  the row scale
+  //   corr  [M]  dzt_t - beta_t tval_t: what the dX contraction adds times
+  //              W's target row (0 when the target is ignored or not in
+  //              these columns)
+  //   tcol, tval [M]  the target's column (-1: none) and its value
+  //              round(dzt_t / beta_t) in the input dtype (round_bf16)
+  uint8_t* shift = nullptr;
+  int64_t ld_shift = 0;       // >= nt, a multiple of 16
   float* beta = nullptr;
   float* corr = nullptr;
+  int* tcol = nullptr;
+  float* tval = nullptr;
+  bool round_bf16 = false;
 };
+
+struct RowRefArgs {
+  void* P; int64_t ldp;  // [M x ldp], the input dtype
+  int M, V, nt;
+  const uint8_t* shift;  // [M x ld_shift], 16-byte aligned rows
+  int64_t ld_shift;      // a multiple of 16, >= nt
+  const int* tcol;
+  const float* tval;
+};
+hipError_t launch_rowref(Dt dt, const RowRefArgs& a, hipStream_t s);
 // Rows per finalize block, hence rows per loss partial: 32 when rows hold
 // at most 256 partial tiles and a chunk of C rows still gives 256 blocks,
 // else 8.  kFinalizeRows is the smaller, which sizes the partial buffer.

@@ -1032,38 +1032,19 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
   __syncthreads();
   // pass 3 (only when the gradient follows): alpha_j = beta 2^(k_j - K),
   // the factor taking tile j's stored exponentials to s valid softmax.
-  // With P (dZ formed inside the dX contraction) the row's exponentials are
-  // brought to 2^K instead: a tile with k_j < K is rewritten in place as
-  // P 2^(k_j - K) (exact unless it flushes to zero; rare, since the
-  // references are multiples of 2^32), and alpha_j = beta for every tile.
+  // With dZ formed inside the contractions (shift non-null) the rows'
+  // exponentials are brought to 2^K by the row-reference pass instead: the
+  // shift byte of tile j is K - k_j (255 for 255 and more: the tile flushes
+  // to zero; 0 for rows with no scale), and alpha_j = beta for every tile.
   if (live && a.backward) {
     const float Kr = s_k[rl], beta = s_beta[rl], sc = s_sc[rl];
-    auto rescale = [&](int j, int sh) {
-      char* const seg = (char*)a.P + ((int64_t)row * a.ldp + (int64_t)j * kPartialWidth) * a.p_es;
-      for (int q = 0; q < kPartialWidth * a.p_es / 16; ++q) {
-        uint4 v = ((const uint4*)seg)[q];
-        if (a.p_es == 2) {
-          float e[8];
-          unpack8_bf16(v, e);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) e[k] = __builtin_ldexpf(e[k], -sh);
-          v = pack8_bf16(e);
-        } else {
-          v.x = __builtin_bit_cast(uint32_t, __builtin_ldexpf(__builtin_bit_cast(float, v.x), -sh));
-          v.y = __builtin_bit_cast(uint32_t, __builtin_ldexpf(__builtin_bit_cast(float, v.y), -sh));
-          v.z = __builtin_bit_cast(uint32_t, __builtin_ldexpf(__builtin_bit_cast(float, v.z), -sh));
-          v.w = __builtin_bit_cast(uint32_t, __builtin_ldexpf(__builtin_bit_cast(float, v.w), -sh));
-        }
-        ((uint4*)seg)[q] = v;
-      }
-    };
     auto put = [&](int j, float mj, float sj) {
       const int64_t o = (int64_t)j * a.ldr + row;
       const float kj = kq_of(mj);
-      if (a.P) {
+      if (a.shift) {
         a.pm[o] = (sj != 0.f) ? beta : 0.f;
-        if (sj != 0.f && kj < Kr && beta != 0.f)
-          rescale(j, (int)__builtin_fminf(Kr - kj, 1024.f));
+        a.shift[(int64_t)row * a.ld_shift + j] =
+            (uint8_t)((sj != 0.f && beta != 0.f) ? __builtin_fminf(Kr - kj, 255.f) : 0.f);
       } else {
         a.pm[o] = (sj != 0.f) ? beta * __builtin_amdgcn_exp2f(kj - Kr) : 0.f;
       }
@@ -1077,35 +1058,29 @@ __global__ void __launch_bounds__(1024) finalize_kernel(FinalizeArgs a) {
     for (int j = sl + kFinCache * kFinSlices; j < a.nt; j += kFinSlices)
       put(j, a.pm[(int64_t)j * a.ldr + row], a.ps[(int64_t)j * a.ldr + row]);
   }
-  if (a.P && a.backward) {
-    // The target's column, after its tile's rewrite above: it holds
-    // round(dzt / beta), so that beta times it is the target's dZ for the
-    // dW contraction; corr = dzt - beta round(dzt / beta) is what the dX
+  if (a.shift && a.backward && live && sl == 0) {
+    // The target's column will hold round(dzt / beta) (the row-reference
+    // pass writes it), so that beta times it is the target's dZ for the dW
+    // contraction; corr = dzt - beta round(dzt / beta) is what the dX
     // contraction adds to it (times W's target row).  A row whose beta is 0
     // with a target (a non-finite sum) keeps corr = dzt, NaN or not.
-    __syncthreads();
-    if (live && sl == 0) {
-      const int yl = s_yl[rl];
-      const float beta = s_beta[rl], dzt = s_dzt[rl];
-      float c = 0.f;
-      if (yl >= 0) {
-        if (beta != 0.f) {
-          float q = dzt / beta;
-          char* const at = (char*)a.P + ((int64_t)row * a.ldp + yl) * a.p_es;
-          if (a.p_es == 2) {
-            const bf16 qb = Elem<bf16>::from_f32(q);
-            *(bf16*)at = qb;
-            q = Elem<bf16>::to_f32(qb);
-          } else {
-            *(float*)at = q;
-          }
-          c = dzt - beta * q;
-        } else {
-          c = dzt;
-        }
+    const int yl = s_yl[rl];
+    const float beta = s_beta[rl], dzt = s_dzt[rl];
+    float c = 0.f, q = 0.f;
+    int col = -1;
+    if (yl >= 0) {
+      if (beta != 0.f) {
+        q = dzt / beta;
+        if (a.round_bf16) q = Elem<bf16>::to_f32(Elem<bf16>::from_f32(q));
+        c = dzt - beta * q;
+        col = yl;
+      } else {
+        c = dzt;
       }
-      a.corr[row] = c;
     }
+    a.corr[row] = c;
+    a.tcol[row] = col;
+    a.tval[row] = q;
   }
   if (threadIdx.x == 0 && a.loss_part) {
     double total = 0.0;
@@ -1122,6 +1097,84 @@ hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(finalize_kernel<8>, dim3(cdiv(a.M, 8)), dim3(1024), 0, s, a);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- row reference ---
+// With dZ formed inside the contractions: brings every row of P to its
+// row's reference (a 128-column segment whose tile reference lies below it
+// is rewritten as P 2^-s, s being the merge's shift byte) and writes the
+// target's column as the merge's tval.  One wave per row: the row's shift
+// bytes come in one 16-byte load per lane (tiles 16 l .. 16 l + 15, up to
+// 1024 tiles; beyond, the wave reads them again per 1024), staged in LDS.
+// A row whose tiles all share its reference is left as it is; otherwise the
+// wave streams the row, 16 bytes per lane and four loads in flight, and
+// rewrites the vectors of the tiles that change.  The target's column is
+// written last, after the wave's stores have completed.
+template <typename T>
+__global__ void __launch_bounds__(256) rowref_kernel(RowRefArgs a) {
+  constexpr int EPV = Elem<T>::kVec;
+  constexpr int VPT = kPartialWidth / EPV;  // 16-byte vectors per tile
+  __shared__ uint8_t s_sh[4][1024];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
+  if (t >= a.M) return;  // wave-uniform
+  T* const prow = (T*)a.P + (int64_t)t * a.ldp;
+  const uint8_t* const srow = a.shift + (int64_t)t * a.ld_shift;
+  for (int j0 = 0; j0 < a.nt; j0 += 1024) {
+    const int nj = min(1024, a.nt - j0);
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (16 * lane < nj) w = *(const uint4*)(srow + j0 + 16 * lane);
+    // bytes of tiles past nt are padding: cleared
+    const int valid = min(16, max(0, nj - 16 * lane));
+    uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int b = 0; b < 16; ++b)
+      if (b >= valid) wd[b >> 2] &= ~(0xffu << (8 * (b & 3)));
+    const bool mine = (wd[0] | wd[1] | wd[2] | wd[3]) != 0;
+    if (!__builtin_amdgcn_ballot_w64(mine)) continue;  // the row keeps these tiles
+    *(uint4*)&s_sh[wv][16 * lane] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    __builtin_amdgcn_wave_barrier();
+    // vectors q of tiles j0 .. j0 + nj - 1, lane-strided, four at a time
+    const int nvec = nj * VPT;
+    uint4* const base = (uint4*)(prow + (int64_t)j0 * kPartialWidth);
+    for (int q0 = lane; q0 < nvec; q0 += 4 * 64) {
+      uint4 v[4];
+      int sb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = q0 + 64 * u;
+        sb[u] = q < nvec ? s_sh[wv][q / VPT] : 0;
+        if (sb[u] != 0) v[u] = base[q];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (sb[u] == 0) continue;
+        T* const e = (T*)&v[u];
+#pragma unroll
+        for (int k = 0; k < EPV; ++k)
+          e[k] = Elem<T>::from_f32(__builtin_ldexpf(Elem<T>::to_f32(e[k]), -sb[u]));
+        base[q0 + 64 * u] = v[u];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  const int tc = a.tcol[t];
+  if (lane == 0 && tc >= 0) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's rewrite of the tile has landed
+    __threadfence_block();
+    prow[tc] = Elem<T>::from_f32(a.tval[t]);
+  }
+}
+
+hipError_t launch_rowref(Dt dt, const RowRefArgs& a, hipStream_t s) {
+  if (a.M <= 0 || a.V <= 0) return hipSuccess;
+  if (a.ld_shift % 16 != 0 || a.ld_shift < a.nt) return hipErrorInvalidValue;
+  const dim3 grid(cdiv(a.M, 4));
+  if (dt == Dt::BF16)
+    hipLaunchKernelGGL(rowref_kernel<bf16>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(rowref_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -67,15 +67,15 @@ def run_full(cfg):
     X, W, y = workloads.to_torch(inp, "cuda")
     chunk, g = CHUNK[cfg]
     op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=chunk, dw_chunks=g,
-                                      weight_copy=workloads.weight_copy(cfg))
+                                      weight_copy=workloads.weight_copy(cfg),
+                                      dz_in_place=workloads.dz_in_place(cfg))
     log(f"workload {cfg} on GPU, chunk {op.chunk_tokens}, dw_chunks {op.dw_chunks}, "
         f"workspace {op.workspace_bytes / 2**20:.0f} MiB")
     out = op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction)
     torch.cuda.synchronize()
-    # the workspace holds logits-shaped chunk buffers of C x Vpad (exp / dZ)
-    # and G C x Vpad (dZ^T of a dW group): together below T x V
-    assert (1 + op.dw_chunks) * op.chunk_tokens < wl.T, "chunk buffers must stay below T x V"
-    # and the whole workspace below a bf16 T x V buffer
+    # the workspace (with its logits-shaped buffers: the exponentials of the
+    # G chunks of a dW group, or one chunk's and the group's dZ^T) stays
+    # below a bf16 T x V buffer
     assert op.workspace_bytes < wl.T * wl.V * 2, (op.workspace_bytes, wl.T * wl.V * 2)
     res = {k: to_np(v) for k, v in out.items()}
     op.close()
