@@ -133,9 +133,10 @@ def short_kernel_name(name: str) -> str:
     import re
     n = name.replace("flce::", "")
     m = re.match(r"void gemm_nt_kernel<([^,]+), (\d+), (\d+), (\d+), (\w+)<([^>]*)>"
-                 r"(?:, (true|false))?", n)
+                 r"(?:, (true|false))?(?:, (true|false))?", n)
     if m:
-        flags = ",Bstored" if m.group(7) == "true" else ""
+        flags = "".join(f",{t}" for t, on in (("Bstored", m.group(7)), ("Astored", m.group(8)))
+                        if on == "true")
         return (f"gemm<{m.group(1)},{m.group(2)}x{m.group(3)},{m.group(4)}w,"
                 f"{m.group(5)}<{m.group(6).strip()}>{flags}>")
     return n.split("(")[0].replace("void ", "")

@@ -84,3 +84,7 @@ def test_short_kernel_names():
         "void flce::gemm_nt_kernel<flce::bf16, 128, 128, 4, flce::StoreEpi<float, false>, "
         "true>(flce::GemmShape, flce::StoreEpi<float, false>)")
     assert n == "gemm<bf16,128x128,4w,StoreEpi<float, false>,Bstored>"
+    n = bench.short_kernel_name(
+        "void flce::gemm_nt_kernel<flce::bf16, 256, 256, 4, flce::StoreEpi<float, true>, "
+        "false, true>(flce::GemmShape, flce::StoreEpi<float, true>)")
+    assert n == "gemm<bf16,256x256,4w,StoreEpi<float, true>,Astored>"
