@@ -3,16 +3,18 @@ and whether the dX contraction reads a transposed copy of W.
 
 The settings are the fastest measured (MI355X, one box, alternating runs)
 for the head shapes the library is tuned on; between them the rule below
-interpolates by hidden size.  They trade workspace for speed: the dZ^T of
-G chunks is kept so that the fp32 dW tiles are read and written once per G
-chunks, and the W^T copy makes the dX contraction read 16-byte fragments.
+interpolates by hidden size.  They trade workspace for speed: the
+exponentials of G chunks are kept so that the fp32 dW tiles are read and
+written once per G chunks, and the W^T copy makes the dX contraction read
+16-byte fragments.
   * H >= 2048: C = 2048, G = 4 up to H = 4096 (at 16384 x 4096 x 128256 a
-    step takes 41.4 ms; G = 2: 42.6, G = 1: 45.2, C = 4096, G = 1: 42.8),
-    G = 2 above (8192 x 8192 x 128256: 40.3 ms; G = 1: 42.9); the W^T copy
+    step takes 38.8 ms at 0.79 of a bf16 T x V buffer; G = 2: 40.4 at 0.53;
+    C = 4096, G = 1: 40.2 at 0.52; W read as stored: 39.5 at 0.54), G = 2
+    above (8192 x 8192 x 128256: 39.4 ms; G = 1: 42.2); the W^T copy
     unless it would be as large as a bf16 T x V buffer (H >= T).
   * H < 2048: C = 8192, G = 1 for batches of 32768 tokens or more
-    (65536 x 512 x 16000), else C = 1024, G = 2 reading W as stored
-    (4096 x 512 x 16000: 0.45 ms; G = 1: 0.48 ms).
+    (65536 x 512 x 16000), else C = 2048, G = 1 reading W as stored
+    (4096 x 512 x 16000: 0.37 ms; C = 1024, G = 2: 0.43 ms).
   * fp32: one chunk of up to 4096 tokens, G = 1.
 C never exceeds the batch (rounded up to 256) and G the number of chunks.
 """
@@ -30,7 +32,7 @@ def suggest_launch(T: int, H: int, V: int, dtype: str = "bf16"):
     elif T >= 32768:
         C, G, wcopy = 8192, 1, True
     else:
-        C, G, wcopy = 1024, 2, False
+        C, G, wcopy = 2048, 1, False
     tpad = max(256, -(-max(T, 1) // 256) * 256)
     C = min(C, tpad)
     G = max(1, min(G, -(-max(T, 1) // C)))

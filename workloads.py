@@ -83,7 +83,7 @@ WORKLOADS = {
 # 8192 tokens deep, so the dW tiles are written twice per call instead of
 # four times.  The large ragged head (T = H = 8192) cannot stay below T x V
 # (W^T alone is H V = T V elements there); it takes the fastest setting.
-LAUNCH = {1: (256, 1), 2: (1024, 2), 3: (8192, 1), 4: (2048, 4), 5: (2048, 2)}
+LAUNCH = {1: (256, 1), 2: (2048, 1), 3: (8192, 1), 4: (2048, 4), 5: (2048, 2)}
 # The other entry points at the Llama-3-8B head's shape, chosen the same
 # way: the forward-only call has no dW GEMM; a vocabulary shard's head is
 # V / N wide; the soft-target head also holds the teacher's chunk of
@@ -94,8 +94,8 @@ LAUNCH_MODES = {"forward": (4096, 1), "shard": (4096, 1), "distill": (2048, 3)}
 # Workloads whose handle reads W as stored in the dX GEMM instead of a
 # transposed copy made per call: the 8192 x 8192 x 128256 head, where that
 # copy alone is as large as a bf16 T x V buffer, and the 4096 x 512 x 16000
-# layer, where dropping it leaves room for two chunks per dW GEMM under that
-# bound (0.62 instead of 0.70 ms per step).
+# layer, where dropping it leaves room for 2048-token chunks under that bound
+# (0.37 ms per step, against 0.42 with the copy and 1024-token chunks).
 NO_WEIGHT_COPY = {2, 5}
 
 
