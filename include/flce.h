@@ -63,15 +63,15 @@ typedef struct {
   int64_t hidden;       /* H: > 0, multiple of 8 (bf16) or 4 (fp32)          */
   int64_t vocab;        /* V: > 0                                              */
   int32_t dtype;        /* flce_dtype_t                                        */
-  int32_t dw_chunks;    /* G: chunks whose dZ^T is kept for one dW GEMM of
-                           depth K = G*C; 0 = default (1), at most 8.  The dW
-                           tiles are then read and written once per G chunks
-                           instead of once per chunk, for (G-1)*C*V more
-                           workspace elements.                                  */
+  int32_t dw_chunks;    /* G: chunks whose exponentials (or dZ^T) are kept for
+                           one dW GEMM of depth K = G*C; 0 = default (1), at
+                           most 8.  The dW tiles are then read and written
+                           once per G chunks instead of once per chunk, for
+                           about (G-1)*C*V more workspace elements.            */
   int64_t chunk_tokens; /* C: tokens per chunk; 0 = default (4096).  Rounded up
-                           to a multiple of 256.  The workspace is
-                           O((1+G)*C*V + V*H) and does not depend on the number
-                           of tokens T.                                         */
+                           to a multiple of 256.  The workspace is O(G*C*V +
+                           V*H) (O((1+G)*C*V + V*H) where dZ^T is written) and
+                           does not depend on the number of tokens T.          */
   int32_t flags;        /* 0, or FLCE_FLAG_NO_WEIGHT_COPY and/or FLCE_FLAG_DZ_IN_PLACE */
 } flce_config_t;
 
@@ -82,18 +82,22 @@ typedef struct {
  * V*H*2 must stay below 2^31 bytes; FLCE_ERR_UNSUPPORTED otherwise. */
 #define FLCE_FLAG_NO_WEIGHT_COPY 1
 
-/* How dZ reaches the dX contraction ("gradient of softmax + CE loss" in
- * "Alisa's book of LLMs": dZ = p - onehot).  By default dZ is formed inside
- * it and never written for it: the logits epilogue stores each (row,
- * 128-column tile) of exponentials relative to a power of two 2^(32 j); the
- * pass that writes dZ^T for the dW contraction also rewrites, in place, the
- * tiles whose power lies below their row's (so a row's exponentials share
- * one), and the dX GEMM reads the exponentials and finishes each output row
- * with the row's scale and the target's correction times that row of W.
- * With this flag the pass instead writes dZ itself over the exponentials
- * (one more T*V write; measured ~2 % slower per call at 16384 x 4096 x
- * 128256) and the dX GEMM reads it.  Same results to the tolerances.  The
- * soft-target call always writes dZ (its rows hold two sets of
+/* How dZ reaches the dX and dW contractions ("gradient of softmax + CE loss"
+ * in "Alisa's book of LLMs": dZ = p - onehot).  By default dZ is formed
+ * inside them and never written: the logits epilogue stores each (row,
+ * 128-column tile) of exponentials relative to a power of two 2^(32 j); a
+ * small pass after the merge rewrites, in place, the tiles whose power lies
+ * below their row's (so a row's exponentials share one, dZ = beta P) and
+ * sets the target's column; the dX GEMM reads the exponentials and finishes
+ * each output row with the row's scale and the target's correction times
+ * that row of W, and the dW GEMM reads them as stored against X^T scaled by
+ * the row scales (bf16, H <= 4096 and G*C*Vpad*2 < 2^31; otherwise a pass
+ * writes dZ^T for it).  With this flag a pass writes dZ over the
+ * exponentials and dZ^T, and both GEMMs read those (one to two more T*V
+ * writes; measured ~4 % slower per call at 16384 x 4096 x 128256, and
+ * faster where many rows' tiles sit far below their row's reference, as
+ * with a few far-outlying rows of W).  Same results to the tolerances.
+ * The soft-target call always writes dZ (its rows hold two sets of
  * exponentials). */
 #define FLCE_FLAG_DZ_IN_PLACE 2
 
