@@ -74,16 +74,16 @@ def parse():
     p.add_argument("--chunk", type=int, default=0,
                    help="tokens per chunk (0 = the workload's launch configuration)")
     p.add_argument("--dw-chunks", type=int, default=0,
-                   help="token chunks per dW GEMM (the dZ^T of that many chunks is kept; "
-                        "more than 1 needs (G - 1) C V more workspace; 0 = the workload's "
-                        "launch configuration)")
+                   help="token chunks per dW GEMM (the exponentials, or the dZ^T, of that "
+                        "many chunks are kept: more than 1 needs (G - 1) C V more workspace; "
+                        "0 = the workload's launch configuration)")
     p.add_argument("--weight-copy", choices=("auto", "on", "off"), default="auto",
                    help="dX through a transposed copy of W made per call (on) or reading W "
                         "as stored (off; bf16, no copy in the workspace); auto = the "
                         "workload's launch configuration")
     p.add_argument("--dz-in-place", choices=("auto", "on", "off"), default="auto",
-                   help="write dZ over the exponentials for the dX contraction "
-                        "(FLCE_FLAG_DZ_IN_PLACE, on) or form it inside that contraction (off); "
+                   help="write dZ over the exponentials and dZ^T for the dX and dW "
+                        "contractions (FLCE_FLAG_DZ_IN_PLACE, on) or form it inside them (off); "
                         "auto = the workload's launch configuration")
     p.add_argument("--cpu-sample", type=int, default=3072,
                    help="tokens of the workload the CPU oracle is timed on (0 = skip)")
@@ -120,12 +120,40 @@ def parse():
     return p.parse_args()
 
 
+def code_tokens(src: str) -> str:
+    """C/C++ source with its comments removed and every run of whitespace
+    made one space (comment markers inside string and character literals are
+    kept): close to what the compiler sees, so that a comment edit leaves the
+    kernels' hash alone."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code (comments and layout ignored)."""
     import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -88,3 +88,12 @@ def test_short_kernel_names():
         "void flce::gemm_nt_kernel<flce::bf16, 256, 256, 4, flce::StoreEpi<float, true>, "
         "false, true>(flce::GemmShape, flce::StoreEpi<float, true>)")
     assert n == "gemm<bf16,256x256,4w,StoreEpi<float, true>,Astored>"
+
+
+def test_the_kernel_hash_follows_the_code_not_the_comments():
+    a = 'int f(int x) { // twice x\n  return 2 * x; /* plain */ }\nconst char* s = "a//b";\n'
+    b = '/* a header comment */\nint f(int x) {\n    return 2 * x;\n}\nconst char* s = "a//b"; // note\n'
+    assert bench.code_tokens(a) == bench.code_tokens(b)
+    assert bench.code_tokens(a) != bench.code_tokens(a.replace("2 * x", "3 * x"))
+    assert bench.code_tokens(a) != bench.code_tokens(a.replace('"a//b"', '"a// b"'))
+    assert bench.code_tokens("char c = '\\''; // x\nint y;") == "char c = '\\''; int y;"

@@ -1,13 +1,15 @@
 """GPU parity of the two ways dZ reaches the dX contraction, against the
 oracle.
 
-Default: the dX contraction reads the stored exponentials and forms dZ
-itself.  Their tile references are powers 2^(32 j); the dZ pass rewrites in
-place the row segments whose reference lies below their row's (so that each
-row's exponentials share one) and writes dZ^T; each output row of dX is
-finished with the row's scale plus the target's correction times that row of
-W.  FLCE_FLAG_DZ_IN_PLACE: the dZ pass writes dZ over the exponentials and
-the dX contraction reads it.
+Default: the dX and dW contractions read the stored exponentials and form
+dZ themselves.  Their tile references are powers 2^(32 j); the row-reference
+pass rewrites in place the row segments whose reference lies below their
+row's (so that each row's exponentials share one) and sets the target column;
+each output row of dX is finished with the row's scale plus the target's
+correction times that row of W, and dW contracts the exponentials as stored
+against the row-scaled X^T (bf16 up to H = 4096; elsewhere the dZ pass writes
+dZ^T for it).  FLCE_FLAG_DZ_IN_PLACE: the dZ pass writes dZ over the
+exponentials and dZ^T, and the contractions read those.
 
 The rest of the GPU suite runs the default; the cases here run the in-place
 mode over every instantiation both paths have (256-wide tiles split in K and
@@ -127,7 +129,7 @@ def straddle_inputs(dtype, seed):
     """A head whose vocabulary tiles sit at logit levels around 32 ln 2 (a
     multiple of the 2^32 reference quantum), so that the rows hold tiles on
     both sides of it with comparable softmax mass, plus two far tiles:
-    per-row references differ and the dZ pass must rescale."""
+    per-row references differ and the row-reference pass must rescale."""
     T, H, V = 640, 64, 1024
     rng = np.random.default_rng(seed)
     levels = np.array([21.4, 21.7, 22.0, 22.3, 22.6, 21.1, -8.0, 4.0])   # 8 tiles of 128
