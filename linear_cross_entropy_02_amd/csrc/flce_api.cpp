@@ -501,7 +501,7 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
   const Dt dt = h->dt;
   const size_t es = elem_size(dt);
   const int64_t H = h->H, V = h->V, C = h->C, Vpad = h->Vpad, nt = h->nt;
-  const int64_t G = h->G, GC = G * C;  // dZ^T / X^T of G chunks side by side
+  const int64_t G = h->G, GC = G * C;  // P or dZ^T, and X^T, of G chunks side by side
   const int rsum = reduction == FLCE_SUM ? 1 : 0;
 
 #define FLCE_LAUNCH(kind, expr)                                      \
@@ -761,7 +761,8 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       }
     }
     // dW (+)= dZ^T X over the chunks of a group (M = V, N = H, K = gs C + Ck)
-    // once its last chunk is in; the first group stores.
+    // once its last chunk is in, as P^T (beta X) when dW reads the
+    // exponentials; the first group stores.
     if (gs == G - 1 || last) {
       const int64_t Kg = gs * C + Ck;
       TileCfg tc;

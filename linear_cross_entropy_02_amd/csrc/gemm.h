@@ -2,10 +2,13 @@
 // ("NT": A is M x K row-major, B is N x K row-major), fp32 accumulation.
 //
 // All three contractions of the fused cross-entropy head run through this
-// one engine (the caller lays every operand out K-contiguous first):
+// one engine (operands K-contiguous, or read as stored in the BT / AT modes
+// below):
 //   logits  Z  = X  * W^T      A = X   (C x H),   B = W   (V x H)
 //   dX         = dZ * W        A = dZ  (C x V),   B = W^T (H x V)
 //   dW        += dZ^T * X      A = dZ^T(V x C),   B = X^T (H x C)
+// (dZ enters both gradients as the stored exponentials with per-row
+// factors applied outside the K loop.)
 //
 // Block tile BM x BN, 4 waves in a 2 x 2 layout; each wave owns a
 // (BM/2) x (BN/2) accumulator tile made of 16 x 16 MFMA fragments.  One

@@ -3,19 +3,26 @@
 // Per token chunk of C rows the host enqueues:
 //   logits GEMM   z = X_c W^T on MFMA, with an epilogue that reduces each row
 //                 over its 128-column wave tile to (max, sum exp(z - max),
-//                 argmax), records the target logit and stores
-//                 exp(z - tile max) -- the online-softmax partials of
-//                 "Alisa's book of LLMs", Numerical stability and other tricks
-//                 (running max with a rescaled denominator);
+//                 argmax), records the target logit and stores the tile's
+//                 exponentials relative to a power of two at or above its
+//                 max -- the online-softmax partials of "Alisa's book of
+//                 LLMs", Numerical stability and other tricks (running max
+//                 with a rescaled denominator);
 //   finalize      merges the partials of every row into lse, argmax and the
-//                 per-token NLL, and turns each tile max into the factor
-//                 alpha = s valid exp(m_tile - lse) that rescales the stored
-//                 exponentials into softmax probabilities;
-//   fixup         forms dZ = s valid (softmax - onehot) ("gradient of
-//                 softmax + CE loss" on the same page) in place and its
-//                 transpose;
-//   dX GEMM       dX_c = dZ W     (K = vocabulary)
-//   dW GEMM       dW  += dZ^T X_c (K = chunk tokens), first chunk stores.
+//                 per-token NLL, and emits the factors that turn the stored
+//                 exponentials into dZ = s valid (softmax - onehot)
+//                 ("gradient of softmax + CE loss" on the same page): a row
+//                 scale beta, the target's correction and, per tile, how far
+//                 its reference lies below the row's;
+//   row reference rewrites the tiles whose reference lies below their row's
+//                 and sets the target column, so that dZ = beta P;
+//   dX GEMM       dX_c = dZ W (K = vocabulary) on P, each row finished as
+//                 beta acc + correction W[target];
+//   dW GEMM       dW += P^T (beta X) over a group of chunks (K = their
+//                 tokens), the first group stores.
+// A dZ pass (fixup) writes dZ in place and its transpose instead where the
+// contractions cannot read P: soft targets, fp32 or wide hidden sizes for dW,
+// or when asked to.
 #include "kernels.h"
 
 #include <type_traits>
@@ -39,9 +46,9 @@ namespace flce {
 // z / tau) is m stores exp2(z log2(e) - k) with k = q ceil(m log2(e) / q),
 // q = kRefQuantum.  Any whole power of two at or above the max would do; a
 // coarse one makes the tiles of a row mostly share it (their maxima would
-// have to straddle a multiple of 32 log2(e) ~ 22 nats), so that the dZ pass
-// can leave those rows' exponentials as they are for the dX contraction and
-// rewrite only the lower tiles of the others.  Values more than ~65 nats
+// have to straddle a multiple of 32 log2(e) ~ 22 nats), so that the
+// row-reference pass can leave those rows' exponentials as they are for the
+// contractions and rewrite only the lower tiles of the others.  Values more than ~65 nats
 // below their tile's max flush to zero; their softmax is < e^-65 of it.
 constexpr float kRefQuantum = 32.f;
 __device__ __forceinline__ float ref_power(float m) {
