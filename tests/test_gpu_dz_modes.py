@@ -125,14 +125,19 @@ def test_vocab_shard_backward(dz_in_place):
     assert np.all(dX[inp.y == wl.ignore_index] == 0.0)
 
 
-def straddle_inputs(dtype, seed):
+def straddle_inputs(dtype, seed, T=640, V=1024):
     """A head whose vocabulary tiles sit at logit levels around 32 ln 2 (a
     multiple of the 2^32 reference quantum), so that the rows hold tiles on
-    both sides of it with comparable softmax mass, plus two far tiles:
-    per-row references differ and the row-reference pass must rescale."""
-    T, H, V = 640, 64, 1024
+    both sides of it with comparable softmax mass, plus far tiles: per-row
+    references differ and the row-reference pass must rescale.  The eight
+    levels repeat over the tiles of a longer vocabulary; the last tile is a
+    low one."""
+    H = 64
     rng = np.random.default_rng(seed)
-    levels = np.array([21.4, 21.7, 22.0, 22.3, 22.6, 21.1, -8.0, 4.0])   # 8 tiles of 128
+    levels = np.array([21.4, 21.7, 22.0, 22.3, 22.6, 21.1, -8.0, 4.0])   # tiles of 128
+    nt = -(-V // 128)
+    tile_level = levels[np.arange(nt) % len(levels)]
+    tile_level[-1] = 4.0
     X = (0.02 * rng.standard_normal((T, H))).astype(np.float32)
     # The levels come from a large first column of X times a small one of W:
     # a tile's common component of W then stays small against W's own rows,
@@ -141,8 +146,8 @@ def straddle_inputs(dtype, seed):
     # target count from a similar softmax mass either.
     X[:, 0] = 1000.0 * (1.0 + 0.02 * rng.standard_normal(T))
     W = (0.02 * rng.standard_normal((V, H))).astype(np.float32)
-    W[:, 0] = (np.repeat(levels, V // len(levels)) + 0.3 * rng.standard_normal(V)) / 1000.0
-    y = rng.integers(V - 128, V, size=T)
+    W[:, 0] = (np.repeat(tile_level, 128)[:V] + 0.3 * rng.standard_normal(V)) / 1000.0
+    y = rng.integers(128 * (nt - 1), V, size=T)
     y[::9] = -100
     base = workloads.WORKLOADS[2] if dtype == "bf16" else workloads.WORKLOADS[1]
     wl = dataclasses.replace(base.with_shape(T=T, H=H, V=V, seed=seed), ignore_index=-100)
@@ -155,19 +160,29 @@ def straddle_inputs(dtype, seed):
     return wl, inp
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_rows_whose_tiles_straddle_a_reference(dtype):
-    wl, inp = straddle_inputs(dtype, 83)
+@pytest.mark.parametrize("dtype,T,V", [("bf16", 640, 1024), ("f32", 640, 1024),
+                                       # rows of 1563 tiles: the row-reference pass
+                                       # reads their shift bytes in two passes of
+                                       # up to 1024 tiles
+                                       ("bf16", 320, 200003), ("f32", 320, 200003)])
+def test_rows_whose_tiles_straddle_a_reference(dtype, T, V):
+    wl, inp = straddle_inputs(dtype, 83, T, V)
     # on the host: the tile references q ceil(max log2 e / q), q = 32, differ
     # within a good share of the rows
-    z = inp.X.astype(np.float64) @ inp.W.astype(np.float64).T
-    kq = np.ceil(z.reshape(wl.T, -1, 128).max(axis=2) * np.log2(np.e) / 32) * 32
-    mixed = (kq != kq.max(axis=1, keepdims=True)).any(axis=1)
+    nt = -(-V // 128)
+    z = np.full((T, 128 * nt), -np.inf)
+    z[:, :V] = inp.X.astype(np.float64) @ inp.W.astype(np.float64).T
+    kq = np.ceil(z.reshape(T, nt, 128).max(axis=2) * np.log2(np.e) / 32) * 32
+    below = kq < kq.max(axis=1, keepdims=True)
+    mixed = below.any(axis=1)
     assert mixed.mean() > 0.3, mixed.mean()
+    if nt > 1024:
+        assert below[:, 1024:].any(axis=1).mean() > 0.3
     # the tiles on either side of the boundary carry comparable mass
     p = np.exp(z - z.max(axis=1, keepdims=True))
-    tile_mass = p.reshape(wl.T, -1, 128).sum(axis=2)
-    low = np.where(kq < kq.max(axis=1, keepdims=True), tile_mass, 0).sum(axis=1)
+    tile_mass = p.reshape(T, nt, 128).sum(axis=2)
+    low = np.where(below, tile_mass, 0).sum(axis=1)
     assert np.median(low[mixed] / tile_mass[mixed].sum(axis=1)) > 0.1
+    del z, p
     _, out = run(wl, 256, inp=inp, dz_in_place=False)
     check_full(out, flce_reference(inp.X, inp.W, inp.y, wl.ignore_index, wl.reduction), inp, wl)

@@ -141,6 +141,25 @@ def test_parity_no_weight_copy(wl, chunk):
         assert torch.equal(out[k], ref[k]), k
 
 
+def test_vocabulary_at_the_size_limit():
+    # the widest vocabulary a handle takes: rows padded to 2^20 columns, 8192
+    # partial tiles per row (the merge's uncached tiles, the row-reference
+    # pass's eight passes over its shift bytes), 256-row operand tiles of
+    # 2^29 bytes at 32-bit offsets, and dW reading two 256-token chunks of
+    # exponentials (2^30 bytes under its one buffer descriptor); W through
+    # the copy, then as stored, bit for bit
+    import torch
+    wl = workloads.WORKLOADS[2].with_shape(T=300, H=64, V=(1 << 20) - 300, seed=48)
+    inp = workloads.generate(wl)
+    inp, out = run(wl, 256, inp=inp, dw_chunks=2)
+    ref = flce_reference(inp.X, inp.W, inp.y, wl.ignore_index, wl.reduction, chunk=64)
+    check_full(out, ref, inp, wl)
+    del ref
+    _, out2 = run(wl, 256, inp=inp, dw_chunks=2, weight_copy=False)
+    for k in ("loss", "dX", "dW", "lse", "argmax", "n_valid"):
+        assert torch.equal(out[k], out2[k]), k
+
+
 def test_no_weight_copy_workspace_and_dtype():
     wl = workloads.WORKLOADS[2].with_shape(T=300, H=256, V=3000, seed=46)
     a = flce.FusedLinearCrossEntropy(wl.H, wl.V, "bf16", chunk_tokens=256)
