@@ -24,10 +24,6 @@ constexpr float kNegInf = -__builtin_inff();
 __device__ __forceinline__ float exp_fast(float x) {
   return __builtin_amdgcn_exp2f(x * kLog2e);
 }
-// ln x through the hardware base-2 logarithm (v_log_f32).
-__device__ __forceinline__ float log_fast(float x) {
-  return __builtin_amdgcn_logf(x) * kLn2;
-}
 
 template <typename T> struct Elem;
 template <> struct Elem<bf16> {
