@@ -12,9 +12,12 @@ written once per G chunks, and the W^T copy makes the dX contraction read
     C = 4096, G = 1: 40.2 at 0.52; W read as stored: 39.5 at 0.54), G = 2
     above (8192 x 8192 x 128256: 39.4 ms; G = 1: 42.2); the W^T copy
     unless it would be as large as a bf16 T x V buffer (H >= T).
-  * H < 2048: C = 8192, G = 1 for batches of 32768 tokens or more
-    (65536 x 512 x 16000), else C = 2048, G = 1 reading W as stored
-    (4096 x 512 x 16000: 0.37 ms; C = 1024, G = 2: 0.43 ms).
+  * H < 2048: for batches of 32768 tokens or more, G = 1 and the largest
+    C of 8192, 16384 and 32768 that is at most half the batch, so that the
+    exponentials stay within half of a T x V buffer (65536 x 512 x 16000:
+    C = 32768 4.00 ms at 0.55 of the buffer, 16384 4.14 ms, 8192 4.43 ms);
+    smaller batches C = 2048, G = 1 reading W as stored (4096 x 512 x 16000:
+    0.37 ms; C = 1024, G = 2: 0.43 ms).
   * fp32: one chunk of up to 4096 tokens, G = 1.
 C never exceeds the batch (rounded up to 256) and G the number of chunks.
 """
@@ -30,7 +33,8 @@ def suggest_launch(T: int, H: int, V: int, dtype: str = "bf16"):
         G = 4 if H <= 4096 else 2
         wcopy = H < T
     elif T >= 32768:
-        C, G, wcopy = 8192, 1, True
+        C = max(c for c in (8192, 16384, 32768) if 2 * c <= T)
+        G, wcopy = 1, True
     else:
         C, G, wcopy = 2048, 1, False
     tpad = max(256, -(-max(T, 1) // 256) * 256)

@@ -83,7 +83,7 @@ WORKLOADS = {
 # 8192 tokens deep, so the dW tiles are written twice per call instead of
 # four times.  The large ragged head (T = H = 8192) cannot stay below T x V
 # (W^T alone is H V = T V elements there); it takes the fastest setting.
-LAUNCH = {1: (256, 1), 2: (2048, 1), 3: (8192, 1), 4: (2048, 4), 5: (2048, 2)}
+LAUNCH = {1: (256, 1), 2: (2048, 1), 3: (32768, 1), 4: (2048, 4), 5: (2048, 2)}
 # The other entry points at the Llama-3-8B head's shape, chosen the same
 # way: the forward-only call has no dW GEMM; a vocabulary shard's head is
 # V / N wide; the soft-target head also holds the teacher's chunk of
