@@ -367,19 +367,28 @@ def measured_traffic(kernel_kind: str, launch):
     return None
 
 
-def per_kernel_rooflines(kernels, T, H, V, dtype, mfma_peak, dz_in_place=False):
+def dw_reads_stored(dtype, H, V, chunk, dw_chunks) -> bool:
+    """Whether the dW contraction reads P (exponentials or dZ) as stored,
+    with no dZ^T written: the rule include/flce.h states (bf16, H <= 4096,
+    the G chunks of P under 2^31 bytes)."""
+    vpad = -(-V // 256) * 256
+    return dtype == "bf16" and H <= 4096 and dw_chunks * chunk * vpad * 2 < 2 ** 31
+
+
+def per_kernel_rooflines(kernels, T, H, V, dtype, mfma_peak, dz_in_place=False, dzt=True):
     """Achieved rate of each timed kernel of one fwd+bwd step against its own
     bound, from algorithmic work only: 2 T H V flops for each contraction;
     for the bandwidth passes the bytes they must move (the dZ pass reads the
-    exponentials and writes dZ^T -- and dZ over the exponentials too with
-    dz_in_place; its rewrite of the few tiles whose reference lies below
-    their row's is not counted; a transpose reads and writes its matrix once;
-    the merge reads the (max, sum, argmax) partials and writes alpha, 16
-    bytes per (token, 128-column tile))."""
+    exponentials and writes dZ over them with dz_in_place and dZ^T with
+    dzt; its rewrite of the few tiles whose reference lies below their
+    row's is not counted; a transpose reads and writes its matrix once; the
+    merge reads the (max, sum, argmax) partials and writes alpha, 16 bytes
+    per (token, 128-column tile))."""
     es = 2 if dtype == "bf16" else 4
     nt = -(-V // 128)
+    fixup_bytes = (1.0 + float(dz_in_place) + float(dzt)) * T * V * es
     work = {"logits_gemm": ("mfma", 2.0 * T * H * V), "dx_gemm": ("mfma", 2.0 * T * H * V),
-            "dw_gemm": ("mfma", 2.0 * T * H * V), "fixup_dz": ("hbm", (3.0 if dz_in_place else 2.0) * T * V * es),
+            "dw_gemm": ("mfma", 2.0 * T * H * V), "fixup_dz": ("hbm", fixup_bytes),
             "transpose_w": ("hbm", 2.0 * V * H * es), "transpose_x": ("hbm", 2.0 * T * H * es),
             "finalize": ("hbm", 16.0 * nt * T)}
     out = {}
@@ -752,8 +761,9 @@ def main():
             roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": 8000.0,
                         "unit": "GB/s", "frac": None, "traffic": None, "source": source}
         if not (fwd_only or n_shards > 1 or Ht > 0):
-            kernel_rooflines = per_kernel_rooflines(kernels, T, H, V, wl.dtype, peak,
-                                                    args.dz_in_place)
+            kernel_rooflines = per_kernel_rooflines(
+                kernels, T, H, V, wl.dtype, peak, args.dz_in_place,
+                not dw_reads_stored(wl.dtype, H, V, op.chunk_tokens, op.dw_chunks))
 
     cpu = None
     if args.cpu_sample > 0 and n_shards == 1 and Ht == 0:

@@ -63,14 +63,15 @@ typedef struct {
   int64_t hidden;       /* H: > 0, multiple of 8 (bf16) or 4 (fp32)          */
   int64_t vocab;        /* V: > 0                                              */
   int32_t dtype;        /* flce_dtype_t                                        */
-  int32_t dw_chunks;    /* G: chunks whose exponentials (or dZ^T) are kept for
+  int32_t dw_chunks;    /* G: chunks whose exponentials, dZ or dZ^T are kept for
                            one dW GEMM of depth K = G*C; 0 = default (1), at
                            most 8.  The dW tiles are then read and written
                            once per G chunks instead of once per chunk, for
                            about (G-1)*C*V more workspace elements.            */
   int64_t chunk_tokens; /* C: tokens per chunk; 0 = default (4096).  Rounded up
                            to a multiple of 256.  The workspace is O(G*C*V +
-                           V*H) (O((1+G)*C*V + V*H) where dZ^T is written) and
+                           V*H) (O((1+G)*C*V + V*H) where dZ^T is written;
+                           the soft-target call adds C*V for the teacher) and
                            does not depend on the number of tokens T.          */
   int32_t flags;        /* 0, or FLCE_FLAG_NO_WEIGHT_COPY and/or FLCE_FLAG_DZ_IN_PLACE */
 } flce_config_t;
@@ -91,14 +92,15 @@ typedef struct {
  * sets the target's column; the dX GEMM reads the exponentials and finishes
  * each output row with the row's scale and the target's correction times
  * that row of W, and the dW GEMM reads them as stored against X^T scaled by
- * the row scales (bf16, H <= 4096 and G*C*Vpad*2 < 2^31; otherwise a pass
- * writes dZ^T for it).  With this flag a pass writes dZ over the
- * exponentials and dZ^T, and both GEMMs read those (one to two more T*V
- * writes; measured ~4 % slower per call at 16384 x 4096 x 128256, and
- * faster where many rows' tiles sit far below their row's reference, as
- * with a few far-outlying rows of W).  Same results to the tolerances.
- * The soft-target call always writes dZ (its rows hold two sets of
- * exponentials). */
+ * the row scales.  With this flag a pass writes dZ over the exponentials
+ * and both GEMMs read it (one more T*V write; measured ~3 % slower per call
+ * at 16384 x 4096 x 128256, and faster where many rows' tiles sit far below
+ * their row's reference, as with a few far-outlying rows of W).  Same
+ * results to the tolerances.  The soft-target call always writes dZ (its
+ * rows hold two sets of exponentials).  Either way the dW GEMM reads P --
+ * exponentials or dZ -- as stored where the dtype is bf16, H <= 4096 and
+ * G*C*Vpad*2 < 2^31 bytes (Vpad = V rounded up to 256); elsewhere the pass
+ * also writes dZ^T for it. */
 #define FLCE_FLAG_DZ_IN_PLACE 2
 
 typedef struct flce_handle* flce_handle_t;

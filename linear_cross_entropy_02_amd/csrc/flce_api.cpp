@@ -48,9 +48,10 @@ const char* kKindNames[K_NUM] = {"count_valid",   "transpose_w", "transpose_x", 
 
 constexpr int64_t kDefaultChunk = 4096;
 constexpr int kMaxDwChunks = 8;
-// The dW GEMM reads the exponentials as stored (no dZ pass, no dZ^T) up to
-// this hidden size: its transposing LDS reads cost ~7 % of that GEMM, whose
-// time grows with H while the pass it replaces does not.
+// The dW GEMM reads P -- the exponentials, or dZ where the dZ pass wrote it
+// in place -- as stored (no dZ^T) up to this hidden size: its transposing
+// LDS reads cost ~7 % of that GEMM, whose time grows with H while the
+// transposed write they replace does not.
 #ifndef FLCE_DW_READS_P_MAX_H
 #define FLCE_DW_READS_P_MAX_H 4096
 #endif
@@ -75,8 +76,10 @@ struct flce_handle {
   int splitk_alloc = 1;  // split-K planes the workspace holds for a full chunk
   bool w_copy = true;      // dX reads W^T (a copy made per call) or W as stored
   bool dz_in_dx = true;    // dZ formed inside the dX contraction (not FLCE_FLAG_DZ_IN_PLACE)
-  // ... and the dW contraction reads the exponentials as stored, G chunks of
-  // them side by side (bf16, hard targets, G C Vpad 2 < 2^31 bytes): no dZ^T
+  // The dW contraction reads P as stored, G chunks of it side by side (bf16,
+  // H up to FLCE_DW_READS_P_MAX_H, G C Vpad 2 < 2^31 bytes): the exponentials
+  // against beta-scaled X^T when dZ is formed inside the contractions, else
+  // the dZ the dZ pass wrote in place; no dZ^T either way
   bool dw_reads_p = false;
   size_t ws_bytes = 0;
   char* ws = nullptr;
@@ -287,8 +290,8 @@ flce_status_t configure(const flce_config_t* cfg, int64_t Ht, flce_handle* h, La
   h->w_copy = !no_wcopy;
   h->dz_in_dx = (cfg->flags & FLCE_FLAG_DZ_IN_PLACE) == 0;
   h->Vpad = round_up(V, 256);
-  // the dW GEMM's one buffer descriptor spans the G chunks' exponentials
-  h->dw_reads_p = h->dz_in_dx && dt == Dt::BF16 && Ht == 0 && H <= FLCE_DW_READS_P_MAX_H &&
+  // the dW GEMM's one buffer descriptor spans the G chunks of P
+  h->dw_reads_p = dt == Dt::BF16 && H <= FLCE_DW_READS_P_MAX_H &&
                   G * C * h->Vpad * 2 < ((int64_t)1 << 31);
   h->nt = cdiv64(V, kPartialWidth);
   {
@@ -537,18 +540,19 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
     // the batch's last is full, so the slots of a group are contiguous in K
     const int64_t gs = c % G;
     const bool last = t0 + Cc >= T;
-    // dZ formed inside the contractions (hard targets); dW reading the
-    // exponentials, each chunk's in its own slot of the G-chunk buffer
+    // dZ formed inside the contractions (hard targets); dW reading P as
+    // stored (the exponentials when fused, else dZ), each chunk's in its own
+    // slot of the G-chunk buffer
     const bool fused = !soft && h->dz_in_dx;
-    const bool dw_p = fused && h->dw_reads_p;
+    const bool dw_p = h->dw_reads_p;
     char* const Pc = (char*)h->P + (dw_p ? (size_t)gs * C * Vpad * es : 0);
     float* const beta_c = h->beta + (dw_p ? gs * C : 0);
 
     // X^T of the whole group at its first chunk (X is an input, all of it
     // available): one transpose per dW GEMM; the previous group's dW GEMM,
     // earlier in the stream, has finished reading the buffer.  When dW reads
-    // the exponentials, X^T carries the rows' beta and is made at the
-    // group's last chunk instead, once all of them are known.
+    // P, X^T is made at the group's last chunk instead, carrying the rows'
+    // beta when P holds the exponentials (all of them known by then).
     if (gs == 0 && !dw_p) {
       const int64_t Cg = (T - t0 < GC) ? (T - t0) : GC;
       FLCE_LAUNCH(K_TRANSPOSE_X, launch_transpose(dt, Xc, (int)Cg, (int)H, H, h->Xt, GC,
@@ -678,13 +682,13 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       FLCE_LAUNCH(K_ROWREF, launch_rowref(dt, ra, s));
     }
 
-    // The dZ pass: dZ^T for the dW contraction (with dZ over the
-    // exponentials too unless dZ is formed inside dX); none when dW reads
-    // the exponentials themselves
+    // The dZ pass: dZ over the exponentials unless dZ is formed inside the
+    // contractions, and dZ^T for the dW contraction unless it reads P;
+    // nothing to do when both hold
     FixupArgs xa{};
     xa.P = Pc;
     xa.ldp = Vpad;
-    xa.Pt = (char*)h->Pt + (size_t)gs * C * es;
+    xa.Pt = dw_p ? nullptr : (char*)h->Pt + (size_t)gs * C * es;
     xa.ldpt = GC;
     xa.M = (int)Cc;
     xa.rows_out = (int)Ck;
@@ -703,7 +707,8 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       xa.alpha_q = h->pmq;
     }
     xa.write_rows = !fused;
-    if (!dw_p) FLCE_LAUNCH(K_FIXUP, launch_fixup(dt, xa, s));
+    xa.write_t = !dw_p;
+    if (xa.write_rows || xa.write_t) FLCE_LAUNCH(K_FIXUP, launch_fixup(dt, xa, s));
 
     // dX_c = dZ W   (M = Cc, N = H, K = vocabulary); without soft targets
     // A holds the exponentials and dZ is formed in the contraction
@@ -761,8 +766,8 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       }
     }
     // dW (+)= dZ^T X over the chunks of a group (M = V, N = H, K = gs C + Ck)
-    // once its last chunk is in, as P^T (beta X) when dW reads the
-    // exponentials; the first group stores.
+    // once its last chunk is in (as P^T (beta X) when dW reads the
+    // exponentials); the first group stores.
     if (gs == G - 1 || last) {
       const int64_t Kg = gs * C + Ck;
       TileCfg tc;
@@ -770,15 +775,17 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       plan_gemm(V, H, Kg, 1, &tc, &splits);
       GemmOutArgs ga{};
       if (dw_p) {
-        // dW = sum_t P_t^T (beta_t X_t): A is the group's exponentials as
-        // stored (token rows, K = its tokens exactly: rows past them read as
-        // zero), B the rows' X^T scaled by beta; the target columns hold
-        // dZ / beta (set by the merge)
+        // dW = sum_t P_t^T (beta_t X_t) with the exponentials (the target
+        // columns hold dZ / beta, set by the merge), or sum_t dZ_t^T X_t with
+        // dZ in place: A is the group's P as stored (token rows, K = its
+        // tokens exactly: rows past them read as zero), B the rows' X^T,
+        // scaled by beta in the first case
         const int64_t g0 = t0 - gs * C;  // the group's first token
         const int64_t Cg = gs * C + Cc;
         FLCE_LAUNCH(K_TRANSPOSE_X,
                     launch_transpose(dt, (const char*)X + (size_t)g0 * H * es, (int)Cg, (int)H, H,
-                                     h->Xt, GC, (int)round_up(Cg, 64), s, h->beta));
+                                     h->Xt, GC, (int)round_up(Cg, 64), s,
+                                     fused ? h->beta : nullptr));
         ga.A = h->P;
         ga.lda = Vpad;
         ga.a_stored = true;

@@ -45,9 +45,9 @@ constexpr int kPartialWidth = 128;
 hipError_t launch_logits(Dt dt, const LogitsArgs& a, hipStream_t s);
 
 // dX = dZ W with dZ formed inside the contraction: A is the chunk's stored
-// exponentials P, scaled in registers by 2^-shift (see FinalizeArgs), and
-// the output row t is beta_t acc_t + corr_t W[y_t - y_shift] (the target
-// term only when that row of W is in [0, V)).
+// exponentials P, brought to one reference per row by the row-reference
+// pass (see FinalizeArgs), and the output row t is beta_t acc_t + corr_t
+// W[y_t - y_shift] (the target term only when that row of W is in [0, V)).
 struct DxFuse {
   const float* beta;
   const float* corr;
@@ -172,7 +172,7 @@ hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
 
 struct FixupArgs {
   void* P; int64_t ldp;          // in: exp(z - m_tile); out: dZ (in place)
-  void* Pt; int64_t ldpt;        // out: dZ^T, [Vpad x ldpt]
+  void* Pt; int64_t ldpt;        // out: dZ^T, [Vpad x ldpt] (unused without write_t)
   int M;                         // valid rows
   int rows_out;                  // rows written to Pt (zero beyond M)
   int V, Vpad, nt;
@@ -186,6 +186,7 @@ struct FixupArgs {
   const void* Pq = nullptr;      // soft targets: teacher exponentials, subtracted
   const float* alpha_q = nullptr;  //   with this scale, [nt x ldr]
   bool write_rows = true;        // false: only dZ^T is written (P keeps the exponentials)
+  bool write_t = true;           // false: only dZ is written (dW reads it as stored)
 };
 hipError_t launch_fixup(Dt dt, const FixupArgs& a, hipStream_t s);
 

@@ -1238,6 +1238,7 @@ __global__ void __launch_bounds__(256) fixup_kernel(FixupArgs a) {
       for (int k = 0; k < EPV; ++k) tile[r][cv * EPV + k] = Elem<T>::from_f32(0.f);
     }
   }
+  if (!a.write_t) return;  // block-uniform
   __syncthreads();
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
@@ -1314,7 +1315,7 @@ __global__ void __launch_bounds__(256) fixup_bf16_kernel(FixupArgs a) {
       for (int k = 0; k < 8; ++k) d[k] = (yl == v + k) ? dz : d[k];
     }
     ov[p] = pack8_bf16(d);
-    tile[r * 32 + (cv ^ ((r >> 3) & 7))] = ov[p];
+    if (a.write_t) tile[r * 32 + (cv ^ ((r >> 3) & 7))] = ov[p];
   }
   if (a.write_rows) {
 #pragma unroll
@@ -1323,6 +1324,7 @@ __global__ void __launch_bounds__(256) fixup_bf16_kernel(FixupArgs a) {
       if (t < a.M) *(uint4*)(P + (int64_t)t * a.ldp + v) = ov[p];
     }
   }
+  if (!a.write_t) return;  // block-uniform: dZ only
   __syncthreads();
   // phase 2: token group tg = tid % 8, column octet vo = tid / 8
   const int tg = tid & 7, vo = tid >> 3;
@@ -1353,6 +1355,7 @@ __global__ void __launch_bounds__(256) fixup_bf16_kernel(FixupArgs a) {
 
 hipError_t launch_fixup(Dt dt, const FixupArgs& a, hipStream_t s) {
   if (a.rows_out <= 0) return hipSuccess;
+  if (!a.write_rows && !a.write_t) return hipSuccess;
   if (dt == Dt::BF16) {
     // Vpad is a multiple of 256 and rows_out of 64: the grid covers them exactly
     dim3 grid(cdiv(a.Vpad, kFixV), cdiv(a.rows_out, kFixT));

@@ -42,6 +42,17 @@ def test_per_kernel_rooflines():
     # dZ written in place as well: one more T x V; fp32 doubles the bytes
     r2 = bench.per_kernel_rooflines(kernels, T, H, V, "f32", 157.3, dz_in_place=True)
     assert r2["fixup_dz"]["achieved"] == round(3.0 * T * V * 4 / 0.5e-3 / 1e9, 1)
+    # in place with dW reading dZ as stored: no dZ^T
+    r3 = bench.per_kernel_rooflines(kernels, T, H, V, "bf16", 2500.0, dz_in_place=True, dzt=False)
+    assert r3["fixup_dz"]["achieved"] == round(2.0 * T * V * 2 / 0.5e-3 / 1e9, 1)
+
+
+def test_dw_reads_stored_rule():
+    assert bench.dw_reads_stored("bf16", 4096, 128256, 2048, 4)        # 2.1 GB of P
+    assert not bench.dw_reads_stored("bf16", 4104, 128256, 2048, 4)    # wider than 4096
+    assert not bench.dw_reads_stored("f32", 512, 16000, 2048, 1)
+    assert bench.dw_reads_stored("bf16", 512, 128256, 8192, 1)        # just under 2^31 bytes
+    assert not bench.dw_reads_stored("bf16", 512, 128256, 8192, 2)    # over 2^31 bytes of P
 
 
 def test_traffic_is_reported_only_for_the_sources_and_launch_it_was_taken_with(tmp_path,

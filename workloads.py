@@ -88,7 +88,7 @@ LAUNCH = {1: (256, 1), 2: (2048, 1), 3: (32768, 1), 4: (2048, 4), 5: (2048, 2)}
 # way: the forward-only call has no dW GEMM; a vocabulary shard's head is
 # V / N wide; the soft-target head also holds the teacher's chunk of
 # exponentials.
-LAUNCH_MODES = {"forward": (4096, 1), "shard": (4096, 1), "distill": (2048, 3)}
+LAUNCH_MODES = {"forward": (4096, 1), "shard": (4096, 1), "distill": (2048, 4)}
 
 
 # Workloads whose handle reads W as stored in the dX GEMM instead of a
