@@ -27,23 +27,26 @@ def noalloc_call(wl, X, W, y, out, chunk, dw_chunks=0, flags=0):
                                      dw_chunks=dw_chunks, flags=flags)
 
 
-@pytest.mark.parametrize("wl,chunk,dwc,wcopy", [
-    (workloads.WORKLOADS[2], 1024, 1, True),                                 # 4096 x 512 x 16000
-    (workloads.WORKLOADS[5].with_shape(T=3000, H=1024, V=9000, seed=61), 1024, 2, False),
-    (workloads.WORKLOADS[1].with_shape(T=600, H=256, V=3000, seed=62), 256, 1, True),  # fp32
-], ids=["layer-shape", "outlier-head-no-wcopy-G2", "fp32"])
-def test_noalloc_equals_handle_on_two_calls(wl, chunk, dwc, wcopy):
+@pytest.mark.parametrize("wl,chunk,dwc,wcopy,in_place", [
+    (workloads.WORKLOADS[2], 1024, 1, True, False),                          # 4096 x 512 x 16000
+    (workloads.WORKLOADS[5].with_shape(T=3000, H=1024, V=9000, seed=61), 1024, 2, False, False),
+    (workloads.WORKLOADS[1].with_shape(T=600, H=256, V=3000, seed=62), 256, 1, True, False),
+    # dZ written in place, which dW reads as stored (G chunks of it)
+    (workloads.WORKLOADS[4].with_shape(T=2000, H=512, V=8000, seed=63), 512, 2, True, True),
+], ids=["layer-shape", "outlier-head-no-wcopy-G2", "fp32", "dz-in-place-G2"])
+def test_noalloc_equals_handle_on_two_calls(wl, chunk, dwc, wcopy, in_place):
     import torch
-    flags = 0 if wcopy else flce.FLCE_FLAG_NO_WEIGHT_COPY
+    flags = (0 if wcopy else flce.FLCE_FLAG_NO_WEIGHT_COPY) | \
+        (flce.FLCE_FLAG_DZ_IN_PLACE if in_place else 0)
     op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=chunk, dw_chunks=dwc,
-                                      weight_copy=wcopy)
+                                      weight_copy=wcopy, dz_in_place=in_place)
     assert op.workspace_bytes <= flce.FLCE_NOALLOC_SCRATCH_BYTES
     for k, T in enumerate((wl.T, wl.T // 3 + 5)):
         w = wl.with_shape(T=T, seed=wl.seed + 100 * k)
         inp = workloads.generate(w, keep_f32=False)
         X, W, y = workloads.to_torch(inp, "cuda")
         print(f"[gpu-noalloc] {w.name} call {k}: T={T} H={w.H} V={w.V} chunk={chunk} G={dwc} "
-              f"wcopy={wcopy}", flush=True)
+              f"wcopy={wcopy} in_place={in_place}", flush=True)
         ref = op.fwd_bwd(X, W, y, w.ignore_index, w.reduction)
         out = op.alloc_outputs(T, "cuda")
         for t in out.values():
