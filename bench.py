@@ -240,7 +240,8 @@ def summarize_profiles(d: str):
     fetch = per_kernel("prof_fetch", "FETCH_SIZE")
     write = per_kernel("prof_write", "WRITE_SIZE")
     import workloads
-    traffic = {"source_hash": kernel_source_hash(), "launch": list(workloads.launch_config(4)),
+    traffic = {"source_hash": kernel_source_hash(),
+               "launch": list(workloads.launch_config(4)) + [workloads.weight_copy(4)],
                "fetch_scale": f_scale, "write_scale": w_scale,
                "kernels": {}}
     lines = ["# HBM traffic per launch, fused linear-CE fwd+bwd, llama3-8b head "
@@ -348,7 +349,8 @@ def summarize_profiles(d: str):
 def measured_traffic(kernel_kind: str, launch):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary, or None when the kernel sources or the launch configuration
-    (chunk, chunks per dW GEMM) differ from those it was taken with."""
+    (chunk, chunks per dW GEMM, W^T copy) differ from those it was taken
+    with."""
     try:
         with open(TRAFFIC_JSON) as f:
             t = json.load(f)
@@ -754,7 +756,7 @@ def main():
                         "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                         "traffic": None if (fwd_only or n_shards > 1 or Ht > 0 or
                                             args.workload != 4) else
-                        measured_traffic(dom, (op.chunk_tokens, op.dw_chunks)),
+                        measured_traffic(dom, (op.chunk_tokens, op.dw_chunks, wcopy)),
                         "flop_per_launch": flop_per_launch,
                         "avg_launch_ms": round(kernels[dom]["avg_ms"], 5), "source": source}
         else:

@@ -7,11 +7,13 @@ interpolates by hidden size.  They trade workspace for speed: the
 exponentials of G chunks are kept so that the fp32 dW tiles are read and
 written once per G chunks, and the W^T copy makes the dX contraction read
 16-byte fragments.
-  * H >= 2048: C = 2048, G = 4 up to H = 4096 (at 16384 x 4096 x 128256 a
-    step takes 38.8 ms at 0.79 of a bf16 T x V buffer; G = 2: 40.4 at 0.53;
-    C = 4096, G = 1: 40.2 at 0.52; W read as stored: 39.5 at 0.54), G = 2
-    above (8192 x 8192 x 128256: 39.4 ms; G = 1: 42.2); the W^T copy
-    unless it would be as large as a bf16 T x V buffer (H >= T).
+  * H >= 2048: C = 2048, G = 4 up to H = 4096, G = 2 above (8192 x 8192 x
+    128256: 39.4 ms; G = 1: 42.2), with W read as stored wherever the
+    library takes it (bf16, V H 2 < 2^31 bytes): at 16384 x 4096 x 128256
+    that costs 1-2 % of a step (41.0 against 40.6 ms on one box, 39.5
+    against 38.8 on another) and takes the workspace from 0.79 to 0.54 of a
+    bf16 T x V buffer (G = 2 with the copy: +4 % at 0.53; C = 4096, G = 1:
+    +3.6 % at 0.52).
   * H < 2048: for batches of 32768 tokens or more, G = 1 and the largest
     C of 8192, 16384 and 32768 that is at most half the batch, so that the
     exponentials stay within half of a T x V buffer (65536 x 512 x 16000:
@@ -31,7 +33,7 @@ def suggest_launch(T: int, H: int, V: int, dtype: str = "bf16"):
     elif H >= 2048:
         C = 2048
         G = 4 if H <= 4096 else 2
-        wcopy = H < T
+        wcopy = V * H * 2 >= 2 ** 31
     elif T >= 32768:
         C = max(c for c in (8192, 16384, 32768) if 2 * c <= T)
         G, wcopy = 1, True

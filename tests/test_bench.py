@@ -57,7 +57,7 @@ def test_dw_reads_stored_rule():
 
 def test_traffic_is_reported_only_for_the_sources_and_launch_it_was_taken_with(tmp_path,
                                                                              monkeypatch):
-    rec = {"source_hash": bench.kernel_source_hash(), "launch": [2048, 4],
+    rec = {"source_hash": bench.kernel_source_hash(), "launch": [2048, 4, False],
            "kernels": {"gemm<bf16,256x256,4w,LogitsEpi<bf16, false>>":
                        {"read_bytes": 3.0e9, "write_bytes": 0.5e9},
                        "gemm<bf16,256x256,4w,StoreEpi<float, false>>":
@@ -67,15 +67,16 @@ def test_traffic_is_reported_only_for_the_sources_and_launch_it_was_taken_with(t
     path = tmp_path / "traffic.json"
     path.write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "TRAFFIC_JSON", str(path))
-    assert bench.measured_traffic("logits_gemm", (2048, 4)) == 3_500_000_000
-    assert bench.measured_traffic("dx_gemm", (2048, 4)) == 2_250_000_000
-    assert bench.measured_traffic("dw_gemm", (2048, 4)) == 11_000_000_000
-    assert bench.measured_traffic("fixup_dz", (2048, 4)) is None
-    assert bench.measured_traffic("logits_gemm", (4096, 1)) is None   # other launch
+    assert bench.measured_traffic("logits_gemm", (2048, 4, False)) == 3_500_000_000
+    assert bench.measured_traffic("dx_gemm", (2048, 4, False)) == 2_250_000_000
+    assert bench.measured_traffic("dw_gemm", (2048, 4, False)) == 11_000_000_000
+    assert bench.measured_traffic("fixup_dz", (2048, 4, False)) is None
+    assert bench.measured_traffic("logits_gemm", (4096, 1, False)) is None   # other launch
+    assert bench.measured_traffic("logits_gemm", (2048, 4, True)) is None    # W^T copy
     path.write_text(json.dumps({**rec, "source_hash": "0" * 16}))
-    assert bench.measured_traffic("logits_gemm", (2048, 4)) is None   # other sources
+    assert bench.measured_traffic("logits_gemm", (2048, 4, False)) is None   # other sources
     monkeypatch.setattr(bench, "TRAFFIC_JSON", str(tmp_path / "missing.json"))
-    assert bench.measured_traffic("logits_gemm", (2048, 4)) is None
+    assert bench.measured_traffic("logits_gemm", (2048, 4, False)) is None
 
 
 def test_committed_traffic_matches_the_current_sources():

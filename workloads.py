@@ -93,10 +93,12 @@ LAUNCH_MODES = {"forward": (4096, 1), "shard": (4096, 1), "distill": (2048, 4)}
 
 # Workloads whose handle reads W as stored in the dX GEMM instead of a
 # transposed copy made per call: the 8192 x 8192 x 128256 head, where that
-# copy alone is as large as a bf16 T x V buffer, and the 4096 x 512 x 16000
+# copy alone is as large as a bf16 T x V buffer; the 4096 x 512 x 16000
 # layer, where dropping it leaves room for 2048-token chunks under that bound
-# (0.37 ms per step, against 0.42 with the copy and 1024-token chunks).
-NO_WEIGHT_COPY = {2, 5}
+# (0.37 ms per step, against 0.42 with the copy and 1024-token chunks); and
+# the 16384 x 4096 x 128256 head, where it takes the workspace from 0.79 to
+# 0.54 of a bf16 T x V buffer for 1-2 % of the step time.
+NO_WEIGHT_COPY = {2, 4, 5}
 
 
 def weight_copy(n: int, mode: str = "fwd_bwd") -> bool:
