@@ -184,6 +184,21 @@ __device__ __forceinline__ constexpr int read_slot(int n) {
   else
     return (n + FM) % (FM + FN);
 }
+// The same order counted in LDS read instructions: a fragment of an operand
+// read as stored (A with TA, B with TB) takes two transposing 8-byte reads,
+// each a slot of its own, so that the schedule spreads them like the others.
+// Returns 4 r + h for fragment r (as read_slot) and h = 0 (the whole
+// fragment), 1 (its first half) or 2 (its second half).
+template <int FM, int FN, int ORDER, bool TA, bool TB>
+__device__ __forceinline__ constexpr int read_part(int p) {
+  for (int n = 0; n < FM + FN; ++n) {
+    const int r = read_slot<FM, FN, ORDER>(n);
+    const bool tr = r < FM ? TA : TB;
+    if (p < (tr ? 2 : 1)) return 4 * r + (tr ? 1 + p : 0);
+    p -= tr ? 2 : 1;
+  }
+  return -1;
+}
 
 template <int FM, int FN>
 __device__ __forceinline__ void drain_fence(f4 (&acc)[FM][FN]) {
@@ -434,46 +449,46 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
             (uint32_t)((int64_t)k0 * g.ldb * ES));
     }
   };
-  // BT fragment: columns n16 .. n16 + 15 of the stage in B buffer bb, substep s
+  // Half h (1: k-rows k0 .. k0 + 3 of each group of 8, 2: the next four) of
+  // a fragment of a stage read as stored: elements c16 .. c16 + 15 of rows
+  // `row_bytes` long in the stage buffer at `buf`, substep s.  Into `f`'s
+  // first (h = 1) or second (h = 2) 8 bytes.
   const int tr_g = lane >> 4, tr_i = (lane >> 2) & 3, tr_q = lane & 3;
-  auto read_b_tr = [&](int bb, int n16, int s) -> uint4 {
-    const uint32_t buf = lds_base + 3 * G::kABufBytes + (uint32_t)bb * G::kBBufBytes;
-    const int u = (n16 >> 3) + (tr_q >> 1);
-    const int k0r = 32 * s + 8 * tr_g + tr_i;
-    const uint2 lo = lds_read_tr16(buf + k0r * (BN * 2) + ((u ^ tr_swz(k0r)) << 4) + (tr_q & 1) * 8);
-    const uint2 hi =
-        lds_read_tr16(buf + (k0r + 4) * (BN * 2) + ((u ^ tr_swz(k0r + 4)) << 4) + (tr_q & 1) * 8);
-    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  auto read_tr_half = [&](uint32_t buf, int row_bytes, int c16, int s, int h, uint4& f) {
+    const int u = (c16 >> 3) + (tr_q >> 1);
+    const int kr = 32 * s + 8 * tr_g + tr_i + (h == 2 ? 4 : 0);
+    const uint2 v = lds_read_tr16(buf + kr * row_bytes + ((u ^ tr_swz(kr)) << 4) + (tr_q & 1) * 8);
+    if (h == 1) {
+      f.x = v.x;
+      f.y = v.y;
+    } else {
+      f.z = v.x;
+      f.w = v.y;
+    }
   };
-  // AT fragment: rows m16 .. m16 + 15 of the stage in A buffer ab, substep s
-  auto read_a_tr = [&](int ab, int m16, int s) -> uint4 {
-    const uint32_t buf = lds_base + (uint32_t)ab * G::kABufBytes;
-    const int u = (m16 >> 3) + (tr_q >> 1);
-    const int k0r = 32 * s + 8 * tr_g + tr_i;
-    const uint2 lo = lds_read_tr16(buf + k0r * (BM * 2) + ((u ^ tr_swz(k0r)) << 4) + (tr_q & 1) * 8);
-    const uint2 hi =
-        lds_read_tr16(buf + (k0r + 4) * (BM * 2) + ((u ^ tr_swz(k0r + 4)) << 4) + (tr_q & 1) * 8);
-    return make_uint4(lo.x, lo.y, hi.x, hi.y);
-  };
-  // Fragment read r of substep s from A buffer ab / B buffer bb: r < FM
-  // reads A fragment r, else B fragment r - FM.
-  auto read_one = [&](int ab, int bb, int s, int r, uint4 (&fa)[FM], uint4 (&fb)[FN]) {
+  // LDS read `code` (read_part) of substep s from A buffer ab / B buffer bb:
+  // fragment r = code / 4 (r < FM: A fragment r, else B fragment r - FM),
+  // whole or one half.
+  auto read_one = [&](int ab, int bb, int s, int code, uint4 (&fa)[FM], uint4 (&fb)[FN]) {
+    const int r = code >> 2, h = code & 3;
     const int kv = 4 * s + (lane >> 4);
     if (r < FM) {
       if constexpr (!AT)
         fa[r] = lds[ab * (G::kABufBytes / 16) + swz(wm * G::WM + 16 * r + (lane & 15), kv)];
       else
-        fa[r] = read_a_tr(ab, wm * G::WM + 16 * r, s);
+        read_tr_half(lds_base + (uint32_t)ab * G::kABufBytes, BM * 2, wm * G::WM + 16 * r, s, h,
+                     fa[r]);
     } else if constexpr (!BT)
       fb[r - FM] = lds[(3 * G::kABufBytes + bb * G::kBBufBytes) / 16 +
                        swz(wn * G::WN + 16 * (r - FM) + (lane & 15), kv)];
     else
-      fb[r - FM] = read_b_tr(bb, wn * G::WN + 16 * (r - FM), s);
+      read_tr_half(lds_base + 3 * G::kABufBytes + (uint32_t)bb * G::kBBufBytes, BN * 2,
+                   wn * G::WN + 16 * (r - FM), s, h, fb[r - FM]);
   };
 
   constexpr int ORD = Epi::kOrder;
   static_assert(ORD >= 0 && ORD <= 2, "MFMA order");
-  constexpr int NR = FM + FN;  // fragment reads per substep
+  constexpr int NR = FM * (AT ? 2 : 1) + FN * (BT ? 2 : 1);  // LDS reads per substep
   constexpr int NM = FM * FN;  // MFMAs per substep
   constexpr int NDMA = A_INS + B_INS;
   // each phase carries NR reads and the DMAs of one operand
@@ -500,7 +515,9 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
     __builtin_amdgcn_s_waitcnt(kWaitStage0);  // initial accumulators and stage 0 landed
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int n = 0; n < NR; ++n) read_one(0, 0, 0, ORD == 2 ? read_slot<FM, FN, ORD>(n) : n, fa0, fb0);
+    for (int n = 0; n < NR; ++n)
+      read_one(0, 0, 0,
+               (AT || BT || ORD == 2) ? read_part<FM, FN, ORD, AT, BT>(n) : 4 * n, fa0, fb0);
     // stage kt sits in A buffer kt % 3 and B buffer kt % 2
     int a_cur = 0, a_nxt = 1, a_dma = 2;
     for (int kt = 0; kt < nk; ++kt) {
@@ -517,7 +534,8 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
           if (k % 3 == 2 && k / 3 < A_INS)
             issue_a(a_dma, k2, k / 3);
           else
-            read_one(a_cur, b_cur, 1, read_slot<FM, FN, ORD>(k - min((k + 1) / 3, A_INS)), fa1, fb1);
+            read_one(a_cur, b_cur, 1, read_part<FM, FN, ORD, AT, BT>(k - min((k + 1) / 3, A_INS)),
+                     fa1, fb1);
         }
       }
       __builtin_amdgcn_s_waitcnt(kWaitMid);  // stage kt + 1 landed, own reads done
@@ -533,7 +551,8 @@ __global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmShape g, Epi ep
           if (k % 3 == 2 && k / 3 < B_INS)
             issue_b(b_cur, k2, k / 3);
           else
-            read_one(a_nxt, b_nxt, 0, read_slot<FM, FN, ORD>(k - min((k + 1) / 3, B_INS)), fa0, fb0);
+            read_one(a_nxt, b_nxt, 0, read_part<FM, FN, ORD, AT, BT>(k - min((k + 1) / 3, B_INS)),
+                     fa0, fb0);
         }
       }
       const int t = a_cur;
