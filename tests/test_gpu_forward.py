@@ -158,3 +158,22 @@ def test_forward_full_size_llama_head():
     check_argmax(to_np(out["argmax"])[rows], ref["argmax"], ref["zmax"], inp.X, inp.W, rows,
                  argmax_margin(inp.X, inp.W, rows))
     op.close()
+
+
+@pytest.mark.parametrize("wl,chunk", [CASES[3], CASES[4]], ids=["zipf-head", "outlier-head"])
+def test_forward_on_a_handle_without_the_weight_copy(wl, chunk):
+    # the forward-only call never runs the dX contraction, so a handle that
+    # reads W as stored (no W^T copy in its workspace) gives the same bits
+    import torch
+    inp = workloads.generate(wl)
+    X, W, y = workloads.to_torch(inp, "cuda")
+    a = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=chunk)
+    b = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=chunk, weight_copy=False)
+    assert b.workspace_bytes < a.workspace_bytes
+    ra = a.forward(X, W, y, wl.ignore_index, wl.reduction)
+    rb = b.forward(X, W, y, wl.ignore_index, wl.reduction)
+    torch.cuda.synchronize()
+    for k in ra:
+        assert torch.equal(ra[k], rb[k]), k
+    a.close()
+    b.close()

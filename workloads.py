@@ -99,10 +99,18 @@ LAUNCH_MODES = {"forward": (4096, 1), "shard": (4096, 1), "distill": (2048, 4)}
 # the 16384 x 4096 x 128256 head, where it takes the workspace from 0.79 to
 # 0.54 of a bf16 T x V buffer for 1-2 % of the step time.
 NO_WEIGHT_COPY = {2, 4, 5}
+# The other entry points at the Llama-3-8B head's shape read W as stored as
+# well: the forward-only call never runs the dX contraction (the copy would
+# sit unused), and a vocabulary shard's head and the soft-target head measured
+# 0.2-0.4 % slower per step for a quarter to a half of a bf16 T x V buffer less
+# workspace.
+NO_WEIGHT_COPY_MODES = {"forward", "shard", "distill"}
 
 
 def weight_copy(n: int, mode: str = "fwd_bwd") -> bool:
-    return not (mode == "fwd_bwd" and n in NO_WEIGHT_COPY)
+    if mode != "fwd_bwd":
+        return mode not in NO_WEIGHT_COPY_MODES
+    return n not in NO_WEIGHT_COPY
 
 
 # Workloads whose handle writes dZ out for the dX contraction
