@@ -647,9 +647,10 @@ def main():
                                                  wl.V, red, lse_g, dXp, dWs)
             assert st1 == flce.FLCE_OK and st2 == flce.FLCE_OK, (st1, st2)
     else:
+        # the forward-only call runs on a forward-only handle (no backward buffers)
         op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=args.chunk,
                                           dw_chunks=args.dw_chunks, weight_copy=wcopy,
-                                          dz_in_place=args.dz_in_place)
+                                          dz_in_place=args.dz_in_place, forward_only=fwd_only)
     if n_shards > 1 or Ht > 0:
         pass  # step() is set above
     elif fwd_only:

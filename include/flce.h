@@ -73,7 +73,8 @@ typedef struct {
                            V*H) (O((1+G)*C*V + V*H) where dZ^T is written;
                            the soft-target call adds C*V for the teacher) and
                            does not depend on the number of tokens T.          */
-  int32_t flags;        /* 0, or FLCE_FLAG_NO_WEIGHT_COPY and/or FLCE_FLAG_DZ_IN_PLACE */
+  int32_t flags;        /* 0, or any of FLCE_FLAG_NO_WEIGHT_COPY, FLCE_FLAG_DZ_IN_PLACE and
+                           FLCE_FLAG_FORWARD_ONLY                             */
 } flce_config_t;
 
 /* The dX GEMM reads W in its stored [V x H] layout instead of a transposed
@@ -102,6 +103,15 @@ typedef struct {
  * G*C*Vpad*2 < 2^31 bytes (Vpad = V rounded up to 256); elsewhere the pass
  * also writes dZ^T for it. */
 #define FLCE_FLAG_DZ_IN_PLACE 2
+
+/* The handle serves only the forward-only calls (flce_forward and
+ * flce_vocab_shard_forward): its workspace holds the merge's partials, about
+ * 12*ceil(V/128)*C bytes, and a few small buffers -- no exponentials, no
+ * W^T, nothing of the backward -- so large chunks cost little memory.
+ * flce_fwd_bwd, flce_vocab_shard_backward and flce_fwd_bwd_noalloc return
+ * INVALID_ARGUMENT for it with nothing enqueued, and flce_distill_create
+ * refuses it (the soft-target call has no forward-only form). */
+#define FLCE_FLAG_FORWARD_ONLY 4
 
 typedef struct flce_handle* flce_handle_t;
 
@@ -168,8 +178,10 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W,
  *   argmax         [T]  int32    per-token argmax of z, lowest index on ties
  *   n_valid        [1]  int64    number of non-ignored tokens
  * Only the logits GEMM and the merge of its partials run: no T x V or
- * C x V values are written.  The handle's workspace is reused, so a handle
- * must not run flce_forward and flce_fwd_bwd concurrently.  Out-of-range
+ * C x V values are written, and a handle created with FLCE_FLAG_FORWARD_ONLY
+ * is enough.  The handle's
+ * workspace is reused, so a handle must not run flce_forward and
+ * flce_fwd_bwd concurrently.  Out-of-range
  * targets are treated as ignored and counted for flce_query_error.
  * Returns without enqueuing anything on an argument error.
  */

@@ -48,6 +48,7 @@ class flce_config_t(ctypes.Structure):
 
 FLCE_FLAG_NO_WEIGHT_COPY = 1
 FLCE_FLAG_DZ_IN_PLACE = 2
+FLCE_FLAG_FORWARD_ONLY = 4
 
 
 class FlceError(RuntimeError):
@@ -280,10 +281,13 @@ class FusedLinearCrossEntropy:
     fwd_bwd(X, W, y) returns a dict of device tensors: loss (float32 scalar),
     dX (X's dtype), dW (float32), lse (float32 [T]), argmax (int32 [T]) and
     n_valid (int64 scalar).  Gradients are for a loss gradient seed of 1.
+    forward_only=True makes a handle for forward() and shard_forward() alone
+    (FLCE_FLAG_FORWARD_ONLY: a workspace of the merge's partials only).
     """
 
     def __init__(self, hidden: int, vocab: int, dtype="bf16", chunk_tokens: int = 0,
-                 dw_chunks: int = 0, weight_copy: bool = True, dz_in_place: bool = False):
+                 dw_chunks: int = 0, weight_copy: bool = True, dz_in_place: bool = False,
+                 forward_only: bool = False):
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("FusedLinearCrossEntropy needs a HIP device")
@@ -291,7 +295,8 @@ class FusedLinearCrossEntropy:
         self.dtype = FLCE_BF16 if dtype == "bf16" else FLCE_F32
         self.hidden, self.vocab = hidden, vocab
         flags = (0 if weight_copy else FLCE_FLAG_NO_WEIGHT_COPY) | \
-            (FLCE_FLAG_DZ_IN_PLACE if dz_in_place else 0)
+            (FLCE_FLAG_DZ_IN_PLACE if dz_in_place else 0) | \
+            (FLCE_FLAG_FORWARD_ONLY if forward_only else 0)
         st, h = flce_create(hidden, vocab, self.dtype, chunk_tokens, dw_chunks, flags)
         if st != FLCE_OK:
             raise FlceError(st, "flce_create")

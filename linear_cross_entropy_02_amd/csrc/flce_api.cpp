@@ -76,6 +76,7 @@ struct flce_handle {
   int splitk_alloc = 1;  // split-K planes the workspace holds for a full chunk
   bool w_copy = true;      // dX reads W^T (a copy made per call) or W as stored
   bool dz_in_dx = true;    // dZ formed inside the dX contraction (not FLCE_FLAG_DZ_IN_PLACE)
+  bool fwd_only = false;   // FLCE_FLAG_FORWARD_ONLY: no buffer of the backward
   // The dW contraction reads P as stored, G chunks of it side by side (bf16,
   // H up to FLCE_DW_READS_P_MAX_H, G C Vpad 2 < 2^31 bytes): the exponentials
   // against beta-scaled X^T when dZ is formed inside the contractions, else
@@ -275,8 +276,11 @@ flce_status_t configure(const flce_config_t* cfg, int64_t Ht, flce_handle* h, La
   C = round_up(C, 256);
   const int64_t G = cfg->dw_chunks ? cfg->dw_chunks : 1;
   if (C * G > (1 << 20)) return FLCE_ERR_UNSUPPORTED;
-  if (cfg->flags & ~(FLCE_FLAG_NO_WEIGHT_COPY | FLCE_FLAG_DZ_IN_PLACE)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (cfg->flags & ~(FLCE_FLAG_NO_WEIGHT_COPY | FLCE_FLAG_DZ_IN_PLACE | FLCE_FLAG_FORWARD_ONLY))
+    return FLCE_ERR_INVALID_ARGUMENT;
   const bool no_wcopy = (cfg->flags & FLCE_FLAG_NO_WEIGHT_COPY) != 0;
+  const bool fwd_only = (cfg->flags & FLCE_FLAG_FORWARD_ONLY) != 0;
+  if (fwd_only && Ht) return FLCE_ERR_INVALID_ARGUMENT;  // the soft-target call has no forward
   // W as stored: bf16 transposing LDS reads; one buffer descriptor spans W,
   // whose size must stay below the out-of-range offset (2^31) that reads 0
   if (no_wcopy && (dt != Dt::BF16 || V * H * 2 >= ((int64_t)1 << 31))) return FLCE_ERR_UNSUPPORTED;
@@ -287,14 +291,16 @@ flce_status_t configure(const flce_config_t* cfg, int64_t Ht, flce_handle* h, La
   h->C = C;
   h->G = (int)G;
   h->Ht = Ht;
-  h->w_copy = !no_wcopy;
+  h->fwd_only = fwd_only;
+  h->w_copy = !no_wcopy && !fwd_only;
   h->dz_in_dx = (cfg->flags & FLCE_FLAG_DZ_IN_PLACE) == 0;
   h->Vpad = round_up(V, 256);
   // the dW GEMM's one buffer descriptor spans the G chunks of P
-  h->dw_reads_p = dt == Dt::BF16 && H <= FLCE_DW_READS_P_MAX_H &&
+  h->dw_reads_p = !fwd_only && dt == Dt::BF16 && H <= FLCE_DW_READS_P_MAX_H &&
                   G * C * h->Vpad * 2 < ((int64_t)1 << 31);
   h->nt = cdiv64(V, kPartialWidth);
-  {
+  h->splitk_alloc = 1;
+  if (!fwd_only) {
     TileCfg tc;
     int sp;
     plan_gemm(C, H, round_up(V, 64), 8, &tc, &sp);
@@ -307,20 +313,23 @@ flce_status_t configure(const flce_config_t* cfg, int64_t Ht, flce_handle* h, La
     off += round_up((int64_t)bytes, 256);
     return o;
   };
+  // a forward-only handle keeps the merge partials, the target logits and
+  // the loss and count partials; nothing of the backward
+  const bool bwd = !fwd_only;
   L->Wt = h->w_copy ? carve((size_t)H * h->Vpad * es) : 0;
-  L->P = carve((size_t)(h->dw_reads_p ? h->G * C : C) * h->Vpad * es);
-  L->Pt = h->dw_reads_p ? 0 : carve((size_t)h->Vpad * h->G * C * es);
-  L->Xt = carve((size_t)H * h->G * C * es);
+  L->P = bwd ? carve((size_t)(h->dw_reads_p ? h->G * C : C) * h->Vpad * es) : 0;
+  L->Pt = bwd && !h->dw_reads_p ? carve((size_t)h->Vpad * h->G * C * es) : 0;
+  L->Xt = bwd ? carve((size_t)H * h->G * C * es) : 0;
   L->pm = carve((size_t)C * h->nt * 4);
   L->ps = carve((size_t)C * h->nt * 4);
   L->pa = carve((size_t)C * h->nt * 4);
   L->zt = carve((size_t)C * 4);
   L->dz = carve((size_t)C * 4);
-  L->be = carve((size_t)(h->dw_reads_p ? h->G * C : C) * 4);
-  L->co = carve((size_t)C * 4);
-  L->sh = carve((size_t)C * round_up(h->nt, 16));
-  L->tc = carve((size_t)C * 4);
-  L->tv = carve((size_t)C * 4);
+  L->be = bwd ? carve((size_t)(h->dw_reads_p ? h->G * C : C) * 4) : 0;
+  L->co = bwd ? carve((size_t)C * 4) : 0;
+  L->sh = bwd ? carve((size_t)C * round_up(h->nt, 16)) : 0;
+  L->tc = bwd ? carve((size_t)C * 4) : 0;
+  L->tv = bwd ? carve((size_t)C * 4) : 0;
   L->lp = carve((size_t)cdiv64(C, kFinalizeRows) * 8);
   L->sk = h->splitk_alloc > 1 ? carve((size_t)h->splitk_alloc * C * H * 4) : 0;
   L->sc = carve(64);
@@ -340,19 +349,20 @@ flce_status_t configure(const flce_config_t* cfg, int64_t Ht, flce_handle* h, La
 void bind_workspace(flce_handle* h, const Layout& L, char* base) {
   h->ws = base;
   h->Wt = h->w_copy ? base + L.Wt : nullptr;
-  h->P = base + L.P;
-  h->Pt = h->dw_reads_p ? nullptr : base + L.Pt;
-  h->Xt = base + L.Xt;
+  const bool bwd = !h->fwd_only;
+  h->P = bwd ? base + L.P : nullptr;
+  h->Pt = bwd && !h->dw_reads_p ? base + L.Pt : nullptr;
+  h->Xt = bwd ? base + L.Xt : nullptr;
   h->pm = (float*)(base + L.pm);
   h->ps = (float*)(base + L.ps);
   h->pa = (int*)(base + L.pa);
   h->ztgt = (float*)(base + L.zt);
   h->dzt = (float*)(base + L.dz);
-  h->beta = (float*)(base + L.be);
-  h->corr = (float*)(base + L.co);
-  h->shift = (uint8_t*)(base + L.sh);
-  h->tcol = (int*)(base + L.tc);
-  h->tval = (float*)(base + L.tv);
+  h->beta = bwd ? (float*)(base + L.be) : nullptr;
+  h->corr = bwd ? (float*)(base + L.co) : nullptr;
+  h->shift = bwd ? (uint8_t*)(base + L.sh) : nullptr;
+  h->tcol = bwd ? (int*)(base + L.tc) : nullptr;
+  h->tval = bwd ? (float*)(base + L.tv) : nullptr;
   h->loss_part = (double*)(base + L.lp);
   h->splitk = h->splitk_alloc > 1 ? (float*)(base + L.sk) : nullptr;
   h->nvalid = (int64_t*)(base + L.sc);
@@ -909,7 +919,7 @@ flce_status_t flce_fwd_bwd(flce_handle_t h, const void* X, const void* W, const 
                            int64_t T, int64_t ignore_index, int32_t reduction, float* loss,
                            void* dX, float* dW, float* lse, int32_t* argmax, int64_t* n_valid,
                            void* stream) {
-  if (!h) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!h || h->fwd_only) return FLCE_ERR_INVALID_ARGUMENT;
   flce_status_t st =
       check_fwd_bwd_args(X, W, targets, T, reduction, loss, dX, dW, lse, argmax, n_valid);
   if (st != FLCE_OK) return st;
@@ -969,7 +979,7 @@ flce_status_t flce_vocab_shard_backward(flce_handle_t h, const void* X, const vo
                                         int64_t vocab_offset, int64_t vocab_total,
                                         int32_t reduction, const float* lse, void* dX_partial,
                                         float* dW_shard, void* stream) {
-  if (!h) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!h || h->fwd_only) return FLCE_ERR_INVALID_ARGUMENT;
   if (T < 0 || bad_shard(h, vocab_offset, vocab_total)) return FLCE_ERR_INVALID_ARGUMENT;
   if (reduction != FLCE_MEAN && reduction != FLCE_SUM) return FLCE_ERR_INVALID_ARGUMENT;
   if (!W_shard || !dW_shard) return FLCE_ERR_INVALID_ARGUMENT;
@@ -1048,6 +1058,7 @@ flce_status_t flce_fwd_bwd_noalloc(const flce_config_t* cfg, const void* X, cons
   Layout L;
   flce_status_t st = configure(cfg, 0, &h, &L);
   if (st != FLCE_OK) return st;
+  if (h.fwd_only) return FLCE_ERR_INVALID_ARGUMENT;
   st = check_fwd_bwd_args(X, W, targets, T, reduction, loss, dX, dW, lse, argmax, n_valid);
   if (st != FLCE_OK) return st;
   if (L.total > (size_t)FLCE_NOALLOC_SCRATCH_BYTES) {

@@ -77,7 +77,7 @@ def test_create_reports_unsupported_sizes_without_device(lib, hidden, vocab, chu
 
 
 @pytest.mark.parametrize("hidden,vocab,dtype,flags,status", [
-    (64, 100, flce.FLCE_BF16, 4, flce.FLCE_ERR_INVALID_ARGUMENT),          # unknown flag bit
+    (64, 100, flce.FLCE_BF16, 8, flce.FLCE_ERR_INVALID_ARGUMENT),          # unknown flag bit
     (64, 100, flce.FLCE_BF16, -1, flce.FLCE_ERR_INVALID_ARGUMENT),
     (64, 100, flce.FLCE_F32, flce.FLCE_FLAG_NO_WEIGHT_COPY, flce.FLCE_ERR_UNSUPPORTED),  # fp32
     # W of 2^31 bytes or more: one buffer descriptor no longer spans it below
@@ -240,3 +240,19 @@ def test_noalloc_rejects_without_device(lib):
 def load_null_cfg(lib):
     return lib.flce_fwd_bwd_noalloc(None, 16, 16, 16, 4, -100, flce.FLCE_MEAN, 16, 16, 16, None,
                                     None, None, None)
+
+
+def test_forward_only_flag_is_refused_by_the_soft_target_handle(lib):
+    # the soft-target call has no forward-only form: refused before any device call
+    st, h = flce.flce_distill_create(64, 100, flce.FLCE_BF16, 64,
+                                     flags=flce.FLCE_FLAG_FORWARD_ONLY)
+    assert st == flce.FLCE_ERR_INVALID_ARGUMENT and not h.value
+
+
+def test_noalloc_refuses_a_forward_only_config(lib):
+    # the allocation-free call is the fused forward+backward: a forward-only
+    # configuration is an argument error, returned before any device call
+    dt = flce.FLCE_BF16
+    st = flce.flce_fwd_bwd_noalloc(64, 100, dt, 16, 16, 16, 4, -100, flce.FLCE_MEAN, 16, 16, 16,
+                                   flags=flce.FLCE_FLAG_FORWARD_ONLY, stream=0)
+    assert st == flce.FLCE_ERR_INVALID_ARGUMENT

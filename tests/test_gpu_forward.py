@@ -177,3 +177,62 @@ def test_forward_on_a_handle_without_the_weight_copy(wl, chunk):
         assert torch.equal(ra[k], rb[k]), k
     a.close()
     b.close()
+
+
+def test_forward_only_handle():
+    """A handle made for the forward-only calls (FLCE_FLAG_FORWARD_ONLY):
+    the same bits as a full handle's forward, a workspace of the merge's
+    partials alone, a whole batch in one chunk, a vocabulary shard's
+    forward step, and the backward entry points refused with nothing
+    enqueued."""
+    import torch
+    wl = workloads.WORKLOADS[4].with_shape(T=3000, H=512, V=30000, seed=56)
+    inp = workloads.generate(wl)
+    X, W, y = workloads.to_torch(inp, "cuda")
+    full = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=1024)
+    fo = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=1024, forward_only=True)
+    nt = -(-wl.V // 128)
+    print(f"[gpu-forward] forward-only handle: workspace {fo.workspace_bytes} against "
+          f"{full.workspace_bytes}", flush=True)
+    assert fo.workspace_bytes <= 12 * nt * 1024 + (64 << 10)
+    a = full.forward(X, W, y, wl.ignore_index, wl.reduction)
+    b = fo.forward(X, W, y, wl.ignore_index, wl.reduction)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+    # the whole batch in one chunk: per-token results do not depend on the
+    # chunking; the loss sums the same terms in another order
+    one = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=3072, forward_only=True)
+    c = one.forward(X, W, y, wl.ignore_index, wl.reduction)
+    torch.cuda.synchronize()
+    for k in ("token_logprob", "lse", "argmax", "n_valid"):
+        assert torch.equal(a[k], c[k]), k
+    assert abs(float(a["loss"].item()) - float(c["loss"].item())) <= 1e-6 * abs(float(a["loss"].item()))
+    ref = flce_reference(inp.X, inp.W, inp.y, wl.ignore_index, wl.reduction, want_grads=False)
+    check_forward(c, ref, inp, wl)
+    # step 1 of a vocabulary shard runs on it too, and matches a full handle's
+    v0, v1 = 7000, 19000
+    sa = flce.FusedLinearCrossEntropy(wl.H, v1 - v0, wl.dtype, chunk_tokens=1024)
+    sb = flce.FusedLinearCrossEntropy(wl.H, v1 - v0, wl.dtype, chunk_tokens=1024,
+                                      forward_only=True)
+    Ws = W[v0:v1].contiguous()
+    ra = sa.shard_forward(X, Ws, y, v0, wl.V, wl.ignore_index)
+    rb = sb.shard_forward(X, Ws, y, v0, wl.V, wl.ignore_index)
+    torch.cuda.synchronize()
+    for k in ra:
+        assert torch.equal(ra[k], rb[k]), k
+    # the fused call and a shard's backward are refused before any work
+    out = full.alloc_outputs(wl.T, "cuda")
+    for t in out.values():
+        t.fill_(7)
+    torch.cuda.synchronize()
+    st = flce.flce_fwd_bwd(fo.handle, X, W, y, wl.T, wl.ignore_index, flce.FLCE_MEAN,
+                           out["loss"], out["dX"], out["dW"], out["lse"], out["argmax"],
+                           out["n_valid"])
+    assert st == flce.FLCE_ERR_INVALID_ARGUMENT
+    with pytest.raises(flce.FlceError):
+        sb.shard_backward(X, Ws, y, a["lse"], v0, wl.V, wl.ignore_index)
+    torch.cuda.synchronize()
+    assert float(out["loss"].item()) == 7.0
+    for op in (full, fo, one, sa, sb):
+        op.close()

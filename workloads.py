@@ -85,10 +85,11 @@ WORKLOADS = {
 # (W^T alone is H V = T V elements there); it takes the fastest setting.
 LAUNCH = {1: (256, 1), 2: (2048, 1), 3: (32768, 1), 4: (2048, 4), 5: (2048, 2)}
 # The other entry points at the Llama-3-8B head's shape, chosen the same
-# way: the forward-only call has no dW GEMM; a vocabulary shard's head is
-# V / N wide; the soft-target head also holds the teacher's chunk of
-# exponentials.
-LAUNCH_MODES = {"forward": (4096, 1), "shard": (4096, 1), "distill": (2048, 4)}
+# way: the forward-only call runs on a forward-only handle (the merge's
+# partials are all its workspace; 8192-token chunks measured faster than
+# 4096 and 16384); a vocabulary shard's head is V / N wide; the soft-target
+# head also holds the teacher's chunk of exponentials.
+LAUNCH_MODES = {"forward": (8192, 1), "shard": (4096, 1), "distill": (2048, 4)}
 
 
 # Workloads whose handle reads W as stored in the dX GEMM instead of a
