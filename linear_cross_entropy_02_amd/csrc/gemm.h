@@ -72,9 +72,10 @@ namespace flce {
 // MFMAs at the end of phase A kept free of side operations in kernels that
 // read B (dX reading W) or A (dW reading the exponentials) as stored (see
 // the K loop): measured on one box, 16 took the first 1.7 % faster and 8
-// the second 0.3 %, against none.
+// the second 0.3 %, against none; with the first's B fragment kept fixed
+// between issues, 24 measured 0.4 % faster than 16 and 8 0.3 % slower.
 #ifndef FLCE_TR_TAIL_B
-#define FLCE_TR_TAIL_B 16
+#define FLCE_TR_TAIL_B 24
 #endif
 #ifndef FLCE_TR_TAIL_A
 #define FLCE_TR_TAIL_A 8
