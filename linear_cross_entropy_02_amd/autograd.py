@@ -39,10 +39,12 @@ _lock = threading.Lock()
 
 
 def _handle(device: torch.device, stream: torch.cuda.Stream, H: int, V: int, dtype: str,
-            chunk_tokens: int, dw_chunks: int, weight_copy: bool = True) -> FusedLinearCrossEntropy:
-    """One handle per (device, stream, shape, dtype, chunking): a handle owns
-    its workspace and must not be used by two streams at once."""
-    key = (device.index, stream.cuda_stream, H, V, dtype, chunk_tokens, dw_chunks, weight_copy)
+            chunk_tokens: int, dw_chunks: int, weight_copy: bool = True,
+            forward_only: bool = False) -> FusedLinearCrossEntropy:
+    """One handle per (device, stream, shape, dtype, chunking, kind): a handle
+    owns its workspace and must not be used by two streams at once."""
+    key = (device.index, stream.cuda_stream, H, V, dtype, chunk_tokens, dw_chunks, weight_copy,
+           forward_only)
     with _lock:
         op = _handles.get(key)
         if op is None:
@@ -53,7 +55,8 @@ def _handle(device: torch.device, stream: torch.cuda.Stream, H: int, V: int, dty
                 old.close()
             with torch.cuda.device(device):
                 op = FusedLinearCrossEntropy(H, V, dtype, chunk_tokens=chunk_tokens,
-                                             dw_chunks=dw_chunks, weight_copy=weight_copy)
+                                             dw_chunks=dw_chunks, weight_copy=weight_copy,
+                                             forward_only=forward_only)
             _handles[key] = op
         else:
             _handles.move_to_end(key)
@@ -117,6 +120,40 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
         return gX, gW, None, None, None, None, None, None, None
 
 
+# Chunk of the forward-only handle that evaluation calls use: its workspace
+# is the merge's partials alone, and 8192-token chunks measured fastest at
+# the 16384 x 4096 x 128256 head.
+FORWARD_CHUNK = 8192
+
+
+def _forward_only(X, W, targets, ignore_index, reduction, chunk_tokens, check_targets):
+    """Loss and lse without gradients: the forward-only call on a
+    forward-only handle (a third of the work, no backward workspace)."""
+    if torch.is_autocast_enabled("cuda"):
+        X, W = X.to(torch.bfloat16), W.to(torch.bfloat16)
+    if X.dim() != 2 or W.dim() != 2 or X.shape[1] != W.shape[1]:
+        raise ValueError("X must be [T, H] and W [V, H]")
+    if X.dtype != W.dtype or X.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("X and W must share a dtype, bf16 or fp32")
+    if reduction not in ("mean", "sum"):
+        raise ValueError("reduction must be 'mean' or 'sum'")
+    dtype = "bf16" if X.dtype == torch.bfloat16 else "f32"
+    X, W, targets = X.contiguous(), W.contiguous(), targets.contiguous()
+    stream = torch.cuda.current_stream(X.device)
+    tpad = max(256, -(-max(X.shape[0], 1) // 256) * 256)
+    C = chunk_tokens or min(FORWARD_CHUNK, tpad)
+    op = _handle(X.device, stream, X.shape[1], W.shape[0], dtype, C, 1, False, forward_only=True)
+    out = op.forward(X, W, targets, ignore_index, reduction)
+    if check_targets:
+        st, bad = flce_query_error(op.handle, stream.cuda_stream)
+        if bad > 0:
+            raise ValueError(f"{bad} target(s) are neither ignore_index ({ignore_index}) nor "
+                             f"in [0, {W.shape[0]})")
+        if st != FLCE_OK:
+            raise FlceError(st, "flce_query_error")
+    return out["loss"], out["lse"]
+
+
 def linear_cross_entropy(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
                          ignore_index: int = -100, reduction: str = "mean",
                          chunk_tokens: int = 0, dw_chunks: int = 0,
@@ -131,10 +168,16 @@ def linear_cross_entropy(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor
     stored instead of a transposed copy made per call, for less memory.
     check_targets=True raises ValueError for a target outside [0, V) that
     is not ignore_index (one stream synchronisation per call); otherwise
-    such tokens are ignored."""
-    loss, lse = LinearCrossEntropyFunction.apply(X, W, targets, ignore_index, reduction,
-                                                 chunk_tokens, dw_chunks, weight_copy,
-                                                 check_targets)
+    such tokens are ignored.  When no gradient is wanted (grad mode off, or
+    neither X nor W requires one) only the forward runs, on a handle made
+    for it (FLCE_FLAG_FORWARD_ONLY)."""
+    if not (torch.is_grad_enabled() and (X.requires_grad or W.requires_grad)):
+        loss, lse = _forward_only(X, W, targets, ignore_index, reduction, chunk_tokens,
+                                  check_targets)
+    else:
+        loss, lse = LinearCrossEntropyFunction.apply(X, W, targets, ignore_index, reduction,
+                                                     chunk_tokens, dw_chunks, weight_copy,
+                                                     check_targets)
     return (loss, lse) if return_lse else loss
 
 

@@ -142,3 +142,41 @@ def test_check_targets_raises_on_out_of_range_ids():
     ok = linear_cross_entropy(X, W, y, WL.ignore_index, WL.reduction, check_targets=True)
     torch.cuda.synchronize()
     assert np.isfinite(float(ok.detach()))
+
+
+def test_no_grad_runs_the_forward_only_call():
+    """Without a gradient to compute (grad mode off, or no input requiring
+    one) the wrapper runs the forward-only call on a forward-only handle:
+    the same loss and lse as with gradients, against the oracle, under
+    autocast too, and the out-of-range target check."""
+    import torch
+    from linear_cross_entropy_02_amd import autograd as ag
+    inp = workloads.generate(WL)
+    X, W, y = leaves(inp, torch.bfloat16)
+    ref = flce_reference(inp.X, inp.W, inp.y, WL.ignore_index, WL.reduction, want_grads=False)
+    loss_g, lse_g = ag.linear_cross_entropy(X, W, y, WL.ignore_index, WL.reduction,
+                                            return_lse=True)
+    ag.clear_handle_cache()
+    with torch.no_grad():
+        loss, lse = ag.linear_cross_entropy(X, W, y, WL.ignore_index, WL.reduction,
+                                            return_lse=True)
+    torch.cuda.synchronize()
+    kinds = [k[-1] for k in ag._handles]
+    assert kinds == [True], kinds                      # one handle, forward-only
+    assert not loss.requires_grad
+    assert abs(float(loss) - ref["loss"]) <= LOSS_RTOL * abs(ref["loss"])
+    assert np.abs(to_np(lse) - ref["lse"]).max() <= LSE_ATOL
+    assert torch.equal(lse, lse_g.detach())             # per-row results do not depend on the chunking
+    assert abs(float(loss) - float(loss_g.detach())) <= 1e-6 * abs(float(loss_g.detach()))
+    # inputs that require no gradient take the same path with grad mode on
+    loss2 = ag.linear_cross_entropy(X.detach(), W.detach(), y, WL.ignore_index, WL.reduction)
+    assert torch.equal(loss2, loss)
+    # fp32 inputs under autocast run the bf16 forward
+    with torch.no_grad(), torch.autocast("cuda", dtype=torch.bfloat16):
+        loss3 = ag.linear_cross_entropy(X.float(), W.float(), y, WL.ignore_index, WL.reduction)
+    assert torch.equal(loss3, loss)
+    y_bad = y.clone()
+    y_bad[3] = WL.V
+    with torch.no_grad(), pytest.raises(ValueError, match="1 target"):
+        ag.linear_cross_entropy(X, W, y_bad, WL.ignore_index, WL.reduction, check_targets=True)
+    ag.clear_handle_cache()
