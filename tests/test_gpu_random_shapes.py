@@ -1,8 +1,9 @@
 """GPU parity on seeded random launch settings and shapes.
 
 Each case draws T, H, V, the chunk size, the chunks per dW GEMM, the dtype,
-the reduction, the share of ignored tokens and (bf16) whether dX reads a
-transposed copy of W or W as stored, from its own seed, so the
+the reduction, the share of ignored tokens, (bf16) whether dX reads a
+transposed copy of W or W as stored, and whether dZ is written in place
+(FLCE_FLAG_DZ_IN_PLACE), from its own seed, so the
 combinations the hand-picked cases do not name (a batch shorter than one
 chunk, a hidden size that is a multiple of 8 but not of 64, a vocabulary
 below one tile, groups cut short by the batch) are compared with the
@@ -37,19 +38,20 @@ def draw(seed):
         ignore_frac=float(rng.choice([0.0, 0.05, 0.3])))
     # from a stream of its own, so the draws above stay what they were
     wcopy = dtype == "f32" or bool(np.random.default_rng(seed + 7919).random() < 0.5)
-    return wl, chunk, g, wcopy
+    in_place = bool(np.random.default_rng(seed + 15485863).random() < 0.3)
+    return wl, chunk, g, wcopy, in_place
 
 
-@pytest.mark.parametrize("seed", list(range(32)))
+@pytest.mark.parametrize("seed", list(range(96)))
 def test_random_shape_vs_oracle(seed):
     import torch
-    wl, chunk, g, wcopy = draw(seed)
+    wl, chunk, g, wcopy, in_place = draw(seed)
     inp = workloads.generate(wl)
     X, W, y = workloads.to_torch(inp, "cuda")
     op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=chunk, dw_chunks=g,
-                                      weight_copy=wcopy)
-    print(f"[gpu-random] {wl.name} {wl.reduction} ignore {wl.ignore_frac} weight_copy {wcopy}",
-          flush=True)
+                                      weight_copy=wcopy, dz_in_place=in_place)
+    print(f"[gpu-random] {wl.name} {wl.reduction} ignore {wl.ignore_frac} weight_copy {wcopy} "
+          f"dz_in_place {in_place}", flush=True)
     out = op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction)
     torch.cuda.synchronize()
     op.close()
