@@ -11,7 +11,7 @@ from oracle import distill_reference, flce_reference
 pytestmark = pytest.mark.gpu
 
 
-def run(wl, Ht, tau, chunk, teacher_seed, same_teacher=False, weight_copy=True):
+def run(wl, Ht, tau, chunk, teacher_seed, same_teacher=False, weight_copy=True, dw_chunks=0):
     import torch
     inp = workloads.generate(wl)
     if same_teacher:
@@ -25,9 +25,9 @@ def run(wl, Ht, tau, chunk, teacher_seed, same_teacher=False, weight_copy=True):
         X, W, y = workloads.to_torch(inp, "cuda")
         Xq, Wq, _ = workloads.to_torch(tinp, "cuda")
     op = flce.FusedDistillationCrossEntropy(wl.H, wl.V, Ht, wl.dtype, chunk_tokens=chunk,
-                                            weight_copy=weight_copy)
+                                            dw_chunks=dw_chunks, weight_copy=weight_copy)
     print(f"[gpu-distill] {wl.name} T={wl.T} H={wl.H} Ht={Ht} V={wl.V} tau={tau} "
-          f"chunk={op.chunk_tokens}", flush=True)
+          f"chunk={op.chunk_tokens} G={op.dw_chunks} wcopy={weight_copy}", flush=True)
     out = op.distill(X, W, Xq, Wq, y, tau, wl.ignore_index, wl.reduction)
     torch.cuda.synchronize()
     res = {k: to_np(v) for k, v in out.items()}
@@ -43,17 +43,22 @@ CASES = [
     (workloads.WORKLOADS[1], 32, 0.7, 0),
     (workloads.WORKLOADS[1].with_shape(T=200, V=777, seed=74), 48, 3.0, 64),
 ]
-CASES = [c + (True,) for c in CASES] + [
+CASES = [c + (True, 0) for c in CASES] + [
     # the student's dX reading W as stored
-    (workloads.WORKLOADS[4].with_shape(T=600, H=512, V=20000, seed=76), 512, 1.0, 256, False),
+    (workloads.WORKLOADS[4].with_shape(T=600, H=512, V=20000, seed=76), 512, 1.0, 256, False, 0),
+    # dW over groups of chunks (5 chunks: groups of 2, 2 and 1), reading the
+    # groups' dZ as stored (bf16) or through dZ^T (fp32)
+    (workloads.WORKLOADS[4].with_shape(T=1100, H=512, V=20000, seed=77), 256, 1.2, 256, False, 2),
+    (workloads.WORKLOADS[1].with_shape(T=300, V=777, seed=78), 48, 2.0, 64, True, 3),
 ]
 
 
-@pytest.mark.parametrize("wl,Ht,tau,chunk,wcopy", CASES,
-                         ids=[f"{c[0].name}-Ht{c[1]}-tau{c[2]}" + ("" if c[4] else "-no-wcopy")
-                              for c in CASES])
-def test_distill_vs_oracle(wl, Ht, tau, chunk, wcopy):
-    inp, res, ref = run(wl, Ht, tau, chunk, teacher_seed=wl.seed + 500, weight_copy=wcopy)
+@pytest.mark.parametrize("wl,Ht,tau,chunk,wcopy,g", CASES,
+                         ids=[f"{c[0].name}-Ht{c[1]}-tau{c[2]}" + ("" if c[4] else "-no-wcopy") +
+                              (f"-G{c[5]}" if c[5] else "") for c in CASES])
+def test_distill_vs_oracle(wl, Ht, tau, chunk, wcopy, g):
+    inp, res, ref = run(wl, Ht, tau, chunk, teacher_seed=wl.seed + 500, weight_copy=wcopy,
+                        dw_chunks=g)
     assert abs(float(res["loss"]) - ref["loss"]) <= LOSS_RTOL * abs(ref["loss"]), \
         (float(res["loss"]), ref["loss"])
     assert int(res["n_valid"]) == ref["n_valid"]
