@@ -18,7 +18,7 @@ from oracle import count_valid, flce_reference, scale_factor
 pytestmark = pytest.mark.gpu
 
 
-def run_sharded(wl, cuts, chunk=256, weight_copy=True):
+def run_sharded(wl, cuts, chunk=256, weight_copy=True, dw_chunks=0, dz_in_place=False):
     import torch
     inp = workloads.generate(wl)
     X, W, y = workloads.to_torch(inp, "cuda")
@@ -27,7 +27,8 @@ def run_sharded(wl, cuts, chunk=256, weight_copy=True):
     shards = []
     for v0, v1 in zip(bounds[:-1], bounds[1:]):
         op = flce.FusedLinearCrossEntropy(wl.H, v1 - v0, wl.dtype, chunk_tokens=chunk,
-                                          weight_copy=weight_copy)
+                                          dw_chunks=dw_chunks, weight_copy=weight_copy,
+                                          dz_in_place=dz_in_place)
         Ws = W[v0:v1].contiguous()
         part = op.shard_forward(X, Ws, y, v0, wl.V, wl.ignore_index)
         shards.append((op, v0, Ws, {k: to_np(v) for k, v in part.items()}))
@@ -63,17 +64,23 @@ CASES = [
     (workloads.WORKLOADS[2].with_shape(T=1000, H=96, V=1000, seed=63), (100, 300, 999)),
     (workloads.WORKLOADS[1].with_shape(T=200, V=777, seed=64), (300,)),
 ]
-CASES = [c + (True,) for c in CASES] + [
+CASES = [c + (True, 0, False) for c in CASES] + [
     # shards whose dX reads W_shard as stored
-    (workloads.WORKLOADS[4].with_shape(T=600, H=512, V=20000, seed=65), (7000, 13001), False),
+    (workloads.WORKLOADS[4].with_shape(T=600, H=512, V=20000, seed=65), (7000, 13001), False, 0,
+     False),
+    # each shard's dW over groups of chunks (5 chunks: groups of 2, 2, 1), with
+    # dZ formed in the contractions and written in place
+    (workloads.WORKLOADS[4].with_shape(T=1100, H=256, V=9000, seed=66), (4000,), False, 2, False),
+    (workloads.WORKLOADS[4].with_shape(T=1100, H=256, V=9000, seed=67), (4000,), True, 2, True),
 ]
 
 
-@pytest.mark.parametrize("wl,cuts,wcopy", CASES,
-                         ids=[f"{c[0].name}-{len(c[1]) + 1}shards" + ("" if c[2] else "-no-wcopy")
+@pytest.mark.parametrize("wl,cuts,wcopy,g,in_place", CASES,
+                         ids=[f"{c[0].name}-{len(c[1]) + 1}shards" + ("" if c[2] else "-no-wcopy") +
+                              (f"-G{c[3]}" if c[3] else "") + ("-in-place" if c[4] else "")
                               for c in CASES])
-def test_vocab_parallel_vs_oracle(wl, cuts, wcopy):
-    inp, got = run_sharded(wl, cuts, weight_copy=wcopy)
+def test_vocab_parallel_vs_oracle(wl, cuts, wcopy, g, in_place):
+    inp, got = run_sharded(wl, cuts, weight_copy=wcopy, dw_chunks=g, dz_in_place=in_place)
     ref = flce_reference(inp.X, inp.W, inp.y, wl.ignore_index, wl.reduction)
     assert abs(got["loss"] - ref["loss"]) <= LOSS_RTOL * abs(ref["loss"])
     assert np.abs(got["lse"] - ref["lse"]).max() <= LSE_ATOL
