@@ -19,18 +19,30 @@ def same(a, b):
     return all(torch.equal(a[k], b[k]) for k in ("loss", "dX", "dW", "lse", "argmax", "n_valid"))
 
 
-@pytest.mark.parametrize("dtype_wl", [workloads.WORKLOADS[2].with_shape(T=700, H=256, V=3000, seed=81),
-                                      workloads.WORKLOADS[1].with_shape(T=200, V=777, seed=82)],
-                         ids=["bf16", "fp32"])
-def test_graph_replays_match_eager(dtype_wl):
+GRAPH_CASES = [
+    (workloads.WORKLOADS[2].with_shape(T=700, H=256, V=3000, seed=81), {}),
+    (workloads.WORKLOADS[1].with_shape(T=200, V=777, seed=82), {}),
+    # as the Llama-3 head is benchmarked: W read as stored, dW over groups of chunks
+    (workloads.WORKLOADS[4].with_shape(T=1100, H=256, V=5000, seed=83),
+     dict(weight_copy=False, dw_chunks=2)),
+    # dZ written in place, read as stored by dW
+    (workloads.WORKLOADS[4].with_shape(T=1100, H=256, V=5000, seed=84),
+     dict(dw_chunks=2, dz_in_place=True)),
+]
+
+
+@pytest.mark.parametrize("dtype_wl,kw", GRAPH_CASES, ids=["bf16", "fp32", "bf16-no-wcopy-G2",
+                                                         "bf16-in-place-G2"])
+def test_graph_replays_match_eager(dtype_wl, kw):
     import torch
     wl = dtype_wl
     inp = workloads.generate(wl)
     X, W, y = workloads.to_torch(inp, "cuda")
     inp2 = workloads.generate(wl.with_shape(seed=wl.seed + 1))
     X2, W2, y2 = workloads.to_torch(inp2, "cuda")
-    op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=256 if wl.T > 256 else 64)
-    print(f"[gpu-graph] {wl.name} T={wl.T} H={wl.H} V={wl.V} {wl.dtype}", flush=True)
+    op = flce.FusedLinearCrossEntropy(wl.H, wl.V, wl.dtype, chunk_tokens=256 if wl.T > 256 else 64,
+                                      **kw)
+    print(f"[gpu-graph] {wl.name} T={wl.T} H={wl.H} V={wl.V} {wl.dtype} {kw}", flush=True)
     eager1 = op.fwd_bwd(X, W, y, wl.ignore_index, wl.reduction)
     eager2 = op.fwd_bwd(X2, W2, y2, wl.ignore_index, wl.reduction)
 
