@@ -82,6 +82,10 @@ struct flce_handle {
   // against beta-scaled X^T when dZ is formed inside the contractions, else
   // the dZ the dZ pass wrote in place; no dZ^T either way
   bool dw_reads_p = false;
+  // ... and then (hard targets, G > 1) the logits GEMM runs once per group of
+  // chunks, its partials kept for the G chunks (one partial round of tiles
+  // per group instead of one per chunk)
+  bool group_logits = false;
   size_t ws_bytes = 0;
   char* ws = nullptr;
   void* Wt = nullptr;      // W^T           [H x Vpad]
@@ -298,6 +302,7 @@ flce_status_t configure(const flce_config_t* cfg, int64_t Ht, flce_handle* h, La
   // the dW GEMM's one buffer descriptor spans the G chunks of P
   h->dw_reads_p = !fwd_only && dt == Dt::BF16 && H <= FLCE_DW_READS_P_MAX_H &&
                   G * C * h->Vpad * 2 < ((int64_t)1 << 31);
+  h->group_logits = h->dw_reads_p && G > 1 && Ht == 0;
   h->nt = cdiv64(V, kPartialWidth);
   h->splitk_alloc = 1;
   if (!fwd_only) {
@@ -320,10 +325,11 @@ flce_status_t configure(const flce_config_t* cfg, int64_t Ht, flce_handle* h, La
   L->P = bwd ? carve((size_t)(h->dw_reads_p ? h->G * C : C) * h->Vpad * es) : 0;
   L->Pt = bwd && !h->dw_reads_p ? carve((size_t)h->Vpad * h->G * C * es) : 0;
   L->Xt = bwd ? carve((size_t)H * h->G * C * es) : 0;
-  L->pm = carve((size_t)C * h->nt * 4);
-  L->ps = carve((size_t)C * h->nt * 4);
-  L->pa = carve((size_t)C * h->nt * 4);
-  L->zt = carve((size_t)C * 4);
+  const int64_t Cp = h->group_logits ? h->G * C : C;  // rows of the logits partials
+  L->pm = carve((size_t)Cp * h->nt * 4);
+  L->ps = carve((size_t)Cp * h->nt * 4);
+  L->pa = carve((size_t)Cp * h->nt * 4);
+  L->zt = carve((size_t)Cp * 4);
   L->dz = carve((size_t)C * 4);
   L->be = bwd ? carve((size_t)(h->dw_reads_p ? h->G * C : C) * 4) : 0;
   L->co = bwd ? carve((size_t)C * 4) : 0;
@@ -557,6 +563,14 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
     const bool dw_p = h->dw_reads_p;
     char* const Pc = (char*)h->P + (dw_p ? (size_t)gs * C * Vpad * es : 0);
     float* const beta_c = h->beta + (dw_p ? gs * C : 0);
+    // logits partials of this chunk: its rows among the group's when the
+    // logits GEMM covers a whole group (launched at the group's first chunk)
+    const bool grp = !soft && h->group_logits;
+    const int64_t ldr = grp ? GC : C;
+    float* const pm_c = h->pm + (grp ? gs * C : 0);
+    float* const ps_c = h->ps + (grp ? gs * C : 0);
+    int* const pa_c = h->pa + (grp ? gs * C : 0);
+    float* const zt_c = h->ztgt + (grp ? gs * C : 0);
 
     // X^T of the whole group at its first chunk (X is an input, all of it
     // available): one transpose per dW GEMM; the previous group's dW GEMM,
@@ -613,39 +627,44 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
       FLCE_LAUNCH(K_FINALIZE, launch_finalize(qf, s));
     }
 
-    LogitsArgs la{};
-    la.X = Xc;
-    la.W = W;
-    la.M = (int)Cc;
-    la.V = (int)V;
-    la.H = (int)H;
-    la.P = Pc;
-    la.ldp = Vpad;
-    la.pm = h->pm;
-    la.ps = h->ps;
-    la.pa = h->pa;
-    la.ldr = C;
-    la.ztgt = h->ztgt;
-    la.y = yc;
-    la.ignore_index = ignore_index;
-    la.y_shift = cols.y_shift;
-    if (soft) {
-      la.inv_temp = soft->inv_temp;
-      la.Pq = h->Pq;
-      la.pc = h->pc;
+    if (!grp || gs == 0) {
+      // this chunk's logits, or those of its whole group (every chunk of a
+      // group but the batch's last is full: the group's rows are contiguous)
+      const int64_t Mr = grp ? ((T - t0 < GC) ? (T - t0) : GC) : Cc;
+      LogitsArgs la{};
+      la.X = Xc;
+      la.W = W;
+      la.M = (int)Mr;
+      la.V = (int)V;
+      la.H = (int)H;
+      la.P = Pc;
+      la.ldp = Vpad;
+      la.pm = pm_c;
+      la.ps = ps_c;
+      la.pa = pa_c;
+      la.ldr = ldr;
+      la.ztgt = zt_c;
+      la.y = yc;
+      la.ignore_index = ignore_index;
+      la.y_shift = cols.y_shift;
+      if (soft) {
+        la.inv_temp = soft->inv_temp;
+        la.Pq = h->Pq;
+        la.pc = h->pc;
+      }
+      FLCE_LAUNCH(K_LOGITS, launch_logits(dt, la, s));
     }
-    FLCE_LAUNCH(K_LOGITS, launch_logits(dt, la, s));
 
     FinalizeArgs fa{};
     fa.block_rows = finalize_rows(nt, C);
     fa.M = (int)Cc;
     fa.nt = (int)nt;
     fa.V = (int)V;
-    fa.pm = h->pm;
-    fa.ps = h->ps;
-    fa.pa = h->pa;
-    fa.ldr = C;
-    fa.ztgt = h->ztgt;
+    fa.pm = pm_c;
+    fa.ps = ps_c;
+    fa.pa = pa_c;
+    fa.ldr = ldr;
+    fa.ztgt = zt_c;
     fa.dzt = h->dzt;
     fa.y = yc;
     fa.ignore_index = ignore_index;
@@ -705,8 +724,8 @@ flce_status_t run_fwd_bwd(flce_handle_t h, const void* X, const void* W, const i
     xa.V = (int)V;
     xa.Vpad = (int)Vpad;
     xa.nt = (int)nt;
-    xa.ldr = C;
-    xa.alpha = h->pm;
+    xa.ldr = ldr;
+    xa.alpha = pm_c;
     xa.dzt = h->dzt;
     xa.y = yc;
     xa.ignore_index = ignore_index;

@@ -11,7 +11,7 @@ written once per G chunks, and the W^T copy makes the dX contraction read
     128256: 39.4 ms; G = 1: 42.2), with W read as stored wherever the
     library takes it (bf16, V H 2 < 2^31 bytes): at 16384 x 4096 x 128256
     that costs 1-2 % of a step (41.0 against 40.6 ms on one box, 39.5
-    against 38.8 on another) and takes the workspace from 0.79 to 0.54 of a
+    against 38.8 on another) and takes the workspace from 0.79 to 0.56 of a
     bf16 T x V buffer (G = 2 with the copy: +4 % at 0.53; C = 4096, G = 1:
     +3.6 % at 0.52).
   * H < 2048: for batches of 32768 tokens or more, G = 1 and the largest

@@ -98,7 +98,7 @@ LAUNCH_MODES = {"forward": (8192, 1), "shard": (4096, 1), "distill": (2048, 4)}
 # layer, where dropping it leaves room for 2048-token chunks under that bound
 # (0.37 ms per step, against 0.42 with the copy and 1024-token chunks); and
 # the 16384 x 4096 x 128256 head, where it takes the workspace from 0.79 to
-# 0.54 of a bf16 T x V buffer for 1-2 % of the step time.
+# 0.56 of a bf16 T x V buffer for 1-2 % of the step time.
 NO_WEIGHT_COPY = {2, 4, 5}
 # The other entry points at the Llama-3-8B head's shape read W as stored as
 # well: the forward-only call never runs the dX contraction (the copy would
